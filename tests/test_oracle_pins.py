@@ -1,0 +1,403 @@
+"""Pins of the float64 oracle against things other than itself.
+
+Each test ties one oracle function to a closed form derived by hand
+(``tests/golden``), a library routine (scipy / torch on the CPU), brute force
+over all candidates, an invariant of the mathematics, or central finite
+differences.  The set is chosen so that a dropped term, a wrong sign or
+index, or a transposed operand in any oracle function fails at least one.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from workloads import bf16_bits, get, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- bf16 decode
+
+def test_decode_bf16_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F, 0x0001], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0, (2.0 - 2.0 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    got = oracle.decode_bf16(bits)
+    assert got.tolist() == want
+    assert np.signbit(got[4])
+
+
+def test_decode_bf16_rejects_other_dtypes():
+    with pytest.raises(TypeError):
+        oracle.decode_bf16(np.zeros(3, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- router
+
+@pytest.mark.parametrize("case", _load("route_closed_form.json")["cases"], ids=lambda c: c["name"])
+def test_route_golden(case):
+    l = np.log(np.array(case["logits_as_ln"], dtype=np.float64))[None, :]
+    idx, w, _ = oracle.route(l, case["k"])
+    assert idx[0].tolist() == case["idx"]
+    np.testing.assert_allclose(w[0], np.array(case["w_num"]) / case["w_den"], rtol=1e-14, atol=0)
+
+
+def test_route_k_equals_E_is_softmax():
+    rng = np.random.default_rng(1)
+    l = rng.standard_normal((16, 9))
+    idx, w, p = oracle.route(l, 9)
+    sm = scipy.special.softmax(l, axis=1)
+    np.testing.assert_allclose(p, sm, rtol=1e-13)
+    order = np.argsort(-l, axis=1, kind="stable")
+    assert (idx == order).all()
+    np.testing.assert_allclose(w, np.take_along_axis(sm, order, axis=1), rtol=1e-13)
+
+
+def test_route_k1_is_argmax_with_unit_weight():
+    rng = np.random.default_rng(2)
+    l = rng.standard_normal((32, 7))
+    l[3, 5] = l[3, 2] = l[3].max() + 1.0   # exact tie: lower id wins
+    idx, w, _ = oracle.route(l, 1)
+    assert (idx[:, 0] == np.argmax(l, axis=1)).all()
+    assert idx[3, 0] == 2
+    assert (w == 1.0).all()
+
+
+def test_route_brute_force_over_subsets():
+    """Top-k set = the k-subset with the largest total probability."""
+    rng = np.random.default_rng(3)
+    E, k = 7, 3
+    l = rng.standard_normal((20, E))
+    idx, w, p = oracle.route(l, k)
+    sm = scipy.special.softmax(l, axis=1)
+    for t in range(l.shape[0]):
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(sm[t, list(s)]))
+        assert sorted(idx[t].tolist()) == sorted(best)
+        # rank order: descending probability
+        assert all(sm[t, idx[t, j]] > sm[t, idx[t, j + 1]] for j in range(k - 1))
+        np.testing.assert_allclose(w[t], sm[t, idx[t]] / sm[t, idx[t]].sum(), rtol=1e-13)
+
+
+def test_route_shift_invariance_and_weight_sum():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((50, 12)) * 3
+    idx, w, _ = oracle.route(l, 4)
+    idx2, w2, _ = oracle.route(l + 123.25, 4)
+    assert (idx == idx2).all()
+    np.testing.assert_allclose(w, w2, rtol=1e-12)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert (np.diff(w, axis=1) <= 0).all()
+
+
+def test_router_logits_matches_torch_and_bias():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((9, 17))
+    Wg = rng.standard_normal((17, 5))
+    b = rng.standard_normal(5)
+    ref = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(Wg.T.copy()), torch.from_numpy(b))
+    np.testing.assert_allclose(oracle.router_logits(x, Wg, b), ref.numpy(), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.router_logits(x, Wg), x @ Wg, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("case", _load("dispatch_closed_form.json")["cases"], ids=lambda c: c["name"])
+def test_dispatch_golden(case):
+    m = oracle.dispatch(np.array(case["idx"], dtype=np.int32), case["e_begin"], case["E_local"], case["G"])
+    for key in ("counts", "offsets", "sorted_token", "sorted_slot", "pair_pos", "token_ready_wave", "wave_rows"):
+        assert m[key].tolist() == case[key], key
+
+
+def _random_idx(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,e_begin,E_local,G", [
+    (1, 4, 2, 0, 4, 2), (37, 8, 3, 0, 8, 4), (64, 16, 4, 4, 8, 2), (200, 32, 8, 0, 32, 4), (5, 3, 3, 1, 2, 1)])
+def test_dispatch_brute_force_and_invariants(T, E, k, e_begin, E_local, G):
+    rng = np.random.default_rng(T * 7 + E)
+    idx = _random_idx(rng, T, E, k)
+    m = oracle.dispatch(idx, e_begin, E_local, G)
+    # brute force: all local pairs sorted by (expert, token)
+    pairs = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k)
+                   if e_begin <= idx[t, j] < e_begin + E_local)
+    assert m["sorted_token"].tolist() == [t for _, t, _ in pairs]
+    assert m["sorted_slot"].tolist() == [j for _, _, j in pairs]
+    P = len(pairs)
+    assert m["counts"].sum() == P and m["offsets"][-1] == P
+    assert (m["offsets"][1:] - m["offsets"][:-1] == m["counts"]).all()
+    # bijection between local pairs and rows
+    pos = m["pair_pos"]
+    rows = sorted(int(r) for r in pos.ravel() if r >= 0)
+    assert rows == list(range(P))
+    for t in range(T):
+        for j in range(k):
+            local = e_begin <= idx[t, j] < e_begin + E_local
+            assert (pos[t, j] >= 0) == local
+            if local:
+                r = pos[t, j]
+                assert m["sorted_token"][r] == t and m["sorted_slot"][r] == j
+                le = idx[t, j] - e_begin
+                assert m["offsets"][le] <= r < m["offsets"][le + 1]
+    # stable: ascending token inside each segment
+    for le in range(E_local):
+        seg = m["sorted_token"][m["offsets"][le]:m["offsets"][le + 1]]
+        assert (np.diff(seg) > 0).all()
+    # ready wave = last wave holding one of the token's local experts
+    for t in range(T):
+        ws = [(int(e) - e_begin) // G for e in idx[t] if e_begin <= e < e_begin + E_local]
+        assert m["token_ready_wave"][t] == (max(ws) if ws else -1)
+    assert m["wave_rows"].tolist() == [int(m["offsets"][w * G]) for w in range(E_local // G)] + [P]
+
+
+def test_dispatch_all_tokens_identical():
+    idx = np.tile(np.array([[5, 1, 3]], dtype=np.int32), (11, 1))
+    m = oracle.dispatch(idx, 0, 8, 2)
+    want = np.zeros(8, dtype=np.int64)
+    want[[1, 3, 5]] = 11
+    assert (m["counts"] == want).all()
+    assert m["sorted_token"].tolist() == list(range(11)) * 3
+
+
+def test_dispatch_rejects_bad_waves():
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.zeros((2, 1), np.int32), 0, 6, 4)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+@pytest.mark.parametrize("case", _load("ffn_closed_form.json")["cases"], ids=lambda c: c["name"])
+def test_expert_ffn_golden(case):
+    X = np.array([[case["x"]]])
+    y, h1, h3, a = oracle.expert_ffn(X, np.array([[np.log(case["W1_as_ln"])]]),
+                                     np.array([[case["W3"]]]), np.array([[case["W2"]]]))
+    np.testing.assert_allclose(y[0, 0], case["y_times_1_over_ln3"] * np.log(3.0), rtol=1e-15, atol=1e-300)
+
+
+def _torch_swiglu(X, W1, W3, W2):
+    X, W1, W3, W2 = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (X, W1, W3, W2))
+    return ((torch.nn.functional.silu(X @ W1) * (X @ W3)) @ W2).numpy()
+
+
+def test_expert_ffn_matches_torch_swiglu():
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((13, 24))
+    W1, W3 = rng.standard_normal((2, 24, 10)) * 0.3
+    W2 = rng.standard_normal((10, 24)) * 0.3
+    y, h1, h3, a = oracle.expert_ffn(X, W1, W3, W2)
+    np.testing.assert_allclose(y, _torch_swiglu(X, W1, W3, W2), rtol=1e-12, atol=1e-13)
+    # the gate is W1 (through silu), the up projection W3 (linear): swapping them changes y
+    assert not np.allclose(y, _torch_swiglu(X, W3, W1, W2))
+
+
+# ---------------------------------------------------------------- forward / combine
+
+def _tiny_layer(seed, T=12, d=16, I=8, E=6, k=2, e_begin=0, E_local=None, bias=False):
+    rng = np.random.default_rng(seed)
+    E_local = E if E_local is None else E_local
+    x = rng.standard_normal((T, d))
+    Wg = rng.standard_normal((d, E)) * 0.5
+    b = rng.standard_normal(E) if bias else None
+    W1 = rng.standard_normal((E_local, d, I)) * 0.3
+    W3 = rng.standard_normal((E_local, d, I)) * 0.3
+    W2 = rng.standard_normal((E_local, I, d)) * 0.3
+    return x, Wg, b, W1, W3, W2
+
+
+@pytest.mark.parametrize("e_begin,E_local,G,bias", [(0, 6, 2, False), (2, 2, 1, True), (0, 6, 6, True)])
+def test_forward_vs_dense_brute_force(e_begin, E_local, G, bias):
+    """Every expert evaluated densely per token with torch; no permutation."""
+    k, E = 2, 6
+    x, Wg, b, W1, W3, W2 = _tiny_layer(7 + e_begin, e_begin=e_begin, E_local=E_local, bias=bias)
+    res = oracle.forward(x, Wg, b, W1, W3, W2, k, e_begin, E_local, G)
+    xt = torch.from_numpy(x)
+    logits = xt @ torch.from_numpy(Wg) + (torch.from_numpy(b) if b is not None else 0)
+    p = torch.softmax(logits, dim=1)
+    top_p, top_i = torch.topk(p, k, dim=1, sorted=True)
+    assert (res["idx"] == top_i.numpy()).all()
+    wts = (top_p / top_p.sum(dim=1, keepdim=True)).numpy()
+    np.testing.assert_allclose(res["w"], wts, rtol=1e-13)
+    ref = np.zeros_like(x)
+    dense = [_torch_swiglu(x, W1[le], W3[le], W2[le]) for le in range(E_local)]
+    for t in range(x.shape[0]):
+        for j in range(k):
+            le = int(top_i[t, j]) - e_begin
+            if 0 <= le < E_local:
+                ref[t] += wts[t, j] * dense[le][t]
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-12, atol=1e-13)
+    # y rows are the per-pair expert outputs in sorted order
+    m = res["meta"]
+    for r in range(int(m["offsets"][-1])):
+        le = int(np.searchsorted(m["offsets"], r, side="right") - 1)
+        np.testing.assert_allclose(res["y"][r], dense[le][m["sorted_token"][r]], rtol=1e-12, atol=1e-13)
+
+
+def test_forward_identical_experts_is_dense_ffn():
+    """With one FFN shared by all experts, sum(w) = 1 makes routing irrelevant."""
+    x, Wg, _, W1, W3, W2 = _tiny_layer(8, E=5, k=3)
+    W1[:] = W1[0]
+    W3[:] = W3[0]
+    W2[:] = W2[0]
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 3, 0, 5, 5)
+    np.testing.assert_allclose(res["out"], _torch_swiglu(x, W1[0], W3[0], W2[0]), rtol=1e-12, atol=1e-13)
+
+
+def test_forward_single_expert_is_dense_swiglu():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(9, E=1, k=1)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 1, 0, 1, 1)
+    np.testing.assert_allclose(res["out"], _torch_swiglu(x, W1[0], W3[0], W2[0]), rtol=1e-12, atol=1e-13)
+
+
+def test_forward_linear_in_W2_and_zero():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(10)
+    base = oracle.forward(x, Wg, None, W1, W3, W2, 2, 0, 6, 3)["out"]
+    scaled = oracle.forward(x, Wg, None, W1, W3, -2.5 * W2, 2, 0, 6, 3)["out"]
+    np.testing.assert_allclose(scaled, -2.5 * base, rtol=1e-12, atol=1e-14)
+    zero = oracle.forward(x, Wg, None, W1, W3, 0 * W2, 2, 0, 6, 3)["out"]
+    assert (zero == 0).all()
+
+
+def test_forward_nonlocal_tokens_are_zero():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(11, T=40, E=8, k=1, e_begin=6, E_local=2)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 1, 6, 2, 1)
+    nonlocal_ = res["idx"][:, 0] < 6
+    assert nonlocal_.any() and (~nonlocal_).any()
+    assert (res["out"][nonlocal_] == 0).all()
+    assert (np.abs(res["out"][~nonlocal_]).sum(axis=1) > 0).all()
+
+
+def test_forward_tokens_matches_forward():
+    x, Wg, b, W1, W3, W2 = _tiny_layer(12, T=20, bias=True)
+    res = oracle.forward(x, Wg, b, W1, W3, W2, 2, 0, 6, 2)
+    sel = np.array([0, 7, 19, 3])
+    part = oracle.forward_tokens(x[sel], res["idx"][sel], res["w"][sel], W1, W3, W2, 0, 6)
+    np.testing.assert_allclose(part, res["out"][sel], rtol=1e-13, atol=1e-14)
+
+
+def test_combine_order_and_weights():
+    y = np.array([[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]])
+    pos = np.array([[2, 0], [-1, 1]])
+    w = np.array([[0.25, 0.75], [0.5, 0.5]])
+    out = oracle.combine(y, pos, w, 2)
+    assert out.tolist() == [[25.75, 51.5], [5.0, 10.0]]
+
+
+# ---------------------------------------------------------------- wgrad
+
+def _loss_and_grads_torch(x, Wg, W1, W3, W2, k, dout):
+    """torch autograd through the dense formulation, routing held fixed."""
+    xt = torch.from_numpy(x)
+    logits = xt @ torch.from_numpy(Wg)
+    p = torch.softmax(logits, dim=1)
+    top_p, top_i = torch.topk(p, k, dim=1, sorted=True)
+    wts = top_p / top_p.sum(dim=1, keepdim=True)
+    w1 = torch.from_numpy(W1).requires_grad_()
+    w3 = torch.from_numpy(W3).requires_grad_()
+    w2 = torch.from_numpy(W2).requires_grad_()
+    out = torch.zeros_like(xt)
+    for t in range(x.shape[0]):
+        for j in range(k):
+            e = int(top_i[t, j])
+            h = torch.nn.functional.silu(xt[t] @ w1[e]) * (xt[t] @ w3[e])
+            out[t] = out[t] + wts[t, j] * (h @ w2[e])
+    loss = (out * torch.from_numpy(dout)).sum()
+    loss.backward()
+    return w1.grad.numpy(), w3.grad.numpy(), w2.grad.numpy()
+
+
+def test_wgrad_matches_autograd():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(13, T=10, d=12, I=5, E=4, k=2)
+    dout = np.random.default_rng(14).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 2, 0, 4, 2)
+    dW1, dW3, dW2 = oracle.wgrad(x, W1, W3, W2, res["meta"], res["w"], dout)
+    g1, g3, g2 = _loss_and_grads_torch(x, Wg, W1, W3, W2, 2, dout)
+    for e in range(4):
+        np.testing.assert_allclose(dW1[e], g1[e], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dW3[e], g3[e], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dW2[e], g2[e], rtol=1e-11, atol=1e-12)
+
+
+def test_wgrad_central_finite_differences():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(15, T=8, d=6, I=4, E=3, k=2)
+    dout = np.random.default_rng(16).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 2, 0, 3, 1)
+    dW1, dW3, dW2 = oracle.wgrad(x, W1, W3, W2, res["meta"], res["w"], dout)
+
+    def loss(a1, a3, a2):
+        return float((oracle.forward(x, Wg, None, a1, a3, a2, 2, 0, 3, 1)["out"] * dout).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(17)
+    for _ in range(12):
+        e, i, j = rng.integers(3), rng.integers(6), rng.integers(4)
+        for which, grad in ((0, dW1), (1, dW3)):
+            A = [W1.copy(), W3.copy(), W2.copy()]
+            B = [W1.copy(), W3.copy(), W2.copy()]
+            A[which][e, i, j] += h
+            B[which][e, i, j] -= h
+            fd = (loss(*A) - loss(*B)) / (2 * h)
+            assert abs(fd - grad[e][i, j]) <= 1e-6 * max(1.0, abs(fd))
+        A = [W1, W3, W2.copy()]
+        B = [W1, W3, W2.copy()]
+        A[2][e, j, i] += h
+        B[2][e, j, i] -= h
+        fd = (loss(*A) - loss(*B)) / (2 * h)
+        assert abs(fd - dW2[e][j, i]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_wgrad_column_subset_and_dout_linearity():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(18, T=14, d=10, I=7, E=4, k=2)
+    dout = np.random.default_rng(19).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 2, 0, 4, 2)
+    full = oracle.wgrad(x, W1, W3, W2, res["meta"], res["w"], dout)
+    cols = np.array([6, 0, 3])
+    part = oracle.wgrad(x, W1, W3, W2, res["meta"], res["w"], dout, experts=[1, 3], cols=cols)
+    for e in (1, 3):
+        np.testing.assert_allclose(part[0][e], full[0][e][:, cols], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(part[1][e], full[1][e][:, cols], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(part[2][e], full[2][e][cols, :], rtol=1e-13, atol=1e-15)
+    twice = oracle.wgrad(x, W1, W3, W2, res["meta"], res["w"], 2 * dout)
+    for e in range(4):
+        np.testing.assert_allclose(twice[0][e], 2 * full[0][e], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_generator_bf16_rounding_is_rne():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -9, 1.0 + 2 ** -8 + 2 ** -20],
+                 dtype=np.float32)
+    bits = bf16_bits(v)
+    # 1+2^-8 ties between 1 and 1+2^-7 -> even (1.0); 1+3*2^-8 ties up to the
+    # even 1+2^-6; just above a tie rounds up
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xBF80, 0x3F81]
+    assert oracle.decode_bf16(bits).tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -1.0, 1.0 + 2 ** -7]
+
+
+def test_generator_tiny_shapes_and_determinism():
+    a = make_inputs("tiny")
+    b = make_inputs("tiny")
+    wl = get("tiny")
+    assert a["x"].shape == (64, 256) and a["x"].dtype == np.float32
+    assert a["W1"].shape == (8, 256, 128) and a["W2"].shape == (8, 128, 256)
+    assert a["Wg"].shape == (256, 8)
+    for key in ("x", "Wg", "W1", "W3", "W2"):
+        assert (a[key] == b[key]).all()
+    assert wl.waves == 2
+
+
+def test_tiny_workload_oracle_runs():
+    inp = make_inputs("tiny")
+    wl = inp["workload"]
+    res = oracle.forward(inp["x"], inp["Wg"], None, inp["W1"], inp["W3"], inp["W2"], wl.k, 0, wl.E_local, wl.G)
+    assert res["out"].shape == (64, 256)
+    assert res["meta"]["counts"].sum() == 64 * 2
+    assert np.isfinite(res["out"]).all()
