@@ -1,0 +1,144 @@
+// dispatch.hip -- deterministic counting sort of routed pairs by local
+// expert, and of tokens by the wave after which they can be combined.
+//
+// 10100.com commentary (section on batch-invariant and deterministic
+// operators): the deterministic kernels pre-sort instead of letting
+// unordered atomics decide positions.  Here no position is ever taken from
+// an atomic counter: every pair's row is a pure function of topk_idx.
+//
+//   1. count  : per 64-token chunk (one wavefront) build, in LDS, a bitmask
+//               per group (local expert, ready-wave slot) of the chunk's
+//               tokens in that group.  Bit OR is order-independent, so the
+//               masks are deterministic.
+//   2. scan   : per group, exclusive scan of popcounts over chunks in
+//               ascending chunk order; then exclusive scan of group totals.
+//   3. scatter: a token's row inside its group is the group start + the
+//               chunk's base + the number of lower lanes in the same mask,
+//               so rows within a group follow ascending token id.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunksPerBlock = 4;  // 4 wavefronts of 64 tokens
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int k, int e_begin, int E_local, int G,
+    int ngroups, unsigned long long* __restrict__ masks, int32_t* __restrict__ ready_wave) {
+  extern __shared__ unsigned long long smask[];  // [kChunksPerBlock][ngroups]
+  const int wave = wave_id(), lane = lane_id();
+  for (int i = threadIdx.x; i < kChunksPerBlock * ngroups; i += blockDim.x) smask[i] = 0ull;
+  __syncthreads();
+  const int chunk = blockIdx.x * kChunksPerBlock + wave;
+  const int t = chunk * kWave + lane;
+  unsigned long long* my = smask + wave * ngroups;
+  if (t < T) {
+    int ready = -1;
+    for (int j = 0; j < k; ++j) {
+      const int le = topk_idx[static_cast<size_t>(t) * k + j] - e_begin;
+      if (le >= 0 && le < E_local) {
+        atomicOr(&my[le], 1ull << lane);
+        ready = max(ready, le / G);
+      }
+    }
+    atomicOr(&my[E_local + 1 + ready], 1ull << lane);
+    ready_wave[t] = ready;
+  }
+  __syncthreads();
+  const int nchunks = (T + kWave - 1) / kWave;
+  for (int i = threadIdx.x; i < kChunksPerBlock * ngroups; i += blockDim.x) {
+    const int c = blockIdx.x * kChunksPerBlock + i / ngroups;
+    if (c < nchunks) masks[static_cast<size_t>(c) * ngroups + i % ngroups] = smask[i];
+  }
+}
+
+// One block.  Thread g owns group g (loops if ngroups > blockDim).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    const unsigned long long* __restrict__ masks, int nchunks, int ngroups, int E_local,
+    int32_t* __restrict__ bases, int32_t* __restrict__ group_off, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ err) {
+  extern __shared__ int32_t stot[];  // [ngroups]
+  if (threadIdx.x == 0) *err = 0;  // a new layer call starts with a clean error word
+  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      bases[static_cast<size_t>(c) * ngroups + g] = run;
+      run += __popcll(masks[static_cast<size_t>(c) * ngroups + g]);
+    }
+    stot[g] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // expert groups and ready-wave groups are two separate sorted orders
+    int run = 0;
+    for (int g = 0; g < E_local; ++g) {
+      group_off[g] = run;
+      offsets[g] = run;
+      counts[g] = stot[g];
+      run += stot[g];
+    }
+    group_off[E_local] = run;
+    offsets[E_local] = run;
+    run = 0;
+    for (int g = E_local; g < ngroups; ++g) {
+      group_off[g + 1] = run;
+      run += stot[g];
+    }
+    // group_off[E_local + 1 + s] = start of ready slot s; last = T
+    group_off[ngroups + 1] = run;
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int k, int e_begin, int E_local, int ngroups,
+    const unsigned long long* __restrict__ masks, const int32_t* __restrict__ bases,
+    const int32_t* __restrict__ group_off, const int32_t* __restrict__ ready_wave,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ ready_list) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int chunk = t / kWave, lane = t % kWave;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const size_t crow = static_cast<size_t>(chunk) * ngroups;
+  for (int j = 0; j < k; ++j) {
+    const int le = topk_idx[static_cast<size_t>(t) * k + j] - e_begin;
+    int32_t row = -1;
+    if (le >= 0 && le < E_local) {
+      row = group_off[le] + bases[crow + le] + __popcll(masks[crow + le] & below);
+      sorted_token[row] = t;
+    }
+    pair_pos[static_cast<size_t>(t) * k + j] = row;
+  }
+  const int slot = ready_wave[t] + 1;
+  const int g = E_local + slot;
+  ready_list[group_off[E_local + 1 + slot] + bases[crow + g] + __popcll(masks[crow + g] & below)] = t;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                           int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s) {
+  auto* masks = reinterpret_cast<unsigned long long*>(ws + L.masks);
+  auto* bases = reinterpret_cast<int32_t*>(ws + L.bases);
+  auto* group_off = reinterpret_cast<int32_t*>(ws + L.group_off);
+  auto* ready_list = reinterpret_cast<int32_t*>(ws + L.ready_list);
+  const int blocks = (L.nchunks + kChunksPerBlock - 1) / kChunksPerBlock;
+  if (p.T > 0) {
+    dispatch_count_kernel<<<blocks, 256, kChunksPerBlock * L.ngroups * sizeof(unsigned long long), s>>>(
+        topk_idx, p.T, p.k, p.e_begin, p.E_local, p.experts_per_wave, L.ngroups, masks, ready_wave);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dispatch_scan_kernel<<<1, 1024, L.ngroups * sizeof(int32_t), s>>>(
+      masks, L.nchunks, L.ngroups, p.E_local, bases, group_off, counts, offsets,
+      reinterpret_cast<int32_t*>(ws + L.err));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.T == 0) return e;
+  dispatch_scatter_kernel<<<(p.T + 255) / 256, 256, 0, s>>>(
+      topk_idx, p.T, p.k, p.e_begin, p.E_local, L.ngroups, masks, bases, group_off, ready_wave,
+      sorted_token, pair_pos, ready_list);
+  return hipGetLastError();
+}
+
+}  // namespace moe

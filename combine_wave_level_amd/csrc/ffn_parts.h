@@ -1,0 +1,156 @@
+// ffn_parts.h -- the pieces of the expert FFN shared by the phase-by-phase
+// kernels and the persistent expert-wave kernel: tile decoding, the GEMM1
+// (gather + gate/up + SwiGLU) tile, the GEMM2 (down) tile, and the combine of
+// one token.  Both schedules call exactly these functions, so they produce
+// the same bits.
+//
+// Layer per token-expert pair (DeepSeek-V4 launch digest, itsolotime.com,
+// section 1.4, compute/communication bullet: gating, up and down
+// projections): h1 = x W1, h3 = x W3, a = silu(h1) * h3, y = a W2.
+#pragma once
+
+#include "gemm_tile.h"
+
+namespace moe {
+
+// Tile shapes of the expert GEMMs.  BT tokens (pair rows) by BW output
+// features, 4 wavefronts as 2 x 2.
+using G1Cfg = TileCfg<128, 128, 2, 2>;
+using G2Cfg = TileCfg<128, 128, 2, 2>;
+constexpr size_t kFfnLds = G1Cfg::LDS_BYTES > G2Cfg::LDS_BYTES ? G1Cfg::LDS_BYTES : G2Cfg::LDS_BYTES;
+constexpr int kMaxLocalExperts = 256;
+
+// Per-workgroup table: m-tile prefix over local experts (rows split into
+// BT-row tiles).  mt_pre[e] = first m-tile of expert e, mt_pre[E_local] =
+// total.  Built from expert_offsets by thread 0.
+__device__ __forceinline__ void build_mtile_prefix(const int32_t* __restrict__ offsets, int E_local,
+                                                   int BT, int32_t* mt_pre) {
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E_local; ++e) {
+      mt_pre[e] = run;
+      run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
+    }
+    mt_pre[E_local] = run;
+  }
+}
+
+// Expert owning global m-tile mt (binary search in mt_pre[lo..hi]).
+__device__ __forceinline__ int expert_of_mtile(const int32_t* mt_pre, int lo, int hi, int mt) {
+  // invariant: mt_pre[lo] <= mt < mt_pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mt_pre[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float silu_mul(float h1, float h3) {
+  // silu(h1) * h3 with silu(h) = h / (1 + exp(-h)); IEEE division
+  return (h1 / (1.0f + expf(-h1))) * h3;
+}
+
+// GEMM1 tile: rows [row0, row0 + BT) of expert e's segment (count rows
+// valid), output features 2*BW/2 packed rows starting at row block
+// nt * BW / 16 of W13, i.e. intermediate indices [nt * BW/2, nt * BW/2 + BW/2).
+// The A-operand rows are pulled straight from the token-order staging
+// buffer xb by sorted_token: the dispatch pull lands in LDS.
+__device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
+                                           const uint16_t* __restrict__ w13e,
+                                           const int32_t* __restrict__ sorted_token,
+                                           uint16_t* __restrict__ act, int row0, int count, int nt,
+                                           int d, int I, uint16_t* lds) {
+  using C = G1Cfg;
+  const uint16_t* trow[C::LT];
+#pragma unroll
+  for (int i = 0; i < C::LT; ++i) {
+    const int r = min(trow_index<C>(i), count - 1);
+    trow[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+  }
+  TileAcc<C> acc;
+  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / 64, trow, lds, acc);
+  const int lane = lane_id(), wave = wave_id();
+  const int wr = wave / C::WT, wt = wave % C::WT;
+#pragma unroll
+  for (int a = 0; a < C::AW; a += 2) {
+    const int nb = nt * (C::BW / 16) + wr * C::AW + a;  // even: W1 block, nb + 1: W3 block
+    const int i0 = (nb / 2) * 16 + 4 * (lane / 16);
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) {
+      const int tr = (wt * C::AT + b) * 16 + (lane & 15);
+      if (tr >= count) continue;
+      const f32x4 h1 = acc.v[a][b], h3 = acc.v[a + 1][b];
+      u32x2 pk;
+      pk.x = pack_bf16x2(silu_mul(h1[0], h3[0]), silu_mul(h1[1], h3[1]));
+      pk.y = pack_bf16x2(silu_mul(h1[2], h3[2]), silu_mul(h1[3], h3[3]));
+      *reinterpret_cast<u32x2*>(act + static_cast<size_t>(row0 + tr) * I + i0) = pk;
+    }
+  }
+}
+
+// GEMM2 tile: y[row0 .. row0 + count) x features [nt * BW, nt * BW + BW).
+__device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ act,
+                                           const uint16_t* __restrict__ w2e, uint16_t* __restrict__ y,
+                                           int row0, int count, int nt, int d, int I, uint16_t* lds) {
+  using C = G2Cfg;
+  const uint16_t* trow[C::LT];
+#pragma unroll
+  for (int i = 0; i < C::LT; ++i) {
+    const int r = min(trow_index<C>(i), count - 1);
+    trow[i] = act + static_cast<size_t>(row0 + r) * I;
+  }
+  TileAcc<C> acc;
+  tile_mma<C>(w2e + frag_offset(nt * (C::BW / 16), 0, I / 32), I / 32, I / 64, trow, lds, acc);
+  const int lane = lane_id(), wave = wave_id();
+  const int wr = wave / C::WT, wt = wave % C::WT;
+#pragma unroll
+  for (int a = 0; a < C::AW; ++a) {
+    const int n0 = (nt * (C::BW / 16) + wr * C::AW + a) * 16 + 4 * (lane / 16);
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) {
+      const int tr = (wt * C::AT + b) * 16 + (lane & 15);
+      if (tr >= count) continue;
+      const f32x4 v = acc.v[a][b];
+      u32x2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2*>(y + static_cast<size_t>(row0 + tr) * d + n0) = pk;
+    }
+  }
+}
+
+// Combine of token t by one wavefront: out[t] = sum_j w[t, j] * y[pair_pos[t, j]]
+// over local picks, fp32 fused multiply-adds in ascending j, one rounding.
+template <bool OUT_BF16>
+__device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict__ y,
+                                              const int32_t* __restrict__ pair_pos,
+                                              const float* __restrict__ topk_w, int k, int d,
+                                              void* __restrict__ out) {
+  const int lane = lane_id();
+  for (int c = lane; c < d / 8; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = pair_pos[static_cast<size_t>(t) * k + j];
+      if (r < 0) continue;
+      const float w = topk_w[static_cast<size_t>(t) * k + j];
+      const u32x4 v = ld16(y + static_cast<size_t>(r) * d + c * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(w, __uint_as_float(v[q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(w, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
+      }
+    }
+    if constexpr (OUT_BF16) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+      st16(static_cast<uint16_t*>(out) + static_cast<size_t>(t) * d + c * 8, o);
+    } else {
+      float* o = static_cast<float*>(out) + static_cast<size_t>(t) * d + c * 8;
+      *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+// moe_api.hip -- the C ABI declared in include/moe.h: argument checks,
+// workspace carve-up and launches.  Host-side checks are O(1) and run before
+// anything is queued (DeepSeek-V4 launch digest, itsolotime.com, section
+// 2.1: per-call host overhead is what a thin generated launcher keeps below
+// a microsecond; here the launcher is this hand-written C++).
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static moe_status_t check_problem(const moe_problem_t* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->T < 0 || p->d <= 0 || p->I <= 0 || p->E_global <= 0 || p->k <= 0 || p->E_local <= 0 ||
+      p->e_begin < 0 || p->experts_per_wave <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (p->k > p->E_global || p->e_begin + p->E_local > p->E_global) return MOE_ERR_INVALID_ARG;
+  if (p->E_local % p->experts_per_wave != 0) return MOE_ERR_INVALID_ARG;
+  const auto dt_ok = [](int32_t t) { return t == MOE_F32 || t == MOE_BF16; };
+  if (!dt_ok(p->x_dtype) || !dt_ok(p->w_dtype) || !dt_ok(p->out_dtype)) return MOE_ERR_INVALID_ARG;
+  if (p->d % 128 != 0 || p->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (p->E_global > 256 || p->k > 64) return MOE_ERR_UNSUPPORTED;
+  if (p->T > (1 << 24) || p->d > (1 << 16) || p->I > (1 << 16)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+WsLayout ws_layout(const moe_problem_t& p) {
+  WsLayout L{};
+  L.nchunks = (p.T + kWave - 1) / kWave;
+  L.W = p.E_local / p.experts_per_wave;
+  L.ngroups = p.E_local + L.W + 1;
+  L.P_max = p.T * (p.k < p.E_local ? p.k : p.E_local);
+  const size_t max_mtiles = static_cast<size_t>(L.P_max) / 128 + p.E_local + 1;
+  L.sync_words = 1 + static_cast<size_t>(L.W) + max_mtiles + 64;
+  const size_t wg_slots = static_cast<size_t>(L.P_max) / kWgradChunkRows;
+  L.wgrad_bytes = wg_slots * 3 * static_cast<size_t>(p.d) * p.I * sizeof(float);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L.err = take(256);
+  L.masks = take(static_cast<size_t>(L.nchunks) * L.ngroups * 8);
+  L.bases = take(static_cast<size_t>(L.nchunks) * L.ngroups * 4);
+  L.group_off = take(static_cast<size_t>(L.ngroups + 2) * 4);
+  L.ready_list = take(static_cast<size_t>(p.T) * 4);
+  L.logits = take(static_cast<size_t>(p.T) * p.E_global * 4);
+  L.xbf = take(p.x_dtype == MOE_F32 ? static_cast<size_t>(p.T) * p.d * 2 : 0);
+  L.act = take(static_cast<size_t>(L.P_max) * p.I * 2);
+  L.sync = take(L.sync_words * 4);
+  L.wgrad = take(align_up(static_cast<size_t>(L.P_max) * p.I * 2 * 3, 256) + L.wgrad_bytes);
+  L.total = off;
+  return L;
+}
+
+static moe_status_t check_ws(const moe_problem_t* p, const void* ws, size_t ws_bytes, WsLayout* L) {
+  *L = ws_layout(*p);
+  if (!ws || !aligned16(ws) || ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_packed_weights_size(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return packed_layout(p->d, p->I, p->E_global, p->E_local, p->x_dtype == MOE_BF16).total;
+}
+
+size_t moe_workspace_size(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return ws_layout(*p).total;
+}
+
+moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void* W1,
+                              const void* W3, const void* W2, void* packed, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!Wg || !W1 || !W3 || !W2 || !packed) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack(*p, Wg, W1, W3, W2, packed, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* packed, const float* bias,
+                       int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!x || !packed || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (packed && !aligned16(packed))) return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits);
+  return hip_status(launch_route(*p, x, packed, bias, topk_idx, topk_w, lg, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* sorted_token, int32_t* pair_pos,
+                          int32_t* token_ready_wave, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!topk_idx || !sorted_token || !pair_pos || !token_ready_wave)) return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  return hip_status(launch_dispatch(*p, L, topk_idx, expert_counts, expert_offsets, sorted_token,
+                                    pair_pos, token_ready_wave, static_cast<char*>(ws),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const void* packed,
+                                  const int32_t* expert_offsets, const int32_t* sorted_token,
+                                  const int32_t* pair_pos, const float* topk_w,
+                                  const int32_t* token_ready_wave, void* y, void* out,
+                                  uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (flags & ~MOE_FLAG_SERIAL) return MOE_ERR_INVALID_ARG;
+  if (!packed || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !sorted_token || !y)) return MOE_ERR_INVALID_ARG;
+  if (out && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || !aligned16(packed) || (y && !aligned16(y)) || (out && !aligned16(out)))
+    return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  return hip_status(launch_ffn(*p, L, x, packed, expert_offsets, sorted_token, pair_pos, topk_w,
+                               token_ready_wave, y, out, flags, static_cast<char*>(ws),
+                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* pair_pos,
+                         const float* topk_w, void* out, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!y || !pair_pos || !topk_w || !out)) return MOE_ERR_INVALID_ARG;
+  if ((y && !aligned16(y)) || (out && !aligned16(out))) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(*p, y, pair_pos, topk_w, out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void* packed,
+                              const int32_t* expert_offsets, const int32_t* sorted_token,
+                              const int32_t* pair_pos, const float* topk_w, const void* dout,
+                              float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                              moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!packed || !expert_offsets || !dW1 || !dW3 || !dW2) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !sorted_token || !pair_pos || !topk_w || !dout)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (dout && !aligned16(dout)) || !aligned16(dW1) || !aligned16(dW3) ||
+      !aligned16(dW2))
+    return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  return hip_status(launch_wgrad(*p, L, x, packed, expert_offsets, sorted_token, pair_pos, topk_w,
+                                 dout, dW1, dW3, dW2, static_cast<char*>(ws),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_check_error(void* ws, moe_stream_t stream) {
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  if (word != 0) {
+    const int32_t zero = 0;
+    if (hipMemcpyAsync(ws, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    return static_cast<moe_status_t>(word);
+  }
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_TIMEOUT: return "device-side wait timed out";
+  }
+  return "unknown status";
+}
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

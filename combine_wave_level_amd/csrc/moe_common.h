@@ -1,0 +1,110 @@
+// moe_common.h -- device-side building blocks shared by the MoE kernels
+// (gfx950 / CDNA4 only).
+//
+// Numeric policy (DeepSeek-V4 launch digest, itsolotime.com, section 2.3:
+// precision first, no fast-math, explicit rounding): every file is compiled
+// with -ffp-contract=off and without fast-math, so each float operation is
+// the one written; fused multiply-adds are written explicitly with fmaf;
+// float -> bf16 is round-to-nearest-even; exp is the device library expf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even.  NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ------------------------------------------------------------------ MFMA
+//
+// One instruction shape for every product in the library:
+// v_mfma_f32_16x16x32_bf16, D[16x16] += A[16x32] * B[32x16] in fp32.
+// Operand fragments: lane l holds 8 consecutive k (group g = l / 16,
+// k = 8g .. 8g+7) of row (A) or column (B) l % 16.  Result: lane l holds
+// D[4 * (l / 16) + r][l % 16] for r = 0..3.  Keeping this single shape and
+// an ascending K order everywhere is what makes each output element's bits
+// independent of the tile it is computed in, hence of the batch.
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ layout
+//
+// Fragment layout of a bf16 matrix M[N][K] (N rows, K the reduction index):
+// fragment (nb, kb) covers rows 16nb .. 16nb+15 and k 32kb .. 32kb+31, is
+// 1 KiB long, and stores M[16nb + (s % 16)][32kb + 8(s / 16) + 0..7] at
+// 16-byte slot s (0..63): exactly lane s's MFMA operand.  Fragments of one
+// row block are consecutive along K.  In elements:
+__host__ __device__ __forceinline__ size_t frag_offset(int nb, int kb, int KB) {
+  return (static_cast<size_t>(nb) * KB + kb) * 512;
+}
+
+// Packed weight buffer (written once by moe_pack_weights):
+//   router   : Wg^T as [Epad][d], Epad = E_global rounded up to 128 rows, in
+//              fragment layout when x is bf16; plain row-major fp32 when x
+//              is fp32 (the router then runs on the vector ALUs).
+//   W13      : per local expert, [2I][d] fragment layout; row block 2b holds
+//              W1 columns 16b .. 16b+15 and row block 2b+1 the W3 columns
+//              with the same indices, so gate and up values of one
+//              intermediate index meet in the same lane.
+//   W2       : per local expert, W2^T as [d][I] in fragment layout.
+//   W2b      : per local expert, W2 as [I][d] in fragment layout (K = d), the
+//              operand of dA = dy W2^T in the weight gradient.
+struct PackedLayout {
+  size_t router, w13, w2, w2b, total;
+  int Epad;
+};
+
+__host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+__host__ __device__ inline PackedLayout packed_layout(int d, int I, int E_global, int E_local,
+                                                      int x_is_bf16) {
+  PackedLayout L;
+  L.Epad = static_cast<int>(align_up(static_cast<size_t>(E_global), 128));
+  size_t off = 0;
+  L.router = off;
+  off += align_up(static_cast<size_t>(L.Epad) * d * (x_is_bf16 ? 2 : 4), 256);
+  L.w13 = off;
+  off += align_up(static_cast<size_t>(E_local) * 2 * I * d * 2, 256);
+  L.w2 = off;
+  off += align_up(static_cast<size_t>(E_local) * d * I * 2, 256);
+  L.w2b = off;
+  off += align_up(static_cast<size_t>(E_local) * d * I * 2, 256);
+  L.total = off;
+  return L;
+}
+
+// ------------------------------------------------------------------ misc
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace moe

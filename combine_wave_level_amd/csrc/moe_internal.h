@@ -1,0 +1,80 @@
+// moe_internal.h -- host-side plumbing shared by the library's translation
+// units: the workspace layout and the kernel launchers.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "moe_common.h"
+
+namespace moe {
+
+// Workspace carve-up.  Every region is 256-byte aligned.
+//   err        int32 device error word (bounded waits write MOE_ERR_TIMEOUT)
+//   masks      uint64 [nchunks][ngroups]: per 64-token chunk, one bit per
+//              token for each local expert it picked (groups 0..E_local-1)
+//              and for its ready wave (groups E_local .. E_local+W: slot 0 =
+//              no local pick, slot w+1 = ready after wave w)
+//   bases      int32 [nchunks][ngroups]: exclusive scan of the chunk counts
+//              over chunks, per group
+//   group_off  int32 [ngroups + 1]: start of each group in its sorted order
+//              (experts: pair rows; ready slots: positions in ready_list)
+//   ready_list int32 [T]: tokens ordered by ready wave, ascending token id
+//              inside a wave
+//   logits     fp32 [T][E_global] router scores
+//   xbf        bf16 [T][d] (only when x is fp32): x rounded for the FFN
+//   act        bf16 [P_max][I]: a = silu(h1) * h3, sorted-row order
+//   sync       int32 counters of the persistent expert-wave kernel
+//   wgrad      fp32 isolated partial buffers of the weight gradient
+struct WsLayout {
+  size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, wgrad, total;
+  int nchunks, W, ngroups, P_max;
+  size_t sync_words, wgrad_bytes;
+};
+
+WsLayout ws_layout(const moe_problem_t& p);
+
+// Rows of the weight-gradient split along the routed rows of one expert:
+// each chunk of this many rows reduces into its own partial slot.
+constexpr int kWgradChunkRows = 2048;
+
+// ------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.  Shapes are validated by the
+// caller (moe_api.hip) before these run.
+
+hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
+                       const void* W2, void* packed, hipStream_t s);
+
+hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packed,
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                        hipStream_t s);
+
+hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                           int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s);
+
+hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
+                      const int32_t* offsets, const int32_t* sorted_token, const int32_t* pair_pos,
+                      const float* topk_w, const int32_t* ready_wave, void* y, void* out,
+                      uint32_t flags, char* ws, hipStream_t s);
+
+// Returns the bf16 token-order staging copy of x used by the expert GEMMs:
+// x itself when it is bf16, else a rounded copy written to the workspace.
+hipError_t stage_x_bf16(const moe_problem_t& p, const WsLayout& L, const void* x, char* ws,
+                        hipStream_t s, const uint16_t** xb);
+
+// Zero-fills n 32-bit words with a kernel (no memset node, so callers may
+// capture the stream into a graph).
+hipError_t fill_zero(void* p, size_t n, hipStream_t s);
+
+hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,
+                          const float* topk_w, void* out, hipStream_t s);
+
+hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
+                        const int32_t* offsets, const int32_t* sorted_token,
+                        const int32_t* pair_pos, const float* topk_w, const void* dout,
+                        float* dW1, float* dW3, float* dW2, char* ws, hipStream_t s);
+
+}  // namespace moe

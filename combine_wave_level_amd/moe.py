@@ -1,0 +1,231 @@
+"""Thin Python binding of ``libmoe.so`` (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  PyTorch provides device memory (tensor storage) and the
+current HIP stream.  The library must be built (``build_lib.build()``); if it
+is missing, loading fails loudly -- there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+MOE_ERR_TIMEOUT = -5
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_FLAG_SERIAL = 0x1
+
+EXPORTED = (
+    "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
+    "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
+    "moe_check_error", "moe_status_string", "moe_version",
+)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "d", "I", "E_global", "k", "e_begin", "E_local", "experts_per_wave",
+        "x_dtype", "w_dtype", "out_dtype")]
+
+    def replace(self, **kw) -> "Problem":
+        q = Problem()
+        for n, _ in self._fields_:
+            setattr(q, n, kw.get(n, getattr(self, n)))
+        return q
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                               "(run combine_wave_level_amd.build_lib.build())")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        P = ctypes.POINTER(Problem)
+        st = ctypes.c_int
+        sig = {
+            "moe_packed_weights_size": (ctypes.c_size_t, [P]),
+            "moe_workspace_size": (ctypes.c_size_t, [P]),
+            "moe_pack_weights": (st, [P, vp, vp, vp, vp, vp, vp]),
+            "moe_route": (st, [P, vp, vp, f32p, i32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
+            "moe_dispatch": (st, [P, i32p, i32p, i32p, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]),
+            "moe_expert_ffn_waved": (st, [P, vp, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
+                                          ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
+            "moe_combine": (st, [P, vp, i32p, f32p, vp, vp]),
+            "moe_expert_wgrad": (st, [P, vp, vp, i32p, i32p, i32p, f32p, vp, f32p, f32p, f32p,
+                                      vp, ctypes.c_size_t, vp]),
+            "moe_check_error": (st, [vp, vp]),
+            "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().moe_status_string(int(s)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def problem(T, d, I, E_global, k, e_begin=0, E_local=None, experts_per_wave=4,
+            x_dtype=MOE_BF16, w_dtype=MOE_BF16, out_dtype=MOE_BF16) -> Problem:
+    E_local = E_global if E_local is None else E_local
+    return Problem(T, d, I, E_global, k, e_begin, E_local, experts_per_wave,
+                   x_dtype, w_dtype, out_dtype)
+
+
+def workspace_size(p: Problem) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(p)))
+
+
+def packed_weights_size(p: Problem) -> int:
+    return int(lib().moe_packed_weights_size(ctypes.byref(p)))
+
+
+def workspace(p: Problem, device="cuda") -> torch.Tensor:
+    n = workspace_size(p)
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, "workspace_size")
+    # zero-filled once, so the device error word starts clean
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pack_weights(p: Problem, Wg, W1, W3, W2) -> torch.Tensor:
+    n = packed_weights_size(p)
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, "packed_weights_size")
+    packed = torch.empty(n, dtype=torch.uint8, device=W1.device)
+    _check(lib().moe_pack_weights(ctypes.byref(p), _p(Wg), _p(W1), _p(W3), _p(W2), _p(packed),
+                                  _stream()), "moe_pack_weights")
+    return packed
+
+
+def route(p: Problem, x, packed, ws, bias=None, want_logits=False):
+    dev = x.device
+    idx = torch.empty((p.T, p.k), dtype=torch.int32, device=dev)
+    w = torch.empty((p.T, p.k), dtype=torch.float32, device=dev)
+    logits = torch.empty((p.T, p.E_global), dtype=torch.float32, device=dev) if want_logits else None
+    _check(lib().moe_route(ctypes.byref(p), _p(x), _p(packed), _p(bias), _p(idx), _p(w), _p(logits),
+                           _p(ws), ws.numel(), _stream()), "moe_route")
+    return idx, w, logits
+
+
+@dataclass
+class Dispatch:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_token: torch.Tensor
+    pair_pos: torch.Tensor
+    ready_wave: torch.Tensor
+
+
+def p_max(p: Problem) -> int:
+    return p.T * min(p.k, p.E_local)
+
+
+def dispatch(p: Problem, topk_idx, ws) -> Dispatch:
+    dev = topk_idx.device
+    d = Dispatch(
+        counts=torch.empty(p.E_local, dtype=torch.int32, device=dev),
+        offsets=torch.empty(p.E_local + 1, dtype=torch.int32, device=dev),
+        sorted_token=torch.empty(max(1, p_max(p)), dtype=torch.int32, device=dev),
+        pair_pos=torch.empty((p.T, p.k), dtype=torch.int32, device=dev),
+        ready_wave=torch.empty(p.T, dtype=torch.int32, device=dev),
+    )
+    _check(lib().moe_dispatch(ctypes.byref(p), _p(topk_idx), _p(d.counts), _p(d.offsets),
+                              _p(d.sorted_token), _p(d.pair_pos), _p(d.ready_wave), _p(ws),
+                              ws.numel(), _stream()), "moe_dispatch")
+    return d
+
+
+def _out_dtype(p: Problem):
+    return torch.bfloat16 if p.out_dtype == MOE_BF16 else torch.float32
+
+
+def ffn_waved(p: Problem, x, packed, disp: Dispatch, topk_w, ws, fused_combine=True,
+              serial=False, y=None, out=None):
+    dev = x.device
+    if y is None:
+        y = torch.empty((max(1, p_max(p)), p.d), dtype=torch.bfloat16, device=dev)
+    if fused_combine and out is None:
+        out = torch.empty((p.T, p.d), dtype=_out_dtype(p), device=dev)
+    flags = MOE_FLAG_SERIAL if serial else 0
+    _check(lib().moe_expert_ffn_waved(
+        ctypes.byref(p), _p(x), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
+        _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y),
+        _p(out) if fused_combine else None, flags, _p(ws), ws.numel(), _stream()),
+        "moe_expert_ffn_waved")
+    return y, (out if fused_combine else None)
+
+
+def combine(p: Problem, y, pair_pos, topk_w, out=None):
+    if out is None:
+        out = torch.empty((p.T, p.d), dtype=_out_dtype(p), device=y.device)
+    _check(lib().moe_combine(ctypes.byref(p), _p(y), _p(pair_pos), _p(topk_w), _p(out), _stream()),
+           "moe_combine")
+    return out
+
+
+def wgrad(p: Problem, x, packed, disp: Dispatch, topk_w, dout, ws):
+    dev = x.device
+    shp13 = (p.E_local, p.d, p.I)
+    dW1 = torch.empty(shp13, dtype=torch.float32, device=dev)
+    dW3 = torch.empty(shp13, dtype=torch.float32, device=dev)
+    dW2 = torch.empty((p.E_local, p.I, p.d), dtype=torch.float32, device=dev)
+    _check(lib().moe_expert_wgrad(
+        ctypes.byref(p), _p(x), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
+        _p(disp.pair_pos), _p(topk_w), _p(dout), _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(),
+        _stream()), "moe_expert_wgrad")
+    return dW1, dW3, dW2
+
+
+def check_error(ws) -> None:
+    _check(lib().moe_check_error(_p(ws), _stream()), "moe_check_error")
+
+
+def forward(p: Problem, x, packed, ws, bias=None, serial=False, want_logits=False):
+    """route -> dispatch -> waved expert FFN with fused combine."""
+    idx, w, logits = route(p, x, packed, ws, bias=bias, want_logits=want_logits)
+    disp = dispatch(p, idx, ws)
+    y, out = ffn_waved(p, x, packed, disp, w, ws, fused_combine=True, serial=serial)
+    return {"idx": idx, "w": w, "logits": logits, "disp": disp, "y": y, "out": out}

@@ -1,0 +1,197 @@
+/*
+ * moe.h -- C ABI of one GPU's share of a fine-grained expert-parallel MoE
+ * layer, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the DeepSeek-V4 report describes it (DeepSeek-V4 launch
+ * digest, itsolotime.com, Thai translation of the report's infrastructure
+ * chapter, section 1.1; 10100.com commentary, section on fine-grained
+ * compute/communication overlap of the EP all-to-all): route each token to
+ * its top-k experts, dispatch the tokens to their experts, run each expert's
+ * FFN (Linear, SwiGLU, Linear), and combine the expert outputs back into
+ * token order weighted by the router.  Experts are processed in waves of a
+ * few experts (digest section 1.2); inside one persistent kernel the current
+ * wave's GEMMs overlap the dispatch pulls of the next wave and the combine of
+ * finished tokens.  Results are batch invariant and deterministic (digest
+ * section 3; 10100.com section on batch-invariant and deterministic
+ * operators): a token's output bits do not depend on the batch it sits in,
+ * and repeated runs give identical bits, including the weight gradient.
+ *
+ * Conventions for every entry point
+ *   - All pointers are device pointers unless stated otherwise; tensors are
+ *     dense, row-major, and 16-byte aligned.  The caller owns every buffer;
+ *     the library never allocates device memory.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  Host-side
+ *     argument checks run first and return an error before anything is
+ *     launched; a failed launch returns MOE_ERR_HIP.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits; every
+ *     rounding to bf16 in the library is round-to-nearest-even.
+ *   - "Local" experts are the global ids [e_begin, e_begin + E_local).
+ *     P (the number of routed pairs that land on local experts) is known
+ *     only on the device; buffers indexed by pair row are sized for the
+ *     upper bound P_max = T * min(k, E_local).
+ *   - No function keeps state between calls; calls on different streams
+ *     with disjoint buffers may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad shape, misaligned buffer  */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle   */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call or launch failed         */
+  MOE_ERR_TIMEOUT = -5      /* a device-side bounded wait expired          */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Shape of one layer share.  Limits checked by every call:
+ *   T >= 0; d, I > 0 with d % 128 == 0 and I % 64 == 0 (MOE_ERR_UNSUPPORTED
+ *   otherwise); 1 <= k <= E_global; E_global <= 256 and k <= 64
+ *   (MOE_ERR_UNSUPPORTED beyond); E_local >= 1; 0 <= e_begin,
+ *   e_begin + E_local <= E_global;
+ *   1 <= experts_per_wave, E_local % experts_per_wave == 0;
+ *   x_dtype in {F32, BF16}; out_dtype in {F32, BF16}. */
+typedef struct {
+  int32_t T;                /* tokens in the batch                         */
+  int32_t d;                /* hidden size                                 */
+  int32_t I;                /* expert intermediate size                    */
+  int32_t E_global;         /* router width (experts over all GPUs)        */
+  int32_t k;                /* experts per token                           */
+  int32_t e_begin;          /* first local expert id                       */
+  int32_t E_local;          /* local experts                               */
+  int32_t experts_per_wave; /* G: experts per wave                         */
+  int32_t x_dtype;          /* moe_dtype_t of x and the router weights     */
+  int32_t w_dtype;          /* moe_dtype_t of the unpacked expert weights  */
+  int32_t out_dtype;        /* moe_dtype_t of the layer output             */
+} moe_problem_t;
+
+/* Flags for moe_expert_ffn_waved. */
+#define MOE_FLAG_SERIAL 0x1u /* run gather+GEMM1, GEMM2, combine as separate
+                                grid-wide phases instead of the persistent
+                                expert-wave kernel (same bits, no overlap)   */
+
+/* ------------------------------------------------------------ sizing */
+
+/* Bytes of the packed weight buffer moe_pack_weights writes. 0 on bad shape. */
+size_t moe_packed_weights_size(const moe_problem_t* p);
+
+/* Bytes of workspace every entry point below needs for problem p.  One
+ * workspace of this size serves all of them (not concurrently).  0 on a bad
+ * shape. */
+size_t moe_workspace_size(const moe_problem_t* p);
+
+/* ------------------------------------------------------------ weights */
+
+/* One-time re-layout of the weights into the library's MFMA fragment
+ * layout (not part of the per-batch path; weights are parameters).
+ *   Wg [d, E_global] in x_dtype (router), W1, W3 [E_local, d, I] and
+ *   W2 [E_local, I, d] in w_dtype, all row-major in math layout
+ *   (h1 = x W1, h3 = x W3, y = a W2).
+ *   packed: moe_packed_weights_size(p) bytes, written entirely.
+ * Expert weights are rounded to bf16 (RNE) when w_dtype is F32. */
+moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void* W1,
+                              const void* W3, const void* W2, void* packed,
+                              moe_stream_t stream);
+
+/* ------------------------------------------------------------ the path */
+
+/* Router (workload definition of the layer: softmax over all E_global
+ * experts, top-k, weights renormalised over the k picks; named as the "MoE
+ * Routing" kernel of TileKernels in digest section 1.3).
+ *   x [T, d] in x_dtype; bias [E_global] fp32 or NULL (added to the logits).
+ *   Out: topk_idx [T, k] int32 global expert ids in rank order (descending
+ *   score, ties to the lower id); topk_w [T, k] fp32; logits [T, E_global]
+ *   fp32 when non-NULL (the router scores the selection was made on).
+ * Logits accumulate in fp32 in a fixed order; selection is made on the fp32
+ * logits; weights are exp(l_j - l_max) / sum over the picks, i.e. softmax
+ * followed by renormalisation. */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* packed,
+                       const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                       void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Dispatch metadata: a deterministic counting sort of the routed pairs by
+ * local expert (10100.com, deterministic operators: pre-sorting instead of
+ * unordered atomics).  Inside an expert, pairs are in ascending token order.
+ *   topk_idx [T, k] int32 (from moe_route or any caller).
+ *   Out: expert_counts [E_local], expert_offsets [E_local + 1] (exclusive
+ *   scan), sorted_token [P_max] (row -> token; rows >= P unwritten),
+ *   pair_pos [T, k] (pair -> row, -1 for non-local experts),
+ *   token_ready_wave [T] (last wave, (e - e_begin) / G, holding one of the
+ *   token's local experts; -1 if none).  All int32.
+ * Also fills the workspace's scheduling tables used by
+ * moe_expert_ffn_waved, so call it with the same workspace first. */
+moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx,
+                          int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* sorted_token, int32_t* pair_pos, int32_t* token_ready_wave,
+                          void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Expert FFN in expert waves (digest sections 1.1, 1.2, 1.4: per pair
+ * h1 = x W1, h3 = x W3, a = silu(h1) * h3, y = a W2).
+ *   x [T, d] in x_dtype: the staging buffer the dispatch pulls gather from.
+ *   packed: from moe_pack_weights.  expert_offsets, sorted_token, pair_pos,
+ *   token_ready_wave: from moe_dispatch (same workspace).  topk_w [T, k].
+ *   Out: y [P_max, d] bf16 expert outputs in sorted-row order; out [T, d] in
+ *   out_dtype when non-NULL: the combine, fused into the same persistent
+ *   kernel (tokens with no local pick get zeros).
+ * Each GEMM accumulates in fp32 over K in one fixed ascending order with one
+ * MFMA shape, never split; a is rounded to bf16 before the second GEMM and y
+ * is rounded to bf16.  flags: MOE_FLAG_SERIAL or 0. */
+moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const void* packed,
+                                  const int32_t* expert_offsets, const int32_t* sorted_token,
+                                  const int32_t* pair_pos, const float* topk_w,
+                                  const int32_t* token_ready_wave, void* y, void* out,
+                                  uint32_t flags, void* ws, size_t ws_bytes,
+                                  moe_stream_t stream);
+
+/* Combine (digest section 1.1; 10100.com deterministic operators): for each
+ * token, out[t] = sum over ranks j = 0..k-1 with pair_pos[t, j] >= 0 of
+ * topk_w[t, j] * y[pair_pos[t, j]], accumulated in fp32 with fused
+ * multiply-adds in ascending j, rounded once to out_dtype.  No atomics.
+ *   y [P_max, d] bf16; pair_pos [T, k]; topk_w [T, k]; out [T, d]. */
+moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* pair_pos,
+                         const float* topk_w, void* out, moe_stream_t stream);
+
+/* Deterministic weight gradient of L = <dout, out> (10100.com deterministic
+ * operators; digest section 3: isolated per-block buffers reduced in a fixed
+ * order, no float atomics).  With dy = topk_w[t, j] * dout[t] per routed row:
+ *   dW2_e = a^T dy,  dW1_e = x^T dH1,  dW3_e = x^T dH3,
+ *   dA = dy W2_e^T,  dH3 = dA * silu(h1),
+ *   dH1 = dA * h3 * s * (1 + h1 (1 - s)),  s = sigmoid(h1),
+ * with h1, h3 recomputed exactly as the forward computes them.
+ *   dout [T, d] bf16.  Out (fp32, math layout): dW1, dW3 [E_local, d, I],
+ *   dW2 [E_local, I, d], every element written. */
+moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void* packed,
+                              const int32_t* expert_offsets, const int32_t* sorted_token,
+                              const int32_t* pair_pos, const float* topk_w, const void* dout,
+                              float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
+/* Synchronises `stream`, then reads the device error word of the workspace
+ * (set by a bounded wait of moe_expert_ffn_waved that expired) and clears
+ * it.  moe_dispatch clears the word when a layer call starts; a workspace
+ * must be zero-filled once when allocated.  Returns MOE_OK, MOE_ERR_TIMEOUT
+ * or MOE_ERR_HIP. */
+moe_status_t moe_check_error(void* ws, moe_stream_t stream);
+
+/* Static English text of a status code. */
+const char* moe_status_string(moe_status_t s);
+
+/* Library build identification (static string). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,139 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/moe.h
+declares, sizes buffers, and rejects bad arguments before any HIP call.
+
+No compute entry point is called with arguments that pass validation here:
+on a machine without a GPU only the host-side checks run.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_wave_level_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == set(moe.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert moe.status_string(0) == "ok"
+    assert "workspace" in moe.status_string(moe.MOE_ERR_WORKSPACE)
+    assert "timed out" in moe.status_string(moe.MOE_ERR_TIMEOUT)
+    assert moe.status_string(12345) == "unknown status"
+    assert b"gfx950" in L.moe_version()
+
+
+def _p(**kw):
+    base = dict(T=64, d=256, I=128, E_global=8, k=2, e_begin=0, E_local=8, experts_per_wave=4,
+                x_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16, out_dtype=moe.MOE_BF16)
+    base.update(kw)
+    return moe.Problem(*[base[n] for n, _ in moe.Problem._fields_])
+
+
+@pytest.mark.parametrize("kw,ok", [
+    ({}, True),
+    ({"T": 0}, True),
+    ({"d": 96}, False),                        # d % 128
+    ({"d": 192}, False),
+    ({"I": 100}, False),                       # I % 64
+    ({"k": 9}, False),                         # k > E_global
+    ({"k": 0}, False),
+    ({"E_local": 6}, False),                   # E_local % G
+    ({"e_begin": 4, "E_local": 8}, False),     # beyond E_global
+    ({"E_global": 512, "E_local": 8}, False),  # router width limit
+    ({"x_dtype": 7}, False),
+    ({"T": -1}, False),
+])
+def test_sizes_accept_and_reject(L, kw, ok):
+    p = _p(**kw)
+    ws = moe.workspace_size(p)
+    pk = moe.packed_weights_size(p)
+    assert (ws > 0) == ok and (pk > 0) == ok
+
+
+def test_packed_size_matches_layout(L):
+    p = _p(T=10, d=4096, I=1024, E_global=16, E_local=16, k=4)
+    epad = 128
+    want = epad * 4096 * 2 + 16 * 2 * 1024 * 4096 * 2 + 2 * (16 * 4096 * 1024 * 2)
+    assert moe.packed_weights_size(p) == want
+
+
+def test_workspace_grows_with_tokens(L):
+    a = moe.workspace_size(_p(T=64))
+    b = moe.workspace_size(_p(T=6400))
+    assert b > a > 0
+
+
+def test_route_rejects_before_launch(L):
+    p = _p()
+    st = L.moe_route(ctypes.byref(p), None, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    bad = _p(d=100)
+    st = L.moe_route(ctypes.byref(bad), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    st = L.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 16, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, 1 << 30, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_route(ctypes.byref(p), ctypes.c_void_p(0x10004), FAKE, None, FAKE, FAKE, None, FAKE,
+                     1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG  # misaligned x
+    st = L.moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+
+
+def test_dispatch_ffn_combine_wgrad_reject_before_launch(L):
+    p = _p()
+    st = L.moe_dispatch(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = L.moe_dispatch(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_expert_ffn_waved(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                0x80, FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG  # unknown flag
+    st = L.moe_expert_ffn_waved(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                0, FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG  # fused combine without pair_pos / weights
+    st = L.moe_expert_ffn_waved(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                0, FAKE, 100, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_combine(ctypes.byref(p), None, FAKE, FAKE, FAKE, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = L.moe_combine(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.c_void_p(0x10008), None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                            FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, 1, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_pack_weights(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_check_error(None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.lib()

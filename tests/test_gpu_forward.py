@@ -1,0 +1,175 @@
+"""GPU parity of the forward path (router, dispatch, waved expert FFN,
+combine) against the float64 oracle, through the C ABI.
+
+Sizes: the tiny layer and a ragged cut of the mid layer are compared in
+full; the mid layer at its benchmark size (T=4096, the launch configuration
+bench.py times), the V3/V4-scale share and the decode sweep are compared on
+all routing/dispatch outputs and on sampled tokens' output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_wave_level_amd import moe
+from helpers import (OUT_TOL, Layer, check_dispatch_exact, check_dispatch_valid, check_routing,
+                     host_f64, oracle_inputs, rel_err_rows)
+from workloads import get, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def inputs(name, T=None):
+    key = (name, T)
+    if key not in _cache:
+        _cache[key] = make_inputs(name, T=T)
+    return _cache[key]
+
+
+def _full_compare(inp, G=None, sample=None, seed=0):
+    """Runs the layer on the GPU and compares every stage with the oracle.
+    sample: number of tokens whose output rows are compared (None = all)."""
+    wl = inp["workload"]
+    L = Layer(inp, G=G)
+    o = oracle_inputs(inp)
+    T = L.T
+    print(f"[case] {wl.name} T={T} G={L.p.experts_per_wave}", flush=True)
+    # 1. router, end to end on the GPU
+    r = L.forward()
+    l64 = oracle.router_logits(o["x"], o["Wg"], o["bias"])
+    idx_g = r["idx"].cpu().numpy()
+    w_g = r["w"].cpu().numpy()
+    tie, m = check_routing(r["logits"].cpu().numpy(), idx_g, w_g, l64, wl.k)
+    check_dispatch_valid(r["disp"], idx_g, wl.e_begin, L.p.E_local, L.p.experts_per_wave)
+    # 2. dispatch + FFN + combine on the oracle's routing
+    idx_o, w_o, _ = oracle.route(l64, wl.k)
+    meta = oracle.dispatch(idx_o, wl.e_begin, L.p.E_local, L.p.experts_per_wave)
+    disp, y, out, w_d = L.ffn_from_routing(idx_o, w_o)
+    check_dispatch_exact(disp, meta, T)
+    w32 = w_d.cpu().numpy().astype(np.float64)   # the weights the GPU was given
+    rng = np.random.default_rng(seed)
+    toks = np.arange(T) if sample is None or sample >= T else np.sort(rng.choice(T, sample, replace=False))
+    ref = oracle.forward_tokens(o["x"][toks], idx_o[toks], w32[toks], o["W1"], o["W3"], o["W2"],
+                                wl.e_begin, L.p.E_local)
+    got = host_f64(out)[toks]
+    err = rel_err_rows(got, ref)
+    print(f"  logits max err {m:.3g}, tie tokens {int(tie.sum())}, out rel err {err:.3g}", flush=True)
+    assert err <= OUT_TOL
+    # y rows of the sampled tokens' local pairs
+    pos = meta["pair_pos"][toks]
+    rows = pos[pos >= 0]
+    if rows.size:
+        yr = host_f64(y)[rows]
+        yo = np.stack([oracle.expert_ffn(o["x"][meta["sorted_token"][rr]][None],
+                                         o["W1"][np.searchsorted(meta["offsets"], rr, "right") - 1],
+                                         o["W3"][np.searchsorted(meta["offsets"], rr, "right") - 1],
+                                         o["W2"][np.searchsorted(meta["offsets"], rr, "right") - 1])[0][0]
+                       for rr in rows[:64]])
+        assert rel_err_rows(yr[:64], yo) <= OUT_TOL
+    # 3. the GPU's own routing end to end: compare tokens outside the tie class
+    ok = ~tie[toks]
+    ref_e2e = oracle.forward_tokens(o["x"][toks][ok], idx_o[toks][ok], w_o[toks][ok], o["W1"], o["W3"],
+                                    o["W2"], wl.e_begin, L.p.E_local)
+    assert rel_err_rows(host_f64(r["out"])[toks][ok], ref_e2e) <= OUT_TOL
+    return L, r, (disp, y, out)
+
+
+def test_tiny_layer_full():
+    L, r, _ = _full_compare(inputs("tiny"))
+    # fp32 output dtype for the fp32 layer
+    assert r["out"].dtype == torch.float32
+
+
+def test_mid_layer_ragged_cut_full():
+    _full_compare(inputs("mid", T=300))
+
+
+def test_mid_layer_benchmark_size_sampled():
+    _full_compare(inputs("mid"), sample=48)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 128])
+def test_decode_sweep(T):
+    _full_compare(inputs("decode", T=T), sample=None if T <= 32 else 32)
+
+
+def test_v4_scale_share_sampled():
+    L, r, _ = _full_compare(inputs("v4share"), sample=32)
+    # tokens without a local pick get exact zeros
+    idx = r["idx"].cpu().numpy()
+    none = ~((idx >= 0) & (idx < 32)).any(axis=1)
+    assert none.any()
+    assert (host_f64(r["out"])[none] == 0).all()
+
+
+def test_persistent_equals_serial_and_standalone_combine():
+    inp = inputs("mid", T=777)
+    L = Layer(inp)
+    a = L.forward(serial=False)
+    b = L.forward(serial=True)
+    assert torch.equal(a["out"], b["out"])
+    P = int(a["disp"].offsets[-1])
+    assert torch.equal(a["y"][:P], b["y"][:P])
+    c = moe.combine(L.p, a["y"], a["disp"].pair_pos, a["w"])
+    torch.cuda.synchronize()
+    assert torch.equal(c, a["out"])
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_output_bits_do_not_depend_on_wave_size(G):
+    inp = inputs("mid", T=500)
+    base = Layer(inp, G=4).forward()
+    other = Layer(inp, G=G).forward()
+    assert torch.equal(base["out"], other["out"])
+    assert torch.equal(base["idx"], other["idx"]) and torch.equal(base["w"], other["w"])
+
+
+def test_edge_empty_batch():
+    inp = inputs("mid", T=300)
+    L = Layer(inp).with_tokens(np.zeros((0, 4096), dtype=np.uint16))
+    r = L.forward()
+    assert r["out"].shape == (0, 4096)
+    assert r["disp"].counts.sum().item() == 0
+
+
+def test_edge_single_token_and_local_window():
+    # a window of 4 local experts of the mid layer's 16, top-4, one wave each
+    inp = dict(inputs("mid", T=300))
+    inp["W1"], inp["W3"], inp["W2"] = inp["W1"][4:8], inp["W3"][4:8], inp["W2"][4:8]
+    for T in (1, 300):
+        sub = dict(inp)
+        sub["x"] = inp["x"][:T]
+        L = Layer(sub, G=1, e_begin=4, E_local=4)
+        o = oracle_inputs(sub)
+        l64 = oracle.router_logits(o["x"], o["Wg"], None)
+        idx_o, w_o, _ = oracle.route(l64, 4)
+        meta = oracle.dispatch(idx_o, 4, 4, 1)
+        disp, y, out, w_d = L.ffn_from_routing(idx_o, w_o)
+        check_dispatch_exact(disp, meta, T)
+        ref = oracle.forward_tokens(o["x"], idx_o, w_d.cpu().numpy().astype(np.float64), o["W1"], o["W3"],
+                                    o["W2"], 4, 4)
+        assert rel_err_rows(host_f64(out), ref) <= OUT_TOL
+
+
+def test_edge_k_equals_E_and_single_expert():
+    inp = inputs("tiny")
+    # k = E: every token visits every expert
+    L = Layer(inp, k=8)
+    o = oracle_inputs(inp)
+    l64 = oracle.router_logits(o["x"], o["Wg"], None)
+    idx_o, w_o, _ = oracle.route(l64, 8)
+    disp, y, out, w_d = L.ffn_from_routing(idx_o, w_o)
+    assert disp.counts.cpu().numpy().tolist() == [64] * 8
+    ref = oracle.forward_tokens(o["x"], idx_o, w_d.cpu().numpy().astype(np.float64), o["W1"], o["W3"], o["W2"], 0, 8)
+    assert rel_err_rows(host_f64(out), ref) <= OUT_TOL
+    # one local expert, top-1, one wave: a dense SwiGLU for the tokens routed to it
+    sub = dict(inp)
+    sub["W1"], sub["W3"], sub["W2"] = inp["W1"][2:3], inp["W3"][2:3], inp["W2"][2:3]
+    L1 = Layer(sub, G=1, k=1, e_begin=2, E_local=1)
+    idx1, w1, _ = oracle.route(l64, 1)
+    disp, y, out, w_d = L1.ffn_from_routing(idx1, w1)
+    ref = oracle.forward_tokens(o["x"], idx1, w_d.cpu().numpy().astype(np.float64), sub["W1"].astype(np.float64),
+                                sub["W3"].astype(np.float64), sub["W2"].astype(np.float64), 2, 1)
+    assert rel_err_rows(host_f64(out), ref) <= OUT_TOL
