@@ -55,12 +55,12 @@ __global__ __launch_bounds__(256) void gemm1_phase_kernel(
   build_mtile_prefix(offsets, E_local, G1Cfg::BT, mt_pre);
   __syncthreads();
   const int NT = 2 * I / G1Cfg::BW;
-  const int total = mt_pre[E_local] * NT;
+  const int total = uniform(mt_pre[E_local] * NT);
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
-    const int e = expert_of_mtile(mt_pre, 0, E_local, mt);
-    const int row0 = offsets[e] + (mt - mt_pre[e]) * G1Cfg::BT;
-    const int count = min(G1Cfg::BT, offsets[e + 1] - row0);
+    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * G1Cfg::BT);
+    const int count = uniform(min(G1Cfg::BT, offsets[e + 1] - row0));
     gemm1_tile(xb, w13 + static_cast<size_t>(e) * 2 * I * d, sorted_token, act, row0, count, nt, d, I, lds);
   }
 }
@@ -73,12 +73,12 @@ __global__ __launch_bounds__(256) void gemm2_phase_kernel(
   build_mtile_prefix(offsets, E_local, G2Cfg::BT, mt_pre);
   __syncthreads();
   const int NT = d / G2Cfg::BW;
-  const int total = mt_pre[E_local] * NT;
+  const int total = uniform(mt_pre[E_local] * NT);
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
-    const int e = expert_of_mtile(mt_pre, 0, E_local, mt);
-    const int row0 = offsets[e] + (mt - mt_pre[e]) * G2Cfg::BT;
-    const int count = min(G2Cfg::BT, offsets[e + 1] - row0);
+    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * G2Cfg::BT);
+    const int count = uniform(min(G2Cfg::BT, offsets[e + 1] - row0));
     gemm2_tile(act, w2 + static_cast<size_t>(e) * d * I, y, row0, count, nt, d, I, lds);
   }
 }
@@ -116,20 +116,45 @@ struct WaveArgs {
   long long timeout_ticks;   // bound of each wait, in wall-clock ticks
 };
 
-// Bounded wait until *p >= target.  Thread 0 polls with relaxed loads,
+// The three primitives below are the only cross-workgroup operations of
+// the persistent kernel.  They are called by all threads, inside the task
+// loop that also contains the tiles' barriers, so none of them contains a
+// lane-divergent branch: "one thread does X" is written as a wave-uniform
+// branch on wave 0 with the lane selection folded into the operand.  (A
+// lane-divergent if around the counter atomics lets the compiler move that
+// block onto the loop's back edge and run the other lanes' next iteration,
+// barriers included, before lane 0's atomics.)
+
+__device__ __forceinline__ int wave_uniform() { return uniform(static_cast<int>(threadIdx.x) / kWave); }
+
+// Claims the next ticket for the workgroup.
+__device__ __forceinline__ int claim_ticket(int32_t* ticket, int32_t* s_ticket) {
+  if (wave_uniform() == 0) {
+    // one increment per workgroup: lane 0 adds 1, the other lanes add 0
+    const int v = __hip_atomic_fetch_add(ticket, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    // lane 0's pre-op value; every lane stores the same value
+    *s_ticket = __shfl(v, 0, kWave);
+  }
+  __syncthreads();
+  const int tk = uniform(*s_ticket);
+  __syncthreads();
+  return tk;
+}
+
+// Bounded wait until *p >= target.  Wave 0 polls with relaxed loads,
 // sleeping between polls: no cache maintenance inside the loop (an acquire
-// load per poll would invalidate the L2's non-local lines on every
-// iteration, from every waiting workgroup, starving the producers it waits
-// for).  The wait is bounded by wall-clock ticks; on expiry it records
-// MOE_ERR_TIMEOUT and stops waiting (results are then invalid, but the
-// kernel still drains).  After the barrier every wave performs one
-// agent-scope acquire, so its following loads see the producers' stores.
+// per poll would invalidate the L2's non-local lines on every iteration and
+// starve the producers).  The wait is bounded by wall-clock ticks; on
+// expiry MOE_ERR_TIMEOUT is recorded and the wait ends (results are then
+// invalid, but the kernel still drains).  After the barrier every wave
+// performs one agent-scope acquire.
 __device__ __forceinline__ void wait_geq(const int32_t* p, int target, long long timeout_ticks,
                                          int32_t* err) {
-  if (threadIdx.x == 0) {
-    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+  if (wave_uniform() == 0) {
+    if (uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
       const long long t0 = wall_clock64();
-      while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      while (uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
         if (wall_clock64() - t0 > timeout_ticks) {
           __hip_atomic_store(err, static_cast<int32_t>(MOE_ERR_TIMEOUT), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -145,11 +170,12 @@ __device__ __forceinline__ void wait_geq(const int32_t* p, int target, long long
 
 // Publish this workgroup's finished global stores, then count them: every
 // wave releases its own stores at agent scope, the barrier orders those
-// releases before thread 0's increment.
+// releases before the increment.
 __device__ __forceinline__ void signal_add(int32_t* p) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave_uniform() == 0)
+    __hip_atomic_fetch_add(p, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool OUT_BF16>
@@ -162,38 +188,44 @@ __global__ __launch_bounds__(256) void ffn_waved_kernel(WaveArgs A) {
     sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, G1Cfg::BT, 2 * A.I / G1Cfg::BW,
                 A.d / G2Cfg::BW, A.out != nullptr);
   __syncthreads();
-  const int total = S.total;
+  const int total = uniform(S.total);
+  const int NT1 = uniform(S.NT1);
   int32_t* ticket = A.sync;
 
-  for (;;) {
-    if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int tk = s_ticket;
-    __syncthreads();
-    if (tk >= total) break;
-    const Task t = sched_decode(S, tk);
+  // Every value that steers this loop is made wave-uniform explicitly (the
+  // ticket and the decoded task come from LDS), so all waves run the same
+  // iterations between barriers.
+  for (int tk = claim_ticket(ticket, &s_ticket); tk < total; tk = claim_ticket(ticket, &s_ticket)) {
+    Task t = sched_decode(S, tk);
+    t.kind = uniform(t.kind);
+    t.wave = uniform(t.wave);
+    t.mt = uniform(t.mt);
+    t.expert = uniform(t.expert);
+    t.nt = uniform(t.nt);
+    t.slot = uniform(t.slot);
+    t.chunk = uniform(t.chunk);
     if (t.kind == kTaskGemm1) {
       // GEMM1 + SwiGLU tile of wave t.wave (its A rows pulled from the staging x)
-      const int row0 = A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * G1Cfg::BT;
-      const int count = min(G1Cfg::BT, A.offsets[t.expert + 1] - row0);
+      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * G1Cfg::BT);
+      const int count = uniform(min(G1Cfg::BT, A.offsets[t.expert + 1] - row0));
       gemm1_tile(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token, A.act,
                  row0, count, t.nt, A.d, A.I, lds);
       signal_add(A.sync + sched_g1done_index(S, t.mt));
     } else if (t.kind == kTaskGemm2) {
       // GEMM2 tile, once every GEMM1 tile of its m-tile is done
-      const int row0 = A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * G2Cfg::BT;
-      const int count = min(G2Cfg::BT, A.offsets[t.expert + 1] - row0);
-      wait_geq(A.sync + sched_g1done_index(S, t.mt), S.NT1, A.timeout_ticks, A.err);
+      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * G2Cfg::BT);
+      const int count = uniform(min(G2Cfg::BT, A.offsets[t.expert + 1] - row0));
+      wait_geq(A.sync + sched_g1done_index(S, t.mt), NT1, A.timeout_ticks, A.err);
       gemm2_tile(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count, t.nt,
                  A.d, A.I, lds);
       signal_add(A.sync + sched_g2done_index(S, t.wave));
     } else {
       // combine of tokens whose last local wave is t.slot - 1
       for (int w = 0; w <= t.slot - 1; ++w)
-        wait_geq(A.sync + sched_g2done_index(S, w), S.n_g2[w], A.timeout_ticks, A.err);
-      const int base = A.ready_off[t.slot] + t.chunk * kCombineTokens;
-      const int end = min(base + kCombineTokens, A.ready_off[t.slot + 1]);
-      for (int i = base + wave_id(); i < end; i += 4)
+        wait_geq(A.sync + sched_g2done_index(S, w), uniform(S.n_g2[w]), A.timeout_ticks, A.err);
+      const int base = uniform(A.ready_off[t.slot] + t.chunk * kCombineTokens);
+      const int end = uniform(min(base + kCombineTokens, A.ready_off[t.slot + 1]));
+      for (int i = base + wave_uniform(); i < end; i += 4)
         combine_token<OUT_BF16>(A.ready_list[i], A.y, A.pair_pos, A.topk_w, A.k, A.d, A.out);
       __syncthreads();
     }

@@ -101,6 +101,13 @@ __host__ __device__ inline PackedLayout packed_layout(int d, int I, int E_global
 
 // ------------------------------------------------------------------ misc
 
+// Marks a value as the same in every lane (it must be: e.g. read from LDS
+// after a barrier).  Loops and branches that contain barriers must be
+// steered by such values only: if the compiler sees a divergent condition
+// it may restructure the loop per lane, and lanes of one wavefront then
+// execute different iterations between barriers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 

@@ -42,22 +42,25 @@ __global__ __launch_bounds__(256) void wgrad_dh_kernel(
   build_mtile_prefix(offsets, E_local, DhCfg13::BT, mt_pre);
   __syncthreads();
   const int NT = I / 64;
-  const int total = mt_pre[E_local] * NT;
+  const int total = uniform(mt_pre[E_local] * NT);
   const int lane = lane_id(), wave = wave_id();
   const int wr = wave / 2, wt = wave % 2;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
-    const int e = expert_of_mtile(mt_pre, 0, E_local, mt);
-    const int row0 = offsets[e] + (mt - mt_pre[e]) * 128;
-    const int count = min(128, offsets[e + 1] - row0);
-    if (threadIdx.x < 128) {
+    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * 128);
+    const int count = uniform(min(128, offsets[e + 1] - row0));
+    {
+      // router weight of each row of the tile (threads 128..255 duplicate
+      // threads 0..127 and store the same value: no divergent branch here)
+      const int r = threadIdx.x & 127;
+      const int row = row0 + min(r, count - 1), t = sorted_token[row];
       float w = 0.f;
-      if (static_cast<int>(threadIdx.x) < count) {
-        const int row = row0 + threadIdx.x, t = sorted_token[row];
-        for (int j = 0; j < k; ++j)
-          if (pair_pos[static_cast<size_t>(t) * k + j] == row) w = topk_w[static_cast<size_t>(t) * k + j];
+      for (int j = 0; j < k; ++j) {
+        const bool hit = pair_pos[static_cast<size_t>(t) * k + j] == row;
+        w = hit ? topk_w[static_cast<size_t>(t) * k + j] : w;
       }
-      wrow[threadIdx.x] = w;
+      wrow[r] = r < count ? w : 0.f;
     }
     // h1, h3: exactly the forward GEMM1 tile
     const uint16_t* trx[DhCfg13::LT];
@@ -125,7 +128,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 // D[u][v] = sum_r P[r][u] * Q[r][v] over rows r of one chunk, written to
 // out[v * Udim + u] (fp32).  P and Q rows are either direct (row index r)
 // or gathered through sorted_token.
-__device__ void wgrad_tile(const uint16_t* __restrict__ P, bool p_gather, int p_ld, int Udim,
+__device__ __forceinline__ void wgrad_tile(const uint16_t* __restrict__ P, bool p_gather, int p_ld, int Udim,
                            const uint16_t* __restrict__ Q, bool q_gather, int q_ld, int Vdim,
                            const int32_t* __restrict__ sorted_token, int rbeg, int rend, int ut,
                            int vt, float* __restrict__ out, uint16_t* lds) {
@@ -172,7 +175,7 @@ __device__ void wgrad_tile(const uint16_t* __restrict__ P, bool p_gather, int p_
       st16(st + ((u / 16) * 2 + ks) * 512 + (slot_hi + (u % 16)) * 8, tr[uu]);
     }
   };
-  const int nk = (rend - rbeg + 63) / 64;
+  const int nk = uniform((rend - rbeg + 63) / 64);
   if (nk > 0) {
     gload(rbeg);
     lstore(0);
@@ -239,20 +242,21 @@ __global__ __launch_bounds__(256) void wgrad_w_kernel(
   }
   __syncthreads();
   const size_t mat = static_cast<size_t>(d) * I;
-  for (int task = blockIdx.x; task < task_pre[E_local]; task += gridDim.x) {
-    const int e = expert_of_mtile(task_pre, 0, E_local, task);
-    int rel = task - task_pre[e];
+  const int total = uniform(task_pre[E_local]);
+  for (int task = blockIdx.x; task < total; task += gridDim.x) {
+    const int e = uniform(expert_of_mtile(task_pre, 0, E_local, task));
+    int rel = task - uniform(task_pre[e]);
     const int c = rel / (3 * tpm);
     rel %= 3 * tpm;
     const int m = rel / tpm, t = rel % tpm;
-    const int r0 = offsets[e], rows = offsets[e + 1] - r0;
+    const int r0 = uniform(offsets[e]), rows = uniform(offsets[e + 1]) - r0;
     const int rbeg = r0 + c * kWgradChunkRows;
     const int rend = r0 + min(rows, (c + 1) * kWgradChunkRows);
     float* base;
     if (c == 0) {
       base = (m == 0 ? dW1 : m == 1 ? dW3 : dW2) + e * mat;
     } else {
-      base = partial + (static_cast<size_t>(slot_pre[e] + c - 1) * 3 + m) * mat;
+      base = partial + (static_cast<size_t>(uniform(slot_pre[e]) + c - 1) * 3 + m) * mat;
     }
     if (m < 2) {
       const int ut = t % tI, vt = t / tI;
