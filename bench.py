@@ -1,0 +1,231 @@
+"""Benchmark of one GPU's share of the expert-parallel MoE layer.
+
+Default workload (the mid layer): T=4096 tokens, d=4096, I=1024, 16 experts,
+top-4, 4 experts per wave, bf16 with fp32 accumulation; synthetic seeded
+inputs (x ~ N(0,1), weights ~ N(0, 0.02)).  A step is one pass of the layer's
+hot path over the batch: router, dispatch, and the persistent expert-wave
+kernel (pull, GEMM1 + SwiGLU, GEMM2, fused combine), all inputs resident in
+HBM.  One JSON line is printed on stdout.
+
+    python bench.py [--steps K] [--warmup W] [--workload mid|v4share|decode|stress]
+                    [--T T] [--no-cpu] [--serial]
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mid")
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--serial", action="store_true", help="time the phase-by-phase path")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, wl, target_s):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: the first n tokens of the batch through route, dispatch,
+    expert FFN and combine; n grows until about target_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    x = oracle.decode_bf16(inp["x"]) if inp["x"].dtype == np.uint16 else inp["x"].astype(np.float64)
+    Wg = oracle.decode_bf16(inp["Wg"]) if inp["Wg"].dtype == np.uint16 else inp["Wg"].astype(np.float64)
+    W1 = oracle.decode_bf16(inp["W1"])
+    W3 = oracle.decode_bf16(inp["W3"])
+    W2 = oracle.decode_bf16(inp["W2"])
+    bias = inp.get("bias")
+    n, spent, done = 32, 0.0, 0
+    while True:
+        n = min(n, x.shape[0])
+        t0 = time.perf_counter()
+        oracle.forward(x[:n], Wg, bias, W1, W3, W2, wl.k, wl.e_begin, wl.E_local, wl.G)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done = n
+        if spent >= target_s or n == x.shape[0]:
+            break
+        n = int(min(x.shape[0], max(2 * n, n * (target_s - spent) / max(dt, 1e-3))))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {done} tokens of the {wl.name} batch, float64 numpy oracle "
+                      f"(route, dispatch, expert FFN, combine), {dt:.1f} s for the last run"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X, no collectives)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from combine_wave_level_amd import moe
+    from workloads import get, make_inputs
+
+    wl = get(args.workload)
+    T = args.T if args.T is not None else wl.T
+    inp = make_inputs(wl, T=T)
+    dev = torch.device("cuda:0")
+
+    def d(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    xdt = moe.MOE_F32 if wl.dtype == "f32" else moe.MOE_BF16
+    p = moe.problem(T=T, d=wl.d, I=wl.I, E_global=wl.E_global, k=wl.k, e_begin=wl.e_begin,
+                    E_local=wl.E_local, experts_per_wave=wl.G, x_dtype=xdt, w_dtype=xdt, out_dtype=xdt)
+    x = d(inp["x"])
+    bias = d(inp["bias"]) if inp.get("bias") is not None else None
+    packed = moe.pack_weights(p, d(inp["Wg"]), d(inp["W1"]), d(inp["W3"]), d(inp["W2"]))
+    ws = moe.workspace(p)
+    idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, wl.k), dtype=torch.float32, device=dev)
+    disp = moe.Dispatch(
+        counts=torch.empty(wl.E_local, dtype=torch.int32, device=dev),
+        offsets=torch.empty(wl.E_local + 1, dtype=torch.int32, device=dev),
+        sorted_token=torch.empty(max(1, moe.p_max(p)), dtype=torch.int32, device=dev),
+        pair_pos=torch.empty((T, wl.k), dtype=torch.int32, device=dev),
+        ready_wave=torch.empty(T, dtype=torch.int32, device=dev))
+    y = torch.empty((max(1, moe.p_max(p)), wl.d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, wl.d), dtype=torch.bfloat16 if xdt == moe.MOE_BF16 else torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    L = moe.lib()
+    import ctypes
+    pp = ctypes.byref(p)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def P(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def check(st, where):
+        if st != moe.MOE_OK:
+            raise moe.MoEError(st, where)
+
+    nws = ws.numel()
+    flags = moe.MOE_FLAG_SERIAL if args.serial else 0
+
+    def step(ev=None, fl=flags):
+        if ev is not None:
+            ev[0].record(stream)
+        check(L.moe_route(pp, P(x), P(packed), P(bias), P(idx), P(w), None, P(ws), nws, sp), "route")
+        if ev is not None:
+            ev[1].record(stream)
+        check(L.moe_dispatch(pp, P(idx), P(disp.counts), P(disp.offsets), P(disp.sorted_token),
+                             P(disp.pair_pos), P(disp.ready_wave), P(ws), nws, sp), "dispatch")
+        if ev is not None:
+            ev[2].record(stream)
+        check(L.moe_expert_ffn_waved(pp, P(x), P(packed), P(disp.offsets), P(disp.sorted_token),
+                                     P(disp.pair_pos), P(w), P(disp.ready_wave), P(y), P(out), fl,
+                                     P(ws), nws, sp), "ffn")
+        if ev is not None:
+            ev[3].record(stream)
+
+    def timed(nsteps, fl):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(nsteps):
+            step(evs[i], fl)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        route = sum(e[0].elapsed_time(e[1]) for e in evs) / nsteps
+        disp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / nsteps
+        ffn = sum(e[2].elapsed_time(e[3]) for e in evs) / nsteps
+        return total / nsteps, route, disp_ms, ffn
+
+    for _ in range(max(0, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    moe.check_error(ws)
+    ms, route_ms, disp_ms, ffn_ms = timed(args.steps, flags)
+    moe.check_error(ws)
+
+    counts = disp.counts.cpu().numpy().astype(np.int64)
+    P_local = int(counts.sum())
+    flops_ffn = 6.0 * wl.d * wl.I * P_local
+    touched = int((counts > 0).sum())
+    weight_bytes = touched * 3.0 * wl.d * wl.I * 2
+    act_bytes = 2.0 * wl.d * (T + 2 * P_local + T)  # x read, y written and read, out written
+    tflops = flops_ffn / (ffn_ms * 1e-3) / 1e12
+    gbs = (weight_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
+    mfma_bound = flops_ffn / (PEAK_BF16_TFLOPS * 1e12) >= (weight_bytes + act_bytes) / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = "ffn_waved_kernel" if not args.serial else "gemm1_phase_kernel+gemm2_phase_kernel+combine_kernel"
+    roof["traffic"] = None
+
+    extra = {"route_ms": round(route_ms, 4), "dispatch_ms": round(disp_ms, 4), "ffn_ms": round(ffn_ms, 4),
+             "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+             "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched}
+    if not args.serial:
+        s_ms, _, _, s_ffn = timed(max(3, args.steps // 4), moe.MOE_FLAG_SERIAL)
+        extra["serial_ms_per_step"] = round(s_ms, 4)
+        extra["serial_ffn_ms"] = round(s_ffn, 4)
+        extra["overlap_speedup_ffn"] = round(s_ffn / ffn_ms, 3)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if xdt == moe.MOE_BF16 else "f32",
+        "data": "synthetic (seeded x ~ N(0,1), weights ~ N(0,0.02), random-init)",
+        "config": {"workload": f"{wl.name}: T={T} d={wl.d} I={wl.I} experts {wl.E_local} local of "
+                               f"{wl.E_global}, top-{wl.k}, {wl.G} experts per wave, "
+                               f"{'serial phases' if args.serial else 'persistent expert-wave kernel'}",
+                   "T": T, "d": wl.d, "I": wl.I, "E_global": wl.E_global, "E_local": wl.E_local,
+                   "k": wl.k, "experts_per_wave": wl.G},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
