@@ -10,16 +10,21 @@
 // On one MI355X the "communication" phases are HBM traffic:
 //   dispatch pull : GEMM1's operand loader gathers x rows by sorted_token
 //                   from the token-order staging buffer straight into LDS;
-//   combine       : tokens whose last local expert has finished are summed
+//   combine       : tokens whose last local wave has finished are summed
 //                   back into token order while later waves still compute.
-// The persistent kernel claims tasks from one ticket counter in a static
-// order; block b of that order holds GEMM1 tiles of wave b, GEMM2 tiles of
-// wave b-1 and combine tasks of the tokens that became ready after wave b-2,
-// so every wait is on work ticketed one block earlier.  A task only ever
-// waits on tasks with smaller tickets, which are held by running
-// workgroups, so the schedule cannot deadlock whatever the grid size.
-// Tickets decide which workgroup runs a tile, never the arithmetic: the
-// result bits equal those of the phase-by-phase kernels (MOE_FLAG_SERIAL).
+// The persistent kernel claims tasks from per-XCD ticket streams in the
+// static order of wave_sched.h.  Tickets decide which workgroup runs a tile,
+// never the arithmetic: the result bits equal those of the phase-by-phase
+// kernels (MOE_FLAG_SERIAL).
+//
+// Coherence on an 8-XCD device (each XCD has its own L2):
+//   GEMM1 -> GEMM2 of one m-tile stay on one XCD.  The producer waits for
+//   its stores to reach the L2 (vmcnt) and bumps a counter; the consumer
+//   polls it and drops its CU's L1 copies.  No L2 write-back or invalidate.
+//   GEMM2 -> combine crosses XCDs.  The last GEMM2 tile of a wave on an XCD
+//   writes that L2 back once (agent-scope release) and adds the XCD's tile
+//   count to a device-wide counter; combine tasks wait for the device-wide
+//   counters and read y with device-coherent (sc1) loads.
 #include "ffn_parts.h"
 #include "moe_internal.h"
 #include "wave_sched.h"
@@ -46,40 +51,44 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, size_t n) {
 
 // ---------------------------------------------------------------- phase kernels
 
+template <class F>
 __global__ __launch_bounds__(256) void gemm1_phase_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     uint16_t* __restrict__ act, int E_local, int d, int I) {
+  using C = typename F::G1;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
-  build_mtile_prefix(offsets, E_local, G1Cfg::BT, mt_pre);
+  build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   __syncthreads();
-  const int NT = 2 * I / G1Cfg::BW;
+  const int NT = 2 * I / C::BW;
   const int total = uniform(mt_pre[E_local] * NT);
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
-    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * G1Cfg::BT);
-    const int count = uniform(min(G1Cfg::BT, offsets[e + 1] - row0));
-    gemm1_tile(xb, w13 + static_cast<size_t>(e) * 2 * I * d, sorted_token, act, row0, count, nt, d, I, lds);
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
+    const int count = uniform(min(C::BT, offsets[e + 1] - row0));
+    gemm1_tile<C>(xb, w13 + static_cast<size_t>(e) * 2 * I * d, sorted_token, act, row0, count, nt, d, I, lds);
   }
 }
 
+template <class F>
 __global__ __launch_bounds__(256) void gemm2_phase_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offsets, uint16_t* __restrict__ y, int E_local, int d, int I) {
+  using C = typename F::G2;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
-  build_mtile_prefix(offsets, E_local, G2Cfg::BT, mt_pre);
+  build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   __syncthreads();
-  const int NT = d / G2Cfg::BW;
+  const int NT = d / C::BW;
   const int total = uniform(mt_pre[E_local] * NT);
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
-    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * G2Cfg::BT);
-    const int count = uniform(min(G2Cfg::BT, offsets[e + 1] - row0));
-    gemm2_tile(act, w2 + static_cast<size_t>(e) * d * I, y, row0, count, nt, d, I, lds);
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
+    const int count = uniform(min(C::BT, offsets[e + 1] - row0));
+    gemm2_tile<C>(act, w2 + static_cast<size_t>(e) * d * I, y, row0, count, nt, d, I, lds);
   }
 }
 
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ topk_w, int T,
                                                       int k, int d, void* __restrict__ out) {
   const int t = blockIdx.x * 4 + wave_id();
-  if (t < T) combine_token<OUT_BF16>(t, y, pair_pos, topk_w, k, d, out);
+  if (t < T) combine_token<OUT_BF16, false>(t, y, pair_pos, topk_w, k, d, out);
 }
 
 // ---------------------------------------------------------------- persistent
@@ -110,15 +119,16 @@ struct WaveArgs {
   uint16_t* act;
   uint16_t* y;
   void* out;                 // nullptr: no fused combine
-  int32_t* sync;             // counters, layout in wave_sched.h
+  int32_t* ctr;              // counters, layout in wave_sched.h
   int32_t* err;
   int E_local, G, W, d, I, k;
+  int region_words;
   long long timeout_ticks;   // bound of each wait, in wall-clock ticks
 };
 
-// The three primitives below are the only cross-workgroup operations of
-// the persistent kernel.  They are called by all threads, inside the task
-// loop that also contains the tiles' barriers, so none of them contains a
+// The primitives below are the only cross-workgroup operations of the
+// persistent kernel.  They are called by all threads, inside the task loop
+// that also contains the tiles' barriers, so none of them contains a
 // lane-divergent branch: "one thread does X" is written as a wave-uniform
 // branch on wave 0 with the lane selection folded into the operand.  (A
 // lane-divergent if around the counter atomics lets the compiler move that
@@ -127,29 +137,30 @@ struct WaveArgs {
 
 __device__ __forceinline__ int wave_uniform() { return uniform(static_cast<int>(threadIdx.x) / kWave); }
 
-// Claims the next ticket for the workgroup.
+__device__ __forceinline__ int xcc_id() {
+  // HW_REG_XCC_ID (hardware register 20), bits [3:0]
+  return static_cast<int>(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11))) & (kXcds - 1);
+}
+
+// Adds v (taken from lane 0) to *p; returns the old value to the whole wave.
+__device__ __forceinline__ int wave0_atomic_add(int32_t* p, int v) {
+  const int r = __hip_atomic_fetch_add(p, lane_id() == 0 ? v : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return uniform(__shfl(r, 0, kWave));
+}
+
+// Claims the next ticket of this XCD's stream for the workgroup.
 __device__ __forceinline__ int claim_ticket(int32_t* ticket, int32_t* s_ticket) {
-  if (wave_uniform() == 0) {
-    // one increment per workgroup: lane 0 adds 1, the other lanes add 0
-    const int v = __hip_atomic_fetch_add(ticket, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    // lane 0's pre-op value; every lane stores the same value
-    *s_ticket = __shfl(v, 0, kWave);
-  }
+  if (wave_uniform() == 0) *s_ticket = wave0_atomic_add(ticket, 1);
   __syncthreads();
   const int tk = uniform(*s_ticket);
   __syncthreads();
   return tk;
 }
 
-// Bounded wait until *p >= target.  Wave 0 polls with relaxed loads,
-// sleeping between polls: no cache maintenance inside the loop (an acquire
-// per poll would invalidate the L2's non-local lines on every iteration and
-// starve the producers).  The wait is bounded by wall-clock ticks; on
-// expiry MOE_ERR_TIMEOUT is recorded and the wait ends (results are then
-// invalid, but the kernel still drains).  After the barrier every wave
-// performs one agent-scope acquire.
-__device__ __forceinline__ void wait_geq(const int32_t* p, int target, long long timeout_ticks,
+// Bounded poll by wave 0 until *p >= target.  Relaxed loads only: no cache
+// maintenance inside the loop.  On expiry MOE_ERR_TIMEOUT is recorded and
+// the wait ends (results are then invalid, but the kernel still drains).
+__device__ __forceinline__ void poll_geq(const int32_t* p, int target, long long timeout_ticks,
                                          int32_t* err) {
   if (wave_uniform() == 0) {
     if (uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
@@ -160,37 +171,46 @@ __device__ __forceinline__ void wait_geq(const int32_t* p, int target, long long
                              __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
-        __builtin_amdgcn_s_sleep(8);
+        __builtin_amdgcn_s_sleep(4);
       }
     }
   }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Publish this workgroup's finished global stores, then count them: every
-// wave releases its own stores at agent scope, the barrier orders those
-// releases before the increment.
-__device__ __forceinline__ void signal_add(int32_t* p) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// XCD-local producer side: every wave's stores have reached the (shared)
+// L2 before the counter moves.
+__device__ __forceinline__ void local_signal(int32_t* p) {
+  wait_vmcnt<0>();
   __syncthreads();
-  if (wave_uniform() == 0)
-    __hip_atomic_fetch_add(p, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave_uniform() == 0) wave0_atomic_add(p, 1);
 }
 
-template <bool OUT_BF16>
+// XCD-local consumer side: after the counter is reached, drop this CU's L1
+// lines so the following loads come from the L2 the producer wrote.
+__device__ __forceinline__ void local_wait(const int32_t* p, int target, long long timeout_ticks,
+                                           int32_t* err) {
+  poll_geq(p, target, timeout_ticks, err);
+  __syncthreads();
+  asm volatile("buffer_inv sc0" ::: "memory");
+}
+
+template <class F, bool OUT_BF16>
 __global__ __launch_bounds__(256) void ffn_waved_kernel(WaveArgs A) {
+  using C1 = typename F::G1;
+  using C2 = typename F::G2;
+  static_assert(C1::BT == C2::BT, "GEMM1 and GEMM2 share the m-tiles");
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ WaveSchedule S;
   __shared__ int32_t s_ticket;
-  static_assert(G1Cfg::BT == G2Cfg::BT, "GEMM1 and GEMM2 share the m-tiles");
+  const int xcd = uniform(xcc_id());
   if (threadIdx.x == 0)
-    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, G1Cfg::BT, 2 * A.I / G1Cfg::BW,
-                A.d / G2Cfg::BW, A.out != nullptr);
+    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
+                A.out != nullptr, xcd);
   __syncthreads();
   const int total = uniform(S.total);
   const int NT1 = uniform(S.NT1);
-  int32_t* ticket = A.sync;
+  const int rw = A.region_words;
+  int32_t* ticket = A.ctr + sched_ticket_index(xcd);
 
   // Every value that steers this loop is made wave-uniform explicitly (the
   // ticket and the decoded task come from LDS), so all waves run the same
@@ -205,73 +225,81 @@ __global__ __launch_bounds__(256) void ffn_waved_kernel(WaveArgs A) {
     t.slot = uniform(t.slot);
     t.chunk = uniform(t.chunk);
     if (t.kind == kTaskGemm1) {
-      // GEMM1 + SwiGLU tile of wave t.wave (its A rows pulled from the staging x)
-      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * G1Cfg::BT);
-      const int count = uniform(min(G1Cfg::BT, A.offsets[t.expert + 1] - row0));
-      gemm1_tile(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token, A.act,
-                 row0, count, t.nt, A.d, A.I, lds);
-      signal_add(A.sync + sched_g1done_index(S, t.mt));
+      // GEMM1 + SwiGLU tile (its operand rows pulled from the staging x)
+      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * C1::BT);
+      const int count = uniform(min(C1::BT, A.offsets[t.expert + 1] - row0));
+      gemm1_tile<C1>(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token,
+                     A.act, row0, count, t.nt, A.d, A.I, lds);
+      local_signal(A.ctr + sched_g1done_index(S, rw, t.mt));
     } else if (t.kind == kTaskGemm2) {
-      // GEMM2 tile, once every GEMM1 tile of its m-tile is done
-      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * G2Cfg::BT);
-      const int count = uniform(min(G2Cfg::BT, A.offsets[t.expert + 1] - row0));
-      wait_geq(A.sync + sched_g1done_index(S, t.mt), NT1, A.timeout_ticks, A.err);
-      gemm2_tile(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count, t.nt,
-                 A.d, A.I, lds);
-      signal_add(A.sync + sched_g2done_index(S, t.wave));
+      // GEMM2 tile, once every GEMM1 tile of its m-tile is done (same XCD)
+      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * C2::BT);
+      const int count = uniform(min(C2::BT, A.offsets[t.expert + 1] - row0));
+      local_wait(A.ctr + sched_g1done_index(S, rw, t.mt), NT1, A.timeout_ticks, A.err);
+      gemm2_tile<C2>(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count,
+                     t.nt, A.d, A.I, lds);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (wave_uniform() == 0) {
+        const int mine = uniform(S.n_g2[t.wave]);
+        const int done = wave0_atomic_add(A.ctr + sched_g2local_index(S, rw, t.wave), 1) + 1;
+        if (done == mine) {
+          // last GEMM2 tile of this wave on this XCD: write the L2 back once,
+          // then publish the XCD's tiles device-wide
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          wave0_atomic_add(A.ctr + sched_g2all_index(S, rw, t.wave), mine);
+        }
+      }
     } else {
       // combine of tokens whose last local wave is t.slot - 1
       for (int w = 0; w <= t.slot - 1; ++w)
-        wait_geq(A.sync + sched_g2done_index(S, w), uniform(S.n_g2[w]), A.timeout_ticks, A.err);
+        poll_geq(A.ctr + sched_g2all_index(S, rw, w), uniform(S.g2_all[w]), A.timeout_ticks, A.err);
+      __syncthreads();
       const int base = uniform(A.ready_off[t.slot] + t.chunk * kCombineTokens);
       const int end = uniform(min(base + kCombineTokens, A.ready_off[t.slot + 1]));
       for (int i = base + wave_uniform(); i < end; i += 4)
-        combine_token<OUT_BF16>(A.ready_list[i], A.y, A.pair_pos, A.topk_w, A.k, A.d, A.out);
+        combine_token<OUT_BF16, true>(A.ready_list[i], A.y, A.pair_pos, A.topk_w, A.k, A.d, A.out);
       __syncthreads();
     }
   }
 }
 
-}  // namespace
+// Mean routed rows per local expert, assuming uniform routing: picks the
+// tile shape.  The shape never changes result bits.
+bool use_small_tiles(const moe_problem_t& p) {
+  const double rows = static_cast<double>(p.T) * p.k / p.E_global;
+  return rows < 96.0 && p.d % FfnSmall::G1::BK == 0 && p.I % FfnSmall::G2::BK == 0 &&
+         (2 * p.I) % FfnSmall::G1::BW == 0 && p.d % FfnSmall::G2::BW == 0;
+}
 
-hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
-                      const int32_t* offsets, const int32_t* sorted_token, const int32_t* pair_pos,
-                      const float* topk_w, const int32_t* ready_wave, void* y, void* out,
-                      uint32_t flags, char* ws, hipStream_t s) {
-  (void)ready_wave;
-  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
-  const char* pk = static_cast<const char*>(packed);
-  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
-  const uint16_t* w2 = reinterpret_cast<const uint16_t*>(pk + PL.w2);
-  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
-  const bool out_bf16 = p.out_dtype == MOE_BF16;
-  const uint16_t* xb = nullptr;
+template <class F>
+hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint16_t* xb,
+                          const uint16_t* w13, const uint16_t* w2, const int32_t* offsets,
+                          const int32_t* sorted_token, const int32_t* pair_pos, const float* topk_w,
+                          void* y, void* out, uint32_t flags, char* ws, hipStream_t s) {
   hipError_t e;
-  if ((e = stage_x_bf16(p, L, x, ws, s, &xb)) != hipSuccess) return e;
   int dev = 0, cus = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-
+  const bool out_bf16 = p.out_dtype == MOE_BF16;
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   if (flags & MOE_FLAG_SERIAL) {
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel, 256, kFfnLds)) != hipSuccess)
+    constexpr size_t l1 = F::G1::LDS_BYTES, l2 = F::G2::LDS_BYTES;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel<F>, 256, l1)) != hipSuccess)
       return e;
-    const int grid = max(1, per_cu) * cus;
-    gemm1_phase_kernel<<<grid, 256, kFfnLds, s>>>(xb, w13, offsets, sorted_token, act, p.E_local, p.d, p.I);
+    gemm1_phase_kernel<F><<<max(1, per_cu) * cus, 256, l1, s>>>(xb, w13, offsets, sorted_token, act,
+                                                                 p.E_local, p.d, p.I);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    gemm2_phase_kernel<<<grid, 256, kFfnLds, s>>>(act, w2, offsets, static_cast<uint16_t*>(y), p.E_local, p.d, p.I);
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm2_phase_kernel<F>, 256, l2)) != hipSuccess)
+      return e;
+    gemm2_phase_kernel<F><<<max(1, per_cu) * cus, 256, l2, s>>>(act, w2, offsets, static_cast<uint16_t*>(y),
+                                                                 p.E_local, p.d, p.I);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (out && p.T > 0) {
-      if (out_bf16)
-        combine_kernel<true><<<(p.T + 3) / 4, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_pos, topk_w, p.T, p.k, p.d, out);
-      else
-        combine_kernel<false><<<(p.T + 3) / 4, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_pos, topk_w, p.T, p.k, p.d, out);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if (out && p.T > 0) return launch_combine(p, y, pair_pos, topk_w, out, s);
     return hipSuccess;
   }
-
-  int32_t* sync = reinterpret_cast<int32_t*>(ws + L.sync);
-  if ((e = fill_zero(sync, L.sync_words, s)) != hipSuccess) return e;
+  int32_t* ctr = reinterpret_cast<int32_t*>(ws + L.sync);
+  if ((e = fill_zero(ctr, L.sync_words, s)) != hipSuccess) return e;
   WaveArgs A;
   A.xb = xb;
   A.w13 = w13;
@@ -285,7 +313,7 @@ hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, 
   A.act = act;
   A.y = static_cast<uint16_t*>(y);
   A.out = out;
-  A.sync = sync;
+  A.ctr = ctr;
   A.err = reinterpret_cast<int32_t*>(ws + L.err);
   A.E_local = p.E_local;
   A.G = p.experts_per_wave;
@@ -293,15 +321,18 @@ hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, 
   A.d = p.d;
   A.I = p.I;
   A.k = p.k;
+  A.region_words = L.ctr_region_words;
   int wall_khz = 0;
   if ((e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
   A.timeout_ticks = static_cast<long long>(max(wall_khz, 1)) * 1000ll * kWaitTimeoutSeconds;
-  auto kern = out_bf16 ? ffn_waved_kernel<true> : ffn_waved_kernel<false>;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, kFfnLds)) != hipSuccess) return e;
-  const int grid = max(1, per_cu) * cus;
-  kern<<<grid, 256, kFfnLds, s>>>(A);
+  auto kern = out_bf16 ? ffn_waved_kernel<F, true> : ffn_waved_kernel<F, false>;
+  constexpr size_t lds = ffn_lds_bytes<F>();
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds)) != hipSuccess) return e;
+  kern<<<max(1, per_cu) * cus, 256, lds, s>>>(A);
   return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t fill_zero(void* p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
@@ -318,6 +349,28 @@ hipError_t stage_x_bf16(const moe_problem_t& p, const WsLayout& L, const void* x
       static_cast<const float*>(x), reinterpret_cast<uint16_t*>(ws + L.xbf), n);
   *xb = reinterpret_cast<const uint16_t*>(ws + L.xbf);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
+                      const int32_t* offsets, const int32_t* sorted_token, const int32_t* pair_pos,
+                      const float* topk_w, const int32_t* ready_wave, void* y, void* out,
+                      uint32_t flags, char* ws, hipStream_t s) {
+  (void)ready_wave;
+  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
+  const char* pk = static_cast<const char*>(packed);
+  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
+  const uint16_t* w2 = reinterpret_cast<const uint16_t*>(pk + PL.w2);
+  const uint16_t* xb = nullptr;
+  hipError_t e;
+  if ((e = stage_x_bf16(p, L, x, ws, s, &xb)) != hipSuccess) return e;
+  if (use_small_tiles(p))
+    return launch_ffn_cfg<FfnSmall>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
+                                    flags, ws, s);
+  if ((2 * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G2::BW == 0)
+    return launch_ffn_cfg<FfnLarge>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
+                                    flags, ws, s);
+  return launch_ffn_cfg<FfnMid>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
+                                flags, ws, s);
 }
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,

@@ -13,11 +13,28 @@
 
 namespace moe {
 
-// Tile shapes of the expert GEMMs.  BT tokens (pair rows) by BW output
-// features, 4 wavefronts as 2 x 2.
-using G1Cfg = TileCfg<128, 128, 2, 2>;
-using G2Cfg = TileCfg<128, 128, 2, 2>;
-constexpr size_t kFfnLds = G1Cfg::LDS_BYTES > G2Cfg::LDS_BYTES ? G1Cfg::LDS_BYTES : G2Cfg::LDS_BYTES;
+// Tile shapes of the expert GEMMs (BW output features x BT pair rows).  The
+// shape only decides which workgroup computes which outputs; every shape
+// runs the same per-element instruction sequence over K.
+//   large : many rows per expert (MFMA bound)
+//   small : a handful of rows per expert (weight streaming, HBM bound)
+//   mid   : any shape the boundary accepts (d % 128 == 0, I % 64 == 0)
+struct FfnLarge {
+  using G1 = TileCfg<256, 128, 2, 2, 64, 3>;
+  using G2 = TileCfg<256, 128, 2, 2, 64, 3>;
+};
+struct FfnMid {
+  using G1 = TileCfg<128, 128, 2, 2, 64, 4>;
+  using G2 = TileCfg<128, 128, 2, 2, 64, 4>;
+};
+struct FfnSmall {
+  using G1 = TileCfg<128, 16, 4, 1, 128, 3>;
+  using G2 = TileCfg<64, 16, 4, 1, 128, 4>;
+};
+template <class F>
+constexpr size_t ffn_lds_bytes() {
+  return F::G1::LDS_BYTES > F::G2::LDS_BYTES ? F::G1::LDS_BYTES : F::G2::LDS_BYTES;
+}
 constexpr int kMaxLocalExperts = 256;
 
 // Per-workgroup table: m-tile prefix over local experts (rows split into
@@ -51,24 +68,25 @@ __device__ __forceinline__ float silu_mul(float h1, float h3) {
 }
 
 // GEMM1 tile: rows [row0, row0 + BT) of expert e's segment (count rows
-// valid), output features 2*BW/2 packed rows starting at row block
-// nt * BW / 16 of W13, i.e. intermediate indices [nt * BW/2, nt * BW/2 + BW/2).
-// The A-operand rows are pulled straight from the token-order staging
-// buffer xb by sorted_token: the dispatch pull lands in LDS.
+// valid), BW packed rows of W13 starting at row block nt * BW / 16, i.e.
+// intermediate indices [nt * BW/2, nt * BW/2 + BW/2).  The operand rows are
+// pulled straight from the token-order staging buffer xb by sorted_token:
+// the dispatch pull lands in LDS.
+template <class C>
 __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            const uint16_t* __restrict__ w13e,
                                            const int32_t* __restrict__ sorted_token,
                                            uint16_t* __restrict__ act, int row0, int count, int nt,
                                            int d, int I, uint16_t* lds) {
-  using C = G1Cfg;
-  const uint16_t* trow[C::LT];
+  static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
+  TokRows<C> trow;
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
     const int r = min(trow_index<C>(i), count - 1);
-    trow[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+    trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
   }
   TileAcc<C> acc;
-  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / 64, trow, lds, acc);
+  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc);
   const int lane = lane_id(), wave = wave_id();
   const int wr = wave / C::WT, wt = wave % C::WT;
 #pragma unroll
@@ -89,18 +107,18 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
 }
 
 // GEMM2 tile: y[row0 .. row0 + count) x features [nt * BW, nt * BW + BW).
+template <class C>
 __device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ act,
                                            const uint16_t* __restrict__ w2e, uint16_t* __restrict__ y,
                                            int row0, int count, int nt, int d, int I, uint16_t* lds) {
-  using C = G2Cfg;
-  const uint16_t* trow[C::LT];
+  TokRows<C> trow;
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
     const int r = min(trow_index<C>(i), count - 1);
-    trow[i] = act + static_cast<size_t>(row0 + r) * I;
+    trow.p[i] = act + static_cast<size_t>(row0 + r) * I;
   }
   TileAcc<C> acc;
-  tile_mma<C>(w2e + frag_offset(nt * (C::BW / 16), 0, I / 32), I / 32, I / 64, trow, lds, acc);
+  tile_mma<C>(w2e + frag_offset(nt * (C::BW / 16), 0, I / 32), I / 32, I / C::BK, trow, lds, acc);
   const int lane = lane_id(), wave = wave_id();
   const int wr = wave / C::WT, wt = wave % C::WT;
 #pragma unroll
@@ -119,9 +137,24 @@ __device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ act,
   }
 }
 
+// 16 bytes of row r of y at element offset c8.  COHERENT: a device-coherent
+// (sc1) load, for y rows another XCD wrote during the same kernel.
+template <bool COHERENT>
+__device__ __forceinline__ u32x4 load_y16(const uint16_t* __restrict__ y, int r, int d, int c8) {
+  const uint16_t* row = y + static_cast<size_t>(r) * d;
+  if constexpr (COHERENT) {
+    // buffer resource over the row: base, stride 0, d * 2 bytes, raw 32-bit format
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row), 0, d * 2, 0x00020000);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, c8 * 2, 0, 16));
+  } else {
+    return ld16(row + c8);
+  }
+}
+
 // Combine of token t by one wavefront: out[t] = sum_j w[t, j] * y[pair_pos[t, j]]
 // over local picks, fp32 fused multiply-adds in ascending j, one rounding.
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool COHERENT>
 __device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict__ y,
                                               const int32_t* __restrict__ pair_pos,
                                               const float* __restrict__ topk_w, int k, int d,
@@ -133,7 +166,7 @@ __device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict_
       const int r = pair_pos[static_cast<size_t>(t) * k + j];
       if (r < 0) continue;
       const float w = topk_w[static_cast<size_t>(t) * k + j];
-      const u32x4 v = ld16(y + static_cast<size_t>(r) * d + c * 8);
+      const u32x4 v = load_y16<COHERENT>(y, r, d, c * 8);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] = fmaf(w, __uint_as_float(v[q] << 16), acc[2 * q]);

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_common.h"
 
 namespace moe {
@@ -31,6 +31,7 @@ namespace moe {
 struct WsLayout {
   size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, wgrad, total;
   int nchunks, W, ngroups, P_max;
+  int ctr_region_words;  // per-XCD counter region of the persistent kernel
   size_t sync_words, wgrad_bytes;
 };
 

@@ -28,14 +28,14 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
   const int nblk_e = (E + C::BW - 1) / C::BW;
   const int et = blockIdx.x % nblk_e, tt = blockIdx.x / nblk_e;
   const int t0 = tt * C::BT;
-  const uint16_t* trow[C::LT];
+  TokRows<C> trow;
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
     const int t = min(t0 + trow_index<C>(i), T - 1);
-    trow[i] = x + static_cast<size_t>(t) * d;
+    trow.p[i] = x + static_cast<size_t>(t) * d;
   }
   TileAcc<C> acc;
-  tile_mma<C>(wg + frag_offset(et * C::BW / 16, 0, d / 32), d / 32, d / 64, trow, lds, acc);
+  tile_mma<C>(wg + frag_offset(et * C::BW / 16, 0, d / 32), d / 32, d / C::BK, trow, lds, acc);
   const int lane = lane_id(), wave = wave_id();
   const int wr = wave / C::WT, wt = wave % C::WT;
 #pragma unroll
@@ -155,11 +155,11 @@ hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packe
   if (xbf) {
     const uint16_t* wg = reinterpret_cast<const uint16_t*>(base + L.router);
     if (p.E_global <= 32)
-      e = launch_logits_mfma<TileCfg<32, 128, 1, 4>>(p, x, wg, bias, logits, s);
+      e = launch_logits_mfma<TileCfg<32, 128, 1, 4, 64, 3>>(p, x, wg, bias, logits, s);
     else if (p.E_global <= 64)
-      e = launch_logits_mfma<TileCfg<64, 128, 2, 2>>(p, x, wg, bias, logits, s);
+      e = launch_logits_mfma<TileCfg<64, 128, 2, 2, 64, 3>>(p, x, wg, bias, logits, s);
     else
-      e = launch_logits_mfma<TileCfg<128, 128, 2, 2>>(p, x, wg, bias, logits, s);
+      e = launch_logits_mfma<TileCfg<128, 128, 2, 2, 64, 3>>(p, x, wg, bias, logits, s);
   } else {
     const size_t n = static_cast<size_t>(p.T) * p.E_global;
     router_logits_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(

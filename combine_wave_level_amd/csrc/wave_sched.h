@@ -3,16 +3,25 @@
 //
 // DeepSeek-V4 launch digest (itsolotime.com), section 1.2: in steady state
 // the compute of the current wave, the dispatch of the next wave's tokens
-// and the return of finished experts' results run at the same time.  The
-// order below realises that: block b of the ticket sequence holds
-//   GEMM1 tiles of wave b          (their operand loads are the pulls),
-//   GEMM2 tiles of wave b-1,
-//   combine tasks of ready slot b-1 (tokens whose last local wave is b-2;
-//                                    slot 0 = tokens with no local pick),
-// for b = 0 .. W+1.  A GEMM2 tile waits for the GEMM1 tiles of its m-tile
-// (ticketed one block earlier); a combine task waits for all GEMM2 tiles of
-// waves <= its slot - 1 (ticketed at least one block earlier).  Every wait
-// is on smaller tickets, so the order is deadlock free for any grid.
+// and the return of finished experts' results run at the same time.
+//
+// MI355X has 8 XCDs, each with its own L2.  The m-tiles (BT-row slices of
+// each expert's sorted rows) are split into 8 contiguous, equal ranges, one
+// per XCD, and every workgroup takes tasks only from its own XCD's ticket
+// stream.  GEMM1 -> GEMM2 dependencies therefore never leave an XCD's L2;
+// only the combine, which reads y rows of every XCD, crosses XCDs.
+//
+// Inside one XCD's stream, block b of the ticket sequence holds
+//   GEMM1 tiles of the XCD's m-tiles in wave b (their operand loads are the
+//                                              dispatch pulls),
+//   GEMM2 tiles of the XCD's m-tiles in wave b-1,
+//   the XCD's share of the combine chunks of ready slot b-1 (tokens whose
+//   last local wave is b-2; slot 0 = tokens with no local pick),
+// for b = 0 .. W+1.  A GEMM2 tile waits for its m-tile's GEMM1 tiles (same
+// stream, smaller tickets).  A combine task waits until every XCD finished
+// the GEMM2 tiles of waves <= its slot - 1; those tiles sit in blocks <=
+// slot of every stream and wait only on smaller tickets of their own
+// stream, so by induction over the waves every wait ends, for any grid.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,17 +29,21 @@
 
 namespace moe {
 
+constexpr int kXcds = 8;                // XCDs of an MI355X
 constexpr int kSchedMaxExperts = 256;
 constexpr int kSchedMaxWaves = 256;
-constexpr int kCombineTokens = 16;  // tokens per combine task
+constexpr int kCombineTokens = 16;      // tokens per combine task
+constexpr int kCtrPad = 64;             // int32 words (256 B) between counters of different XCDs
 
 struct WaveSchedule {
-  int W, G, NT1, NT2, total;
+  int W, G, NT1, NT2, total, xcd, mt_lo, mt_hi;
   int32_t mt_pre[kSchedMaxExperts + 1];  // first m-tile of each local expert
   int32_t blk_start[kSchedMaxWaves + 3]; // first ticket of block b, b = 0 .. W+2
-  int32_t n_g1[kSchedMaxWaves + 1];
-  int32_t n_g2[kSchedMaxWaves + 1];
-  int32_t n_cb[kSchedMaxWaves + 2];
+  int32_t mlo[kSchedMaxWaves];           // first m-tile of this XCD in wave w
+  int32_t n_g1[kSchedMaxWaves];          // this XCD's GEMM1 tiles of wave w
+  int32_t n_g2[kSchedMaxWaves];          // this XCD's GEMM2 tiles of wave w
+  int32_t g2_all[kSchedMaxWaves];        // GEMM2 tiles of wave w over all XCDs
+  int32_t n_cb[kSchedMaxWaves + 1];      // this XCD's combine chunks of slot s
 };
 
 enum TaskKind { kTaskGemm1 = 0, kTaskGemm2 = 1, kTaskCombine = 2 };
@@ -42,7 +55,7 @@ struct Task {
   int expert;    // local expert (GEMM1 / GEMM2)
   int nt;        // output-feature tile (GEMM1 / GEMM2)
   int slot;      // combine: ready slot
-  int chunk;     // combine: chunk of kCombineTokens tokens inside the slot
+  int chunk;     // combine: global chunk of kCombineTokens tokens inside the slot
 };
 
 // Binary search: the expert whose m-tile range holds mt, with
@@ -55,31 +68,47 @@ __host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, in
   return lo;
 }
 
-// Builds the schedule from the dispatch tables.  offsets [E_local + 1] =
-// first pair row of each local expert; ready_off [W + 2] = first position of
-// each ready slot in the ready list.  BT = rows per m-tile.  NT1 / NT2 =
+// First m-tile of XCD x when nmt m-tiles are split into kXcds equal ranges.
+__host__ __device__ inline int sched_xcd_first_mtile(int nmt, int x) {
+  return static_cast<int>((static_cast<long long>(nmt) * x) / kXcds);
+}
+
+// Builds XCD xcd's schedule from the dispatch tables.  offsets [E_local + 1]
+// = first pair row of each local expert; ready_off [W + 2] = first position
+// of each ready slot in the ready list.  BT = rows per m-tile.  NT1 / NT2 =
 // output tiles of GEMM1 / GEMM2 per m-tile.  with_combine = 0 drops the
 // combine tasks (no fused combine).
 __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offsets,
                                             const int32_t* ready_off, int E_local, int G, int BT,
-                                            int NT1, int NT2, int with_combine) {
+                                            int NT1, int NT2, int with_combine, int xcd) {
   S.W = E_local / G;
   S.G = G;
   S.NT1 = NT1;
   S.NT2 = NT2;
+  S.xcd = xcd;
   int run = 0;
   for (int e = 0; e < E_local; ++e) {
     S.mt_pre[e] = run;
     run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
   }
   S.mt_pre[E_local] = run;
+  S.mt_lo = sched_xcd_first_mtile(run, xcd);
+  S.mt_hi = sched_xcd_first_mtile(run, xcd + 1);
   for (int w = 0; w < S.W; ++w) {
-    const int mts = S.mt_pre[(w + 1) * G] - S.mt_pre[w * G];
-    S.n_g1[w] = mts * NT1;
-    S.n_g2[w] = mts * NT2;
+    const int a = S.mt_pre[w * G], b = S.mt_pre[(w + 1) * G];
+    const int lo = a > S.mt_lo ? a : S.mt_lo;
+    const int hi = b < S.mt_hi ? b : S.mt_hi;
+    const int cnt = hi > lo ? hi - lo : 0;
+    S.mlo[w] = lo;
+    S.n_g1[w] = cnt * NT1;
+    S.n_g2[w] = cnt * NT2;
+    S.g2_all[w] = (b - a) * NT2;
   }
-  for (int s = 0; s <= S.W; ++s)
-    S.n_cb[s] = with_combine ? (ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens : 0;
+  for (int s = 0; s <= S.W; ++s) {
+    const int chunks =
+        with_combine ? (ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens : 0;
+    S.n_cb[s] = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
+  }
   run = 0;
   for (int b = 0; b <= S.W + 1; ++b) {
     S.blk_start[b] = run;
@@ -91,7 +120,7 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
   S.total = run;
 }
 
-// Decodes ticket tk (0 <= tk < S.total).
+// Decodes ticket tk (0 <= tk < S.total) of this XCD's stream.
 __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   int b = 0;
   while (S.blk_start[b + 1] <= tk) ++b;
@@ -102,7 +131,7 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   if (rel < g1n) {
     t.kind = kTaskGemm1;
     t.wave = b;
-    t.mt = S.mt_pre[b * S.G] + rel / S.NT1;
+    t.mt = S.mlo[b] + rel / S.NT1;
     t.nt = rel % S.NT1;
     t.expert = sched_expert_of(S.mt_pre, b * S.G, (b + 1) * S.G, t.mt);
     return t;
@@ -111,7 +140,7 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   if (rel < g2n) {
     t.kind = kTaskGemm2;
     t.wave = b - 1;
-    t.mt = S.mt_pre[(b - 1) * S.G] + rel / S.NT2;
+    t.mt = S.mlo[b - 1] + rel / S.NT2;
     t.nt = rel % S.NT2;
     t.expert = sched_expert_of(S.mt_pre, (b - 1) * S.G, b * S.G, t.mt);
     return t;
@@ -119,13 +148,34 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   rel -= g2n;
   t.kind = kTaskCombine;
   t.slot = b - 1;
-  t.chunk = rel;
+  t.chunk = S.xcd + kXcds * rel;
   return t;
 }
 
-// Counter layout of the persistent kernel: [0] ticket, [1 .. W] GEMM2 tiles
-// finished per wave, [1 + W ..] GEMM1 tiles finished per m-tile.
-__host__ __device__ inline int sched_g2done_index(const WaveSchedule&, int w) { return 1 + w; }
-__host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int mt) { return 1 + S.W + mt; }
+// Counter layout (int32 words) of the persistent kernel.  Counters touched
+// by different XCDs never share a 256-byte span:
+//   [x * kCtrPad]                   ticket of XCD x
+//   region(x) = kXcds * kCtrPad + x * region_words:
+//     region(x) + w                 GEMM2 tiles of wave w finished on XCD x
+//     region(x) + W + (mt - mt_lo)  GEMM1 tiles of m-tile mt finished (on XCD x)
+//   kXcds * (kCtrPad + region_words) + w   GEMM2 tiles of wave w finished, all XCDs
+// region_words >= W + (m-tiles of one XCD), rounded up to kCtrPad.
+__host__ __device__ inline int sched_region_words(int W, int max_mtiles) {
+  const int per_xcd = (max_mtiles + kXcds - 1) / kXcds + 1;
+  return ((W + per_xcd + kCtrPad - 1) / kCtrPad) * kCtrPad;
+}
+__host__ __device__ inline size_t sched_counter_words(int W, int max_mtiles) {
+  return static_cast<size_t>(kXcds) * (kCtrPad + sched_region_words(W, max_mtiles)) + W + kCtrPad;
+}
+__host__ __device__ inline int sched_ticket_index(int xcd) { return xcd * kCtrPad; }
+__host__ __device__ inline int sched_g2local_index(const WaveSchedule& S, int rw, int w) {
+  return kXcds * kCtrPad + S.xcd * rw + w;
+}
+__host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int rw, int mt) {
+  return kXcds * kCtrPad + S.xcd * rw + S.W + (mt - S.mt_lo);
+}
+__host__ __device__ inline int sched_g2all_index(const WaveSchedule& S, int rw, int w) {
+  return kXcds * (kCtrPad + rw) + w;
+}
 
 }  // namespace moe

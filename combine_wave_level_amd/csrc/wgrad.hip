@@ -26,8 +26,8 @@
 namespace moe {
 namespace {
 
-using DhCfg13 = G1Cfg;                   // 128 packed rows = 64 (h1, h3) pairs
-using DhCfgG = TileCfg<64, 128, 2, 2>;   // 64 rows of W2 (as [I][d])
+using DhCfg13 = TileCfg<128, 128, 2, 2, 64, 3>;  // 128 packed rows = 64 (h1, h3) pairs
+using DhCfgG = TileCfg<64, 128, 2, 2, 64, 3>;    // 64 rows of W2 (as [I][d])
 static_assert(DhCfg13::BT == DhCfgG::BT, "same row tile");
 
 __global__ __launch_bounds__(256) void wgrad_dh_kernel(
@@ -63,24 +63,24 @@ __global__ __launch_bounds__(256) void wgrad_dh_kernel(
       wrow[r] = r < count ? w : 0.f;
     }
     // h1, h3: exactly the forward GEMM1 tile
-    const uint16_t* trx[DhCfg13::LT];
-    const uint16_t* trd[DhCfgG::LT];
+    TokRows<DhCfg13> trx;
+    TokRows<DhCfgG> trd;
 #pragma unroll
     for (int i = 0; i < DhCfg13::LT; ++i) {
       const int r = min(trow_index<DhCfg13>(i), count - 1);
-      trx[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+      trx.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
     }
 #pragma unroll
     for (int i = 0; i < DhCfgG::LT; ++i) {
       const int r = min(trow_index<DhCfgG>(i), count - 1);
-      trd[i] = dout + static_cast<size_t>(sorted_token[row0 + r]) * d;
+      trd.p[i] = dout + static_cast<size_t>(sorted_token[row0 + r]) * d;
     }
     TileAcc<DhCfg13> acc13;
     tile_mma<DhCfg13>(w13 + static_cast<size_t>(e) * 2 * I * d + frag_offset(nt * 8, 0, d / 32), d / 32,
-                      d / 64, trx, lds, acc13);
+                      d / DhCfg13::BK, trx, lds, acc13);
     TileAcc<DhCfgG> accg;
     tile_mma<DhCfgG>(w2b + static_cast<size_t>(e) * I * d + frag_offset(nt * 4, 0, d / 32), d / 32,
-                     d / 64, trd, lds, accg);
+                     d / DhCfgG::BK, trd, lds, accg);
     // wave (wr, wt): acc13 row blocks 4wr..4wr+3 = (h1, h3) pairs of
     // intermediate blocks 2wr, 2wr+1 of this tile; accg row blocks 2wr, 2wr+1.
 #pragma unroll
@@ -132,7 +132,7 @@ __device__ __forceinline__ void wgrad_tile(const uint16_t* __restrict__ P, bool 
                            const uint16_t* __restrict__ Q, bool q_gather, int q_ld, int Vdim,
                            const int32_t* __restrict__ sorted_token, int rbeg, int rend, int ut,
                            int vt, float* __restrict__ out, uint16_t* lds) {
-  using C = TileCfg<128, 128, 2, 2>;
+  using C = TileCfg<128, 128, 2, 2, 64, 2>;
   const int lane = lane_id(), wave = wave_id();
   const int wr = wave / C::WT, wt = wave % C::WT;
   // thread's 8x8 block: operand (P for tid < 128), row group rg, u group ug
@@ -331,7 +331,7 @@ hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const void* x
                                               sorted_token, pair_pos, topk_w, p.E_local, p.d, p.I, p.k,
                                               dH1, dH3, aw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  using C = TileCfg<128, 128, 2, 2>;
+  using C = TileCfg<128, 128, 2, 2, 64, 2>;
   wgrad_w_kernel<<<cus * 2, 256, C::LDS_BYTES, s>>>(xb, static_cast<const uint16_t*>(dout), dH1, dH3, aw,
                                                     offsets, sorted_token, p.E_local, p.d, p.I, dW1, dW3,
                                                     dW2, partial);

@@ -1,4 +1,4 @@
-"""CPU check of the persistent expert-wave kernel's static task order.
+"""CPU check of the persistent expert-wave kernel's static task order (8 per-XCD streams).
 
 tests/native/sched_emu.cpp includes the same host+device schedule header the
 kernel uses (combine_wave_level_amd/csrc/wave_sched.h) and checks, for the
@@ -30,7 +30,7 @@ def emu(tmp_path_factory):
     return exe
 
 
-def _run(emu, counts, ready_counts, G, NT1, NT2, with_cb=1, threads=16, seed=1):
+def _run(emu, counts, ready_counts, G, NT1, NT2, with_cb=1, threads=2, seed=1):
     E_local = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(int)
     ready_off = np.concatenate([[0], np.cumsum(ready_counts)]).astype(int)
@@ -74,19 +74,19 @@ def test_empty_experts_and_waves(emu):
     W = 4
     rng = np.random.default_rng(0)
     ready = list(rng.integers(0, 50, size=W + 1))
-    _run(emu, counts, ready, G=4, NT1=4, NT2=8, threads=32)
+    _run(emu, counts, ready, G=4, NT1=4, NT2=8, threads=4)
 
 
 def test_many_waves_one_expert_each(emu):
     rng = np.random.default_rng(1)
     counts = list(rng.integers(0, 400, size=64))
     ready = list(rng.integers(0, 30, size=65))
-    _run(emu, counts, ready, G=1, NT1=3, NT2=5, threads=48, seed=7)
+    _run(emu, counts, ready, G=1, NT1=3, NT2=5, threads=5, seed=7)
 
 
 def test_without_fused_combine_and_single_expert(emu):
     _run(emu, [1000], [0, 7], G=1, NT1=16, NT2=56, with_cb=0)
-    _run(emu, [1], [3, 1], G=1, NT1=2, NT2=2, threads=2)
+    _run(emu, [1], [3, 1], G=1, NT1=2, NT2=2, threads=1)
 
 
 def test_all_tokens_without_local_pick(emu):
