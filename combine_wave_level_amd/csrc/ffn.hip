@@ -52,7 +52,7 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, size_t n) {
 // ---------------------------------------------------------------- phase kernels
 
 template <class F>
-__global__ __launch_bounds__(256) void gemm1_phase_kernel(
+__global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     uint16_t* __restrict__ act, int E_local, int d, int I) {
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void gemm1_phase_kernel(
 }
 
 template <class F>
-__global__ __launch_bounds__(256) void gemm2_phase_kernel(
+__global__ __launch_bounds__(F::NT) void gemm2_phase_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ offsets, uint16_t* __restrict__ y, int E_local, int d, int I) {
   using C = typename F::G2;
@@ -195,7 +195,7 @@ __device__ __forceinline__ void local_wait(const int32_t* p, int target, long lo
 }
 
 template <class F, bool OUT_BF16>
-__global__ __launch_bounds__(256) void ffn_waved_kernel(WaveArgs A) {
+__global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   using C1 = typename F::G1;
   using C2 = typename F::G2;
   static_assert(C1::BT == C2::BT, "GEMM1 and GEMM2 share the m-tiles");
@@ -230,12 +230,12 @@ __global__ __launch_bounds__(256) void ffn_waved_kernel(WaveArgs A) {
       const int count = uniform(min(C1::BT, A.offsets[t.expert + 1] - row0));
       gemm1_tile<C1>(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token,
                      A.act, row0, count, t.nt, A.d, A.I, lds);
-      local_signal(A.ctr + sched_g1done_index(S, rw, t.mt));
+      local_signal(A.ctr + sched_g1done_index(S, rw, t.wave, t.mt));
     } else if (t.kind == kTaskGemm2) {
       // GEMM2 tile, once every GEMM1 tile of its m-tile is done (same XCD)
       const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * C2::BT);
       const int count = uniform(min(C2::BT, A.offsets[t.expert + 1] - row0));
-      local_wait(A.ctr + sched_g1done_index(S, rw, t.mt), NT1, A.timeout_ticks, A.err);
+      local_wait(A.ctr + sched_g1done_index(S, rw, t.wave, t.mt), NT1, A.timeout_ticks, A.err);
       gemm2_tile<C2>(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count,
                      t.nt, A.d, A.I, lds);
       wait_vmcnt<0>();
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void ffn_waved_kernel(WaveArgs A) {
       __syncthreads();
       const int base = uniform(A.ready_off[t.slot] + t.chunk * kCombineTokens);
       const int end = uniform(min(base + kCombineTokens, A.ready_off[t.slot + 1]));
-      for (int i = base + wave_uniform(); i < end; i += 4)
+      for (int i = base + wave_uniform(); i < end; i += F::NT / kWave)
         combine_token<OUT_BF16, true>(A.ready_list[i], A.y, A.pair_pos, A.topk_w, A.k, A.d, A.out);
       __syncthreads();
     }
@@ -285,14 +285,14 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   if (flags & MOE_FLAG_SERIAL) {
     constexpr size_t l1 = F::G1::LDS_BYTES, l2 = F::G2::LDS_BYTES;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel<F>, 256, l1)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel<F>, F::NT, l1)) != hipSuccess)
       return e;
-    gemm1_phase_kernel<F><<<max(1, per_cu) * cus, 256, l1, s>>>(xb, w13, offsets, sorted_token, act,
+    gemm1_phase_kernel<F><<<max(1, per_cu) * cus, F::NT, l1, s>>>(xb, w13, offsets, sorted_token, act,
                                                                  p.E_local, p.d, p.I);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm2_phase_kernel<F>, 256, l2)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm2_phase_kernel<F>, F::NT, l2)) != hipSuccess)
       return e;
-    gemm2_phase_kernel<F><<<max(1, per_cu) * cus, 256, l2, s>>>(act, w2, offsets, static_cast<uint16_t*>(y),
+    gemm2_phase_kernel<F><<<max(1, per_cu) * cus, F::NT, l2, s>>>(act, w2, offsets, static_cast<uint16_t*>(y),
                                                                  p.E_local, p.d, p.I);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (out && p.T > 0) return launch_combine(p, y, pair_pos, topk_w, out, s);
@@ -327,8 +327,8 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   A.timeout_ticks = static_cast<long long>(max(wall_khz, 1)) * 1000ll * kWaitTimeoutSeconds;
   auto kern = out_bf16 ? ffn_waved_kernel<F, true> : ffn_waved_kernel<F, false>;
   constexpr size_t lds = ffn_lds_bytes<F>();
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds)) != hipSuccess) return e;
-  kern<<<max(1, per_cu) * cus, 256, lds, s>>>(A);
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, F::NT, lds)) != hipSuccess) return e;
+  kern<<<max(1, per_cu) * cus, F::NT, lds, s>>>(A);
   return hipGetLastError();
 }
 

@@ -16,23 +16,30 @@ namespace moe {
 // Tile shapes of the expert GEMMs (BW output features x BT pair rows).  The
 // shape only decides which workgroup computes which outputs; every shape
 // runs the same per-element instruction sequence over K.
-//   large : many rows per expert (MFMA bound)
-//   small : a handful of rows per expert (weight streaming, HBM bound)
+//   large : many rows per expert (MFMA bound): 256 x 256 tiles, 8 wavefronts
+//           of 64 x 128, two per SIMD
 //   mid   : any shape the boundary accepts (d % 128 == 0, I % 64 == 0)
+//   small : a handful of rows per expert (weight streaming, HBM bound)
+// GEMM1 and GEMM2 of one shape use the same workgroup size (NT threads).
 struct FfnLarge {
-  using G1 = TileCfg<256, 128, 2, 2, 64, 3>;
-  using G2 = TileCfg<256, 128, 2, 2, 64, 3>;
+  using G1 = TileCfg<256, 256, 4, 2, 32, 4>;
+  using G2 = TileCfg<256, 256, 4, 2, 32, 4>;
+  static constexpr int NT = 512;
 };
 struct FfnMid {
-  using G1 = TileCfg<128, 128, 2, 2, 64, 4>;
-  using G2 = TileCfg<128, 128, 2, 2, 64, 4>;
+  using G1 = TileCfg<128, 256, 2, 4, 32, 4>;
+  using G2 = TileCfg<128, 256, 2, 4, 32, 4>;
+  static constexpr int NT = 512;
 };
 struct FfnSmall {
   using G1 = TileCfg<128, 16, 4, 1, 128, 3>;
   using G2 = TileCfg<64, 16, 4, 1, 128, 4>;
+  static constexpr int NT = 256;
 };
 template <class F>
 constexpr size_t ffn_lds_bytes() {
+  static_assert(F::G1::NTHREADS == F::NT && F::G2::NTHREADS == F::NT, "one workgroup size per shape");
+  static_assert(F::G1::BT == F::G2::BT, "GEMM1 and GEMM2 share the m-tiles");
   return F::G1::LDS_BYTES > F::G2::LDS_BYTES ? F::G1::LDS_BYTES : F::G2::LDS_BYTES;
 }
 constexpr int kMaxLocalExperts = 256;
@@ -86,9 +93,9 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
     trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
   }
   TileAcc<C> acc;
-  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc);
-  const int lane = lane_id(), wave = wave_id();
-  const int wr = wave / C::WT, wt = wave % C::WT;
+  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc, count);
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
 #pragma unroll
   for (int a = 0; a < C::AW; a += 2) {
     const int nb = nt * (C::BW / 16) + wr * C::AW + a;  // even: W1 block, nb + 1: W3 block
@@ -118,9 +125,9 @@ __device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ act,
     trow.p[i] = act + static_cast<size_t>(row0 + r) * I;
   }
   TileAcc<C> acc;
-  tile_mma<C>(w2e + frag_offset(nt * (C::BW / 16), 0, I / 32), I / 32, I / C::BK, trow, lds, acc);
-  const int lane = lane_id(), wave = wave_id();
-  const int wr = wave / C::WT, wt = wave % C::WT;
+  tile_mma<C>(w2e + frag_offset(nt * (C::BW / 16), 0, I / 32), I / 32, I / C::BK, trow, lds, acc, count);
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
 #pragma unroll
   for (int a = 0; a < C::AW; ++a) {
     const int n0 = (nt * (C::BW / 16) + wr * C::AW + a) * 16 + 4 * (lane / 16);

@@ -29,22 +29,39 @@ namespace moe {
 template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_>
 struct TileCfg {
   static constexpr int BW = BW_, BT = BT_, WR = WR_, WT = WT_, BK = BK_, NST = NST_;
-  static_assert(WR * WT == 4, "4 wavefronts per workgroup");
+  static constexpr int NW = WR * WT;            // wavefronts per workgroup
+  static constexpr int NTHREADS = 64 * NW;
+  static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts per workgroup");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
   static_assert(BK % 32 == 0 && BK >= 32, "K step is whole MFMA k-slices");
   static_assert(BW % (16 * WR) == 0 && BT % (16 * WT) == 0, "wave tile must hold whole MFMA blocks");
   static constexpr int KS = BK / 32;            // MFMA k-slices per K step
   static constexpr int NFW = BW / 16 * KS;      // weight fragments per K step
   static constexpr int NFT = BT / 16 * KS;      // token fragments per K step
-  static_assert(NFW % 4 == 0 && NFT % 4 == 0, "fragments split evenly over the 4 wavefronts");
-  static constexpr int LW = NFW / 4;            // weight fragments each wave loads per step
-  static constexpr int LT = NFT / 4;            // token fragments each wave loads per step
+  static_assert(NFW % NW == 0 && NFT % NW == 0, "fragments split evenly over the wavefronts");
+  static constexpr int LW = NFW / NW;           // weight fragments each wave loads per step
+  static constexpr int LT = NFT / NW;           // token fragments each wave loads per step
   static constexpr int AW = BW / WR / 16;       // MFMA row blocks per wave
   static constexpr int AT = BT / WT / 16;       // MFMA column blocks per wave
   static constexpr int STAGE = (NFW + NFT) * 512;  // bf16 elements per LDS stage
   static constexpr size_t LDS_BYTES = static_cast<size_t>(NST) * STAGE * 2;
-  static_assert(LW + LT <= 63 / (NST > 1 ? NST - 1 : 1), "vmcnt budget");
+  static_assert((NST - 1) * (LW + LT) <= 63, "vmcnt budget: NST-1 steps of loads in flight");
+  // Register double-buffering of the MFMA operands (4 wavefronts, one per
+  // SIMD).  With 8 wavefronts two share a SIMD and hide each other's LDS
+  // latency; their register budget (256 per lane) has no room for a second
+  // operand set.
+  static constexpr bool DBUF = (NW == 4);
 };
+
+// Wave w of the workgroup computes weight row blocks wr * AW .. + AW - 1 and
+// token blocks wt * AT .. + AT - 1 of the tile, wr = w % WR, wt = w / WR.
+// With 8 wavefronts, waves w and w + 4 (which usually share a SIMD) hold the
+// same weight rows and different tokens, so a partly filled token tile
+// leaves each SIMD with the same amount of work.
+template <class C>
+__device__ __forceinline__ int tile_wr() { return wave_id() % C::WR; }
+template <class C>
+__device__ __forceinline__ int tile_wt() { return wave_id() / C::WR; }
 
 // Accumulators of one wave: v[a][b] is the 16x16 block of weight row block
 // (wr * AW + a) and token block (wt * AT + b) of the tile.
@@ -62,14 +79,30 @@ struct TokRows {
 // Token fragment i of this wave (i < C::LT) covers token block tb and k-slice
 // kc of the step; its rows in the tile are tb * 16 + (lane % 16).
 template <class C>
-__device__ __forceinline__ int tok_frag_block(int i) { return (4 * i + wave_id()) / C::KS; }
+__device__ __forceinline__ int tok_frag_block(int i) { return (C::NW * i + wave_id()) / C::KS; }
 template <class C>
-__device__ __forceinline__ int tok_frag_slice(int i) { return (4 * i + wave_id()) % C::KS; }
+__device__ __forceinline__ int tok_frag_slice(int i) { return (C::NW * i + wave_id()) % C::KS; }
 
 // Row index (0..BT-1) inside the tile of the token fragment i this lane loads.
 template <class C>
 __device__ __forceinline__ int trow_index(int i) {
   return tok_frag_block<C>(i) * 16 + (lane_id() & 15);
+}
+
+// s_waitcnt lgkmcnt(0) as the builtin, so that the compiler's own wait
+// insertion knows LDS reads issued before it are complete; the empty asm
+// keeps memory operations from moving across it.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the waits of __syncthreads (which would drain
+// the loads of later stages); the empty asm statements keep the compiler
+// from moving memory operations across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
 }
 
 template <int N>
@@ -86,19 +119,146 @@ __device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, i
   uint16_t* st = lds + (kt % C::NST) * C::STAGE;
 #pragma unroll
   for (int i = 0; i < C::LW; ++i) {
-    const int f = 4 * i + wave;  // weight fragment of the step
+    const int f = C::NW * i + wave;  // weight fragment of the step
     const int nb = f / C::KS, kc = f % C::KS;
-    __builtin_amdgcn_global_load_lds(wtile + frag_offset(nb, kt * C::KS + kc, KB) + lane * 8,
-                                     st + f * 512, 16, 0, 0);
+    lds_dma16(wtile + frag_offset(nb, kt * C::KS + kc, KB) + lane * 8, st + f * 512);
   }
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
-    const int f = 4 * i + wave;  // token fragment of the step
+    const int f = C::NW * i + wave;  // token fragment of the step
     const int kc = f % C::KS;
-    __builtin_amdgcn_global_load_lds(trow.p[i] + kt * C::BK + kc * 32 + (lane >> 4) * 8,
-                                     st + (C::NFW + f) * 512, 16, 0, 0);
+    lds_dma16(trow.p[i] + kt * C::BK + kc * 32 + (lane >> 4) * 8, st + (C::NFW + f) * 512);
   }
 }
+
+// MFMA operands of one 32-wide k-slice for one wave.
+template <class C>
+struct TileFrags {
+  u32x4 a[C::AW];
+  u32x4 b[C::AT];
+};
+
+// ACT = false: none of this wave's token rows is valid; the wave then neither
+// reads operands nor multiplies (its accumulators stay unused) but still
+// takes part in the loads and barriers.
+template <class C, bool ACT>
+__device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, TileFrags<C>& f) {
+  if constexpr (!ACT) return;
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
+#pragma unroll
+  for (int a = 0; a < C::AW; ++a) f.a[a] = ld16(st + ((wr * C::AW + a) * C::KS + ks) * 512 + lane * 8);
+#pragma unroll
+  for (int b = 0; b < C::AT; ++b)
+    f.b[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
+}
+
+template <class C, bool ACT>
+__device__ __forceinline__ void tile_mfma(const TileFrags<C>& f, TileAcc<C>& acc) {
+  if constexpr (!ACT) return;
+#pragma unroll
+  for (int a = 0; a < C::AW; ++a)
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) acc.v[a][b] = mfma16x16x32(f.a[a], f.b[b], acc.v[a][b]);
+}
+
+// vmcnt wait that leaves `later` K steps of this wave's loads outstanding
+// (0 <= later <= NST - 2; wave-uniform).
+template <class C>
+__device__ __forceinline__ void wait_steps_left(int later) {
+  constexpr int L = C::LW + C::LT;
+  if (later <= 0) {
+    wait_vmcnt<0>();
+  } else if constexpr (C::NST >= 3) {
+    if (later == 1) wait_vmcnt<L>();
+    else if constexpr (C::NST >= 4) wait_vmcnt<2 * L>();
+  }
+}
+
+// One K step kt of the main loop.  On entry the operands of the step's first
+// k-slice are in (or on their way to) the register set of parity PAR.  Each
+// k-slice first starts the LDS reads of the next slice into the other set,
+// then runs its MFMAs, so LDS latency hides behind the matrix core.  At the
+// last slice the wave waits for step kt + 1, the workgroup passes a barrier
+// (after which stage kt is fully consumed), step kt + NST is issued into that
+// stage, and the next step's first slice is read.
+template <class C, int PAR, bool ACT>
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, int KB, int nk, int kt,
+                                          const TokRows<C>& trow, uint16_t* lds, TileFrags<C>& f0,
+                                          TileFrags<C>& f1, TileAcc<C>& acc) {
+  const uint16_t* st = lds + (kt % C::NST) * C::STAGE;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    TileFrags<C>& cur = ((PAR + ks) & 1) ? f1 : f0;
+    TileFrags<C>& nxt = ((PAR + ks) & 1) ? f0 : f1;
+    // this slice's operands (read one slice earlier) have arrived; waiting
+    // here, before the next reads go out, keeps the compiler from waiting
+    // on those as well
+    wait_lgkm0();
+    if (ks + 1 < C::KS) {
+      tile_read_frags<C, ACT>(st, ks + 1, nxt);
+    } else if (kt + 1 < nk) {
+      wait_steps_left<C>(min(C::NST - 2, nk - 2 - kt));
+      raw_barrier();
+      if (kt + C::NST < nk) tile_issue<C>(wtile, KB, trow, lds, kt + C::NST);
+      tile_read_frags<C, ACT>(lds + ((kt + 1) % C::NST) * C::STAGE, 0, nxt);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tile_mfma<C, ACT>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <class C, bool ACT>
+__device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile, int KB, int nk,
+                                             const TokRows<C>& trow, uint16_t* lds, TileAcc<C>& acc) {
+
+  if constexpr (!C::DBUF) {
+    // single operand set: steps 0 .. NST-2 in flight; step kt waits for its
+    // own loads, passes a barrier (stage kt-1 is then free), issues step
+    // kt + NST - 1 into that stage and computes from LDS
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+      if (s < nk) tile_issue<C>(wtile, KB, trow, lds, s);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_steps_left<C>(min(C::NST - 2, nk - 1 - kt));
+      raw_barrier();
+      if (kt + C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, kt + C::NST - 1);
+      const uint16_t* st = lds + (kt % C::NST) * C::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        TileFrags<C> f;
+        tile_read_frags<C, ACT>(st, ks, f);
+        tile_mfma<C, ACT>(f, acc);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    raw_barrier();
+    return;
+  }
+  // prologue: steps 0 .. NST-2 in flight, wait for step 0, then issue step
+  // NST-1 (at most NST-1 steps of loads are ever outstanding)
+#pragma unroll
+  for (int s = 0; s < C::NST - 1; ++s)
+    if (s < nk) tile_issue<C>(wtile, KB, trow, lds, s);
+  wait_steps_left<C>(min(C::NST - 2, nk - 1));
+  if (C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, C::NST - 1);
+  raw_barrier();
+  TileFrags<C> f0, f1;
+  tile_read_frags<C, ACT>(lds, 0, f0);
+
+  constexpr int P1 = C::KS & 1;  // register-set parity of the step after an even step
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc);
+    tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc);
+  }
+  if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc);
+  // all LDS reads of this tile done before anyone refills the stages
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  raw_barrier();
+}
+
 
 // Computes one tile.
 //   wtile : packed weights, fragment (first row block of the tile, kb = 0)
@@ -108,55 +268,25 @@ __device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, i
 //           element k = 0 of this lane's token row (gathered and clamped to a
 //           valid row by the caller)
 //   lds   : C::LDS_BYTES of shared memory
-// All 256 threads must call it.  On entry no direct-to-LDS load of this
+//   tvalid: rows 0 .. tvalid-1 of the token tile are valid (wave-uniform);
+//           a wave whose token rows all lie past them skips its MFMA work,
+//           and its accumulators hold no meaningful values
+// All C::NTHREADS threads must call it.  On entry no direct-to-LDS load of this
 // workgroup may be in flight; on exit none is, and a barrier has passed, so
 // the caller may reuse lds right away.
 template <class C>
 __device__ __forceinline__ void tile_mma(const uint16_t* __restrict__ wtile, int KB, int nk,
                                          const TokRows<C>& trow, uint16_t* lds,
-                                         TileAcc<C>& acc) {
-  const int lane = lane_id(), wave = wave_id();
-  const int wr = wave / C::WT, wt = wave % C::WT;
+                                         TileAcc<C>& acc, int tvalid = C::BT) {
 #pragma unroll
   for (int a = 0; a < C::AW; ++a)
 #pragma unroll
     for (int b = 0; b < C::AT; ++b) acc.v[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // prologue: NST-1 steps in flight
-#pragma unroll
-  for (int s = 0; s < C::NST - 1; ++s)
-    if (s < nk) tile_issue<C>(wtile, KB, trow, lds, s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of step kt are done once at most the later in-flight
-    // steps remain outstanding
-    const int later = min(C::NST - 2, nk - 1 - kt);
-    if (later <= 0) {
-      wait_vmcnt<0>();
-    } else if constexpr (C::NST >= 3) {
-      if (later == 1) wait_vmcnt<(C::LW + C::LT)>();
-      else wait_vmcnt<(C::NST - 2) * (C::LW + C::LT)>();
-    }
-    __builtin_amdgcn_s_barrier();  // every wave's step-kt data is in LDS; stage (kt-1) is free
-    if (kt + C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, kt + C::NST - 1);
-    const uint16_t* st = lds + (kt % C::NST) * C::STAGE;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 af[C::AW], bfr[C::AT];
-#pragma unroll
-      for (int a = 0; a < C::AW; ++a) af[a] = ld16(st + ((wr * C::AW + a) * C::KS + ks) * 512 + lane * 8);
-#pragma unroll
-      for (int b = 0; b < C::AT; ++b)
-        bfr[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
-#pragma unroll
-      for (int a = 0; a < C::AW; ++a)
-#pragma unroll
-        for (int b = 0; b < C::AT; ++b) acc.v[a][b] = mfma16x16x32(af[a], bfr[b], acc.v[a][b]);
-    }
-  }
-  // all LDS reads of this tile done before anyone refills the stages
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
+  // both paths pass the same barriers in the same order
+  if (uniform(tile_wt<C>() * C::AT * 16) < tvalid)
+    tile_mma_run<C, true>(wtile, KB, nk, trow, lds, acc);
+  else
+    tile_mma_run<C, false>(wtile, KB, nk, trow, lds, acc);
 }
 
 }  // namespace moe

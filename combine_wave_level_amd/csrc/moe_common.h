@@ -112,6 +112,13 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// 16-byte direct-to-LDS load (global_load_lds_dwordx4): lane l copies 16
+// bytes at g into LDS at (wave's base) + 16 l.  Kept out of templates so that
+// the builtin is checked once, in device compilation only.
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace moe

@@ -36,8 +36,8 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
   }
   TileAcc<C> acc;
   tile_mma<C>(wg + frag_offset(et * C::BW / 16, 0, d / 32), d / 32, d / C::BK, trow, lds, acc);
-  const int lane = lane_id(), wave = wave_id();
-  const int wr = wave / C::WT, wt = wave % C::WT;
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
 #pragma unroll
   for (int a = 0; a < C::AW; ++a) {
     const int e0 = et * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);

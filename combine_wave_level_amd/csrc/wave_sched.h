@@ -6,10 +6,13 @@
 // and the return of finished experts' results run at the same time.
 //
 // MI355X has 8 XCDs, each with its own L2.  The m-tiles (BT-row slices of
-// each expert's sorted rows) are split into 8 contiguous, equal ranges, one
-// per XCD, and every workgroup takes tasks only from its own XCD's ticket
-// stream.  GEMM1 -> GEMM2 dependencies therefore never leave an XCD's L2;
-// only the combine, which reads y rows of every XCD, crosses XCDs.
+// each expert's sorted rows) of every expert wave are split into 8
+// contiguous ranges, one per XCD (when a wave's m-tiles do not divide by 8,
+// the extra ones go to the XCDs after those that took the previous wave's
+// extras, so the XCDs stay within one m-tile of each other), and every
+// workgroup takes tasks only from its own XCD's ticket stream.  GEMM1 ->
+// GEMM2 dependencies therefore never leave an XCD's L2; only the combine,
+// which reads y rows of every XCD, crosses XCDs.
 //
 // Inside one XCD's stream, block b of the ticket sequence holds
 //   GEMM1 tiles of the XCD's m-tiles in wave b (their operand loads are the
@@ -36,10 +39,11 @@ constexpr int kCombineTokens = 16;      // tokens per combine task
 constexpr int kCtrPad = 64;             // int32 words (256 B) between counters of different XCDs
 
 struct WaveSchedule {
-  int W, G, NT1, NT2, total, xcd, mt_lo, mt_hi;
+  int W, G, NT1, NT2, total, xcd, n_local;
   int32_t mt_pre[kSchedMaxExperts + 1];  // first m-tile of each local expert
   int32_t blk_start[kSchedMaxWaves + 3]; // first ticket of block b, b = 0 .. W+2
   int32_t mlo[kSchedMaxWaves];           // first m-tile of this XCD in wave w
+  int32_t loc_pre[kSchedMaxWaves];       // this XCD's m-tiles in waves < w
   int32_t n_g1[kSchedMaxWaves];          // this XCD's GEMM1 tiles of wave w
   int32_t n_g2[kSchedMaxWaves];          // this XCD's GEMM2 tiles of wave w
   int32_t g2_all[kSchedMaxWaves];        // GEMM2 tiles of wave w over all XCDs
@@ -68,9 +72,10 @@ __host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, in
   return lo;
 }
 
-// First m-tile of XCD x when nmt m-tiles are split into kXcds equal ranges.
-__host__ __device__ inline int sched_xcd_first_mtile(int nmt, int x) {
-  return static_cast<int>((static_cast<long long>(nmt) * x) / kXcds);
+// Share of XCD x when n m-tiles of one wave are split over the XCDs and the
+// n % kXcds extra m-tiles go to XCDs rot, rot + 1, ... (mod kXcds).
+__host__ __device__ inline int sched_xcd_share(int n, int rot, int x) {
+  return n / kXcds + (((x - rot + kXcds) % kXcds) < (n % kXcds) ? 1 : 0);
 }
 
 // Builds XCD xcd's schedule from the dispatch tables.  offsets [E_local + 1]
@@ -92,18 +97,21 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
   }
   S.mt_pre[E_local] = run;
-  S.mt_lo = sched_xcd_first_mtile(run, xcd);
-  S.mt_hi = sched_xcd_first_mtile(run, xcd + 1);
+  int rot = 0, loc = 0;
   for (int w = 0; w < S.W; ++w) {
-    const int a = S.mt_pre[w * G], b = S.mt_pre[(w + 1) * G];
-    const int lo = a > S.mt_lo ? a : S.mt_lo;
-    const int hi = b < S.mt_hi ? b : S.mt_hi;
-    const int cnt = hi > lo ? hi - lo : 0;
+    const int a = S.mt_pre[w * G], n = S.mt_pre[(w + 1) * G] - a;
+    int lo = a;
+    for (int y = 0; y < xcd; ++y) lo += sched_xcd_share(n, rot, y);
+    const int cnt = sched_xcd_share(n, rot, xcd);
     S.mlo[w] = lo;
+    S.loc_pre[w] = loc;
+    loc += cnt;
     S.n_g1[w] = cnt * NT1;
     S.n_g2[w] = cnt * NT2;
-    S.g2_all[w] = (b - a) * NT2;
+    S.g2_all[w] = n * NT2;
+    rot = (rot + n % kXcds) % kXcds;
   }
+  S.n_local = loc;
   for (int s = 0; s <= S.W; ++s) {
     const int chunks =
         with_combine ? (ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens : 0;
@@ -157,11 +165,13 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
 //   [x * kCtrPad]                   ticket of XCD x
 //   region(x) = kXcds * kCtrPad + x * region_words:
 //     region(x) + w                 GEMM2 tiles of wave w finished on XCD x
-//     region(x) + W + (mt - mt_lo)  GEMM1 tiles of m-tile mt finished (on XCD x)
+//     region(x) + W + j             GEMM1 tiles finished of XCD x's j-th m-tile
+//                                   (j = loc_pre[w] + mt - mlo[w])
 //   kXcds * (kCtrPad + region_words) + w   GEMM2 tiles of wave w finished, all XCDs
-// region_words >= W + (m-tiles of one XCD), rounded up to kCtrPad.
+// region_words >= W + (m-tiles of one XCD), rounded up to kCtrPad; one XCD
+// holds at most max_mtiles / kXcds + W m-tiles (one extra per wave at most).
 __host__ __device__ inline int sched_region_words(int W, int max_mtiles) {
-  const int per_xcd = (max_mtiles + kXcds - 1) / kXcds + 1;
+  const int per_xcd = max_mtiles / kXcds + W + 1;
   return ((W + per_xcd + kCtrPad - 1) / kCtrPad) * kCtrPad;
 }
 __host__ __device__ inline size_t sched_counter_words(int W, int max_mtiles) {
@@ -171,8 +181,8 @@ __host__ __device__ inline int sched_ticket_index(int xcd) { return xcd * kCtrPa
 __host__ __device__ inline int sched_g2local_index(const WaveSchedule& S, int rw, int w) {
   return kXcds * kCtrPad + S.xcd * rw + w;
 }
-__host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int rw, int mt) {
-  return kXcds * kCtrPad + S.xcd * rw + S.W + (mt - S.mt_lo);
+__host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int rw, int w, int mt) {
+  return kXcds * kCtrPad + S.xcd * rw + S.W + S.loc_pre[w] + (mt - S.mlo[w]);
 }
 __host__ __device__ inline int sched_g2all_index(const WaveSchedule& S, int rw, int w) {
   return kXcds * (kCtrPad + rw) + w;

@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) void wgrad_dh_kernel(
   __syncthreads();
   const int NT = I / 64;
   const int total = uniform(mt_pre[E_local] * NT);
-  const int lane = lane_id(), wave = wave_id();
-  const int wr = wave / 2, wt = wave % 2;
+  const int lane = lane_id();
+  static_assert(DhCfg13::WR == 2 && DhCfg13::WT == 2 && DhCfgG::WR == 2 && DhCfgG::WT == 2, "epilogue below");
+  const int wr = tile_wr<DhCfg13>(), wt = tile_wt<DhCfg13>();
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));

@@ -7,10 +7,13 @@
 // stdin: E_local G BT NT1 NT2 with_combine threads_per_xcd seed
 //        offsets[E_local + 1]  ready_off[W + 2]
 // Checks (exit status 0 = all hold):
-//   1. structure: over the 8 streams every GEMM1 / GEMM2 tile (m-tile x
+//   1. structure: each wave's m-tiles are split into contiguous per-XCD
+//      ranges whose sizes differ by at most one, and the XCDs' totals by at
+//      most one; over the 8 streams every GEMM1 / GEMM2 tile (m-tile x
 //      output tile) and every combine chunk has exactly one ticket; both
 //      GEMM tiles of an m-tile live in the stream of the XCD owning it;
 //      decoded experts own their m-tiles and belong to the decoded wave;
+//      every XCD's counters fit its region;
 //   2. every GEMM2 tile waits only on smaller tickets of its own stream;
 //   3. an emulated run completes and every counter ends at its target.
 #include <atomic>
@@ -54,9 +57,29 @@ int main() {
     const int chunks = with_cb ? (ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens : 0;
     cb_seen[s].assign(chunks, 0);
   }
+  for (int w = 0; w < W; ++w) {
+    int expect = S[0].mt_pre[w * G], lo = 1 << 30, hi = -1;
+    for (int x = 0; x < kXcds; ++x) {
+      if (S[x].mlo[w] != expect) fail("per-wave XCD ranges not contiguous", w, x);
+      const int cnt = NT1 > 0 ? S[x].n_g1[w] / NT1 : 0;
+      expect += cnt;
+      lo = cnt < lo ? cnt : lo;
+      hi = cnt > hi ? cnt : hi;
+      if (S[x].loc_pre[w] + cnt > S[x].n_local) fail("local m-tile prefix", w, x);
+    }
+    if (expect != S[0].mt_pre[(w + 1) * G]) fail("per-wave XCD ranges do not cover the wave", w);
+    if (hi - lo > 1) fail("per-wave XCD shares differ by more than one", w);
+  }
+  {
+    int lo = 1 << 30, hi = -1;
+    for (int x = 0; x < kXcds; ++x) {
+      lo = S[x].n_local < lo ? S[x].n_local : lo;
+      hi = S[x].n_local > hi ? S[x].n_local : hi;
+      if (W + S[x].n_local > rw) fail("counter region too small", x, S[x].n_local);
+    }
+    if (hi - lo > 1) fail("XCD totals differ by more than one", lo, hi);
+  }
   for (int x = 0; x < kXcds; ++x) {
-    if (S[x].mt_lo != sched_xcd_first_mtile(nmt, x) || S[x].mt_hi != sched_xcd_first_mtile(nmt, x + 1))
-      fail("m-tile range", x);
     for (int tk = 0; tk < S[x].total; ++tk) {
       const Task t = sched_decode(S[x], tk);
       if (t.kind == kTaskCombine) {
@@ -65,7 +88,8 @@ int main() {
         if (cb_seen[t.slot][t.chunk]++) fail("combine chunk twice", t.slot, t.chunk);
         continue;
       }
-      if (t.mt < S[x].mt_lo || t.mt >= S[x].mt_hi) fail("m-tile outside the XCD's range", x, t.mt);
+      if (t.mt < S[x].mlo[t.wave] || t.mt >= S[x].mlo[t.wave] + S[x].n_g1[t.wave] / (NT1 > 0 ? NT1 : 1))
+        fail("m-tile outside the XCD's range", x, t.mt);
       if (t.mt < S[x].mt_pre[t.expert] || t.mt >= S[x].mt_pre[t.expert + 1]) fail("expert does not own m-tile", tk, t.mt);
       if (t.expert / G != t.wave) fail("expert not in wave", tk, t.expert);
       const int NT = t.kind == kTaskGemm1 ? NT1 : NT2;
@@ -113,9 +137,9 @@ int main() {
       const Task t = sched_decode(s, tk);
       if (rng() % 4 == 0) std::this_thread::sleep_for(std::chrono::microseconds(rng() % 200));
       if (t.kind == kTaskGemm1) {
-        ctr[sched_g1done_index(s, rw, t.mt)].fetch_add(1, std::memory_order_release);
+        ctr[sched_g1done_index(s, rw, t.wave, t.mt)].fetch_add(1, std::memory_order_release);
       } else if (t.kind == kTaskGemm2) {
-        wait_geq(sched_g1done_index(s, rw, t.mt), s.NT1);
+        wait_geq(sched_g1done_index(s, rw, t.wave, t.mt), s.NT1);
         const int done = ctr[sched_g2local_index(s, rw, t.wave)].fetch_add(1) + 1;
         if (done == s.n_g2[t.wave]) ctr[sched_g2all_index(s, rw, t.wave)].fetch_add(done);
       } else {
@@ -132,8 +156,9 @@ int main() {
   for (int x = 0; x < kXcds; ++x) total += S[x].total;
   if (done_tasks.load() != total) fail("tasks done", done_tasks.load(), total);
   for (int x = 0; x < kXcds; ++x)
-    for (int mt = S[x].mt_lo; mt < S[x].mt_hi; ++mt)
-      if (ctr[sched_g1done_index(S[x], rw, mt)].load() != NT1) fail("g1done count", mt);
+    for (int w = 0; w < W; ++w)
+      for (int mt = S[x].mlo[w]; mt < S[x].mlo[w] + S[x].n_g1[w] / (NT1 > 0 ? NT1 : 1); ++mt)
+        if (ctr[sched_g1done_index(S[x], rw, w, mt)].load() != NT1) fail("g1done count", mt);
   for (int w = 0; w < W; ++w)
     if (ctr[sched_g2all_index(S[0], rw, w)].load() != S[0].g2_all[w]) fail("g2 all count", w);
   std::printf("OK total=%d W=%d mtiles=%d\n", total, W, nmt);
