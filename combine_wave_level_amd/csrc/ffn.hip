@@ -92,13 +92,16 @@ __global__ __launch_bounds__(F::NT) void gemm2_phase_kernel(
   }
 }
 
+// One wavefront per (token, column part); blockIdx.y = part.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ topk_w, int T,
-                                                      int k, int d, void* __restrict__ out) {
+                                                      int k, int d, int parts, void* __restrict__ out) {
   const int t = blockIdx.x * 4 + wave_id();
-  if (t < T) combine_token<OUT_BF16, false>(t, y, pair_pos, topk_w, k, d, out);
+  int cb, ce;
+  combine_cols(d, parts, blockIdx.y, cb, ce);
+  if (t < T) combine_token<OUT_BF16, false>(t, y, pair_pos, topk_w, k, d, cb, ce, out);
 }
 
 // ---------------------------------------------------------------- persistent
@@ -123,6 +126,7 @@ struct WaveArgs {
   int32_t* err;
   int E_local, G, W, d, I, k;
   int region_words;
+  int cb_parts;              // column parts of a combine task
   long long timeout_ticks;   // bound of each wait, in wall-clock ticks
 };
 
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   const int xcd = uniform(xcc_id());
   if (threadIdx.x == 0)
     sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
-                A.out != nullptr, xcd);
+                A.out != nullptr ? A.cb_parts : 0, xcd);
   __syncthreads();
   const int total = uniform(S.total);
   const int NT1 = uniform(S.NT1);
@@ -255,21 +259,39 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
       for (int w = 0; w <= t.slot - 1; ++w)
         poll_geq(A.ctr + sched_g2all_index(S, rw, w), uniform(S.g2_all[w]), A.timeout_ticks, A.err);
       __syncthreads();
-      const int base = uniform(A.ready_off[t.slot] + t.chunk * kCombineTokens);
+      const int parts = A.cb_parts;
+      const int base = uniform(A.ready_off[t.slot] + (t.chunk / parts) * kCombineTokens);
       const int end = uniform(min(base + kCombineTokens, A.ready_off[t.slot + 1]));
+      int cb, ce;
+      combine_cols(A.d, parts, t.chunk % parts, cb, ce);
       for (int i = base + wave_uniform(); i < end; i += F::NT / kWave)
-        combine_token<OUT_BF16, true>(A.ready_list[i], A.y, A.pair_pos, A.topk_w, A.k, A.d, A.out);
+        combine_token<OUT_BF16, true>(A.ready_list[i], A.y, A.pair_pos, A.topk_w, A.k, A.d, cb, ce, A.out);
       __syncthreads();
     }
   }
 }
 
-// Mean routed rows per local expert, assuming uniform routing: picks the
-// tile shape.  The shape never changes result bits.
-bool use_small_tiles(const moe_problem_t& p) {
+// Tile shape of the expert GEMMs.  The shape never changes result bits.
+//   small batches (mean routed rows per expert under 96, assuming uniform
+//   routing): token tiles of 32 rows for T <= 32 (all rows of an expert: a
+//   token picks an expert at most once), else 64;
+//   otherwise 256 x 256 tiles when the widths allow, else the mid shape.
+enum class FfnShape { Small, Small64, Large, Mid };
+
+template <class F>
+bool ffn_shape_fits(const moe_problem_t& p) {
+  return p.d % F::G1::BK == 0 && p.I % F::G2::BK == 0 && (2 * p.I) % F::G1::BW == 0 &&
+         p.d % F::G2::BW == 0;
+}
+
+FfnShape pick_ffn_shape(const moe_problem_t& p) {
   const double rows = static_cast<double>(p.T) * p.k / p.E_global;
-  return rows < 96.0 && p.d % FfnSmall::G1::BK == 0 && p.I % FfnSmall::G2::BK == 0 &&
-         (2 * p.I) % FfnSmall::G1::BW == 0 && p.d % FfnSmall::G2::BW == 0;
+  if (rows < 96.0) {
+    if (p.T <= FfnSmall::G1::BT && ffn_shape_fits<FfnSmall>(p)) return FfnShape::Small;
+    if (ffn_shape_fits<FfnSmall64>(p)) return FfnShape::Small64;
+  }
+  if (ffn_shape_fits<FfnLarge>(p)) return FfnShape::Large;
+  return FfnShape::Mid;
 }
 
 template <class F>
@@ -322,6 +344,7 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   A.I = p.I;
   A.k = p.k;
   A.region_words = L.ctr_region_words;
+  A.cb_parts = combine_parts(p.T, p.d);
   int wall_khz = 0;
   if ((e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
   A.timeout_ticks = static_cast<long long>(max(wall_khz, 1)) * 1000ll * kWaitTimeoutSeconds;
@@ -363,23 +386,33 @@ hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, 
   const uint16_t* xb = nullptr;
   hipError_t e;
   if ((e = stage_x_bf16(p, L, x, ws, s, &xb)) != hipSuccess) return e;
-  if (use_small_tiles(p))
-    return launch_ffn_cfg<FfnSmall>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
-                                    flags, ws, s);
-  if ((2 * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G2::BW == 0)
-    return launch_ffn_cfg<FfnLarge>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
-                                    flags, ws, s);
-  return launch_ffn_cfg<FfnMid>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
-                                flags, ws, s);
+  switch (pick_ffn_shape(p)) {
+    case FfnShape::Small:
+      return launch_ffn_cfg<FfnSmall>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+                                      out, flags, ws, s);
+    case FfnShape::Small64:
+      return launch_ffn_cfg<FfnSmall64>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+                                         out, flags, ws, s);
+    case FfnShape::Large:
+      return launch_ffn_cfg<FfnLarge>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+                                      out, flags, ws, s);
+    default:
+      return launch_ffn_cfg<FfnMid>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+                                    out, flags, ws, s);
+  }
 }
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
+  const int parts = combine_parts(p.T, p.d);
+  const dim3 grid((p.T + 3) / 4, parts);
   if (p.out_dtype == MOE_BF16)
-    combine_kernel<true><<<(p.T + 3) / 4, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_pos, topk_w, p.T, p.k, p.d, out);
+    combine_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_pos, topk_w, p.T, p.k, p.d,
+                                              parts, out);
   else
-    combine_kernel<false><<<(p.T + 3) / 4, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_pos, topk_w, p.T, p.k, p.d, out);
+    combine_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_pos, topk_w, p.T, p.k, p.d,
+                                               parts, out);
   return hipGetLastError();
 }
 

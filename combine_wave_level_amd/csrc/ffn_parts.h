@@ -19,7 +19,10 @@ namespace moe {
 //   large : many rows per expert (MFMA bound): 256 x 256 tiles, 8 wavefronts
 //           of 64 x 128, two per SIMD
 //   mid   : any shape the boundary accepts (d % 128 == 0, I % 64 == 0)
-//   small : a handful of rows per expert (weight streaming, HBM bound)
+//   small : a handful of rows per expert (weight streaming, HBM bound):
+//           token tiles of 32 or 64 rows (empty 16-row blocks skipped) and
+//           6 to 7 LDS stages, so that each workgroup keeps 80 to 96 KiB of
+//           weights in flight
 // GEMM1 and GEMM2 of one shape use the same workgroup size (NT threads).
 struct FfnLarge {
   using G1 = TileCfg<256, 256, 4, 2, 32, 4>;
@@ -32,8 +35,13 @@ struct FfnMid {
   static constexpr int NT = 512;
 };
 struct FfnSmall {
-  using G1 = TileCfg<128, 16, 4, 1, 128, 3>;
-  using G2 = TileCfg<64, 16, 4, 1, 128, 4>;
+  using G1 = TileCfg<128, 32, 4, 1, 64, 7, true>;
+  using G2 = TileCfg<64, 32, 4, 1, 128, 6, true>;
+  static constexpr int NT = 256;
+};
+struct FfnSmall64 {
+  using G1 = TileCfg<128, 64, 4, 1, 64, 6, true>;
+  using G2 = TileCfg<64, 64, 4, 1, 64, 8, true>;
   static constexpr int NT = 256;
 };
 template <class F>
@@ -159,37 +167,89 @@ __device__ __forceinline__ u32x4 load_y16(const uint16_t* __restrict__ y, int r,
   }
 }
 
-// Combine of token t by one wavefront: out[t] = sum_j w[t, j] * y[pair_pos[t, j]]
-// over local picks, fp32 fused multiply-adds in ascending j, one rounding.
+// Column split of the combine.  For a small batch the tokens alone give too
+// few tasks to spread the combine's reads over the chip, so each token's d
+// columns are split into `parts` ranges handled independently (each range
+// at least 64 16-byte chunks, one per lane).  The split never changes a
+// result bit: every output element is still one accumulation over j.
+__host__ __device__ inline int combine_parts(int T, int d) {
+  const int max_parts = d / 512 > 1 ? d / 512 : 1;
+  const int tok_tasks = (T + 7) / 8;
+  const int want = tok_tasks > 0 ? (512 + tok_tasks - 1) / tok_tasks : 1;
+  return want < 1 ? 1 : (want > max_parts ? max_parts : want);
+}
+// 16-byte column chunks [cb, ce) of part `part` of `parts`.
+__host__ __device__ inline void combine_cols(int d, int parts, int part, int& cb, int& ce) {
+  const int u = d / 8;
+  cb = static_cast<int>(static_cast<long long>(u) * part / parts);
+  ce = static_cast<int>(static_cast<long long>(u) * (part + 1) / parts);
+}
+
+// Combine of token t, 16-byte column chunks [cb, ce), by one wavefront:
+// out[t] = sum_j w[t, j] * y[pair_pos[t, j]] over local picks, fp32 fused
+// multiply-adds in ascending j, one rounding.  Each lane takes two chunks
+// at a time and the picks kCombineGroup at a time; all of a group's loads
+// are issued before its first multiply-add, so a lane keeps up to
+// 2 * kCombineGroup row reads in flight (the accumulation order stays
+// ascending j).
+constexpr int kCombineGroup = 4;
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void combine_store(void* __restrict__ out, int t, int d, int c, const float (&acc)[8]) {
+  if constexpr (OUT_BF16) {
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    st16(static_cast<uint16_t*>(out) + static_cast<size_t>(t) * d + c * 8, o);
+  } else {
+    float* o = static_cast<float*>(out) + static_cast<size_t>(t) * d + c * 8;
+    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+__device__ __forceinline__ void combine_fma(float w, const u32x4& v, float (&acc)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] = fmaf(w, __uint_as_float(v[e] << 16), acc[2 * e]);
+    acc[2 * e + 1] = fmaf(w, __uint_as_float(v[e] & 0xffff0000u), acc[2 * e + 1]);
+  }
+}
+
 template <bool OUT_BF16, bool COHERENT>
 __device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict__ y,
                                               const int32_t* __restrict__ pair_pos,
-                                              const float* __restrict__ topk_w, int k, int d,
-                                              void* __restrict__ out) {
+                                              const float* __restrict__ topk_w, int k, int d, int cb,
+                                              int ce, void* __restrict__ out) {
   const int lane = lane_id();
-  for (int c = lane; c < d / 8; c += kWave) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = pair_pos[static_cast<size_t>(t) * k + j];
-      if (r < 0) continue;
-      const float w = topk_w[static_cast<size_t>(t) * k + j];
-      const u32x4 v = load_y16<COHERENT>(y, r, d, c * 8);
+  const int32_t* pp = pair_pos + static_cast<size_t>(t) * k;
+  const float* pw = topk_w + static_cast<size_t>(t) * k;
+  for (int c0 = cb; c0 < ce; c0 += 2 * kWave) {
+    const int c1 = c0 + lane, c2 = c0 + kWave + lane;
+    const bool h1 = c1 < ce, h2 = c2 < ce;
+    float a1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float a2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+      int r[kCombineGroup];
+      u32x4 v1[kCombineGroup], v2[kCombineGroup];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(w, __uint_as_float(v[q] << 16), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(w, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
+      for (int q = 0; q < kCombineGroup; ++q) {
+        r[q] = uniform(j0 + q < k ? pp[j0 + q] : -1);
+        if (r[q] >= 0) {
+          if (h1) v1[q] = load_y16<COHERENT>(y, r[q], d, c1 * 8);
+          if (h2) v2[q] = load_y16<COHERENT>(y, r[q], d, c2 * 8);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kCombineGroup; ++q) {
+        if (r[q] < 0) continue;
+        const float w = pw[j0 + q];
+        combine_fma(w, v1[q], a1);
+        combine_fma(w, v2[q], a2);
       }
     }
-    if constexpr (OUT_BF16) {
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      st16(static_cast<uint16_t*>(out) + static_cast<size_t>(t) * d + c * 8, o);
-    } else {
-      float* o = static_cast<float*>(out) + static_cast<size_t>(t) * d + c * 8;
-      *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    }
+    if (h1) combine_store<OUT_BF16>(out, t, d, c1, a1);
+    if (h2) combine_store<OUT_BF16>(out, t, d, c2, a2);
   }
 }
 

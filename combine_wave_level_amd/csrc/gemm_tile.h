@@ -26,13 +26,17 @@
 
 namespace moe {
 
-template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_>
+template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_, bool SKIPB_ = false>
 struct TileCfg {
   static constexpr int BW = BW_, BT = BT_, WR = WR_, WT = WT_, BK = BK_, NST = NST_;
+  // SKIPB: skip the MFMA work of every 16-row token block past the valid
+  // rows (for tall token tiles that are mostly empty, as in small batches);
+  // otherwise only a wave whose token rows are all invalid skips its work.
+  static constexpr bool SKIPB = SKIPB_;
   static constexpr int NW = WR * WT;            // wavefronts per workgroup
   static constexpr int NTHREADS = 64 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts per workgroup");
-  static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
+  static_assert(NST >= 2 && NST <= 8, "2 to 8 LDS stages");
   static_assert(BK % 32 == 0 && BK >= 32, "K step is whole MFMA k-slices");
   static_assert(BW % (16 * WR) == 0 && BT % (16 * WT) == 0, "wave tile must hold whole MFMA blocks");
   static constexpr int KS = BK / 32;            // MFMA k-slices per K step
@@ -141,8 +145,10 @@ struct TileFrags {
 // ACT = false: none of this wave's token rows is valid; the wave then neither
 // reads operands nor multiplies (its accumulators stay unused) but still
 // takes part in the loads and barriers.
+// nbv (C::SKIPB only, wave-uniform): token blocks of this wave that hold
+// valid rows; blocks b >= nbv are neither read nor multiplied.
 template <class C, bool ACT>
-__device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, TileFrags<C>& f) {
+__device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, TileFrags<C>& f, int nbv) {
   if constexpr (!ACT) return;
   const int lane = lane_id();
   const int wr = tile_wr<C>(), wt = tile_wt<C>();
@@ -150,29 +156,33 @@ __device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, Tile
   for (int a = 0; a < C::AW; ++a) f.a[a] = ld16(st + ((wr * C::AW + a) * C::KS + ks) * 512 + lane * 8);
 #pragma unroll
   for (int b = 0; b < C::AT; ++b)
-    f.b[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
+    if (!C::SKIPB || b < nbv) f.b[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
 }
 
 template <class C, bool ACT>
-__device__ __forceinline__ void tile_mfma(const TileFrags<C>& f, TileAcc<C>& acc) {
+__device__ __forceinline__ void tile_mfma(const TileFrags<C>& f, TileAcc<C>& acc, int nbv) {
   if constexpr (!ACT) return;
 #pragma unroll
-  for (int a = 0; a < C::AW; ++a)
+  for (int b = 0; b < C::AT; ++b)
+    if (!C::SKIPB || b < nbv) {
 #pragma unroll
-    for (int b = 0; b < C::AT; ++b) acc.v[a][b] = mfma16x16x32(f.a[a], f.b[b], acc.v[a][b]);
+      for (int a = 0; a < C::AW; ++a) acc.v[a][b] = mfma16x16x32(f.a[a], f.b[b], acc.v[a][b]);
+    }
 }
 
 // vmcnt wait that leaves `later` K steps of this wave's loads outstanding
 // (0 <= later <= NST - 2; wave-uniform).
+template <class C, int N>
+__device__ __forceinline__ void wait_steps_left_from(int later) {
+  if constexpr (N <= C::NST - 2) {
+    if (later == N) wait_vmcnt<N * (C::LW + C::LT)>();
+    else wait_steps_left_from<C, N + 1>(later);
+  }
+}
 template <class C>
 __device__ __forceinline__ void wait_steps_left(int later) {
-  constexpr int L = C::LW + C::LT;
-  if (later <= 0) {
-    wait_vmcnt<0>();
-  } else if constexpr (C::NST >= 3) {
-    if (later == 1) wait_vmcnt<L>();
-    else if constexpr (C::NST >= 4) wait_vmcnt<2 * L>();
-  }
+  if (later <= 0) wait_vmcnt<0>();
+  else wait_steps_left_from<C, 1>(later);
 }
 
 // One K step kt of the main loop.  On entry the operands of the step's first
@@ -185,7 +195,7 @@ __device__ __forceinline__ void wait_steps_left(int later) {
 template <class C, int PAR, bool ACT>
 __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, int KB, int nk, int kt,
                                           const TokRows<C>& trow, uint16_t* lds, TileFrags<C>& f0,
-                                          TileFrags<C>& f1, TileAcc<C>& acc) {
+                                          TileFrags<C>& f1, TileAcc<C>& acc, int nbv) {
   const uint16_t* st = lds + (kt % C::NST) * C::STAGE;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
@@ -196,22 +206,23 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, in
     // on those as well
     wait_lgkm0();
     if (ks + 1 < C::KS) {
-      tile_read_frags<C, ACT>(st, ks + 1, nxt);
+      tile_read_frags<C, ACT>(st, ks + 1, nxt, nbv);
     } else if (kt + 1 < nk) {
       wait_steps_left<C>(min(C::NST - 2, nk - 2 - kt));
       raw_barrier();
       if (kt + C::NST < nk) tile_issue<C>(wtile, KB, trow, lds, kt + C::NST);
-      tile_read_frags<C, ACT>(lds + ((kt + 1) % C::NST) * C::STAGE, 0, nxt);
+      tile_read_frags<C, ACT>(lds + ((kt + 1) % C::NST) * C::STAGE, 0, nxt, nbv);
     }
     __builtin_amdgcn_sched_barrier(0);
-    tile_mfma<C, ACT>(cur, acc);
+    tile_mfma<C, ACT>(cur, acc, nbv);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <class C, bool ACT>
 __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile, int KB, int nk,
-                                             const TokRows<C>& trow, uint16_t* lds, TileAcc<C>& acc) {
+                                             const TokRows<C>& trow, uint16_t* lds, TileAcc<C>& acc,
+                                             int nbv) {
 
   if constexpr (!C::DBUF) {
     // single operand set: steps 0 .. NST-2 in flight; step kt waits for its
@@ -228,8 +239,8 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         TileFrags<C> f;
-        tile_read_frags<C, ACT>(st, ks, f);
-        tile_mfma<C, ACT>(f, acc);
+        tile_read_frags<C, ACT>(st, ks, f, nbv);
+        tile_mfma<C, ACT>(f, acc, nbv);
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -245,15 +256,15 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
   if (C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, C::NST - 1);
   raw_barrier();
   TileFrags<C> f0, f1;
-  tile_read_frags<C, ACT>(lds, 0, f0);
+  tile_read_frags<C, ACT>(lds, 0, f0, nbv);
 
   constexpr int P1 = C::KS & 1;  // register-set parity of the step after an even step
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc);
-    tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc);
+    tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv);
+    tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc, nbv);
   }
-  if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc);
+  if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv);
   // all LDS reads of this tile done before anyone refills the stages
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   raw_barrier();
@@ -269,8 +280,9 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
 //           valid row by the caller)
 //   lds   : C::LDS_BYTES of shared memory
 //   tvalid: rows 0 .. tvalid-1 of the token tile are valid (wave-uniform);
-//           a wave whose token rows all lie past them skips its MFMA work,
-//           and its accumulators hold no meaningful values
+//           MFMA work on token rows past them is skipped (whole waves, or
+//           whole 16-row blocks with C::SKIPB), and the accumulators of
+//           skipped rows hold no meaningful values
 // All C::NTHREADS threads must call it.  On entry no direct-to-LDS load of this
 // workgroup may be in flight; on exit none is, and a barrier has passed, so
 // the caller may reuse lds right away.
@@ -283,10 +295,12 @@ __device__ __forceinline__ void tile_mma(const uint16_t* __restrict__ wtile, int
 #pragma unroll
     for (int b = 0; b < C::AT; ++b) acc.v[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   // both paths pass the same barriers in the same order
-  if (uniform(tile_wt<C>() * C::AT * 16) < tvalid)
-    tile_mma_run<C, true>(wtile, KB, nk, trow, lds, acc);
+  const int first = uniform(tile_wt<C>() * C::AT * 16);
+  const int nbv = C::SKIPB ? min(C::AT, (tvalid - first + 15) / 16) : C::AT;
+  if (first < tvalid)
+    tile_mma_run<C, true>(wtile, KB, nk, trow, lds, acc, nbv);
   else
-    tile_mma_run<C, false>(wtile, KB, nk, trow, lds, acc);
+    tile_mma_run<C, false>(wtile, KB, nk, trow, lds, acc, nbv);
 }
 
 }  // namespace moe

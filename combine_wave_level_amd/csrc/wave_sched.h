@@ -35,7 +35,7 @@ namespace moe {
 constexpr int kXcds = 8;                // XCDs of an MI355X
 constexpr int kSchedMaxExperts = 256;
 constexpr int kSchedMaxWaves = 256;
-constexpr int kCombineTokens = 16;      // tokens per combine task
+constexpr int kCombineTokens = 8;       // tokens per combine task
 constexpr int kCtrPad = 64;             // int32 words (256 B) between counters of different XCDs
 
 struct WaveSchedule {
@@ -59,7 +59,8 @@ struct Task {
   int expert;    // local expert (GEMM1 / GEMM2)
   int nt;        // output-feature tile (GEMM1 / GEMM2)
   int slot;      // combine: ready slot
-  int chunk;     // combine: global chunk of kCombineTokens tokens inside the slot
+  int chunk;     // combine: global chunk inside the slot: token chunk (of
+                 // kCombineTokens) chunk / cb_parts, column part chunk % cb_parts
 };
 
 // Binary search: the expert whose m-tile range holds mt, with
@@ -81,11 +82,12 @@ __host__ __device__ inline int sched_xcd_share(int n, int rot, int x) {
 // Builds XCD xcd's schedule from the dispatch tables.  offsets [E_local + 1]
 // = first pair row of each local expert; ready_off [W + 2] = first position
 // of each ready slot in the ready list.  BT = rows per m-tile.  NT1 / NT2 =
-// output tiles of GEMM1 / GEMM2 per m-tile.  with_combine = 0 drops the
-// combine tasks (no fused combine).
+// output tiles of GEMM1 / GEMM2 per m-tile.  cb_parts = column parts per
+// combine chunk of kCombineTokens tokens (0: no combine tasks, no fused
+// combine).
 __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offsets,
                                             const int32_t* ready_off, int E_local, int G, int BT,
-                                            int NT1, int NT2, int with_combine, int xcd) {
+                                            int NT1, int NT2, int cb_parts, int xcd) {
   S.W = E_local / G;
   S.G = G;
   S.NT1 = NT1;
@@ -113,8 +115,7 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
   }
   S.n_local = loc;
   for (int s = 0; s <= S.W; ++s) {
-    const int chunks =
-        with_combine ? (ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens : 0;
+    const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     S.n_cb[s] = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
   }
   run = 0;

@@ -4,7 +4,7 @@
 // (grouped into the 8 per-XCD streams) with std::atomic counters in place of
 // the device counters.
 //
-// stdin: E_local G BT NT1 NT2 with_combine threads_per_xcd seed
+// stdin: E_local G BT NT1 NT2 cb_parts threads_per_xcd seed   (cb_parts 0: no combine)
 //        offsets[E_local + 1]  ready_off[W + 2]
 // Checks (exit status 0 = all hold):
 //   1. structure: each wave's m-tiles are split into contiguous per-XCD
@@ -35,9 +35,9 @@ static int fail(const char* msg, long a = 0, long b = 0) {
 }
 
 int main() {
-  int E_local, G, BT, NT1, NT2, with_cb, per_xcd;
+  int E_local, G, BT, NT1, NT2, cb_parts, per_xcd;
   unsigned seed;
-  if (std::scanf("%d %d %d %d %d %d %d %u", &E_local, &G, &BT, &NT1, &NT2, &with_cb, &per_xcd, &seed) != 8)
+  if (std::scanf("%d %d %d %d %d %d %d %u", &E_local, &G, &BT, &NT1, &NT2, &cb_parts, &per_xcd, &seed) != 8)
     return fail("input");
   const int W = E_local / G;
   std::vector<int32_t> offsets(E_local + 1), ready_off(W + 2);
@@ -45,7 +45,7 @@ int main() {
   for (auto& v : ready_off) if (std::scanf("%d", &v) != 1) return fail("ready_off");
   static WaveSchedule S[kXcds];
   for (int x = 0; x < kXcds; ++x)
-    sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, with_cb, x);
+    sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x);
   const int nmt = S[0].mt_pre[E_local];
   const int rw = sched_region_words(W, nmt);
 
@@ -54,7 +54,7 @@ int main() {
   std::vector<int> g1_ticket(g1_owner.size(), -1), g2_ticket(g2_owner.size(), -1);
   std::vector<std::vector<int>> cb_seen(W + 1);
   for (int s = 0; s <= W; ++s) {
-    const int chunks = with_cb ? (ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens : 0;
+    const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     cb_seen[s].assign(chunks, 0);
   }
   for (int w = 0; w < W; ++w) {

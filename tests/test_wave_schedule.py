@@ -30,12 +30,12 @@ def emu(tmp_path_factory):
     return exe
 
 
-def _run(emu, counts, ready_counts, G, NT1, NT2, with_cb=1, threads=2, seed=1):
+def _run(emu, counts, ready_counts, G, NT1, NT2, cb_parts=1, threads=2, seed=1):
     E_local = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(int)
     ready_off = np.concatenate([[0], np.cumsum(ready_counts)]).astype(int)
     assert len(ready_off) == E_local // G + 2
-    inp = f"{E_local} {G} {BT} {NT1} {NT2} {with_cb} {threads} {seed}\n"
+    inp = f"{E_local} {G} {BT} {NT1} {NT2} {cb_parts} {threads} {seed}\n"
     inp += " ".join(map(str, offsets)) + "\n" + " ".join(map(str, ready_off)) + "\n"
     r = subprocess.run([emu], input=inp, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.startswith("OK"), r.stdout + r.stderr
@@ -85,9 +85,18 @@ def test_many_waves_one_expert_each(emu):
 
 
 def test_without_fused_combine_and_single_expert(emu):
-    _run(emu, [1000], [0, 7], G=1, NT1=16, NT2=56, with_cb=0)
+    _run(emu, [1000], [0, 7], G=1, NT1=16, NT2=56, cb_parts=0)
     _run(emu, [1], [3, 1], G=1, NT1=2, NT2=2, threads=1)
 
 
 def test_all_tokens_without_local_pick(emu):
     _run(emu, [0, 0, 0, 0], [64, 0, 0], G=2, NT1=2, NT2=2)
+
+
+def test_combine_split_into_column_parts(emu):
+    # small batch: every combine chunk of tokens split into 14 column ranges
+    rng = np.random.default_rng(3)
+    counts = list(rng.integers(0, 40, size=32))
+    ready = list(rng.integers(0, 20, size=9))
+    out = _run(emu, counts, ready, G=4, NT1=32, NT2=112, cb_parts=14, threads=3, seed=5)
+    assert "W=8" in out
