@@ -187,7 +187,13 @@ def main():
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
     roof["kernel"] = "ffn_waved_kernel" if not args.serial else "gemm1_phase_kernel+gemm2_phase_kernel+combine_kernel"
-    roof["traffic"] = None
+    # HBM bytes per launch from the committed rocprofv3 counter runs
+    # (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy), reported only
+    # while the kernel sources are the ones that were measured
+    from combine_wave_level_amd import profiling
+    trec = None if args.serial else profiling.load_traffic(
+        os.path.join(ROOT, "profiles", f"traffic_ffn_waved_kernel_{wl.name}_T{T}.json"), wl.name, T)
+    roof["traffic"] = trec["traffic_bytes"] if trec else None
 
     extra = {"route_ms": round(route_ms, 4), "dispatch_ms": round(disp_ms, 4), "ffn_ms": round(ffn_ms, 4),
              "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -152,9 +152,18 @@ __device__ __forceinline__ int wave0_atomic_add(int32_t* p, int v) {
   return uniform(__shfl(r, 0, kWave));
 }
 
-// Claims the next ticket of this XCD's stream for the workgroup.
-__device__ __forceinline__ int claim_ticket(int32_t* ticket, int32_t* s_ticket) {
-  if (wave_uniform() == 0) *s_ticket = wave0_atomic_add(ticket, 1);
+// Ticket claims are split in two so that the atomic's round trip overlaps
+// a task: wave 0 issues the claim of the next ticket when a task starts
+// (claim_issue; lane 0 adds 1, every lane gets its own return value) and
+// the workgroup reads it when the task ends (claim_finish).  A workgroup
+// thus holds one claimed ticket while it works on the previous one; since
+// every task waits only on smaller tickets, the smallest unfinished ticket
+// is always being worked on and every wait still ends.
+__device__ __forceinline__ int claim_issue(int32_t* ticket) {
+  return __hip_atomic_fetch_add(ticket, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int claim_finish(int r, int32_t* s_ticket) {
+  if (wave_uniform() == 0) *s_ticket = uniform(__shfl(r, 0, kWave));
   __syncthreads();
   const int tk = uniform(*s_ticket);
   __syncthreads();
@@ -205,12 +214,24 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   static_assert(C1::BT == C2::BT, "GEMM1 and GEMM2 share the m-tiles");
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ WaveSchedule S;
+  __shared__ int32_t s_off[kMaxLocalExperts + 1];  // expert row offsets
   __shared__ int32_t s_ticket;
   const int xcd = uniform(xcc_id());
-  if (threadIdx.x == 0)
-    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
-                A.out != nullptr ? A.cb_parts : 0, xcd);
+  if (threadIdx.x == 0) {
+    // GEMM2 lag: enough GEMM1 tiles in between for every workgroup of the XCD
+    const int NT1 = 2 * A.I / C1::BW;
+    const int per_xcd = (static_cast<int>(gridDim.x) + kXcds - 1) / kXcds;
+    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, NT1, A.d / C2::BW,
+                A.out != nullptr ? A.cb_parts : 0, xcd, (per_xcd + NT1 - 1) / NT1);
+  }
+  for (int e = threadIdx.x; e <= A.E_local; e += F::NT) s_off[e] = A.offsets[e];
   __syncthreads();
+  if (uniform(S.err) != 0) {
+    // more m-tiles on this XCD than the schedule holds (the host bounds this)
+    if (wave_uniform() == 0 && lane_id() == 0)
+      __hip_atomic_store(A.err, static_cast<int32_t>(MOE_ERR_UNSUPPORTED), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const int total = uniform(S.total);
   const int NT1 = uniform(S.NT1);
   const int rw = A.region_words;
@@ -219,10 +240,14 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   // Every value that steers this loop is made wave-uniform explicitly (the
   // ticket and the decoded task come from LDS), so all waves run the same
   // iterations between barriers.
-  for (int tk = claim_ticket(ticket, &s_ticket); tk < total; tk = claim_ticket(ticket, &s_ticket)) {
+  int claim = 0;
+  if (wave_uniform() == 0) claim = claim_issue(ticket);
+  for (int tk = claim_finish(claim, &s_ticket); tk < total; tk = claim_finish(claim, &s_ticket)) {
+    if (wave_uniform() == 0) claim = claim_issue(ticket);
     Task t = sched_decode(S, tk);
     t.kind = uniform(t.kind);
     t.wave = uniform(t.wave);
+    t.loc = uniform(t.loc);
     t.mt = uniform(t.mt);
     t.expert = uniform(t.expert);
     t.nt = uniform(t.nt);
@@ -230,22 +255,22 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
     t.chunk = uniform(t.chunk);
     if (t.kind == kTaskGemm1) {
       // GEMM1 + SwiGLU tile (its operand rows pulled from the staging x)
-      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * C1::BT);
-      const int count = uniform(min(C1::BT, A.offsets[t.expert + 1] - row0));
+      const int row0 = uniform(s_off[t.expert] + (t.mt - S.mt_pre[t.expert]) * C1::BT);
+      const int count = uniform(min(C1::BT, s_off[t.expert + 1] - row0));
       gemm1_tile<C1>(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token,
                      A.act, row0, count, t.nt, A.d, A.I, lds);
-      local_signal(A.ctr + sched_g1done_index(S, rw, t.wave, t.mt));
+      local_signal(A.ctr + sched_g1done_index(S, rw, t.loc));
     } else if (t.kind == kTaskGemm2) {
       // GEMM2 tile, once every GEMM1 tile of its m-tile is done (same XCD)
-      const int row0 = uniform(A.offsets[t.expert] + (t.mt - S.mt_pre[t.expert]) * C2::BT);
-      const int count = uniform(min(C2::BT, A.offsets[t.expert + 1] - row0));
-      local_wait(A.ctr + sched_g1done_index(S, rw, t.wave, t.mt), NT1, A.timeout_ticks, A.err);
+      const int row0 = uniform(s_off[t.expert] + (t.mt - S.mt_pre[t.expert]) * C2::BT);
+      const int count = uniform(min(C2::BT, s_off[t.expert + 1] - row0));
+      local_wait(A.ctr + sched_g1done_index(S, rw, t.loc), NT1, A.timeout_ticks, A.err);
       gemm2_tile<C2>(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count,
                      t.nt, A.d, A.I, lds);
       wait_vmcnt<0>();
       __syncthreads();
       if (wave_uniform() == 0) {
-        const int mine = uniform(S.n_g2[t.wave]);
+        const int mine = uniform(sched_g2_of_wave(S, t.wave));
         const int done = wave0_atomic_add(A.ctr + sched_g2local_index(S, rw, t.wave), 1) + 1;
         if (done == mine) {
           // last GEMM2 tile of this wave on this XCD: write the L2 back once,
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
     } else {
       // combine of tokens whose last local wave is t.slot - 1
       for (int w = 0; w <= t.slot - 1; ++w)
-        poll_geq(A.ctr + sched_g2all_index(S, rw, w), uniform(S.g2_all[w]), A.timeout_ticks, A.err);
+        poll_geq(A.ctr + sched_g2all_index(S, rw, w), uniform(sched_g2_all(S, w)), A.timeout_ticks, A.err);
       __syncthreads();
       const int parts = A.cb_parts;
       const int base = uniform(A.ready_off[t.slot] + (t.chunk / parts) * kCombineTokens);
@@ -305,6 +330,10 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   const bool out_bf16 = p.out_dtype == MOE_BF16;
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+  // the persistent schedule holds at most kSchedMaxLocal m-tiles per XCD;
+  // larger problems run the phase-by-phase path (same kernels, same bits)
+  const long long mt_bound = static_cast<long long>(L.P_max) / F::G1::BT + p.E_local + 1;
+  if (mt_bound / kXcds + L.W + 1 > kSchedMaxLocal) flags |= MOE_FLAG_SERIAL;
   if (flags & MOE_FLAG_SERIAL) {
     constexpr size_t l1 = F::G1::LDS_BYTES, l2 = F::G2::LDS_BYTES;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel<F>, F::NT, l1)) != hipSuccess)

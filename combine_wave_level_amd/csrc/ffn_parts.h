@@ -36,12 +36,12 @@ struct FfnMid {
 };
 struct FfnSmall {
   using G1 = TileCfg<128, 32, 4, 1, 64, 7, true>;
-  using G2 = TileCfg<64, 32, 4, 1, 128, 6, true>;
+  using G2 = TileCfg<128, 32, 4, 1, 64, 7, true>;
   static constexpr int NT = 256;
 };
 struct FfnSmall64 {
   using G1 = TileCfg<128, 64, 4, 1, 64, 6, true>;
-  using G2 = TileCfg<64, 64, 4, 1, 64, 8, true>;
+  using G2 = TileCfg<128, 64, 4, 1, 64, 6, true>;
   static constexpr int NT = 256;
 };
 template <class F>

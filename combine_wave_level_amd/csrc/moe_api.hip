@@ -33,10 +33,8 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.W = p.E_local / p.experts_per_wave;
   L.ngroups = p.E_local + L.W + 1;
   L.P_max = p.T * (p.k < p.E_local ? p.k : p.E_local);
-  // m-tiles of the smallest tile shape (16 rows) bound every shape's count
-  const int max_mtiles = L.P_max / 16 + p.E_local + 1;
-  L.ctr_region_words = sched_region_words(L.W, max_mtiles);
-  L.sync_words = sched_counter_words(L.W, max_mtiles);
+  L.ctr_region_words = sched_region_words(L.W);
+  L.sync_words = sched_counter_words(L.W);
   const size_t wg_slots = static_cast<size_t>(L.P_max) / kWgradChunkRows;
   L.wgrad_bytes = wg_slots * 3 * static_cast<size_t>(p.d) * p.I * sizeof(float);
   size_t off = 0;

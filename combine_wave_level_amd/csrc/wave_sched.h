@@ -14,17 +14,23 @@
 // GEMM2 dependencies therefore never leave an XCD's L2; only the combine,
 // which reads y rows of every XCD, crosses XCDs.
 //
-// Inside one XCD's stream, block b of the ticket sequence holds
-//   GEMM1 tiles of the XCD's m-tiles in wave b (their operand loads are the
-//                                              dispatch pulls),
-//   GEMM2 tiles of the XCD's m-tiles in wave b-1,
-//   the XCD's share of the combine chunks of ready slot b-1 (tokens whose
-//   last local wave is b-2; slot 0 = tokens with no local pick),
-// for b = 0 .. W+1.  A GEMM2 tile waits for its m-tile's GEMM1 tiles (same
-// stream, smaller tickets).  A combine task waits until every XCD finished
-// the GEMM2 tiles of waves <= its slot - 1; those tiles sit in blocks <=
-// slot of every stream and wait only on smaller tickets of their own
-// stream, so by induction over the waves every wait ends, for any grid.
+// Inside one XCD's stream the XCD's m-tiles are taken in wave order,
+// m_0 .. m_{n-1}, and the tickets run through positions i = 0 .. n+L-1:
+//   the GEMM1 tiles of m_i (i < n; their operand loads are the dispatch
+//   pulls),
+//   the GEMM2 tiles of m_{i-L} (i >= L),
+//   the XCD's share of the combine chunks of every ready slot s whose
+//   position is i (tokens whose last local wave is s-1; slot 0 = tokens with
+//   no local pick): the position of the GEMM2 tiles of the XCD's last m-tile
+//   of a wave <= s + 1.
+// GEMM2 of an m-tile thus trails its GEMM1 by L m-tiles, L chosen so that
+// the GEMM1 tiles in between occupy every workgroup of the XCD while the
+// m-tile's own GEMM1 tiles finish.  A GEMM2 tile waits for its m-tile's
+// GEMM1 tiles (same stream, smaller tickets).  A combine task waits until
+// every XCD finished the GEMM2 tiles of waves <= its slot - 1; in every
+// stream those tiles sit at smaller tickets than that stream's combine
+// tasks of the slot and wait only on smaller tickets of their own stream,
+// so every wait ends, for any grid.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,19 +41,19 @@ namespace moe {
 constexpr int kXcds = 8;                // XCDs of an MI355X
 constexpr int kSchedMaxExperts = 256;
 constexpr int kSchedMaxWaves = 256;
+constexpr int kSchedMaxLocal = 640;     // m-tiles of one XCD
+constexpr int kSchedMaxLag = 64;       // GEMM2 lag, in m-tiles
 constexpr int kCombineTokens = 8;       // tokens per combine task
 constexpr int kCtrPad = 64;             // int32 words (256 B) between counters of different XCDs
 
 struct WaveSchedule {
-  int W, G, NT1, NT2, total, xcd, n_local;
+  int W, G, NT1, NT2, total, xcd, n_local, lag, err;
   int32_t mt_pre[kSchedMaxExperts + 1];  // first m-tile of each local expert
-  int32_t blk_start[kSchedMaxWaves + 3]; // first ticket of block b, b = 0 .. W+2
   int32_t mlo[kSchedMaxWaves];           // first m-tile of this XCD in wave w
-  int32_t loc_pre[kSchedMaxWaves];       // this XCD's m-tiles in waves < w
-  int32_t n_g1[kSchedMaxWaves];          // this XCD's GEMM1 tiles of wave w
-  int32_t n_g2[kSchedMaxWaves];          // this XCD's GEMM2 tiles of wave w
-  int32_t g2_all[kSchedMaxWaves];        // GEMM2 tiles of wave w over all XCDs
-  int32_t n_cb[kSchedMaxWaves + 1];      // this XCD's combine chunks of slot s
+  int32_t loc_pre[kSchedMaxWaves + 1];   // this XCD's m-tiles in waves < w (loc_pre[W] = n_local)
+  int32_t cb_pre[kSchedMaxWaves + 2];    // this XCD's combine tasks of slots < s
+  int32_t pos[kSchedMaxLocal + kSchedMaxLag + 1];     // first ticket of position i, i = 0 .. n+L
+  int32_t cb_pos[kSchedMaxLocal + kSchedMaxLag + 1];  // this XCD's combine tasks at positions < i
 };
 
 enum TaskKind { kTaskGemm1 = 0, kTaskGemm2 = 1, kTaskCombine = 2 };
@@ -55,6 +61,7 @@ enum TaskKind { kTaskGemm1 = 0, kTaskGemm2 = 1, kTaskCombine = 2 };
 struct Task {
   int kind;
   int wave;      // GEMM1 / GEMM2: expert wave of the tile
+  int loc;       // GEMM1 / GEMM2: index of the m-tile among this XCD's m-tiles
   int mt;        // global m-tile index (GEMM1 / GEMM2)
   int expert;    // local expert (GEMM1 / GEMM2)
   int nt;        // output-feature tile (GEMM1 / GEMM2)
@@ -63,14 +70,18 @@ struct Task {
                  // kCombineTokens) chunk / cb_parts, column part chunk % cb_parts
 };
 
-// Binary search: the expert whose m-tile range holds mt, with
-// mt_pre[lo] <= mt < mt_pre[hi].
-__host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, int hi, int mt) {
+// Largest i in [lo, hi) with a[i] <= v, given a[lo] <= v (a nondecreasing).
+__host__ __device__ inline int sched_last_leq(const int32_t* a, int lo, int hi, int v) {
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (mt_pre[mid] <= mt) lo = mid; else hi = mid;
+    if (a[mid] <= v) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+// The expert whose m-tile range holds mt, with mt_pre[lo] <= mt < mt_pre[hi].
+__host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, int hi, int mt) {
+  return sched_last_leq(mt_pre, lo, hi, mt);
 }
 
 // Share of XCD x when n m-tiles of one wave are split over the XCDs and the
@@ -84,15 +95,18 @@ __host__ __device__ inline int sched_xcd_share(int n, int rot, int x) {
 // of each ready slot in the ready list.  BT = rows per m-tile.  NT1 / NT2 =
 // output tiles of GEMM1 / GEMM2 per m-tile.  cb_parts = column parts per
 // combine chunk of kCombineTokens tokens (0: no combine tasks, no fused
-// combine).
+// combine).  lag = L (1 .. kSchedMaxLag).  S.err = 1 if the XCD holds more
+// than kSchedMaxLocal m-tiles (the schedule is then empty).
 __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offsets,
                                             const int32_t* ready_off, int E_local, int G, int BT,
-                                            int NT1, int NT2, int cb_parts, int xcd) {
+                                            int NT1, int NT2, int cb_parts, int xcd, int lag) {
   S.W = E_local / G;
+  S.lag = lag < 1 ? 1 : (lag > kSchedMaxLag ? kSchedMaxLag : lag);
   S.G = G;
   S.NT1 = NT1;
   S.NT2 = NT2;
   S.xcd = xcd;
+  S.err = 0;
   int run = 0;
   for (int e = 0; e < E_local; ++e) {
     S.mt_pre[e] = run;
@@ -104,60 +118,100 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     const int a = S.mt_pre[w * G], n = S.mt_pre[(w + 1) * G] - a;
     int lo = a;
     for (int y = 0; y < xcd; ++y) lo += sched_xcd_share(n, rot, y);
-    const int cnt = sched_xcd_share(n, rot, xcd);
     S.mlo[w] = lo;
     S.loc_pre[w] = loc;
-    loc += cnt;
-    S.n_g1[w] = cnt * NT1;
-    S.n_g2[w] = cnt * NT2;
-    S.g2_all[w] = n * NT2;
+    loc += sched_xcd_share(n, rot, xcd);
     rot = (rot + n % kXcds) % kXcds;
   }
+  S.loc_pre[S.W] = loc;
   S.n_local = loc;
+  if (loc > kSchedMaxLocal) {
+    S.err = 1;
+    S.n_local = 0;
+    S.total = 0;
+    return;
+  }
+  // combine tasks of this XCD per slot, and the position of each slot
+  const int L = S.lag, npos = loc + L;  // positions 0 .. npos - 1
+  int cb = 0;
+  for (int i = 0; i <= npos; ++i) S.cb_pos[i] = 0;
   for (int s = 0; s <= S.W; ++s) {
+    S.cb_pre[s] = cb;
     const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
-    S.n_cb[s] = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
+    const int mine = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
+    cb += mine;
+    // position of the GEMM2 tiles of the last m-tile of a wave <= s + 1
+    // (slot s needs waves <= s - 1 of every XCD: two waves of slack for
+    // XCDs that run behind this one)
+    const int last = S.loc_pre[s + 2 < S.W ? s + 2 : S.W] - 1;
+    const int at = last >= 0 ? last + L : 0;
+    S.cb_pos[at + 1] += mine;  // counted from position at + 1 on
   }
+  S.cb_pre[S.W + 1] = cb;
+  // cb_pos[i] = combine tasks at positions < i (prefix of the per-position counts)
+  for (int i = 1; i <= npos; ++i) S.cb_pos[i] += S.cb_pos[i - 1];
   run = 0;
-  for (int b = 0; b <= S.W + 1; ++b) {
-    S.blk_start[b] = run;
-    if (b < S.W) run += S.n_g1[b];
-    if (b >= 1 && b <= S.W) run += S.n_g2[b - 1];
-    if (b >= 1) run += S.n_cb[b - 1];
+  for (int i = 0; i < npos; ++i) {
+    S.pos[i] = run;
+    if (i < loc) run += NT1;
+    if (i >= L) run += NT2;
+    run += S.cb_pos[i + 1] - S.cb_pos[i];
   }
-  S.blk_start[S.W + 2] = run;
+  S.pos[npos] = run;
   S.total = run;
+}
+
+// GEMM2 tiles of wave w on this XCD.
+__host__ __device__ inline int sched_g2_of_wave(const WaveSchedule& S, int w) {
+  return (S.loc_pre[w + 1] - S.loc_pre[w]) * S.NT2;
+}
+// GEMM2 tiles of wave w over all XCDs.
+__host__ __device__ inline int sched_g2_all(const WaveSchedule& S, int w) {
+  return (S.mt_pre[(w + 1) * S.G] - S.mt_pre[w * S.G]) * S.NT2;
+}
+
+// Fills the m-tile fields of t for this XCD's m-tile j.
+__host__ __device__ inline void sched_local_mtile(const WaveSchedule& S, int j, Task& t) {
+  // wave w with loc_pre[w] <= j < loc_pre[w + 1] (waves without local m-tiles skipped)
+  int w = sched_last_leq(S.loc_pre, 0, S.W, j);
+  while (S.loc_pre[w + 1] <= j) ++w;
+  t.wave = w;
+  t.loc = j;
+  t.mt = S.mlo[w] + (j - S.loc_pre[w]);
+  t.expert = sched_expert_of(S.mt_pre, w * S.G, (w + 1) * S.G, t.mt);
 }
 
 // Decodes ticket tk (0 <= tk < S.total) of this XCD's stream.
 __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
-  int b = 0;
-  while (S.blk_start[b + 1] <= tk) ++b;
-  int rel = tk - S.blk_start[b];
+  const int n = S.n_local, L = S.lag;
+  const int i = sched_last_leq(S.pos, 0, n + L, tk);
+  int o = tk - S.pos[i];
   Task t{};
-  const int g1n = (b < S.W) ? S.n_g1[b] : 0;
-  const int g2n = (b >= 1 && b <= S.W) ? S.n_g2[b - 1] : 0;
-  if (rel < g1n) {
-    t.kind = kTaskGemm1;
-    t.wave = b;
-    t.mt = S.mlo[b] + rel / S.NT1;
-    t.nt = rel % S.NT1;
-    t.expert = sched_expert_of(S.mt_pre, b * S.G, (b + 1) * S.G, t.mt);
-    return t;
+  if (i < n) {
+    if (o < S.NT1) {
+      t.kind = kTaskGemm1;
+      t.nt = o;
+      sched_local_mtile(S, i, t);
+      return t;
+    }
+    o -= S.NT1;
   }
-  rel -= g1n;
-  if (rel < g2n) {
-    t.kind = kTaskGemm2;
-    t.wave = b - 1;
-    t.mt = S.mlo[b - 1] + rel / S.NT2;
-    t.nt = rel % S.NT2;
-    t.expert = sched_expert_of(S.mt_pre, (b - 1) * S.G, b * S.G, t.mt);
-    return t;
+  if (i >= L) {
+    if (o < S.NT2) {
+      t.kind = kTaskGemm2;
+      t.nt = o;
+      sched_local_mtile(S, i - L, t);
+      return t;
+    }
+    o -= S.NT2;
   }
-  rel -= g2n;
   t.kind = kTaskCombine;
-  t.slot = b - 1;
-  t.chunk = S.xcd + kXcds * rel;
+  const int idx = S.cb_pos[i] + o;
+  // slot s with cb_pre[s] <= idx < cb_pre[s + 1] (slots without tasks skipped)
+  int sl = sched_last_leq(S.cb_pre, 0, S.W + 1, idx);
+  while (S.cb_pre[sl + 1] <= idx) ++sl;
+  t.slot = sl;
+  t.chunk = S.xcd + kXcds * (idx - S.cb_pre[sl]);
   return t;
 }
 
@@ -166,24 +220,21 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
 //   [x * kCtrPad]                   ticket of XCD x
 //   region(x) = kXcds * kCtrPad + x * region_words:
 //     region(x) + w                 GEMM2 tiles of wave w finished on XCD x
-//     region(x) + W + j             GEMM1 tiles finished of XCD x's j-th m-tile
-//                                   (j = loc_pre[w] + mt - mlo[w])
+//     region(x) + W + j             GEMM1 tiles finished of XCD x's m-tile j
 //   kXcds * (kCtrPad + region_words) + w   GEMM2 tiles of wave w finished, all XCDs
-// region_words >= W + (m-tiles of one XCD), rounded up to kCtrPad; one XCD
-// holds at most max_mtiles / kXcds + W m-tiles (one extra per wave at most).
-__host__ __device__ inline int sched_region_words(int W, int max_mtiles) {
-  const int per_xcd = max_mtiles / kXcds + W + 1;
-  return ((W + per_xcd + kCtrPad - 1) / kCtrPad) * kCtrPad;
+// region_words >= W + kSchedMaxLocal, rounded up to kCtrPad.
+__host__ __device__ inline int sched_region_words(int W) {
+  return ((W + kSchedMaxLocal + kCtrPad - 1) / kCtrPad) * kCtrPad;
 }
-__host__ __device__ inline size_t sched_counter_words(int W, int max_mtiles) {
-  return static_cast<size_t>(kXcds) * (kCtrPad + sched_region_words(W, max_mtiles)) + W + kCtrPad;
+__host__ __device__ inline size_t sched_counter_words(int W) {
+  return static_cast<size_t>(kXcds) * (kCtrPad + sched_region_words(W)) + W + kCtrPad;
 }
 __host__ __device__ inline int sched_ticket_index(int xcd) { return xcd * kCtrPad; }
 __host__ __device__ inline int sched_g2local_index(const WaveSchedule& S, int rw, int w) {
   return kXcds * kCtrPad + S.xcd * rw + w;
 }
-__host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int rw, int w, int mt) {
-  return kXcds * kCtrPad + S.xcd * rw + S.W + S.loc_pre[w] + (mt - S.mlo[w]);
+__host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int rw, int loc) {
+  return kXcds * kCtrPad + S.xcd * rw + S.W + loc;
 }
 __host__ __device__ inline int sched_g2all_index(const WaveSchedule& S, int rw, int w) {
   return kXcds * (kCtrPad + rw) + w;

@@ -1,0 +1,161 @@
+"""Profiling helpers: HBM-traffic calibration and rocprofv3 summaries.
+
+    python -m combine_wave_level_amd.profiling copy [--mib N] [--reps R]
+        A plain device-to-device copy of N MiB (R times): the reference whose
+        FETCH_SIZE / WRITE_SIZE counters calibrate the traffic counters.
+
+    python -m combine_wave_level_amd.profiling summarize --stats S.csv
+        --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
+        --kernel NAME --workload W --T T --command "..." --out-md X.md
+        --out-json X.json [--copy-mib N]
+        Writes a short markdown summary (kernel durations from the
+        --kernel-trace --stats run, HBM bytes per launch of NAME) and the JSON
+        record bench.py reports as roofline.traffic.
+
+The traffic record carries a digest of the HIP sources; bench.py reports it
+only while the sources still hash to the same digest (a changed kernel makes
+the measured bytes stale).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and headers of the library, in name order."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(path: str, workload: str, T: int):
+    """The traffic record at path if it matches the workload, T and the
+    current sources; else None."""
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest() or rec.get("workload") != workload or rec.get("T") != T:
+        return None
+    return rec
+
+
+def _copy(args) -> None:
+    import torch
+
+    n = args.mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": args.reps}))
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _kernel_counter(path, pattern, counter):
+    """Mean per dispatch of `counter` over dispatches whose name matches."""
+    vals = [float(r["Counter_Value"]) for r in _rows(path)
+            if re.search(pattern, r["Kernel_Name"]) and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for /{pattern}/ in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _short(name: str) -> str:
+    name = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    name = re.sub(r"\([^()]*\)$", "", name)  # argument list
+    return name.replace("moe::", "")
+
+
+def _summarize(a) -> None:
+    stats = _rows(a.stats)
+    lines = [f"# {a.kernel}: {a.workload}, T={a.T}", "",
+             "Commands (from /tmp on the GPU host, TMPDIR=/tmp; REPO = repository root, OUT = $REPO/gpurun_out/prof):", ""]
+    for c in a.command:
+        lines.append(f"    {c}")
+    lines += ["", "Kernel durations (--kernel-trace --stats):", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    fetch_kib, nf = _kernel_counter(a.fetch, a.kernel, "FETCH_SIZE")
+    write_kib, nw = _kernel_counter(a.write, a.kernel, "WRITE_SIZE")
+    cf_kib, _ = _kernel_counter(a.copy_fetch, a.copy_kernel, "FETCH_SIZE")
+    cw_kib, _ = _kernel_counter(a.copy_write, a.copy_kernel, "WRITE_SIZE")
+    copy_bytes = a.copy_mib * (1 << 20)
+    f_fetch = cf_kib * 1024.0 / copy_bytes
+    f_write = cw_kib * 1024.0 / copy_bytes
+    fetch_b = fetch_kib * 1024.0 / f_fetch
+    write_b = write_kib * 1024.0 / f_write
+    avg_ns = [float(r["AverageNs"]) for r in stats if re.search(a.kernel, r["Name"])]
+    lines += ["", f"HBM traffic per launch of {a.kernel} (--pmc FETCH_SIZE, --pmc WRITE_SIZE; "
+              f"{nf} and {nw} dispatches):", "",
+              f"- FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch;",
+              f"- a plain {a.copy_mib} MiB copy reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE "
+              f"{cw_kib:.0f} KiB: factors {f_fetch:.3f} (fetch) and {f_write:.3f} (write) per byte moved;",
+              f"- calibrated: {fetch_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written = "
+              f"{(fetch_b + write_b) / 1e6:.1f} MB per launch"]
+    if avg_ns:
+        lines.append(f"- at the average duration {avg_ns[0] / 1e3:.1f} us: "
+                     f"{(fetch_b + write_b) / (avg_ns[0] * 1e-9) / 1e9:.0f} GB/s")
+    rec = {"kernel": a.kernel, "workload": a.workload, "T": a.T, "source_digest": source_digest(),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "traffic_bytes": round(fetch_b + write_b), "fetch_factor": round(f_fetch, 4),
+           "write_factor": round(f_write, 4), "avg_us": round(avg_ns[0] / 1e3, 2) if avg_ns else None}
+    lines += ["", f"Source digest of the measured kernels: `{rec['source_digest'][:16]}`", ""]
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines))
+    with open(a.out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(prog="python -m combine_wave_level_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=3)
+    s = sub.add_parser("summarize")
+    s.add_argument("--stats", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--copy-fetch", required=True)
+    s.add_argument("--copy-write", required=True)
+    s.add_argument("--copy-mib", type=int, default=1024)
+    s.add_argument("--copy-kernel", default="copy|Copy")
+    s.add_argument("--kernel", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--T", type=int, required=True)
+    s.add_argument("--command", action="append", default=[])
+    s.add_argument("--out-md", required=True)
+    s.add_argument("--out-json", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "copy":
+        _copy(a)
+    else:
+        _summarize(a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

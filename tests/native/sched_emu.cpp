@@ -4,7 +4,7 @@
 // (grouped into the 8 per-XCD streams) with std::atomic counters in place of
 // the device counters.
 //
-// stdin: E_local G BT NT1 NT2 cb_parts threads_per_xcd seed   (cb_parts 0: no combine)
+// stdin: E_local G BT NT1 NT2 cb_parts threads_per_xcd seed lag   (cb_parts 0: no combine)
 //        offsets[E_local + 1]  ready_off[W + 2]
 // Checks (exit status 0 = all hold):
 //   1. structure: each wave's m-tiles are split into contiguous per-XCD
@@ -14,7 +14,9 @@
 //      GEMM tiles of an m-tile live in the stream of the XCD owning it;
 //      decoded experts own their m-tiles and belong to the decoded wave;
 //      every XCD's counters fit its region;
-//   2. every GEMM2 tile waits only on smaller tickets of its own stream;
+//   2. every GEMM2 tile waits only on smaller tickets of its own stream, and
+//      every combine task of slot s comes after all of its stream's GEMM2
+//      tiles of waves < s (no stream can block on its own later tickets);
 //   3. an emulated run completes and every counter ends at its target.
 #include <atomic>
 #include <chrono>
@@ -35,9 +37,9 @@ static int fail(const char* msg, long a = 0, long b = 0) {
 }
 
 int main() {
-  int E_local, G, BT, NT1, NT2, cb_parts, per_xcd;
+  int E_local, G, BT, NT1, NT2, cb_parts, per_xcd, lag;
   unsigned seed;
-  if (std::scanf("%d %d %d %d %d %d %d %u", &E_local, &G, &BT, &NT1, &NT2, &cb_parts, &per_xcd, &seed) != 8)
+  if (std::scanf("%d %d %d %d %d %d %d %u %d", &E_local, &G, &BT, &NT1, &NT2, &cb_parts, &per_xcd, &seed, &lag) != 9)
     return fail("input");
   const int W = E_local / G;
   std::vector<int32_t> offsets(E_local + 1), ready_off(W + 2);
@@ -45,9 +47,11 @@ int main() {
   for (auto& v : ready_off) if (std::scanf("%d", &v) != 1) return fail("ready_off");
   static WaveSchedule S[kXcds];
   for (int x = 0; x < kXcds; ++x)
-    sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x);
+    sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag);
+  for (int x = 0; x < kXcds; ++x)
+    if (S[x].err) fail("schedule overflow", x, S[x].n_local);
   const int nmt = S[0].mt_pre[E_local];
-  const int rw = sched_region_words(W, nmt);
+  const int rw = sched_region_words(W);
 
   // ---- 1. structure, 2. in-stream dependencies
   std::vector<int> g1_owner(static_cast<size_t>(nmt) * NT1, -1), g2_owner(static_cast<size_t>(nmt) * NT2, -1);
@@ -61,7 +65,7 @@ int main() {
     int expect = S[0].mt_pre[w * G], lo = 1 << 30, hi = -1;
     for (int x = 0; x < kXcds; ++x) {
       if (S[x].mlo[w] != expect) fail("per-wave XCD ranges not contiguous", w, x);
-      const int cnt = NT1 > 0 ? S[x].n_g1[w] / NT1 : 0;
+      const int cnt = S[x].loc_pre[w + 1] - S[x].loc_pre[w];
       expect += cnt;
       lo = cnt < lo ? cnt : lo;
       hi = cnt > hi ? cnt : hi;
@@ -88,8 +92,9 @@ int main() {
         if (cb_seen[t.slot][t.chunk]++) fail("combine chunk twice", t.slot, t.chunk);
         continue;
       }
-      if (t.mt < S[x].mlo[t.wave] || t.mt >= S[x].mlo[t.wave] + S[x].n_g1[t.wave] / (NT1 > 0 ? NT1 : 1))
+      if (t.mt < S[x].mlo[t.wave] || t.mt >= S[x].mlo[t.wave] + (S[x].loc_pre[t.wave + 1] - S[x].loc_pre[t.wave]))
         fail("m-tile outside the XCD's range", x, t.mt);
+      if (t.loc != S[x].loc_pre[t.wave] + (t.mt - S[x].mlo[t.wave])) fail("local m-tile index", x, t.loc);
       if (t.mt < S[x].mt_pre[t.expert] || t.mt >= S[x].mt_pre[t.expert + 1]) fail("expert does not own m-tile", tk, t.mt);
       if (t.expert / G != t.wave) fail("expert not in wave", tk, t.expert);
       const int NT = t.kind == kTaskGemm1 ? NT1 : NT2;
@@ -100,6 +105,19 @@ int main() {
       if (own[id] != -1) fail("tile twice", tk, t.mt);
       own[id] = x;
       tck[id] = tk;
+    }
+  }
+  for (int x = 0; x < kXcds; ++x) {
+    std::vector<int> last_g2(W, -1);
+    for (int tk = 0; tk < S[x].total; ++tk) {
+      const Task t = sched_decode(S[x], tk);
+      if (t.kind == kTaskGemm2) last_g2[t.wave] = tk;
+    }
+    for (int tk = 0; tk < S[x].total; ++tk) {
+      const Task t = sched_decode(S[x], tk);
+      if (t.kind != kTaskCombine) continue;
+      for (int w = 0; w < t.slot; ++w)
+        if (last_g2[w] > tk) fail("combine task before its stream's GEMM2 of an earlier wave", x, tk);
     }
   }
   for (int v : g1_owner) if (v < 0) fail("GEMM1 tile without ticket");
@@ -117,7 +135,7 @@ int main() {
     }
 
   // ---- 3. emulated run
-  const size_t nctr = sched_counter_words(W, nmt);
+  const size_t nctr = sched_counter_words(W);
   std::vector<std::atomic<int>> ctr(nctr);
   for (auto& c : ctr) c.store(0);
   std::atomic<int> done_tasks{0};
@@ -137,13 +155,13 @@ int main() {
       const Task t = sched_decode(s, tk);
       if (rng() % 4 == 0) std::this_thread::sleep_for(std::chrono::microseconds(rng() % 200));
       if (t.kind == kTaskGemm1) {
-        ctr[sched_g1done_index(s, rw, t.wave, t.mt)].fetch_add(1, std::memory_order_release);
+        ctr[sched_g1done_index(s, rw, t.loc)].fetch_add(1, std::memory_order_release);
       } else if (t.kind == kTaskGemm2) {
-        wait_geq(sched_g1done_index(s, rw, t.wave, t.mt), s.NT1);
+        wait_geq(sched_g1done_index(s, rw, t.loc), s.NT1);
         const int done = ctr[sched_g2local_index(s, rw, t.wave)].fetch_add(1) + 1;
-        if (done == s.n_g2[t.wave]) ctr[sched_g2all_index(s, rw, t.wave)].fetch_add(done);
+        if (done == sched_g2_of_wave(s, t.wave)) ctr[sched_g2all_index(s, rw, t.wave)].fetch_add(done);
       } else {
-        for (int w = 0; w < t.slot; ++w) wait_geq(sched_g2all_index(s, rw, w), s.g2_all[w]);
+        for (int w = 0; w < t.slot; ++w) wait_geq(sched_g2all_index(s, rw, w), sched_g2_all(s, w));
       }
       done_tasks.fetch_add(1);
     }
@@ -156,11 +174,10 @@ int main() {
   for (int x = 0; x < kXcds; ++x) total += S[x].total;
   if (done_tasks.load() != total) fail("tasks done", done_tasks.load(), total);
   for (int x = 0; x < kXcds; ++x)
-    for (int w = 0; w < W; ++w)
-      for (int mt = S[x].mlo[w]; mt < S[x].mlo[w] + S[x].n_g1[w] / (NT1 > 0 ? NT1 : 1); ++mt)
-        if (ctr[sched_g1done_index(S[x], rw, w, mt)].load() != NT1) fail("g1done count", mt);
+    for (int j = 0; j < S[x].n_local; ++j)
+      if (ctr[sched_g1done_index(S[x], rw, j)].load() != NT1) fail("g1done count", x, j);
   for (int w = 0; w < W; ++w)
-    if (ctr[sched_g2all_index(S[0], rw, w)].load() != S[0].g2_all[w]) fail("g2 all count", w);
+    if (ctr[sched_g2all_index(S[0], rw, w)].load() != sched_g2_all(S[0], w)) fail("g2 all count", w);
   std::printf("OK total=%d W=%d mtiles=%d\n", total, W, nmt);
   return 0;
 }

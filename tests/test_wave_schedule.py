@@ -30,12 +30,12 @@ def emu(tmp_path_factory):
     return exe
 
 
-def _run(emu, counts, ready_counts, G, NT1, NT2, cb_parts=1, threads=2, seed=1):
+def _run(emu, counts, ready_counts, G, NT1, NT2, cb_parts=1, threads=2, seed=1, lag=1):
     E_local = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(int)
     ready_off = np.concatenate([[0], np.cumsum(ready_counts)]).astype(int)
     assert len(ready_off) == E_local // G + 2
-    inp = f"{E_local} {G} {BT} {NT1} {NT2} {cb_parts} {threads} {seed}\n"
+    inp = f"{E_local} {G} {BT} {NT1} {NT2} {cb_parts} {threads} {seed} {lag}\n"
     inp += " ".join(map(str, offsets)) + "\n" + " ".join(map(str, ready_off)) + "\n"
     r = subprocess.run([emu], input=inp, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.startswith("OK"), r.stdout + r.stderr
@@ -59,13 +59,13 @@ def test_tiny_layer_tables(emu):
     assert "W=2" in out
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 16])
-def test_mid_layer_cut_tables(emu, G):
+@pytest.mark.parametrize("G,lag", [(1, 1), (2, 4), (4, 1), (4, 4), (16, 64)])
+def test_mid_layer_cut_tables(emu, G, lag):
     inp = make_inputs("mid", T=300, weights=False)
     l = oracle.router_logits(oracle.decode_bf16(inp["x"]), oracle.decode_bf16(inp["Wg"]))
     idx, _, _ = oracle.route(l, 4)
     counts, ready = _tables_from_routing(idx, 0, 16, G)
-    _run(emu, counts, ready, G=G, NT1=2 * 1024 // 128, NT2=4096 // 128)
+    _run(emu, counts, ready, G=G, NT1=2 * 1024 // 128, NT2=4096 // 128, lag=lag)
 
 
 def test_empty_experts_and_waves(emu):
@@ -74,14 +74,14 @@ def test_empty_experts_and_waves(emu):
     W = 4
     rng = np.random.default_rng(0)
     ready = list(rng.integers(0, 50, size=W + 1))
-    _run(emu, counts, ready, G=4, NT1=4, NT2=8, threads=4)
+    _run(emu, counts, ready, G=4, NT1=4, NT2=8, threads=4, lag=3)
 
 
 def test_many_waves_one_expert_each(emu):
     rng = np.random.default_rng(1)
     counts = list(rng.integers(0, 400, size=64))
     ready = list(rng.integers(0, 30, size=65))
-    _run(emu, counts, ready, G=1, NT1=3, NT2=5, threads=5, seed=7)
+    _run(emu, counts, ready, G=1, NT1=3, NT2=5, threads=5, seed=7, lag=11)
 
 
 def test_without_fused_combine_and_single_expert(emu):
@@ -100,3 +100,12 @@ def test_combine_split_into_column_parts(emu):
     ready = list(rng.integers(0, 20, size=9))
     out = _run(emu, counts, ready, G=4, NT1=32, NT2=112, cb_parts=14, threads=3, seed=5)
     assert "W=8" in out
+
+
+def test_many_mtiles_per_xcd(emu):
+    # 64 experts of up to 40 m-tiles, one expert per wave: hundreds of
+    # m-tiles per XCD, within the schedule's capacity
+    rng = np.random.default_rng(11)
+    counts = list(rng.integers(0, 40 * 128, size=64))
+    ready = list(rng.integers(0, 50, size=65))
+    _run(emu, counts, ready, G=1, NT1=2, NT2=3, threads=4, seed=9, lag=16)
