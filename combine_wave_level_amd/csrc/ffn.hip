@@ -222,7 +222,7 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
     const int NT1 = 2 * A.I / C1::BW;
     const int per_xcd = (static_cast<int>(gridDim.x) + kXcds - 1) / kXcds;
     sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, NT1, A.d / C2::BW,
-                A.out != nullptr ? A.cb_parts : 0, xcd, (per_xcd + NT1 - 1) / NT1);
+                A.out != nullptr ? A.cb_parts : 0, xcd, (per_xcd + NT1 - 1) / NT1, F::WHOLE_EXPERTS);
   }
   for (int e = threadIdx.x; e <= A.E_local; e += F::NT) s_off[e] = A.offsets[e];
   __syncthreads();

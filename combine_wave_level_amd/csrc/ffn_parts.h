@@ -17,7 +17,7 @@ namespace moe {
 // shape only decides which workgroup computes which outputs; every shape
 // runs the same per-element instruction sequence over K.
 //   large : many rows per expert (MFMA bound): 256 x 256 tiles, 8 wavefronts
-//           of 64 x 128, two per SIMD
+//           of 128 x 64, two per SIMD
 //   mid   : any shape the boundary accepts (d % 128 == 0, I % 64 == 0)
 //   small : a handful of rows per expert (weight streaming, HBM bound):
 //           token tiles of 32 or 64 rows (empty 16-row blocks skipped) and
@@ -25,25 +25,30 @@ namespace moe {
 //           weights in flight
 // GEMM1 and GEMM2 of one shape use the same workgroup size (NT threads).
 struct FfnLarge {
-  using G1 = TileCfg<256, 256, 4, 2, 32, 4>;
-  using G2 = TileCfg<256, 256, 4, 2, 32, 4>;
+  using G1 = TileCfg<256, 256, 2, 4, 32, 4>;
+  using G2 = TileCfg<256, 256, 2, 4, 32, 4>;
   static constexpr int NT = 512;
+  static constexpr bool WHOLE_EXPERTS = true;  // deal experts whole to XCDs
 };
 struct FfnMid {
   using G1 = TileCfg<128, 256, 2, 4, 32, 4>;
   using G2 = TileCfg<128, 256, 2, 4, 32, 4>;
   static constexpr int NT = 512;
+  static constexpr bool WHOLE_EXPERTS = true;
 };
 struct FfnSmall {
   using G1 = TileCfg<128, 32, 4, 1, 64, 7, true>;
   using G2 = TileCfg<128, 32, 4, 1, 64, 7, true>;
   static constexpr int NT = 256;
+  static constexpr bool WHOLE_EXPERTS = false;  // deal single m-tiles: balance
 };
 struct FfnSmall64 {
   using G1 = TileCfg<128, 64, 4, 1, 64, 6, true>;
   using G2 = TileCfg<128, 64, 4, 1, 64, 6, true>;
   static constexpr int NT = 256;
+  static constexpr bool WHOLE_EXPERTS = false;
 };
+
 template <class F>
 constexpr size_t ffn_lds_bytes() {
   static_assert(F::G1::NTHREADS == F::NT && F::G2::NTHREADS == F::NT, "one workgroup size per shape");
@@ -82,6 +87,42 @@ __device__ __forceinline__ float silu_mul(float h1, float h3) {
   return (h1 / (1.0f + expf(-h1))) * h3;
 }
 
+// Output staging through LDS.  A tile's BT x COLS bf16 results are written
+// to LDS as [row][16-byte chunk] with the chunk index XOR-swizzled by the
+// row (the 8-byte writes of a lane group's 16 rows then hit distinct banks),
+// and leave LDS as whole rows, 16 contiguous bytes per lane: every global
+// store instruction writes full 128-byte lines instead of 32-byte pieces of
+// 16 rows.
+template <int COLS>
+struct OutStage {
+  static constexpr int CH = COLS / 8;  // 16-byte chunks per row
+  static_assert((CH & (CH - 1)) == 0 && CH >= 4 && CH <= 64, "chunks per row: a power of 2, 4..64");
+  static constexpr int RPI = 64 / CH;  // rows one wavefront instruction covers
+  __device__ static int slot(int t, int c) { return t * CH + (c ^ (t % CH)); }
+};
+
+// Puts 4 values (row t, columns n .. n+3 of the tile, n % 4 == 0) into the stage.
+template <int COLS>
+__device__ __forceinline__ void out_put(uint16_t* lds, int t, int n, const u32x2& v) {
+  *reinterpret_cast<u32x2*>(lds + OutStage<COLS>::slot(t, n / 8) * 8 + ((n / 4) & 1) * 4) = v;
+}
+
+// Rows 0 .. count-1 of the stage to dst + t * ld.  Brackets itself with
+// barriers: the stage is complete before it is read and fully read before
+// the caller reuses LDS.
+template <int COLS, int NW>
+__device__ __forceinline__ void out_flush(const uint16_t* lds, uint16_t* __restrict__ dst, size_t ld,
+                                          int count) {
+  using O = OutStage<COLS>;
+  __syncthreads();
+  const int lane = lane_id(), c = lane % O::CH;
+  for (int r0 = wave_id() * O::RPI; r0 < count; r0 += NW * O::RPI) {
+    const int t = r0 + lane / O::CH;
+    if (t < count) st16(dst + static_cast<size_t>(t) * ld + c * 8, ld16(lds + O::slot(t, c) * 8));
+  }
+  __syncthreads();
+}
+
 // GEMM1 tile: rows [row0, row0 + BT) of expert e's segment (count rows
 // valid), BW packed rows of W13 starting at row block nt * BW / 16, i.e.
 // intermediate indices [nt * BW/2, nt * BW/2 + BW/2).  The operand rows are
@@ -94,6 +135,8 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            uint16_t* __restrict__ act, int row0, int count, int nt,
                                            int d, int I, uint16_t* lds) {
   static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
+  constexpr int COLS = C::BW / 2;
+  static_assert(static_cast<size_t>(C::BT) * COLS * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
   TokRows<C> trow;
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
@@ -105,20 +148,21 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
   const int lane = lane_id();
   const int wr = tile_wr<C>(), wt = tile_wt<C>();
 #pragma unroll
-  for (int a = 0; a < C::AW; a += 2) {
-    const int nb = nt * (C::BW / 16) + wr * C::AW + a;  // even: W1 block, nb + 1: W3 block
-    const int i0 = (nb / 2) * 16 + 4 * (lane / 16);
+  for (int b = 0; b < C::AT; ++b) {
+    if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones
+    const int t = (wt * C::AT + b) * 16 + (lane & 15);
 #pragma unroll
-    for (int b = 0; b < C::AT; ++b) {
-      const int tr = (wt * C::AT + b) * 16 + (lane & 15);
-      if (tr >= count) continue;
+    for (int a = 0; a < C::AW; a += 2) {
+      // row blocks wr * AW + a (W1) and + 1 (W3): intermediate block (wr * AW + a) / 2 of the tile
+      const int n = ((wr * C::AW + a) / 2) * 16 + 4 * (lane / 16);
       const f32x4 h1 = acc.v[a][b], h3 = acc.v[a + 1][b];
       u32x2 pk;
       pk.x = pack_bf16x2(silu_mul(h1[0], h3[0]), silu_mul(h1[1], h3[1]));
       pk.y = pack_bf16x2(silu_mul(h1[2], h3[2]), silu_mul(h1[3], h3[3]));
-      *reinterpret_cast<u32x2*>(act + static_cast<size_t>(row0 + tr) * I + i0) = pk;
+      out_put<COLS>(lds, t, n, pk);
     }
   }
+  out_flush<COLS, C::NW>(lds, act + static_cast<size_t>(row0) * I + nt * COLS, I, count);
 }
 
 // GEMM2 tile: y[row0 .. row0 + count) x features [nt * BW, nt * BW + BW).
@@ -126,6 +170,8 @@ template <class C>
 __device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ act,
                                            const uint16_t* __restrict__ w2e, uint16_t* __restrict__ y,
                                            int row0, int count, int nt, int d, int I, uint16_t* lds) {
+  constexpr int COLS = C::BW;
+  static_assert(static_cast<size_t>(C::BT) * COLS * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
   TokRows<C> trow;
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
@@ -137,19 +183,20 @@ __device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ act,
   const int lane = lane_id();
   const int wr = tile_wr<C>(), wt = tile_wt<C>();
 #pragma unroll
-  for (int a = 0; a < C::AW; ++a) {
-    const int n0 = (nt * (C::BW / 16) + wr * C::AW + a) * 16 + 4 * (lane / 16);
+  for (int b = 0; b < C::AT; ++b) {
+    if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones
+    const int t = (wt * C::AT + b) * 16 + (lane & 15);
 #pragma unroll
-    for (int b = 0; b < C::AT; ++b) {
-      const int tr = (wt * C::AT + b) * 16 + (lane & 15);
-      if (tr >= count) continue;
+    for (int a = 0; a < C::AW; ++a) {
+      const int n = (wr * C::AW + a) * 16 + 4 * (lane / 16);
       const f32x4 v = acc.v[a][b];
       u32x2 pk;
       pk.x = pack_bf16x2(v[0], v[1]);
       pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<u32x2*>(y + static_cast<size_t>(row0 + tr) * d + n0) = pk;
+      out_put<COLS>(lds, t, n, pk);
     }
   }
+  out_flush<COLS, C::NW>(lds, y + static_cast<size_t>(row0) * d + nt * COLS, d, count);
 }
 
 // 16 bytes of row r of y at element offset c8.  COHERENT: a device-coherent

@@ -6,13 +6,15 @@
 // and the return of finished experts' results run at the same time.
 //
 // MI355X has 8 XCDs, each with its own L2.  The m-tiles (BT-row slices of
-// each expert's sorted rows) of every expert wave are split into 8
-// contiguous ranges, one per XCD (when a wave's m-tiles do not divide by 8,
-// the extra ones go to the XCDs after those that took the previous wave's
-// extras, so the XCDs stay within one m-tile of each other), and every
-// workgroup takes tasks only from its own XCD's ticket stream.  GEMM1 ->
-// GEMM2 dependencies therefore never leave an XCD's L2; only the combine,
-// which reads y rows of every XCD, crosses XCDs.
+// each expert's sorted rows) are dealt to the XCDs in expert (= wave) order,
+// each deal to the XCD with the least m-tiles so far (lowest id on ties).
+// For compute-bound shapes an expert is dealt whole, so its weights are read
+// by one XCD only (an expert with more m-tiles than an eighth of all, a hot
+// expert, is dealt in chunks of at most that many); for weight-streaming
+// shapes, where every m-tile streams its expert's weights anyway, m-tiles
+// are dealt one by one, which balances the XCDs to within one m-tile.  Every workgroup takes tasks only from its own XCD's
+// ticket stream, so GEMM1 -> GEMM2 dependencies never leave an XCD's L2;
+// only the combine, which reads y rows of every XCD, crosses XCDs.
 //
 // Inside one XCD's stream the XCD's m-tiles are taken in wave order,
 // m_0 .. m_{n-1}, and the tickets run through positions i = 0 .. n+L-1:
@@ -41,7 +43,7 @@ namespace moe {
 constexpr int kXcds = 8;                // XCDs of an MI355X
 constexpr int kSchedMaxExperts = 256;
 constexpr int kSchedMaxWaves = 256;
-constexpr int kSchedMaxLocal = 640;     // m-tiles of one XCD
+constexpr int kSchedMaxLocal = 512;     // m-tiles of one XCD
 constexpr int kSchedMaxLag = 64;       // GEMM2 lag, in m-tiles
 constexpr int kCombineTokens = 8;       // tokens per combine task
 constexpr int kCtrPad = 64;             // int32 words (256 B) between counters of different XCDs
@@ -49,7 +51,7 @@ constexpr int kCtrPad = 64;             // int32 words (256 B) between counters 
 struct WaveSchedule {
   int W, G, NT1, NT2, total, xcd, n_local, lag, err;
   int32_t mt_pre[kSchedMaxExperts + 1];  // first m-tile of each local expert
-  int32_t mlo[kSchedMaxWaves];           // first m-tile of this XCD in wave w
+  int32_t loc_mt[kSchedMaxLocal];        // global m-tile of this XCD's j-th m-tile (ascending)
   int32_t loc_pre[kSchedMaxWaves + 1];   // this XCD's m-tiles in waves < w (loc_pre[W] = n_local)
   int32_t cb_pre[kSchedMaxWaves + 2];    // this XCD's combine tasks of slots < s
   int32_t pos[kSchedMaxLocal + kSchedMaxLag + 1];     // first ticket of position i, i = 0 .. n+L
@@ -84,22 +86,18 @@ __host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, in
   return sched_last_leq(mt_pre, lo, hi, mt);
 }
 
-// Share of XCD x when n m-tiles of one wave are split over the XCDs and the
-// n % kXcds extra m-tiles go to XCDs rot, rot + 1, ... (mod kXcds).
-__host__ __device__ inline int sched_xcd_share(int n, int rot, int x) {
-  return n / kXcds + (((x - rot + kXcds) % kXcds) < (n % kXcds) ? 1 : 0);
-}
-
 // Builds XCD xcd's schedule from the dispatch tables.  offsets [E_local + 1]
 // = first pair row of each local expert; ready_off [W + 2] = first position
 // of each ready slot in the ready list.  BT = rows per m-tile.  NT1 / NT2 =
 // output tiles of GEMM1 / GEMM2 per m-tile.  cb_parts = column parts per
 // combine chunk of kCombineTokens tokens (0: no combine tasks, no fused
-// combine).  lag = L (1 .. kSchedMaxLag).  S.err = 1 if the XCD holds more
-// than kSchedMaxLocal m-tiles (the schedule is then empty).
+// combine).  lag = L (1 .. kSchedMaxLag).  whole_experts: deal experts whole
+// (else single m-tiles).  S.err = 1 if the XCD holds more than
+// kSchedMaxLocal m-tiles (the schedule is then empty).
 __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offsets,
                                             const int32_t* ready_off, int E_local, int G, int BT,
-                                            int NT1, int NT2, int cb_parts, int xcd, int lag) {
+                                            int NT1, int NT2, int cb_parts, int xcd, int lag,
+                                            bool whole_experts) {
   S.W = E_local / G;
   S.lag = lag < 1 ? 1 : (lag > kSchedMaxLag ? kSchedMaxLag : lag);
   S.G = G;
@@ -113,17 +111,32 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
   }
   S.mt_pre[E_local] = run;
-  int rot = 0, loc = 0;
-  for (int w = 0; w < S.W; ++w) {
-    const int a = S.mt_pre[w * G], n = S.mt_pre[(w + 1) * G] - a;
-    int lo = a;
-    for (int y = 0; y < xcd; ++y) lo += sched_xcd_share(n, rot, y);
-    S.mlo[w] = lo;
-    S.loc_pre[w] = loc;
-    loc += sched_xcd_share(n, rot, xcd);
-    rot = (rot + n % kXcds) % kXcds;
+  // deal the m-tiles to the least-loaded XCD (lowest id on ties): whole
+  // experts (above the share in chunks of the share) or single m-tiles
+  const int share = (run + kXcds - 1) / kXcds;
+  int load[kXcds];
+  for (int y = 0; y < kXcds; ++y) load[y] = 0;
+  int loc = 0, w_next = 0;
+  for (int e = 0; e < E_local; ++e) {
+    while (w_next <= e / G && w_next < S.W) S.loc_pre[w_next++] = loc;
+    int first = S.mt_pre[e];
+    int n = S.mt_pre[e + 1] - first;
+    while (n > 0) {
+      int x = 0;
+      for (int y = 1; y < kXcds; ++y) x = load[y] < load[x] ? y : x;
+      const int take = whole_experts ? (n > share ? share : n) : 1;
+      load[x] += take;
+      if (x == xcd) {
+        for (int q = 0; q < take; ++q) {
+          if (loc < kSchedMaxLocal) S.loc_mt[loc] = first + q;
+          ++loc;
+        }
+      }
+      first += take;
+      n -= take;
+    }
   }
-  S.loc_pre[S.W] = loc;
+  while (w_next <= S.W) S.loc_pre[w_next++] = loc;
   S.n_local = loc;
   if (loc > kSchedMaxLocal) {
     S.err = 1;
@@ -177,7 +190,7 @@ __host__ __device__ inline void sched_local_mtile(const WaveSchedule& S, int j, 
   while (S.loc_pre[w + 1] <= j) ++w;
   t.wave = w;
   t.loc = j;
-  t.mt = S.mlo[w] + (j - S.loc_pre[w]);
+  t.mt = S.loc_mt[j];
   t.expert = sched_expert_of(S.mt_pre, w * S.G, (w + 1) * S.G, t.mt);
 }
 

@@ -4,12 +4,12 @@
 // (grouped into the 8 per-XCD streams) with std::atomic counters in place of
 // the device counters.
 //
-// stdin: E_local G BT NT1 NT2 cb_parts threads_per_xcd seed lag   (cb_parts 0: no combine)
+// stdin: E_local G BT NT1 NT2 cb_parts threads_per_xcd seed lag whole_experts   (cb_parts 0: no combine)
 //        offsets[E_local + 1]  ready_off[W + 2]
 // Checks (exit status 0 = all hold):
-//   1. structure: each wave's m-tiles are split into contiguous per-XCD
-//      ranges whose sizes differ by at most one, and the XCDs' totals by at
-//      most one; over the 8 streams every GEMM1 / GEMM2 tile (m-tile x
+//   1. structure: every expert with at most an eighth of all m-tiles lives
+//      on one XCD, the XCDs' m-tile counts differ by at most the largest
+//      dealt chunk; over the 8 streams every GEMM1 / GEMM2 tile (m-tile x
 //      output tile) and every combine chunk has exactly one ticket; both
 //      GEMM tiles of an m-tile live in the stream of the XCD owning it;
 //      decoded experts own their m-tiles and belong to the decoded wave;
@@ -37,9 +37,9 @@ static int fail(const char* msg, long a = 0, long b = 0) {
 }
 
 int main() {
-  int E_local, G, BT, NT1, NT2, cb_parts, per_xcd, lag;
+  int E_local, G, BT, NT1, NT2, cb_parts, per_xcd, lag, whole;
   unsigned seed;
-  if (std::scanf("%d %d %d %d %d %d %d %u %d", &E_local, &G, &BT, &NT1, &NT2, &cb_parts, &per_xcd, &seed, &lag) != 9)
+  if (std::scanf("%d %d %d %d %d %d %d %u %d %d", &E_local, &G, &BT, &NT1, &NT2, &cb_parts, &per_xcd, &seed, &lag, &whole) != 10)
     return fail("input");
   const int W = E_local / G;
   std::vector<int32_t> offsets(E_local + 1), ready_off(W + 2);
@@ -47,7 +47,7 @@ int main() {
   for (auto& v : ready_off) if (std::scanf("%d", &v) != 1) return fail("ready_off");
   static WaveSchedule S[kXcds];
   for (int x = 0; x < kXcds; ++x)
-    sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag);
+    sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag, whole != 0);
   for (int x = 0; x < kXcds; ++x)
     if (S[x].err) fail("schedule overflow", x, S[x].n_local);
   const int nmt = S[0].mt_pre[E_local];
@@ -61,28 +61,39 @@ int main() {
     const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     cb_seen[s].assign(chunks, 0);
   }
-  for (int w = 0; w < W; ++w) {
-    int expect = S[0].mt_pre[w * G], lo = 1 << 30, hi = -1;
-    for (int x = 0; x < kXcds; ++x) {
-      if (S[x].mlo[w] != expect) fail("per-wave XCD ranges not contiguous", w, x);
-      const int cnt = S[x].loc_pre[w + 1] - S[x].loc_pre[w];
-      expect += cnt;
-      lo = cnt < lo ? cnt : lo;
-      hi = cnt > hi ? cnt : hi;
-      if (S[x].loc_pre[w] + cnt > S[x].n_local) fail("local m-tile prefix", w, x);
-    }
-    if (expect != S[0].mt_pre[(w + 1) * G]) fail("per-wave XCD ranges do not cover the wave", w);
-    if (hi - lo > 1) fail("per-wave XCD shares differ by more than one", w);
-  }
   {
+    // owner XCD of every m-tile, from the local lists
+    std::vector<int> owner(nmt, -1);
+    for (int x = 0; x < kXcds; ++x)
+      for (int j = 0; j < S[x].n_local; ++j) {
+        const int mt = S[x].loc_mt[j];
+        if (mt < 0 || mt >= nmt || owner[mt] != -1) fail("m-tile dealt twice or out of range", x, mt);
+        if (j > 0 && S[x].loc_mt[j - 1] >= mt) fail("local m-tiles not ascending", x, j);
+        owner[mt] = x;
+      }
+    const int share = (nmt + kXcds - 1) / kXcds;
+    int chunk_max = 0;
+    for (int e = 0; e < E_local; ++e) {
+      const int a = S[0].mt_pre[e], b = S[0].mt_pre[e + 1];
+      for (int mt = a; mt < b; ++mt) if (owner[mt] < 0) fail("m-tile not dealt", e, mt);
+      if (whole && b - a <= share)
+        for (int mt = a; mt < b; ++mt) if (owner[mt] != owner[a]) fail("expert split over XCDs", e, mt);
+      const int c = whole ? (b - a < share ? b - a : share) : (b > a ? 1 : 0);
+      chunk_max = c > chunk_max ? c : chunk_max;
+    }
     int lo = 1 << 30, hi = -1;
     for (int x = 0; x < kXcds; ++x) {
       lo = S[x].n_local < lo ? S[x].n_local : lo;
       hi = S[x].n_local > hi ? S[x].n_local : hi;
-      if (W + S[x].n_local > rw) fail("counter region too small", x, S[x].n_local);
+      for (int w = 0; w < W; ++w)
+        for (int j = S[x].loc_pre[w]; j < S[x].loc_pre[w + 1]; ++j)
+          if (S[0].mt_pre[w * G] > S[x].loc_mt[j] || S[x].loc_mt[j] >= S[0].mt_pre[(w + 1) * G])
+            fail("local wave prefix", x, j);
     }
-    if (hi - lo > 1) fail("XCD totals differ by more than one", lo, hi);
+    if (hi - lo > chunk_max) fail("XCD loads differ by more than one dealt chunk", lo, hi);
   }
+  for (int x = 0; x < kXcds; ++x)
+    if (W + S[x].n_local > rw) fail("counter region too small", x, S[x].n_local);
   for (int x = 0; x < kXcds; ++x) {
     for (int tk = 0; tk < S[x].total; ++tk) {
       const Task t = sched_decode(S[x], tk);
@@ -92,9 +103,8 @@ int main() {
         if (cb_seen[t.slot][t.chunk]++) fail("combine chunk twice", t.slot, t.chunk);
         continue;
       }
-      if (t.mt < S[x].mlo[t.wave] || t.mt >= S[x].mlo[t.wave] + (S[x].loc_pre[t.wave + 1] - S[x].loc_pre[t.wave]))
-        fail("m-tile outside the XCD's range", x, t.mt);
-      if (t.loc != S[x].loc_pre[t.wave] + (t.mt - S[x].mlo[t.wave])) fail("local m-tile index", x, t.loc);
+      if (t.loc < S[x].loc_pre[t.wave] || t.loc >= S[x].loc_pre[t.wave + 1] || S[x].loc_mt[t.loc] != t.mt)
+        fail("m-tile not this XCD's m-tile of the decoded wave", x, t.mt);
       if (t.mt < S[x].mt_pre[t.expert] || t.mt >= S[x].mt_pre[t.expert + 1]) fail("expert does not own m-tile", tk, t.mt);
       if (t.expert / G != t.wave) fail("expert not in wave", tk, t.expert);
       const int NT = t.kind == kTaskGemm1 ? NT1 : NT2;

@@ -30,12 +30,12 @@ def emu(tmp_path_factory):
     return exe
 
 
-def _run(emu, counts, ready_counts, G, NT1, NT2, cb_parts=1, threads=2, seed=1, lag=1):
+def _run(emu, counts, ready_counts, G, NT1, NT2, cb_parts=1, threads=2, seed=1, lag=1, whole=1):
     E_local = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(int)
     ready_off = np.concatenate([[0], np.cumsum(ready_counts)]).astype(int)
     assert len(ready_off) == E_local // G + 2
-    inp = f"{E_local} {G} {BT} {NT1} {NT2} {cb_parts} {threads} {seed} {lag}\n"
+    inp = f"{E_local} {G} {BT} {NT1} {NT2} {cb_parts} {threads} {seed} {lag} {whole}\n"
     inp += " ".join(map(str, offsets)) + "\n" + " ".join(map(str, ready_off)) + "\n"
     r = subprocess.run([emu], input=inp, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.startswith("OK"), r.stdout + r.stderr
@@ -59,13 +59,13 @@ def test_tiny_layer_tables(emu):
     assert "W=2" in out
 
 
-@pytest.mark.parametrize("G,lag", [(1, 1), (2, 4), (4, 1), (4, 4), (16, 64)])
-def test_mid_layer_cut_tables(emu, G, lag):
+@pytest.mark.parametrize("G,lag,whole", [(1, 1, 1), (2, 4, 0), (4, 1, 1), (4, 4, 0), (16, 64, 1)])
+def test_mid_layer_cut_tables(emu, G, lag, whole):
     inp = make_inputs("mid", T=300, weights=False)
     l = oracle.router_logits(oracle.decode_bf16(inp["x"]), oracle.decode_bf16(inp["Wg"]))
     idx, _, _ = oracle.route(l, 4)
     counts, ready = _tables_from_routing(idx, 0, 16, G)
-    _run(emu, counts, ready, G=G, NT1=2 * 1024 // 128, NT2=4096 // 128, lag=lag)
+    _run(emu, counts, ready, G=G, NT1=2 * 1024 // 128, NT2=4096 // 128, lag=lag, whole=whole)
 
 
 def test_empty_experts_and_waves(emu):
@@ -98,7 +98,7 @@ def test_combine_split_into_column_parts(emu):
     rng = np.random.default_rng(3)
     counts = list(rng.integers(0, 40, size=32))
     ready = list(rng.integers(0, 20, size=9))
-    out = _run(emu, counts, ready, G=4, NT1=32, NT2=112, cb_parts=14, threads=3, seed=5)
+    out = _run(emu, counts, ready, G=4, NT1=32, NT2=112, cb_parts=14, threads=3, seed=5, whole=0)
     assert "W=8" in out
 
 
@@ -109,3 +109,11 @@ def test_many_mtiles_per_xcd(emu):
     counts = list(rng.integers(0, 40 * 128, size=64))
     ready = list(rng.integers(0, 50, size=65))
     _run(emu, counts, ready, G=1, NT1=2, NT2=3, threads=4, seed=9, lag=16)
+
+
+def test_hot_expert_dealt_in_chunks(emu):
+    # one expert holds most rows: it is split over XCDs in chunks of the
+    # share, every other expert stays whole on one XCD
+    counts = [30 * 128] + [128 * 2] * 15
+    ready = [5, 40, 3, 9, 60]
+    _run(emu, counts, ready, G=4, NT1=8, NT2=16, threads=3, seed=4, lag=4)
