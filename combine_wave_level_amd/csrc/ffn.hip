@@ -198,8 +198,10 @@ __device__ __forceinline__ void local_signal(int32_t* p) {
   if (wave_uniform() == 0) wave0_atomic_add(p, 1);
 }
 
-// XCD-local consumer side: after the counter is reached, drop this CU's L1
-// lines so the following loads come from the L2 the producer wrote.
+// XCD-local consumer side: bounded poll of the counter (device-scope loads,
+// which skip the CU's L1; a workgroup-scope load may keep returning the L1
+// line it first read), then drop this CU's L1 lines so the following loads
+// come from the L2 the producer wrote.
 __device__ __forceinline__ void local_wait(const int32_t* p, int target, long long timeout_ticks,
                                            int32_t* err) {
   poll_geq(p, target, timeout_ticks, err);
@@ -218,11 +220,13 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   __shared__ int32_t s_ticket;
   const int xcd = uniform(xcc_id());
   if (threadIdx.x == 0) {
-    // GEMM2 lag: enough GEMM1 tiles in between for every workgroup of the XCD
-    const int NT1 = 2 * A.I / C1::BW;
-    const int per_xcd = (static_cast<int>(gridDim.x) + kXcds - 1) / kXcds;
-    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, NT1, A.d / C2::BW,
-                A.out != nullptr ? A.cb_parts : 0, xcd, (per_xcd + NT1 - 1) / NT1, F::WHOLE_EXPERTS);
+    // GEMM2 lag: kSchedMaxLag m-tiles, i.e. an XCD runs the GEMM1 tiles of
+    // (nearly) all its m-tiles before their GEMM2 tiles.  Interleaving the two
+    // closer puts both operand sets (x and W1/W3, act and W2) through the
+    // XCD's L2 at once; measured on the mid layer the short lags (2 to 4
+    // m-tiles) cost 20% against 8 and more.
+    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
+                A.out != nullptr ? A.cb_parts : 0, xcd, kSchedMaxLag, F::WHOLE_EXPERTS);
   }
   for (int e = threadIdx.x; e <= A.E_local; e += F::NT) s_off[e] = A.offsets[e];
   __syncthreads();

@@ -25,9 +25,9 @@
 //   position is i (tokens whose last local wave is s-1; slot 0 = tokens with
 //   no local pick): the position of the GEMM2 tiles of the XCD's last m-tile
 //   of a wave <= s + 1.
-// GEMM2 of an m-tile thus trails its GEMM1 by L m-tiles, L chosen so that
-// the GEMM1 tiles in between occupy every workgroup of the XCD while the
-// m-tile's own GEMM1 tiles finish.  A GEMM2 tile waits for its m-tile's
+// GEMM2 of an m-tile thus trails its GEMM1 by L m-tiles (the kernel uses a
+// long lag: an XCD's GEMM1 tiles mostly run before its GEMM2 tiles, which
+// keeps the two operand sets from sharing the XCD's L2 at the same time).  A GEMM2 tile waits for its m-tile's
 // GEMM1 tiles (same stream, smaller tickets).  A combine task waits until
 // every XCD finished the GEMM2 tiles of waves <= its slot - 1; in every
 // stream those tiles sit at smaller tickets than that stream's combine
