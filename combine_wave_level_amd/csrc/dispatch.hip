@@ -10,8 +10,9 @@
 //               per group (local expert, ready-wave slot) of the chunk's
 //               tokens in that group.  Bit OR is order-independent, so the
 //               masks are deterministic.
-//   2. scan   : per group, exclusive scan of popcounts over chunks in
-//               ascending chunk order; then exclusive scan of group totals.
+//   2. scan   : per group (one wavefront), exclusive scan of popcounts over
+//               chunks in ascending chunk order; then exclusive scan of group
+//               totals.
 //   3. scatter: a token's row inside its group is the group start + the
 //               chunk's base + the number of lower lanes in the same mask,
 //               so rows within a group follow ascending token id.
@@ -52,20 +53,32 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
   }
 }
 
-// One block.  Thread g owns group g (loops if ngroups > blockDim).
+// One block of 1024 threads; wavefront w owns groups w, w + 16, ...
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const unsigned long long* __restrict__ masks, int nchunks, int ngroups, int E_local,
     int32_t* __restrict__ bases, int32_t* __restrict__ group_off, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ err) {
   extern __shared__ int32_t stot[];  // [ngroups]
   if (threadIdx.x == 0) *err = 0;  // a new layer call starts with a clean error word
-  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      bases[static_cast<size_t>(c) * ngroups + g] = run;
-      run += __popcll(masks[static_cast<size_t>(c) * ngroups + g]);
+  // one wavefront per group: lanes take 64 chunks at a time, an exclusive
+  // prefix sum of their popcounts (shuffles) gives the chunks' bases, and
+  // the running total carries over to the next 64 chunks
+  const int lane = lane_id(), nwaves = blockDim.x / kWave;
+  for (int g = wave_id(); g < ngroups; g += nwaves) {
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += kWave) {
+      const int c = c0 + lane;
+      const int v = c < nchunks ? __popcll(masks[static_cast<size_t>(c) * ngroups + g]) : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        incl += lane >= off ? o : 0;
+      }
+      if (c < nchunks) bases[static_cast<size_t>(c) * ngroups + g] = carry + incl - v;
+      carry += __shfl(incl, kWave - 1, kWave);
     }
-    stot[g] = run;
+    if (lane == 0) stot[g] = carry;
   }
   __syncthreads();
   if (threadIdx.x == 0) {

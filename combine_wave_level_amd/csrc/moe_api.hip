@@ -48,7 +48,7 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.bases = take(static_cast<size_t>(L.nchunks) * L.ngroups * 4);
   L.group_off = take(static_cast<size_t>(L.ngroups + 2) * 4);
   L.ready_list = take(static_cast<size_t>(p.T) * 4);
-  L.logits = take(static_cast<size_t>(p.T) * p.E_global * 4);
+  L.logits = take(static_cast<size_t>(router_splits(p.d, p.E_global, p.x_dtype == MOE_BF16)) * p.T * p.E_global * 4);
   L.xbf = take(p.x_dtype == MOE_F32 ? static_cast<size_t>(p.T) * p.d * 2 : 0);
   L.act = take(static_cast<size_t>(L.P_max) * p.I * 2);
   L.sync = take(L.sync_words * 4);
@@ -100,8 +100,9 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* packed
   if ((x && !aligned16(x)) || (packed && !aligned16(packed))) return MOE_ERR_INVALID_ARG;
   WsLayout L;
   if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
-  float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits);
-  return hip_status(launch_route(*p, x, packed, bias, topk_idx, topk_w, lg, static_cast<hipStream_t>(stream)));
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits);
+  return hip_status(launch_route(*p, x, packed, bias, topk_idx, topk_w, logits, partial,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_counts,

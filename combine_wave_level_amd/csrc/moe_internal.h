@@ -23,7 +23,7 @@ namespace moe {
 //              (experts: pair rows; ready slots: positions in ready_list)
 //   ready_list int32 [T]: tokens ordered by ready wave, ascending token id
 //              inside a wave
-//   logits     fp32 [T][E_global] router scores
+//   logits     fp32 [splits][T][E_global] partial router logits (K split)
 //   xbf        bf16 [T][d] (only when x is fp32): x rounded for the FFN
 //   act        bf16 [P_max][I]: a = silu(h1) * h3, sorted-row order
 //   sync       int32 counters of the persistent expert-wave kernel
@@ -50,7 +50,10 @@ hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, c
 
 hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packed,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
-                        hipStream_t s);
+                        float* partial, hipStream_t s);
+// Fixed number of ranges the router's reduction over d is cut into (bf16 x;
+// depends on the layer only: d and E_global).
+int router_splits(int d, int E_global, bool x_bf16);
 
 hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* sorted_token,

@@ -113,9 +113,12 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void
  *   Out: topk_idx [T, k] int32 global expert ids in rank order (descending
  *   score, ties to the lower id); topk_w [T, k] fp32; logits [T, E_global]
  *   fp32 when non-NULL (the router scores the selection was made on).
- * Logits accumulate in fp32 in a fixed order; selection is made on the fp32
- * logits; weights are exp(l_j - l_max) / sum over the picks, i.e. softmax
- * followed by renormalisation. */
+ * Logits accumulate in fp32 in a fixed order that depends on the layer only
+ * (for bf16 x the reduction over d is cut into up to 8 equal ranges, 2 when
+ * E_global > 64, each summed in ascending index order, and the ranges are
+ * added in ascending order; then the bias); selection is made on the fp32 logits; weights are
+ * exp(l_j - l_max) / sum over the picks, i.e. softmax followed by
+ * renormalisation.  ws holds the partial logits (moe_workspace_size). */
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* packed,
                        const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
                        void* ws, size_t ws_bytes, moe_stream_t stream);
