@@ -14,4 +14,6 @@ from .moe_oracle import (  # noqa: F401
     forward,
     forward_tokens,
     wgrad,
+    backward,
+    backward_tokens,
 )

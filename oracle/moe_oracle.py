@@ -34,7 +34,12 @@ notes of this repository):
 * no capacity limit and no token dropping: every routed pair is processed
   exactly once;
 * the oracle computes everything in float64 from the exact input values
-  (bf16 inputs decoded exactly); it rounds no intermediate.
+  (bf16 inputs decoded exactly); it rounds no intermediate;
+* the backward holds the routing fixed: the top-k selection is piecewise
+  constant in the logits, so gradients flow only through the k renormalised
+  weights; on an expert-parallel share (some picks owned by other GPUs) the
+  loss is <dout, out> of this GPU's partial output, whose gradient is this
+  GPU's additive share of the full layer's gradient.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, library routines, brute force and finite differences.
@@ -53,6 +58,8 @@ __all__ = [
     "forward",
     "forward_tokens",
     "wgrad",
+    "backward",
+    "backward_tokens",
 ]
 
 
@@ -303,3 +310,114 @@ def wgrad(x_ffn, W1, W3, W2, meta, w, dout, experts=None, cols=None):
         dW1[le] = X.T @ dH1
         dW3[le] = X.T @ dH3
     return dW1, dW3, dW2
+
+
+def _gate_backward(w: np.ndarray, dw: np.ndarray) -> np.ndarray:
+    """Gradient of the k renormalised weights with respect to the picked
+    logits.  w_j = exp(l_j) / sum_j' exp(l_j') over the picks (softmax then
+    renormalisation, the workload definition), so
+    dl_j = sum_m dw_m dw_m/dl_j = w_j (dw_j - sum_m w_m dw_m)."""
+    s = (w * dw).sum(axis=1, keepdims=True)
+    return w * (dw - s)
+
+
+def backward(x, Wg, W1, W3, W2, idx, w, meta, dout, x_ffn=None):
+    """Data and router gradients of L = <dout, out>, float64.
+
+    Chain rule through the layer of the workload definition ([V4-TH] §1.1
+    and §1.4: route, dispatch, SwiGLU expert FFN, router-weighted combine),
+    with the routing held fixed:
+      per routed row r = (t, j) of local expert e:
+        h1 = x_t W1_e, h3 = x_t W3_e, s = sigmoid(h1), a = h1 s h3, y = a W2_e,
+        dw[t, j] = <dout_t, y>                       (combine: out += w y)
+        dA  = w[t, j] dout_t W2_e^T,
+        dH3 = dA h1 s,  dH1 = dA h3 s (1 + h1 (1 - s)),
+        dx_ffn[t] += dH1 W1_e^T + dH3 W3_e^T;
+      picks of non-local experts contribute nothing to out, so their dw is 0;
+      per token: dl[t, idx_j] = w_j (dw_j - sum_m w_m dw_m), 0 off the picks;
+      router (l = x Wg + b): dWg = x^T dl, dx_router = dl Wg^T;
+      dx = dx_router + dx_ffn.
+    ``x`` feeds the router and ``x_ffn`` (default ``x``) the experts; a cast
+    between them passes the gradient through unchanged.  [ZH-10100]
+    (deterministic operators): the GPU's fixed reduction orders are its own
+    property; the oracle sums in float64 with matmuls.
+
+    Returns a dict with dw [T, k], dl [T, E], dWg [d, E], dx_router,
+    dx_ffn and dx [T, d].
+    """
+    xr = np.asarray(x, dtype=np.float64)
+    xf = xr if x_ffn is None else np.asarray(x_ffn, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    Wg64 = np.asarray(Wg, dtype=np.float64)
+    T, k = idx.shape
+    d = xf.shape[1]
+    E = Wg64.shape[1]
+    dw = np.zeros((T, k), dtype=np.float64)
+    dx_ffn = np.zeros((T, d), dtype=np.float64)
+    off = meta["offsets"]
+    for le in range(len(off) - 1):
+        r0, r1 = int(off[le]), int(off[le + 1])
+        if r1 == r0:
+            continue
+        toks = meta["sorted_token"][r0:r1]
+        slots = meta["sorted_slot"][r0:r1]
+        W1e = np.asarray(W1[le], dtype=np.float64)
+        W3e = np.asarray(W3[le], dtype=np.float64)
+        W2e = np.asarray(W2[le], dtype=np.float64)
+        X = xf[toks]
+        h1 = X @ W1e
+        h3 = X @ W3e
+        s = 1.0 / (1.0 + np.exp(-h1))
+        a = h1 * s * h3
+        y = a @ W2e
+        dw[toks, slots] = (dout[toks] * y).sum(axis=1)
+        dA = (w[toks, slots][:, None] * dout[toks]) @ W2e.T
+        dH3 = dA * h1 * s
+        dH1 = dA * h3 * s * (1.0 + h1 * (1.0 - s))
+        # a token picks an expert at most once: toks has no repeats here
+        dx_ffn[toks] += dH1 @ W1e.T + dH3 @ W3e.T
+    dl_picks = _gate_backward(np.asarray(w, dtype=np.float64), dw)
+    dl = np.zeros((T, E), dtype=np.float64)
+    rows = np.repeat(np.arange(T), k)
+    dl[rows, np.asarray(idx).reshape(-1)] = dl_picks.reshape(-1)
+    dWg = xr.T @ dl
+    dx_router = dl @ Wg64.T
+    return {"dw": dw, "dl": dl, "dWg": dWg, "dx_router": dx_router, "dx_ffn": dx_ffn,
+            "dx": dx_router + dx_ffn}
+
+
+def backward_tokens(x_rows, x_ffn_rows, idx_rows, w_rows, dout_rows, Wg, W1, W3, W2, e_begin, E_local):
+    """dx, dw and the picked dl of a subset of tokens, one token at a time.
+
+    A token's data gradient depends only on its own row, picks, weights and
+    dout (the layer is token-local apart from the weights), so a sample of
+    tokens can be checked at any batch size.  Same formulas as ``backward``.
+    Returns (dx [n, d], dw [n, k], dl [n, k]) with dl in rank order.
+    """
+    xr = np.asarray(x_rows, dtype=np.float64)
+    xf = np.asarray(x_ffn_rows, dtype=np.float64)
+    dout = np.asarray(dout_rows, dtype=np.float64)
+    w = np.asarray(w_rows, dtype=np.float64)
+    Wg64 = np.asarray(Wg, dtype=np.float64)
+    n, k = idx_rows.shape
+    dx = np.zeros_like(xf)
+    dw = np.zeros((n, k), dtype=np.float64)
+    for i in range(n):
+        for j in range(k):
+            le = int(idx_rows[i, j]) - e_begin
+            if not 0 <= le < E_local:
+                continue
+            W1e = np.asarray(W1[le], dtype=np.float64)
+            W3e = np.asarray(W3[le], dtype=np.float64)
+            W2e = np.asarray(W2[le], dtype=np.float64)
+            h1 = xf[i] @ W1e
+            h3 = xf[i] @ W3e
+            s = 1.0 / (1.0 + np.exp(-h1))
+            dw[i, j] = dout[i] @ ((h1 * s * h3) @ W2e)
+            dA = W2e @ (w[i, j] * dout[i])
+            dx[i] += W1e @ (dA * h3 * s * (1.0 + h1 * (1.0 - s))) + W3e @ (dA * h1 * s)
+    dl = _gate_backward(w, dw)
+    for i in range(n):
+        for j in range(k):
+            dx[i] += dl[i, j] * Wg64[:, int(idx_rows[i, j])]
+    return dx, dw, dl

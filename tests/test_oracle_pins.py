@@ -370,6 +370,146 @@ def test_wgrad_column_subset_and_dout_linearity():
         np.testing.assert_allclose(twice[0][e], 2 * full[0][e], rtol=1e-13, atol=1e-15)
 
 
+# ---------------------------------------------------------------- data and router gradient
+
+def _autograd_backward(x, Wg, b, W1, W3, W2, k, e_begin, E_local, dout):
+    """torch autograd (float64, CPU) through the dense per-token formulation of
+    the layer share: no permutation, routing from torch.topk held fixed."""
+    xt = torch.from_numpy(x.copy()).requires_grad_()
+    wg = torch.from_numpy(Wg.copy()).requires_grad_()
+    logits = xt @ wg + (torch.from_numpy(b) if b is not None else 0)
+    logits.retain_grad()
+    p = torch.softmax(logits, dim=1)
+    top_p, top_i = torch.topk(p, k, dim=1, sorted=True)
+    wts = top_p / top_p.sum(dim=1, keepdim=True)
+    wts.retain_grad()
+    w1, w3, w2 = (torch.from_numpy(a) for a in (W1, W3, W2))
+    rows = []
+    for t in range(x.shape[0]):
+        acc = torch.zeros(x.shape[1], dtype=torch.float64)
+        for j in range(k):
+            le = int(top_i[t, j]) - e_begin
+            if 0 <= le < E_local:
+                h = torch.nn.functional.silu(xt[t] @ w1[le]) * (xt[t] @ w3[le])
+                acc = acc + wts[t, j] * (h @ w2[le])
+        rows.append(acc)
+    out = torch.stack(rows)
+    (out * torch.from_numpy(dout)).sum().backward()
+    return {"dx": xt.grad.numpy(), "dWg": wg.grad.numpy(), "dl": logits.grad.numpy(),
+            "dw": wts.grad.numpy(), "idx": top_i.numpy()}
+
+
+@pytest.mark.parametrize("e_begin,E_local,k,bias", [(0, 6, 2, False), (2, 3, 3, True), (0, 6, 6, False)])
+def test_backward_matches_autograd(e_begin, E_local, k, bias):
+    x, Wg, b, W1, W3, W2 = _tiny_layer(21 + e_begin, T=11, d=9, I=5, E=6, k=k, e_begin=e_begin,
+                                       E_local=E_local, bias=bias)
+    dout = np.random.default_rng(22).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, b, W1, W3, W2, k, e_begin, E_local, 1)
+    g = oracle.backward(x, Wg, W1, W3, W2, res["idx"], res["w"], res["meta"], dout)
+    ref = _autograd_backward(x, Wg, b, W1, W3, W2, k, e_begin, E_local, dout)
+    assert (ref["idx"] == res["idx"]).all()
+    np.testing.assert_allclose(g["dx"], ref["dx"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dWg"], ref["dWg"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dl"], ref["dl"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dw"], ref["dw"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dx_router"] + g["dx_ffn"], g["dx"], rtol=0, atol=0)
+
+
+def test_backward_central_finite_differences():
+    """dx (router and expert paths separately) and dWg against central
+    differences of L = <dout, out>, with x for the router and x_ffn for the
+    experts perturbed independently; the routing must not change."""
+    x, Wg, _, W1, W3, W2 = _tiny_layer(23, T=7, d=6, I=4, E=5, k=2, e_begin=1, E_local=3)
+    xf = x + 0.25 * np.random.default_rng(24).standard_normal(x.shape)
+    dout = np.random.default_rng(25).standard_normal(x.shape)
+    base = oracle.forward(x, Wg, None, W1, W3, W2, 2, 1, 3, 1, x_ffn=xf)
+    g = oracle.backward(x, Wg, W1, W3, W2, base["idx"], base["w"], base["meta"], dout, x_ffn=xf)
+
+    def loss(xr, wg, xe):
+        r = oracle.forward(xr, wg, None, W1, W3, W2, 2, 1, 3, 1, x_ffn=xe)
+        assert (r["idx"] == base["idx"]).all()
+        return float((r["out"] * dout).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(26)
+    for _ in range(10):
+        t, i, e = rng.integers(7), rng.integers(6), rng.integers(5)
+        A, B = x.copy(), x.copy()
+        A[t, i] += h
+        B[t, i] -= h
+        fd = (loss(A, Wg, xf) - loss(B, Wg, xf)) / (2 * h)
+        assert abs(fd - g["dx_router"][t, i]) <= 1e-6 * max(1.0, abs(fd))
+        A, B = xf.copy(), xf.copy()
+        A[t, i] += h
+        B[t, i] -= h
+        fd = (loss(x, Wg, A) - loss(x, Wg, B)) / (2 * h)
+        assert abs(fd - g["dx_ffn"][t, i]) <= 1e-6 * max(1.0, abs(fd))
+        A, B = Wg.copy(), Wg.copy()
+        A[i, e] += h
+        B[i, e] -= h
+        fd = (loss(x, A, xf) - loss(x, B, xf)) / (2 * h)
+        assert abs(fd - g["dWg"][i, e]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_backward_dw_is_the_combine_derivative():
+    """out is linear in the router weights, so one unit step of w[t, j] changes
+    L by exactly dw[t, j] (up to float64 rounding); non-local picks give 0."""
+    x, Wg, _, W1, W3, W2 = _tiny_layer(27, T=9, d=8, I=4, E=6, k=3, e_begin=2, E_local=2)
+    dout = np.random.default_rng(28).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 3, 2, 2, 1)
+    g = oracle.backward(x, Wg, W1, W3, W2, res["idx"], res["w"], res["meta"], dout)
+    pos = res["meta"]["pair_pos"]
+
+    def L(w):
+        return float((oracle.combine(res["y"], pos, w, 8) * dout).sum())
+
+    for t in range(9):
+        for j in range(3):
+            step = np.zeros_like(res["w"])
+            step[t, j] = 1.0
+            want = L(res["w"] + step) - L(res["w"])
+            assert abs(g["dw"][t, j] - want) <= 1e-12 * max(1.0, abs(want))
+            if pos[t, j] < 0:
+                assert g["dw"][t, j] == 0.0
+
+
+def test_backward_invariants():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(29, T=10, d=8, I=6, E=5, k=3)
+    dout = np.random.default_rng(30).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 3, 0, 5, 5)
+    g = oracle.backward(x, Wg, W1, W3, W2, res["idx"], res["w"], res["meta"], dout)
+    # adding a constant to every logit changes nothing, so each dl row sums to 0
+    np.testing.assert_allclose(g["dl"].sum(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(g["dWg"].sum(axis=1), 0.0, atol=1e-12)
+    # dl is zero off the picks
+    mask = np.zeros_like(g["dl"], dtype=bool)
+    mask[np.repeat(np.arange(10), 3), res["idx"].reshape(-1)] = True
+    assert (g["dl"][~mask] == 0).all()
+    # linear in dout
+    g2 = oracle.backward(x, Wg, W1, W3, W2, res["idx"], res["w"], res["meta"], -3.0 * dout)
+    for key in ("dx", "dWg", "dl", "dw"):
+        np.testing.assert_allclose(g2[key], -3.0 * g[key], rtol=1e-12, atol=1e-13)
+    # k = 1: the single renormalised weight is 1 whatever the logits: no router gradient
+    r1 = oracle.forward(x, Wg, None, W1, W3, W2, 1, 0, 5, 5)
+    g1 = oracle.backward(x, Wg, W1, W3, W2, r1["idx"], r1["w"], r1["meta"], dout)
+    assert (g1["dl"] == 0).all() and (g1["dWg"] == 0).all() and (g1["dx_router"] == 0).all()
+
+
+def test_backward_tokens_matches_backward():
+    x, Wg, _, W1, W3, W2 = _tiny_layer(31, T=13, d=10, I=6, E=6, k=2, e_begin=1, E_local=4)
+    xf = x + 0.1
+    dout = np.random.default_rng(32).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, None, W1, W3, W2, 2, 1, 4, 2, x_ffn=xf)
+    g = oracle.backward(x, Wg, W1, W3, W2, res["idx"], res["w"], res["meta"], dout, x_ffn=xf)
+    sel = np.array([12, 0, 5, 7])
+    dx, dw, dl = oracle.backward_tokens(x[sel], xf[sel], res["idx"][sel], res["w"][sel], dout[sel], Wg,
+                                        W1, W3, W2, 1, 4)
+    np.testing.assert_allclose(dx, g["dx"][sel], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dw, g["dw"][sel], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dl, np.take_along_axis(g["dl"][sel], res["idx"][sel].astype(np.int64), 1),
+                               rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_bf16_rounding_is_rne():
