@@ -12,9 +12,10 @@
         --kernel-trace --stats run, HBM bytes per launch of NAME) and the JSON
         record bench.py reports as roofline.traffic.
 
-The traffic record carries a digest of the HIP sources; bench.py reports it
-only while the sources still hash to the same digest (a changed kernel makes
-the measured bytes stale).
+The traffic record carries a digest of the sources the measured kernel is
+built from (its .hip file and the device headers it includes); bench.py
+reports it only while those still hash to the same digest (a changed kernel
+makes the measured bytes stale).
 """
 from __future__ import annotations
 
@@ -31,10 +32,23 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources and headers of the library, in name order."""
+# Sources each measured kernel is compiled from (device code and its launch).
+KERNEL_SOURCES = {
+    "ffn_waved_kernel": ["ffn.hip", "ffn_parts.h", "gemm_tile.h", "moe_common.h", "wave_sched.h"],
+}
+
+
+def _sources(kernel: str | None):
+    if kernel in KERNEL_SOURCES:
+        return [os.path.join(CSRC, n) for n in KERNEL_SOURCES[kernel]]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+
+
+def source_digest(kernel: str | None = None) -> str:
+    """sha256 over the sources of `kernel` (all library sources when it is not
+    listed in KERNEL_SOURCES), in a fixed order."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+    for p in _sources(kernel):
         h.update(os.path.basename(p).encode())
         with open(p, "rb") as f:
             h.update(f.read())
@@ -49,7 +63,8 @@ def load_traffic(path: str, workload: str, T: int):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != source_digest() or rec.get("workload") != workload or rec.get("T") != T:
+    if (rec.get("source_digest") != source_digest(rec.get("kernel")) or rec.get("workload") != workload
+            or rec.get("T") != T):
         return None
     return rec
 
@@ -118,7 +133,8 @@ def _summarize(a) -> None:
     if avg_ns:
         lines.append(f"- at the average duration {avg_ns[0] / 1e3:.1f} us: "
                      f"{(fetch_b + write_b) / (avg_ns[0] * 1e-9) / 1e9:.0f} GB/s")
-    rec = {"kernel": a.kernel, "workload": a.workload, "T": a.T, "source_digest": source_digest(),
+    rec = {"kernel": a.kernel, "workload": a.workload, "T": a.T, "source_digest": source_digest(a.kernel),
+           "sources": [os.path.basename(p) for p in _sources(a.kernel)],
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "traffic_bytes": round(fetch_b + write_b), "fetch_factor": round(f_fetch, 4),
            "write_factor": round(f_write, 4), "avg_us": round(avg_ns[0] / 1e3, 2) if avg_ns else None}
