@@ -8,7 +8,12 @@ kernel (pull, GEMM1 + SwiGLU, GEMM2, fused combine), all inputs resident in
 HBM.  One JSON line is printed on stdout.
 
     python bench.py [--steps K] [--warmup W] [--workload mid|v4share|decode|stress]
-                    [--T T] [--no-cpu] [--serial]
+                    [--T T] [--no-cpu] [--serial] [--backward]
+
+--backward also times the layer's backward on the same batch (data gradient,
+combine-weight and logits gradients, dWg and the expert weight gradient, one
+moe_backward call) and reports it under "extra"; the headline value stays the
+forward step.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -39,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--serial", action="store_true", help="time the phase-by-phase path")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--backward", action="store_true", help="also time the backward")
     return ap.parse_args()
 
 
@@ -77,6 +83,41 @@ def cpu_baseline(inp, wl, target_s):
                       f"(route, dispatch, expert FFN, combine), {dt:.1f} s for the last run"}
 
 
+def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local):
+    """Times moe_backward (all outputs) on the forward's routing; returns the
+    figures reported under extra.backward."""
+    import torch
+
+    from combine_wave_level_amd import moe
+
+    packed_bwd = moe.pack_weights_bwd(p, d(inp["Wg"]), d(inp["W1"]), d(inp["W3"]))
+    dout = d(inp["dout"])
+
+    def run():
+        return moe.backward(p, x, packed, packed_bwd, idx, w, disp, dout, ws, want_dtopk_w=True,
+                            want_dlogits=False, want_dwg=True, want_dw=True)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 2)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(n):
+        run()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    moe.check_error(ws)
+    ms = t0.elapsed_time(t1) / n
+    # recompute of h1, h3 (4 d I) + dA (2 d I) + dx rows (4 d I) + dW (6 d I)
+    # per routed pair, plus the dense dWg product (2 d E per token)
+    flops = 16.0 * wl.d * wl.I * P_local + 2.0 * T * wl.d * wl.E_global
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_per_step": flops, "tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -91,7 +132,7 @@ def main():
 
     wl = get(args.workload)
     T = args.T if args.T is not None else wl.T
-    inp = make_inputs(wl, T=T)
+    inp = make_inputs(wl, T=T, need_dout=args.backward)
     dev = torch.device("cuda:0")
 
     def d(a):
@@ -203,6 +244,9 @@ def main():
         extra["serial_ms_per_step"] = round(s_ms, 4)
         extra["serial_ffn_ms"] = round(s_ffn, 4)
         extra["overlap_speedup_ffn"] = round(s_ffn / ffn_ms, 3)
+
+    if args.backward:
+        extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local)
 
     cpu = None
     if not args.no_cpu:

@@ -1,0 +1,667 @@
+// backward.hip -- deterministic backward of the layer share: the weight
+// gradient of the experts (dW1, dW3, dW2), the data gradient dx, and the
+// router's gradients (of the combine weights, of the logits, of Wg).
+//
+// 10100.com commentary (batch-invariant and deterministic operators) and
+// the DeepSeek-V4 launch digest (itsolotime.com, section 3): gradients must
+// be bitwise identical across repeated backward passes, so there are no
+// unordered float atomics: work is pre-sorted, each unit writes an isolated
+// buffer, and a final reduction sums the buffers in a fixed order.
+//
+// L = <dout, out>, out[t] = sum_j w[t, j] y[pair_pos[t, j]] over local picks,
+// routing held fixed.  Per local expert e with routed rows r (token t_r,
+// router weight w_r):
+//   stage 1 (per row tile x 64 intermediate indices)
+//     h1, h3   = x_r W1, x_r W3   (the forward's GEMM1 tile, same bits)
+//     g        = dout_t W2^T      (fp32),   dA = w_r g
+//     s        = sigmoid(h1),     silu = h1 s,   a = silu h3
+//     dH3      = dA silu,         dH1 = dA h3 s (1 + h1 (1 - s))
+//     aw       = w_r a
+//     -> dH1 | dH3 (one [P][2I] row) and aw rounded to bf16, sorted-row
+//        order; the combine-weight gradient dw_r = <dout_t, y_r> = <g, a>
+//        as fixed partial sums over 32 intermediate indices each
+//   gate (one wavefront per token)
+//     dw_j  = partials of the pick's row summed in ascending order (0 for a
+//             pick whose expert is not local),
+//     dl_j  = w_j (dw_j - sum_m w_m dw_m): the renormalised softmax over
+//             the picks, differentiated (the top-k choice itself is
+//             piecewise constant)
+//   dX (per row tile x output tile): dx_r = [dH1 | dH3] [W1 | W3]^T, K = 2I
+//     ascending, the forward GEMM2's tile with W13^T as the weights
+//   scatter (per token): dx[t] = sum_j dx_{pair_pos[t, j]} (fp32, ascending
+//     j) + sum_j dl_j Wg[:, idx_j] (fused multiply-adds, ascending j), one
+//     rounding to the dtype of x
+//   dWg = x^T dl: fixed chunks of kDwgChunkRows tokens, each an isolated
+//     partial, summed in ascending chunk order
+//   weight gradient (per output tile, per fixed chunk of kWgradChunkRows
+//   rows)
+//     dW1_e += x^T dH1,  dW3_e += x^T dH3,  dW2_e += aw^T dout
+//     the K (= row) index is walked in ascending order inside a chunk; the
+//     first chunk of an expert writes dW directly, chunk c >= 1 writes its
+//     own partial slot; then dW_e += partial slots in ascending chunk order.
+// Every per-token result (dx, dw, dl) depends on the token's own rows only,
+// so it is batch invariant as the forward is.
+#include "ffn_parts.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+using DhCfg13 = TileCfg<128, 128, 2, 2, 64, 3>;  // 128 packed rows = 64 (h1, h3) pairs
+using DhCfgG = TileCfg<64, 128, 2, 2, 64, 3>;    // 64 rows of W2 (as [I][d])
+static_assert(DhCfg13::BT == DhCfgG::BT, "same row tile");
+
+// ---------------------------------------------------------------- stage 1
+
+// dwp: [P_max][I / 32] partial sums of the combine-weight gradient (wave wr
+// of tile nt owns intermediate indices nt * 64 + wr * 32 .. + 31); aw and
+// dwp may be null.
+__global__ __launch_bounds__(256) void bwd_dh_kernel(
+    const uint16_t* __restrict__ xb, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ w13, const uint16_t* __restrict__ w2b,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d,
+    int I, int k, uint16_t* __restrict__ dh, uint16_t* __restrict__ aw, float* __restrict__ dwp) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ float wrow[128];
+  build_mtile_prefix(offsets, E_local, DhCfg13::BT, mt_pre);
+  __syncthreads();
+  const int NT = I / 64, NQ = I / 32;
+  const int total = uniform(mt_pre[E_local] * NT);
+  const int lane = lane_id();
+  static_assert(DhCfg13::WR == 2 && DhCfg13::WT == 2 && DhCfgG::WR == 2 && DhCfgG::WT == 2, "epilogue below");
+  const int wr = tile_wr<DhCfg13>(), wt = tile_wt<DhCfg13>();
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int mt = tile / NT, nt = tile % NT;
+    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * 128);
+    const int count = uniform(min(128, offsets[e + 1] - row0));
+    {
+      // router weight of each row of the tile (threads 128..255 duplicate
+      // threads 0..127 and store the same value: no divergent branch here)
+      const int r = threadIdx.x & 127;
+      const int row = row0 + min(r, count - 1), t = sorted_token[row];
+      float w = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const bool hit = pair_pos[static_cast<size_t>(t) * k + j] == row;
+        w = hit ? topk_w[static_cast<size_t>(t) * k + j] : w;
+      }
+      wrow[r] = r < count ? w : 0.f;
+    }
+    // h1, h3: exactly the forward GEMM1 tile
+    TokRows<DhCfg13> trx;
+    TokRows<DhCfgG> trd;
+#pragma unroll
+    for (int i = 0; i < DhCfg13::LT; ++i) {
+      const int r = min(trow_index<DhCfg13>(i), count - 1);
+      trx.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+    }
+#pragma unroll
+    for (int i = 0; i < DhCfgG::LT; ++i) {
+      const int r = min(trow_index<DhCfgG>(i), count - 1);
+      trd.p[i] = dout + static_cast<size_t>(sorted_token[row0 + r]) * d;
+    }
+    TileAcc<DhCfg13> acc13;
+    tile_mma<DhCfg13>(w13 + static_cast<size_t>(e) * 2 * I * d + frag_offset(nt * 8, 0, d / 32), d / 32,
+                      d / DhCfg13::BK, trx, lds, acc13);
+    TileAcc<DhCfgG> accg;
+    tile_mma<DhCfgG>(w2b + static_cast<size_t>(e) * I * d + frag_offset(nt * 4, 0, d / 32), d / 32,
+                     d / DhCfgG::BK, trd, lds, accg);
+    // wave (wr, wt): acc13 row blocks 4wr..4wr+3 = (h1, h3) pairs of
+    // intermediate blocks 2wr, 2wr+1 of this tile; accg row blocks 2wr, 2wr+1.
+    // Lane l holds intermediate indices 4 (l / 16) + 0..3 of each block for
+    // tile row (wt * 4 + b) * 16 + l % 16.
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int tr = (wt * 4 + b) * 16 + (lane & 15);
+      const bool valid = tr < count;
+      const float w = wrow[tr];
+      float part = 0.f;  // <g, a> over this lane's 8 indices, a-major then r
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int i0 = nt * 64 + (wr * 2 + a) * 16 + 4 * (lane / 16);
+        float v1[4], v3[4], va[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float h1 = acc13.v[2 * a][b][r], h3 = acc13.v[2 * a + 1][b][r];
+          const float g = accg.v[a][b][r];
+          const float dA = w * g;
+          const float s = 1.0f / (1.0f + expf(-h1));
+          const float silu = h1 * s;
+          const float act = silu * h3;
+          v3[r] = dA * silu;
+          v1[r] = ((dA * h3) * s) * (1.0f + h1 * (1.0f - s));
+          va[r] = w * act;
+          part = fmaf(g, act, part);
+        }
+        if (valid) {
+          const size_t o = static_cast<size_t>(row0 + tr) * 2 * I + i0;
+          *reinterpret_cast<u32x2*>(dh + o) = u32x2{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+          *reinterpret_cast<u32x2*>(dh + o + I) = u32x2{pack_bf16x2(v3[0], v3[1]), pack_bf16x2(v3[2], v3[3])};
+          if (aw) {
+            const size_t oa = static_cast<size_t>(row0 + tr) * I + i0;
+            *reinterpret_cast<u32x2*>(aw + oa) = u32x2{pack_bf16x2(va[0], va[1]), pack_bf16x2(va[2], va[3])};
+          }
+        }
+      }
+      if (dwp) {
+        // the four lane groups of one row: a fixed butterfly (every lane
+        // ends with the same, commutatively equal sum)
+        part += __shfl_xor(part, 16, kWave);
+        part += __shfl_xor(part, 32, kWave);
+        if (valid && lane < 16) dwp[static_cast<size_t>(row0 + tr) * NQ + nt * 2 + wr] = part;
+      }
+    }
+    __syncthreads();  // wrow reused by the next tile
+  }
+}
+
+// ---------------------------------------------------------------- gate
+
+// One wavefront per token; lane j < k handles pick j.  dtopk_w, dlogits and
+// dld may be null.  dlc [T][k] receives the picked logits' gradients; dld
+// [T][Ep] the dense logits gradient in bf16 (the dWg product's operand).
+__global__ __launch_bounds__(256) void bwd_gate_kernel(
+    const float* __restrict__ dwp, int NQ, const int32_t* __restrict__ pair_pos,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int k, int E, int Ep,
+    float* __restrict__ dtopk_w, float* __restrict__ dlc, float* __restrict__ dlogits,
+    uint16_t* __restrict__ dld) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  float w = 0.f, dw = 0.f;
+  int e = -1;
+  if (lane < k) {
+    const size_t o = static_cast<size_t>(t) * k + lane;
+    w = topk_w[o];
+    e = topk_idx[o];
+    const int r = pair_pos[o];
+    if (r >= 0) {
+      const float* q = dwp + static_cast<size_t>(r) * NQ;
+      for (int i = 0; i < NQ; ++i) dw += q[i];
+    }
+  }
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s = fmaf(__shfl(w, j, kWave), __shfl(dw, j, kWave), s);
+  const float dl = w * (dw - s);
+  if (lane < k) {
+    const size_t o = static_cast<size_t>(t) * k + lane;
+    if (dtopk_w) dtopk_w[o] = dw;
+    dlc[o] = dl;
+  }
+  if (dlogits || dld) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int ej = __shfl(e, j, kWave);
+      const float gj = __shfl(dl, j, kWave);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q == ej) v[q] = gj;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = lane + 64 * q;
+      if (dlogits && col < E) dlogits[static_cast<size_t>(t) * E + col] = v[q];
+      if (dld && col < Ep) dld[static_cast<size_t>(t) * Ep + col] = f32_to_bf16(v[q]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dX
+
+// dx rows of one row tile x BW output features: the GEMM2 tile of the
+// forward with A = [dH1 | dH3] (K = 2I) and the W13^T fragments.
+template <class F>
+__global__ __launch_bounds__(F::NT) void bwd_dx_gemm_kernel(
+    const uint16_t* __restrict__ dh, const uint16_t* __restrict__ w13t,
+    const int32_t* __restrict__ offsets, uint16_t* __restrict__ dxr, int E_local, int d, int I) {
+  using C = typename F::G2;
+  extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  __syncthreads();
+  const int NT = d / C::BW;
+  const int total = uniform(mt_pre[E_local] * NT);
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int mt = tile / NT, nt = tile % NT;
+    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
+    const int count = uniform(min(C::BT, offsets[e + 1] - row0));
+    gemm2_tile<C>(dh, w13t + static_cast<size_t>(e) * d * 2 * I, dxr, row0, count, nt, d, 2 * I, lds);
+  }
+}
+
+// 8 consecutive elements of row e of Wg^T (bf16 or fp32) as floats.
+template <bool XBF>
+__device__ __forceinline__ void load_wgt8(const void* __restrict__ wgt, int e, int d, int c, float (&v)[8]) {
+  if constexpr (XBF) {
+    const u32x4 q = ld16(static_cast<const uint16_t*>(wgt) + static_cast<size_t>(e) * d + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  } else {
+    const float* p = static_cast<const float*>(wgt) + static_cast<size_t>(e) * d + c * 8;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
+
+// One wavefront per (token, column part), 16-byte column chunks of dx:
+//   dx[t] = sum_j dxr[pair_pos[t, j]] (fp32 adds, ascending j, local picks)
+//         + sum_j dl[t, j] Wg[:, idx[t, j]] (fused multiply-adds, ascending j)
+// rounded once to the dtype of x.  Up to kCombineGroup row reads in flight.
+template <bool XBF>
+__global__ __launch_bounds__(256) void bwd_dx_scatter_kernel(
+    const uint16_t* __restrict__ dxr, const int32_t* __restrict__ pair_pos,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dlc, const void* __restrict__ wgt,
+    int T, int k, int d, int E, int parts, void* __restrict__ dx) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  int cb, ce;
+  combine_cols(d, parts, blockIdx.y, cb, ce);
+  const int32_t* pp = pair_pos + static_cast<size_t>(t) * k;
+  const int32_t* pi = topk_idx + static_cast<size_t>(t) * k;
+  const float* pg = dlc + static_cast<size_t>(t) * k;
+  for (int c = cb + lane; c < ce; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+      int r[kCombineGroup];
+      u32x4 v[kCombineGroup];
+#pragma unroll
+      for (int q = 0; q < kCombineGroup; ++q) {
+        r[q] = uniform(j0 + q < k ? pp[j0 + q] : -1);
+        if (r[q] >= 0) v[q] = ld16(dxr + static_cast<size_t>(r[q]) * d + c * 8);
+      }
+#pragma unroll
+      for (int q = 0; q < kCombineGroup; ++q) {
+        if (r[q] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = acc[2 * i] + __uint_as_float(v[q][i] << 16);
+          acc[2 * i + 1] = acc[2 * i + 1] + __uint_as_float(v[q][i] & 0xffff0000u);
+        }
+      }
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = uniform(pi[j]);
+      if (e < 0 || e >= E) continue;  // not a router id: no router row to read
+      const float g = pg[j];
+      float wv[8];
+      load_wgt8<XBF>(wgt, e, d, c, wv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, wv[i], acc[i]);
+    }
+    if constexpr (XBF) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      st16(static_cast<uint16_t*>(dx) + static_cast<size_t>(t) * d + c * 8, o);
+    } else {
+      float* o = static_cast<float*>(dx) + static_cast<size_t>(t) * d + c * 8;
+      *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- products over rows
+
+// 8x8 bf16 transpose: in[j] holds row j (8 values along u); returns, for
+// each u, the 8 values along rows packed in 4 words (row pairs).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[u][q] = __builtin_amdgcn_perm(in[2 * q + 1][u >> 1], in[2 * q][u >> 1], sel);
+  }
+}
+
+// D[u][v] = sum_r P[r][u] * Q[r][v] over rows r of one chunk, written to
+// out[v * Udim + u] (fp32).  P and Q rows are either direct (row index r)
+// or gathered through sorted_token.
+__device__ __forceinline__ void wgrad_tile(const uint16_t* __restrict__ P, bool p_gather, int p_ld, int Udim,
+                           const uint16_t* __restrict__ Q, bool q_gather, int q_ld, int Vdim,
+                           const int32_t* __restrict__ sorted_token, int rbeg, int rend, int ut,
+                           int vt, float* __restrict__ out, uint16_t* lds) {
+  using C = TileCfg<128, 128, 2, 2, 64, 2>;
+  const int lane = lane_id(), wave = wave_id();
+  const int wr = wave / C::WT, wt = wave % C::WT;
+  // thread's 8x8 block: operand (P for tid < 128), row group rg, u group ug
+  const int tid = threadIdx.x;
+  const bool isP = tid < 128;
+  const int rg = (tid & 127) / 16, ug = tid & 15;
+  const uint16_t* M = isP ? P : Q;
+  const bool gather = isP ? p_gather : q_gather;
+  const int ld = isP ? p_ld : q_ld;
+  const int dim = isP ? Udim : Vdim;
+  const int col0 = (isP ? ut : vt) * 128 + ug * 8;
+  const bool col_ok = col0 < dim;  // dims are multiples of 64, so 8-groups are whole
+  f32x4 acc[C::AW][C::AT];
+#pragma unroll
+  for (int a = 0; a < C::AW; ++a)
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 raw[8];
+  auto gload = [&](int kbase) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = kbase + rg * 8 + j;
+      if (r < rend && col_ok) {
+        const size_t row = gather ? static_cast<size_t>(sorted_token[r]) : static_cast<size_t>(r);
+        raw[j] = ld16(M + row * ld + col0);
+      } else {
+        raw[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    u32x4 tr[8];
+    transpose8x8(raw, tr);
+    uint16_t* st = lds + buf * C::STAGE + (isP ? 0 : C::NFW * 512);
+    const int ks = rg / 4, slot_hi = (rg % 4) * 16;
+#pragma unroll
+    for (int uu = 0; uu < 8; ++uu) {
+      const int u = ug * 8 + uu;  // 0..127 inside the tile
+      st16(st + ((u / 16) * 2 + ks) * 512 + (slot_hi + (u % 16)) * 8, tr[uu]);
+    }
+  };
+  const int nk = uniform((rend - rbeg + 63) / 64);
+  if (nk > 0) {
+    gload(rbeg);
+    lstore(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    __syncthreads();
+    if (kt + 1 < nk) gload(rbeg + (kt + 1) * 64);
+    const uint16_t* st = lds + cur * C::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 af[C::AW], bfr[C::AT];
+#pragma unroll
+      for (int a = 0; a < C::AW; ++a) af[a] = ld16(st + ((wr * C::AW + a) * 2 + ks) * 512 + lane * 8);
+#pragma unroll
+      for (int b = 0; b < C::AT; ++b) bfr[b] = ld16(st + (C::NFW + (wt * C::AT + b) * 2 + ks) * 512 + lane * 8);
+#pragma unroll
+      for (int a = 0; a < C::AW; ++a)
+#pragma unroll
+        for (int b = 0; b < C::AT; ++b) acc[a][b] = mfma16x16x32(af[a], bfr[b], acc[a][b]);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < C::AW; ++a) {
+    const int u = ut * 128 + (wr * C::AW + a) * 16 + 4 * (lane / 16);
+    if (u >= Udim) continue;
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) {
+      const int v = vt * 128 + (wt * C::AT + b) * 16 + (lane & 15);
+      if (v >= Vdim) continue;
+      *reinterpret_cast<f32x4*>(out + static_cast<size_t>(v) * Udim + u) = acc[a][b];
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------- dWg
+
+// bf16 x: part[c][i][e] = sum over tokens of chunk c of x[t][i] dld[t][e].
+__global__ __launch_bounds__(256) void bwd_dwg_kernel(const uint16_t* __restrict__ dld,
+                                                      const uint16_t* __restrict__ xb, int T, int d,
+                                                      int Ep, float* __restrict__ part) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int tU = (Ep + 127) / 128, tV = d / 128;
+  const int tpc = tU * tV;
+  const int total = tpc * ((T + kDwgChunkRows - 1) / kDwgChunkRows);
+  for (int task = blockIdx.x; task < total; task += gridDim.x) {
+    const int c = task / tpc, rel = task % tpc;
+    const int ut = rel % tU, vt = rel / tU;
+    const int rbeg = c * kDwgChunkRows, rend = min(T, rbeg + kDwgChunkRows);
+    wgrad_tile(dld, false, Ep, Ep, xb, false, d, d, nullptr, rbeg, rend, ut, vt,
+               part + static_cast<size_t>(c) * d * Ep, lds);
+  }
+}
+
+// dWg[i][e] = sum of the chunk partials in ascending chunk order.
+__global__ __launch_bounds__(256) void bwd_dwg_reduce_kernel(const float* __restrict__ part, int nch,
+                                                             int d, int E, int Ep, float* __restrict__ dWg) {
+  const size_t id = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= static_cast<size_t>(d) * E) return;
+  const size_t i = id / E, e = id % E;
+  const size_t mat = static_cast<size_t>(d) * Ep;
+  float acc = part[i * Ep + e];
+  for (int c = 1; c < nch; ++c) acc += part[c * mat + i * Ep + e];
+  dWg[id] = acc;
+}
+
+// fp32 x (the router then runs on fp32 values): dWg[i][e] = sum over tokens
+// in ascending order, picks in ascending j, of x[t][i] dl[t, j] where
+// idx[t, j] = e; one thread per element, fused multiply-adds.
+__global__ __launch_bounds__(256) void bwd_dwg_f32_kernel(const float* __restrict__ x,
+                                                          const int32_t* __restrict__ topk_idx,
+                                                          const float* __restrict__ dlc, int T, int k,
+                                                          int d, int E, float* __restrict__ dWg) {
+  const size_t id = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= static_cast<size_t>(d) * E) return;
+  const int i = static_cast<int>(id / E), e = static_cast<int>(id % E);
+  float acc = 0.f;
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j)
+      if (topk_idx[static_cast<size_t>(t) * k + j] == e)
+        acc = fmaf(x[static_cast<size_t>(t) * d + i], dlc[static_cast<size_t>(t) * k + j], acc);
+  dWg[id] = acc;
+}
+
+// ---------------------------------------------------------------- weight gradient
+
+__device__ __forceinline__ int n_chunks(int rows) {
+  return rows <= kWgradChunkRows ? 1 : (rows + kWgradChunkRows - 1) / kWgradChunkRows;
+}
+
+__global__ __launch_bounds__(256) void wgrad_w_kernel(
+    const uint16_t* __restrict__ xb, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ dh, const uint16_t* __restrict__ aw, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_token, int E_local, int d, int I, float* __restrict__ dW1,
+    float* __restrict__ dW3, float* __restrict__ dW2, float* __restrict__ partial) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ int32_t task_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t slot_pre[kMaxLocalExperts + 1];
+  const int tI = (I + 127) / 128, tD = (d + 127) / 128;
+  const int tpm = tI * tD;  // tiles per matrix (dW1/dW3: u = i, v = f; dW2: u = n, v = i)
+  if (threadIdx.x == 0) {
+    int run = 0, srun = 0;
+    for (int e = 0; e < E_local; ++e) {
+      const int nc = n_chunks(offsets[e + 1] - offsets[e]);
+      task_pre[e] = run;
+      slot_pre[e] = srun;
+      run += nc * 3 * tpm;
+      srun += nc - 1;
+    }
+    task_pre[E_local] = run;
+    slot_pre[E_local] = srun;
+  }
+  __syncthreads();
+  const size_t mat = static_cast<size_t>(d) * I;
+  const int total = uniform(task_pre[E_local]);
+  for (int task = blockIdx.x; task < total; task += gridDim.x) {
+    const int e = uniform(expert_of_mtile(task_pre, 0, E_local, task));
+    int rel = task - uniform(task_pre[e]);
+    const int c = rel / (3 * tpm);
+    rel %= 3 * tpm;
+    const int m = rel / tpm, t = rel % tpm;
+    const int r0 = uniform(offsets[e]), rows = uniform(offsets[e + 1]) - r0;
+    const int rbeg = r0 + c * kWgradChunkRows;
+    const int rend = r0 + min(rows, (c + 1) * kWgradChunkRows);
+    float* base;
+    if (c == 0) {
+      base = (m == 0 ? dW1 : m == 1 ? dW3 : dW2) + e * mat;
+    } else {
+      base = partial + (static_cast<size_t>(uniform(slot_pre[e]) + c - 1) * 3 + m) * mat;
+    }
+    if (m < 2) {
+      const int ut = t % tI, vt = t / tI;
+      wgrad_tile(m == 0 ? dh : dh + I, false, 2 * I, I, xb, true, d, d, sorted_token, rbeg, rend, ut, vt,
+                 base, lds);
+    } else {
+      const int ut = t % tD, vt = t / tD;
+      wgrad_tile(dout, true, d, d, aw, false, I, I, sorted_token, rbeg, rend, ut, vt, base, lds);
+    }
+  }
+}
+
+// dW_e += partial slots of chunks 1 .. n-1 in ascending order.
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int32_t* __restrict__ offsets,
+                                                           int E_local, size_t mat,
+                                                           float* __restrict__ dW1,
+                                                           float* __restrict__ dW3,
+                                                           float* __restrict__ dW2,
+                                                           const float* __restrict__ partial) {
+  int slot = 0;
+  for (int e = 0; e < E_local; ++e) {
+    const int nc = n_chunks(offsets[e + 1] - offsets[e]);
+    if (nc > 1) {
+      for (size_t i = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < 3 * mat;
+           i += static_cast<size_t>(gridDim.x) * blockDim.x * 4) {
+        const int m = static_cast<int>(i / mat);
+        const size_t o = i % mat;
+        float* dst = (m == 0 ? dW1 : m == 1 ? dW3 : dW2) + e * mat + o;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(dst);
+        for (int c = 1; c < nc; ++c) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(partial + (static_cast<size_t>(slot + c - 1) * 3 + m) * mat + o);
+          acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+        }
+        *reinterpret_cast<f32x4*>(dst) = acc;
+      }
+    }
+    slot += nc - 1;
+  }
+}
+
+
+// Tile shape of the dX product (rows per expert decide, as in the forward).
+enum class DxShape { Small, Small64, Large, Mid };
+
+DxShape pick_dx_shape(const moe_problem_t& p) {
+  const double rows = static_cast<double>(p.T) * p.k / p.E_global;
+  if (rows < 96.0) return p.T <= FfnSmall::G2::BT ? DxShape::Small : DxShape::Small64;
+  if (p.d % FfnLarge::G2::BW == 0) return DxShape::Large;
+  return DxShape::Mid;
+}
+
+template <class F>
+hipError_t launch_dx_gemm(const moe_problem_t& p, const uint16_t* dh, const uint16_t* w13t,
+                          const int32_t* offsets, uint16_t* dxr, int cus, hipStream_t s) {
+  int per_cu = 0;
+  hipError_t e;
+  constexpr size_t lds = F::G2::LDS_BYTES;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dx_gemm_kernel<F>, F::NT, lds)) != hipSuccess)
+    return e;
+  bwd_dx_gemm_kernel<F><<<max(1, per_cu) * cus, F::NT, lds, s>>>(dh, w13t, offsets, dxr, p.E_local, p.d, p.I);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, char* ws,
+                           hipStream_t s) {
+  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
+  const char* pk = static_cast<const char*>(a.packed);
+  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
+  const uint16_t* w2b = reinterpret_cast<const uint16_t*>(pk + PL.w2b);
+  const bool want_dw = a.dW1 != nullptr;
+  const bool want_data = a.dx != nullptr;
+  const bool xbf = p.x_dtype == MOE_BF16;
+  uint16_t* dh = reinterpret_cast<uint16_t*>(ws + L.bwd_dh);
+  uint16_t* aw = want_dw ? reinterpret_cast<uint16_t*>(ws + L.bwd_aw) : nullptr;
+  float* dwp = want_data ? reinterpret_cast<float*>(ws + L.bwd_dwp) : nullptr;
+  float* dlc = reinterpret_cast<float*>(ws + L.bwd_dlc);
+  uint16_t* dld = (want_data && a.dWg && xbf) ? reinterpret_cast<uint16_t*>(ws + L.bwd_dld) : nullptr;
+  uint16_t* dxr = reinterpret_cast<uint16_t*>(ws + L.bwd_dxr);
+  float* partial = reinterpret_cast<float*>(ws + L.wgrad);
+  const uint16_t* xb = nullptr;
+  hipError_t e;
+  int dev = 0, cus = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  // the same bf16 staging copy of x that the forward GEMM1 reads
+  if ((e = stage_x_bf16(p, L, a.x, ws, s, &xb)) != hipSuccess) return e;
+  const size_t words = static_cast<size_t>(p.E_local) * p.d * p.I;
+  if (p.T == 0) {
+    // no rows: every gradient is zero (dx, dtopk_w and dlogits are empty)
+    if (want_dw) {
+      if ((e = fill_zero(a.dW1, words, s)) != hipSuccess) return e;
+      if ((e = fill_zero(a.dW3, words, s)) != hipSuccess) return e;
+      if ((e = fill_zero(a.dW2, words, s)) != hipSuccess) return e;
+    }
+    if (a.dWg) return fill_zero(a.dWg, static_cast<size_t>(p.d) * p.E_global, s);
+    return hipSuccess;
+  }
+  const size_t lds13 = DhCfg13::LDS_BYTES > DhCfgG::LDS_BYTES ? DhCfg13::LDS_BYTES : DhCfgG::LDS_BYTES;
+  bwd_dh_kernel<<<cus * 2, 256, lds13, s>>>(xb, static_cast<const uint16_t*>(a.dout), w13, w2b, a.offsets,
+                                            a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k,
+                                            dh, aw, dwp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (want_data) {
+    const PackedBwdLayout BL = packed_bwd_layout(p);
+    const char* pb = static_cast<const char*>(a.packed_bwd);
+    const uint16_t* w13t = reinterpret_cast<const uint16_t*>(pb + BL.w13t);
+    const void* wgt = pb + BL.wgt;
+    bwd_gate_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(dwp, p.I / 32, a.pair_pos, a.topk_idx, a.topk_w, p.T, p.k,
+                                                  p.E_global, L.Ep, a.dtopk_w, dlc, a.dlogits, dld);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    switch (pick_dx_shape(p)) {
+      case DxShape::Small: e = launch_dx_gemm<FfnSmall>(p, dh, w13t, a.offsets, dxr, cus, s); break;
+      case DxShape::Small64: e = launch_dx_gemm<FfnSmall64>(p, dh, w13t, a.offsets, dxr, cus, s); break;
+      case DxShape::Large: e = launch_dx_gemm<FfnLarge>(p, dh, w13t, a.offsets, dxr, cus, s); break;
+      default: e = launch_dx_gemm<FfnMid>(p, dh, w13t, a.offsets, dxr, cus, s); break;
+    }
+    if (e != hipSuccess) return e;
+    const int parts = combine_parts(p.T, p.d);
+    const dim3 grid((p.T + 3) / 4, parts);
+    if (xbf)
+      bwd_dx_scatter_kernel<true><<<grid, 256, 0, s>>>(dxr, a.pair_pos, a.topk_idx, dlc, wgt, p.T, p.k, p.d,
+                                                       p.E_global, parts, a.dx);
+    else
+      bwd_dx_scatter_kernel<false><<<grid, 256, 0, s>>>(dxr, a.pair_pos, a.topk_idx, dlc, wgt, p.T, p.k, p.d,
+                                                        p.E_global, parts, a.dx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.dWg) {
+      const size_t n = static_cast<size_t>(p.d) * p.E_global;
+      const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+      if (xbf) {
+        using C = TileCfg<128, 128, 2, 2, 64, 2>;
+        float* part = reinterpret_cast<float*>(ws + L.bwd_dwg);
+        bwd_dwg_kernel<<<cus * 2, 256, C::LDS_BYTES, s>>>(dld, xb, p.T, p.d, L.Ep, part);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        bwd_dwg_reduce_kernel<<<blocks, 256, 0, s>>>(part, (p.T + kDwgChunkRows - 1) / kDwgChunkRows, p.d,
+                                                     p.E_global, L.Ep, a.dWg);
+      } else {
+        bwd_dwg_f32_kernel<<<blocks, 256, 0, s>>>(static_cast<const float*>(a.x), a.topk_idx, dlc, p.T, p.k,
+                                                  p.d, p.E_global, a.dWg);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  if (!want_dw) return hipSuccess;
+  using C = TileCfg<128, 128, 2, 2, 64, 2>;
+  wgrad_w_kernel<<<cus * 2, 256, C::LDS_BYTES, s>>>(xb, static_cast<const uint16_t*>(a.dout), dh, aw,
+                                                    a.offsets, a.sorted_token, p.E_local, p.d, p.I, a.dW1,
+                                                    a.dW3, a.dW2, partial);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  wgrad_reduce_kernel<<<cus * 4, 256, 0, s>>>(a.offsets, p.E_local, static_cast<size_t>(p.d) * p.I, a.dW1,
+                                              a.dW3, a.dW2, partial);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -33,6 +33,7 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.W = p.E_local / p.experts_per_wave;
   L.ngroups = p.E_local + L.W + 1;
   L.P_max = p.T * (p.k < p.E_local ? p.k : p.E_local);
+  L.Ep = static_cast<int>(align_up(static_cast<size_t>(p.E_global), 64));
   L.ctr_region_words = sched_region_words(L.W);
   L.sync_words = sched_counter_words(L.W);
   const size_t wg_slots = static_cast<size_t>(L.P_max) / kWgradChunkRows;
@@ -52,7 +53,15 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.xbf = take(p.x_dtype == MOE_F32 ? static_cast<size_t>(p.T) * p.d * 2 : 0);
   L.act = take(static_cast<size_t>(L.P_max) * p.I * 2);
   L.sync = take(L.sync_words * 4);
-  L.wgrad = take(align_up(static_cast<size_t>(L.P_max) * p.I * 2 * 3, 256) + L.wgrad_bytes);
+  const bool xbf = p.x_dtype == MOE_BF16;
+  L.bwd_dh = take(static_cast<size_t>(L.P_max) * 2 * p.I * 2);
+  L.bwd_aw = take(static_cast<size_t>(L.P_max) * p.I * 2);
+  L.wgrad = take(L.wgrad_bytes);
+  L.bwd_dwp = take(static_cast<size_t>(L.P_max) * (p.I / 32) * 4);
+  L.bwd_dlc = take(static_cast<size_t>(p.T) * p.k * 4);
+  L.bwd_dld = take(xbf ? static_cast<size_t>(p.T) * L.Ep * 2 : 0);
+  L.bwd_dxr = take(static_cast<size_t>(L.P_max) * p.d * 2);
+  L.bwd_dwg = take(xbf ? static_cast<size_t>((p.T + kDwgChunkRows - 1) / kDwgChunkRows) * p.d * L.Ep * 4 : 0);
   L.total = off;
   return L;
 }
@@ -79,6 +88,20 @@ size_t moe_packed_weights_size(const moe_problem_t* p) {
 size_t moe_workspace_size(const moe_problem_t* p) {
   if (check_problem(p) != MOE_OK) return 0;
   return ws_layout(*p).total;
+}
+
+size_t moe_packed_bwd_size(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return packed_bwd_layout(*p).total;
+}
+
+moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const void* W1, const void* W3,
+                                  void* packed_bwd, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!Wg || !W1 || !W3 || !packed_bwd) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed_bwd) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_bwd(*p, Wg, W1, W3, packed_bwd, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void* W1,
@@ -162,9 +185,57 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
     return MOE_ERR_INVALID_ARG;
   WsLayout L;
   if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
-  return hip_status(launch_wgrad(*p, L, x, packed, expert_offsets, sorted_token, pair_pos, topk_w,
-                                 dout, dW1, dW3, dW2, static_cast<char*>(ws),
-                                 static_cast<hipStream_t>(stream)));
+  BackwardArgs a{};
+  a.x = x;
+  a.packed = packed;
+  a.topk_w = topk_w;
+  a.offsets = expert_offsets;
+  a.sorted_token = sorted_token;
+  a.pair_pos = pair_pos;
+  a.dout = dout;
+  a.dW1 = dW1;
+  a.dW3 = dW3;
+  a.dW2 = dW2;
+  return hip_status(launch_backward(*p, L, a, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* packed,
+                          const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
+                          const int32_t* expert_offsets, const int32_t* sorted_token,
+                          const int32_t* pair_pos, const void* dout, void* dx, float* dtopk_w,
+                          float* dlogits, float* dWg, float* dW1, float* dW3, float* dW2, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!packed || !packed_bwd || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !topk_idx || !topk_w || !sorted_token || !pair_pos || !dout || !dx))
+    return MOE_ERR_INVALID_ARG;
+  const bool any_w = dW1 || dW3 || dW2, all_w = dW1 && dW3 && dW2;
+  if (any_w && !all_w) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || !aligned16(packed) || !aligned16(packed_bwd) || (dout && !aligned16(dout)) ||
+      (dx && !aligned16(dx)) || (dW1 && !aligned16(dW1)) || (dW3 && !aligned16(dW3)) ||
+      (dW2 && !aligned16(dW2)))
+    return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  BackwardArgs a{};
+  a.x = x;
+  a.packed = packed;
+  a.packed_bwd = packed_bwd;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.offsets = expert_offsets;
+  a.sorted_token = sorted_token;
+  a.pair_pos = pair_pos;
+  a.dout = dout;
+  a.dx = p->T > 0 ? dx : nullptr;
+  a.dtopk_w = dtopk_w;
+  a.dlogits = dlogits;
+  a.dWg = dWg;
+  a.dW1 = dW1;
+  a.dW3 = dW3;
+  a.dW2 = dW2;
+  return hip_status(launch_backward(*p, L, a, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_check_error(void* ws, moe_stream_t stream) {

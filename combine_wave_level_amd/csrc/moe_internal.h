@@ -27,10 +27,21 @@ namespace moe {
 //   xbf        bf16 [T][d] (only when x is fp32): x rounded for the FFN
 //   act        bf16 [P_max][I]: a = silu(h1) * h3, sorted-row order
 //   sync       int32 counters of the persistent expert-wave kernel
+//   bwd_dh     bf16 [P_max][2I]: dH1 | dH3 per routed row (backward)
+//   bwd_aw     bf16 [P_max][I]: w * a per routed row (weight gradient)
 //   wgrad      fp32 isolated partial buffers of the weight gradient
+//   bwd_dwp    fp32 [P_max][I / 32]: partial sums of the combine-weight
+//              gradient of each routed row
+//   bwd_dlc    fp32 [T][k]: gradient of the picked logits
+//   bwd_dld    bf16 [T][Ep]: dense logits gradient (bf16 x only)
+//   bwd_dxr    bf16 [P_max][d]: data gradient of each routed row
+//   bwd_dwg    fp32 [ceil(T / kDwgChunkRows)][d][Ep]: isolated partials of
+//              dWg (bf16 x only)
 struct WsLayout {
-  size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, wgrad, total;
+  size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, bwd_dh, bwd_aw, wgrad,
+      bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, total;
   int nchunks, W, ngroups, P_max;
+  int Ep;                // E_global rounded up to 64 (columns of the dense logits gradient)
   int ctr_region_words;  // per-XCD counter region of the persistent kernel
   size_t sync_words, wgrad_bytes;
 };
@@ -40,6 +51,50 @@ WsLayout ws_layout(const moe_problem_t& p);
 // Rows of the weight-gradient split along the routed rows of one expert:
 // each chunk of this many rows reduces into its own partial slot.
 constexpr int kWgradChunkRows = 2048;
+// Tokens per isolated partial of the router-weight gradient dWg.
+constexpr int kDwgChunkRows = 1024;
+
+// Backward weight buffer (moe_pack_weights_bwd):
+//   wgt  : Wg^T as [E_global][d] row-major in the dtype of x (router rows
+//          for the router's share of dx);
+//   w13t : per local expert, [W1 | W3]^T as [d][2I] in fragment layout
+//          (K = 2I: the W1 columns, then the W3 columns), the weights of
+//          dx = dH1 W1^T + dH3 W3^T.
+struct PackedBwdLayout {
+  size_t wgt, w13t, total;
+};
+
+inline PackedBwdLayout packed_bwd_layout(const moe_problem_t& p) {
+  PackedBwdLayout L;
+  size_t off = 0;
+  L.wgt = off;
+  off += align_up(static_cast<size_t>(p.E_global) * p.d * (p.x_dtype == MOE_BF16 ? 2 : 4), 256);
+  L.w13t = off;
+  off += align_up(static_cast<size_t>(p.E_local) * p.d * 2 * p.I * 2, 256);
+  L.total = off;
+  return L;
+}
+
+// Arguments of one backward call (pointers as passed to moe_backward;
+// dx == nullptr: weight gradient only; dW1 == nullptr: no weight gradient).
+struct BackwardArgs {
+  const void* x;
+  const void* packed;
+  const void* packed_bwd;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* sorted_token;
+  const int32_t* pair_pos;
+  const void* dout;
+  void* dx;
+  float* dtopk_w;
+  float* dlogits;
+  float* dWg;
+  float* dW1;
+  float* dW3;
+  float* dW2;
+};
 
 // ------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.  Shapes are validated by the
@@ -47,6 +102,8 @@ constexpr int kWgradChunkRows = 2048;
 
 hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
                        const void* W2, void* packed, hipStream_t s);
+hipError_t launch_pack_bwd(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
+                           void* packed_bwd, hipStream_t s);
 
 hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packed,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
@@ -76,9 +133,7 @@ hipError_t fill_zero(void* p, size_t n, hipStream_t s);
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s);
 
-hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
-                        const int32_t* offsets, const int32_t* sorted_token,
-                        const int32_t* pair_pos, const float* topk_w, const void* dout,
-                        float* dW1, float* dW3, float* dW2, char* ws, hipStream_t s);
+hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, char* ws,
+                           hipStream_t s);
 
 }  // namespace moe

@@ -24,6 +24,8 @@ __device__ __forceinline__ uint16_t src_bf16(const void* src, size_t k, size_t n
 //         2b+1 <- W3 columns 16b.. (S = W1, S2 = W3, each [K][N/2]).
 // mode 2: no transpose: the source already is M[N][K] (row stride K); the
 //         8 values of a slot are one contiguous 16-byte read.
+// mode 3: no transpose, K concatenated: k < K/2 from S, k >= K/2 from S2,
+//         each [N][K/2] (row stride K/2).
 template <bool SRC_BF16, int MODE>
 __global__ void pack_frag_kernel(const void* __restrict__ S, const void* __restrict__ S2,
                                  uint16_t* __restrict__ dst, int K, int N, int n_src,
@@ -42,6 +44,11 @@ __global__ void pack_frag_kernel(const void* __restrict__ S, const void* __restr
   uint16_t v[8];
   if (MODE == 2) {
     for (int e = 0; e < 8; ++e) v[e] = src_bf16<SRC_BF16>(base, row, static_cast<size_t>(kg) * 8 + e, K);
+  } else if (MODE == 3) {
+    const size_t half = static_cast<size_t>(K / 2), k0 = static_cast<size_t>(kg) * 8;
+    const void* src = k0 < half ? base : base2;
+    const size_t kk = k0 < half ? k0 : k0 - half;
+    for (int e = 0; e < 8; ++e) v[e] = src_bf16<SRC_BF16>(src, row, kk + e, half);
   } else if (MODE == 0) {
     for (int e = 0; e < 8; ++e)
       v[e] = row < n_src ? src_bf16<SRC_BF16>(base, static_cast<size_t>(kg) * 8 + e, row, n_src) : 0;
@@ -71,7 +78,44 @@ __global__ void pack_router_f32_kernel(const float* __restrict__ Wg, float* __re
   dst[i] = col < E ? Wg[static_cast<size_t>(row) * E + col] : 0.f;
 }
 
+// Wg [d][E] -> Wg^T [E][d], element type kept (uint16 bf16 bits or fp32).
+template <class T>
+__global__ void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int d, int E) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<size_t>(d) * E) return;
+  const size_t e = i / d, row = i % d;
+  dst[i] = src[row * E + e];
+}
+
 }  // namespace
+
+hipError_t launch_pack_bwd(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
+                           void* packed_bwd, hipStream_t s) {
+  const PackedBwdLayout L = packed_bwd_layout(p);
+  char* base = static_cast<char*>(packed_bwd);
+  const int threads = 256;
+  const size_t n = static_cast<size_t>(p.d) * p.E_global;
+  const unsigned blocks = static_cast<unsigned>((n + threads - 1) / threads);
+  if (p.x_dtype == MOE_BF16)
+    transpose_kernel<uint16_t><<<blocks, threads, 0, s>>>(static_cast<const uint16_t*>(Wg),
+                                                          reinterpret_cast<uint16_t*>(base + L.wgt), p.d, p.E_global);
+  else
+    transpose_kernel<float><<<blocks, threads, 0, s>>>(static_cast<const float*>(Wg),
+                                                       reinterpret_cast<float*>(base + L.wgt), p.d, p.E_global);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // [W1 | W3]^T: [d][2I] per expert, K = 2I
+  const size_t slots = static_cast<size_t>(p.d) * (2 * p.I / 8);
+  dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
+  const size_t src_stride = static_cast<size_t>(p.d) * p.I;
+  const size_t dst_stride = static_cast<size_t>(p.d) * 2 * p.I;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(base + L.w13t);
+  if (p.w_dtype == MOE_BF16)
+    pack_frag_kernel<true, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
+  else
+    pack_frag_kernel<false, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
                        const void* W2, void* packed, hipStream_t s) {

@@ -28,6 +28,7 @@ MOE_FLAG_SERIAL = 0x1
 EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
+    "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
             "moe_combine": (st, [P, vp, i32p, f32p, vp, vp]),
             "moe_expert_wgrad": (st, [P, vp, vp, i32p, i32p, i32p, f32p, vp, f32p, f32p, f32p,
                                       vp, ctypes.c_size_t, vp]),
+            "moe_packed_bwd_size": (ctypes.c_size_t, [P]),
+            "moe_pack_weights_bwd": (st, [P, vp, vp, vp, vp, vp]),
+            "moe_backward": (st, [P, vp, vp, vp, i32p, f32p, i32p, i32p, i32p, vp, vp, f32p, f32p, f32p,
+                                  f32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
             "moe_check_error": (st, [vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_version": (ctypes.c_char_p, []),
@@ -217,6 +222,42 @@ def wgrad(p: Problem, x, packed, disp: Dispatch, topk_w, dout, ws):
         _p(disp.pair_pos), _p(topk_w), _p(dout), _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(),
         _stream()), "moe_expert_wgrad")
     return dW1, dW3, dW2
+
+
+def packed_bwd_size(p: Problem) -> int:
+    return int(lib().moe_packed_bwd_size(ctypes.byref(p)))
+
+
+def pack_weights_bwd(p: Problem, Wg, W1, W3) -> torch.Tensor:
+    n = packed_bwd_size(p)
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, "packed_bwd_size")
+    packed = torch.empty(n, dtype=torch.uint8, device=W1.device)
+    _check(lib().moe_pack_weights_bwd(ctypes.byref(p), _p(Wg), _p(W1), _p(W3), _p(packed), _stream()),
+           "moe_pack_weights_bwd")
+    return packed
+
+
+def backward(p: Problem, x, packed, packed_bwd, topk_idx, topk_w, disp: Dispatch, dout, ws,
+             want_dtopk_w=True, want_dlogits=False, want_dwg=True, want_dw=False):
+    """Data gradient dx (always) and, on request, dtopk_w, dlogits, dWg and the
+    expert weight gradient, in one call."""
+    dev = x.device
+    f32 = torch.float32
+    dx = torch.empty((p.T, p.d), dtype=x.dtype, device=dev)
+    dtw = torch.empty((p.T, p.k), dtype=f32, device=dev) if want_dtopk_w else None
+    dlg = torch.empty((p.T, p.E_global), dtype=f32, device=dev) if want_dlogits else None
+    dwg = torch.empty((p.d, p.E_global), dtype=f32, device=dev) if want_dwg else None
+    dW1 = dW3 = dW2 = None
+    if want_dw:
+        dW1 = torch.empty((p.E_local, p.d, p.I), dtype=f32, device=dev)
+        dW3 = torch.empty((p.E_local, p.d, p.I), dtype=f32, device=dev)
+        dW2 = torch.empty((p.E_local, p.I, p.d), dtype=f32, device=dev)
+    _check(lib().moe_backward(
+        ctypes.byref(p), _p(x), _p(packed), _p(packed_bwd), _p(topk_idx), _p(topk_w), _p(disp.offsets),
+        _p(disp.sorted_token), _p(disp.pair_pos), _p(dout), _p(dx), _p(dtw), _p(dlg), _p(dwg),
+        _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(), _stream()), "moe_backward")
+    return {"dx": dx, "dtopk_w": dtw, "dlogits": dlg, "dWg": dwg, "dW1": dW1, "dW3": dW3, "dW2": dW2}
 
 
 def check_error(ws) -> None:

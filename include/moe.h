@@ -104,6 +104,19 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void
                               const void* W3, const void* W2, void* packed,
                               moe_stream_t stream);
 
+/* Bytes of the backward weight buffer moe_pack_weights_bwd writes. 0 on a
+ * bad shape. */
+size_t moe_packed_bwd_size(const moe_problem_t* p);
+
+/* One-time re-layout of the weights the data gradient reads (weights are
+ * parameters; forward-only callers never need this buffer): Wg^T in the
+ * dtype of x, and per local expert [W1 | W3]^T in the MFMA fragment layout.
+ *   Wg [d, E_global] in x_dtype; W1, W3 [E_local, d, I] in w_dtype (rounded
+ *   to bf16 when F32).  packed_bwd: moe_packed_bwd_size(p) bytes, written
+ *   entirely. */
+moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const void* W1,
+                                  const void* W3, void* packed_bwd, moe_stream_t stream);
+
 /* ------------------------------------------------------------ the path */
 
 /* Router (workload definition of the layer: softmax over all E_global
@@ -179,6 +192,44 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
                               const int32_t* pair_pos, const float* topk_w, const void* dout,
                               float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
                               moe_stream_t stream);
+
+/* Backward of the layer share: data gradient, router gradients and
+ * (optionally) the expert weight gradient of L = <dout, out>, with the
+ * routing held fixed (the top-k choice is piecewise constant in the logits).
+ * Deterministic and batch invariant (10100.com deterministic operators;
+ * digest section 3): no float atomics; every per-token result depends on
+ * the token's own rows only; reductions over tokens use fixed chunks summed
+ * in ascending order.  With dy = topk_w[t, j] * dout[t] per routed row and
+ * h1, h3 recomputed exactly as the forward computes them:
+ *   dA = dy W2^T, dH3 = dA * silu(h1), dH1 = dA * h3 * s * (1 + h1 (1 - s)),
+ *   dtopk_w[t, j] = <dout[t], y> = <dout[t] W2^T, silu(h1) * h3> for a local
+ *     pick (summed from fixed partials over 32 intermediate indices), 0 for a
+ *     pick whose expert is not local;
+ *   dl[t, j] = topk_w[t, j] * (dtopk_w[t, j] - sum_m topk_w[t, m] dtopk_w[t, m])
+ *     (renormalised softmax over the picks), 0 off the picks;
+ *   dx[t] = sum_j [local] (dH1 W1^T + dH3 W3^T) of the pick's row (each row
+ *     rounded to bf16, summed in fp32 in ascending j) + sum_j dl[t, j]
+ *     Wg[:, idx[t, j]] (fp32 fused multiply-adds, ascending j), rounded once
+ *     to x_dtype;
+ *   dWg = x^T dl (bf16 x: dl rounded to bf16, MFMA products over chunks of
+ *     1024 tokens, chunk partials summed in ascending order; fp32 x: fp32
+ *     fused multiply-adds in ascending token order).
+ * On an expert-parallel share these are this GPU's additive shares of the
+ * layer's gradients (out is this GPU's partial sum).
+ *   x, packed, topk_idx, topk_w, expert_offsets, sorted_token, pair_pos: as
+ *   in the forward (same workspace after moe_dispatch); packed_bwd from
+ *   moe_pack_weights_bwd; dout [T, d] bf16.
+ *   Out: dx [T, d] in x_dtype (required when T > 0); dtopk_w [T, k] fp32,
+ *   dlogits [T, E_global] fp32 (dense, zeros off the picks), dWg
+ *   [d, E_global] fp32: each optional (NULL = not computed); dW1, dW3 [E_local,
+ *   d, I] and dW2 [E_local, I, d] fp32: all three or none, the same bits as
+ *   moe_expert_wgrad. */
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* packed,
+                          const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
+                          const int32_t* expert_offsets, const int32_t* sorted_token,
+                          const int32_t* pair_pos, const void* dout, void* dx, float* dtopk_w,
+                          float* dlogits, float* dWg, float* dW1, float* dW3, float* dW2, void* ws,
+                          size_t ws_bytes, moe_stream_t stream);
 
 /* Synchronises `stream`, then reads the device error word of the workspace
  * (set by a bounded wait of moe_expert_ffn_waved that expired) and clears

@@ -132,6 +132,28 @@ def test_dispatch_ffn_combine_wgrad_reject_before_launch(L):
     assert L.moe_check_error(None, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_backward_rejects_before_launch(L):
+    p = _p()
+    args = [FAKE] * 9  # x, packed, packed_bwd, idx, w, offsets, sorted_token, pair_pos, dout
+
+    def call(*, a=None, dx=FAKE, dtw=None, dlg=None, dwg=None, dw=(None, None, None), ws=FAKE, nbytes=1 << 30):
+        a = args if a is None else a
+        return L.moe_backward(ctypes.byref(p), *a, dx, dtw, dlg, dwg, *dw, ws, nbytes, None)
+
+    assert call(dx=None) == moe.MOE_ERR_INVALID_ARG                      # dx required for T > 0
+    assert call(a=[FAKE, FAKE, None] + [FAKE] * 6) == moe.MOE_ERR_INVALID_ARG  # no backward weights
+    assert call(dw=(FAKE, None, FAKE)) == moe.MOE_ERR_INVALID_ARG          # dW trio incomplete
+    assert call(dx=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG    # misaligned dx
+    assert call(nbytes=64) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_pack_weights_bwd(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights_bwd(ctypes.byref(_p(d=96)), FAKE, FAKE, FAKE, FAKE, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_packed_bwd_size(ctypes.byref(_p(d=96))) == 0
+    # Wg^T (E_global x d bf16) + [W1 | W3]^T per local expert (d x 2I bf16)
+    assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(moe, "_lib", None)
