@@ -5,14 +5,16 @@
 // the compute of the current wave, the dispatch of the next wave's tokens
 // and the return of finished experts' results run at the same time.
 //
-// MI355X has 8 XCDs, each with its own L2.  The m-tiles (BT-row slices of
-// each expert's sorted rows) are dealt to the XCDs in expert (= wave) order,
-// each deal to the XCD with the least m-tiles so far (lowest id on ties).
-// For compute-bound shapes an expert is dealt whole, so its weights are read
-// by one XCD only (an expert with more m-tiles than an eighth of all, a hot
-// expert, is dealt in chunks of at most that many); for weight-streaming
-// shapes, where every m-tile streams its expert's weights anyway, m-tiles
-// are dealt one by one, which balances the XCDs to within one m-tile.  Every workgroup takes tasks only from its own XCD's
+// MI355X has 8 XCDs, each with its own L2.  Every XCD gets the same number
+// of m-tiles (BT-row slices of each expert's sorted rows), to within one: XCD
+// x may take at most cap_x = floor(n / 8) (+ 1 for the first n % 8 XCDs).
+// The m-tiles are dealt in expert (= wave) order, each deal to the XCD with
+// the most room left (lowest id on ties).  For compute-bound shapes a deal
+// is as much of the expert as fits that room, so an expert is split only
+// when the roomiest XCD fills up and its weights are mostly read by one XCD;
+// for weight-streaming shapes, where every m-tile streams its expert's
+// weights anyway, m-tiles are dealt one by one, which also spreads every
+// wave over the XCDs.  Every workgroup takes tasks only from its own XCD's
 // ticket stream, so GEMM1 -> GEMM2 dependencies never leave an XCD's L2;
 // only the combine, which reads y rows of every XCD, crosses XCDs.
 //
@@ -54,6 +56,7 @@ struct WaveSchedule {
   int32_t loc_mt[kSchedMaxLocal];        // global m-tile of this XCD's j-th m-tile (ascending)
   int32_t loc_pre[kSchedMaxWaves + 1];   // this XCD's m-tiles in waves < w (loc_pre[W] = n_local)
   int32_t cb_pre[kSchedMaxWaves + 2];    // this XCD's combine tasks of slots < s
+  int32_t need[kSchedMaxWaves + 1];      // work units by which every XCD ends waves < s (see sched_build)
   int32_t pos[kSchedMaxLocal + kSchedMaxLag + 1];     // first ticket of position i, i = 0 .. n+L
   int32_t cb_pos[kSchedMaxLocal + kSchedMaxLag + 1];  // this XCD's combine tasks at positions < i
 };
@@ -111,11 +114,21 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
   }
   S.mt_pre[E_local] = run;
-  // deal the m-tiles to the least-loaded XCD (lowest id on ties): whole
-  // experts (above the share in chunks of the share) or single m-tiles
-  const int share = (run + kXcds - 1) / kXcds;
-  int load[kXcds];
-  for (int y = 0; y < kXcds; ++y) load[y] = 0;
+  // deal the m-tiles to the XCD with the most room (lowest id on ties): as
+  // much of the expert as fits, or single m-tiles; the rooms sum to the
+  // m-tiles still to deal, so every deal finds room
+  int room[kXcds], cap[kXcds], cnt[kXcds];
+  for (int y = 0; y < kXcds; ++y) {
+    cap[y] = room[y] = run / kXcds + (y < run % kXcds ? 1 : 0);
+    cnt[y] = 0;
+  }
+  // Work model for placing the combine (an m-tile's GEMM1 tiles cost 2
+  // units: K = d over 2I features; its GEMM2 tiles 1 unit: K = I over d
+  // features): XCD y's stream ends the GEMM2 tiles of its first c m-tiles
+  // after 2 min(c + L, cap_y) + c units.  need[s] = the largest such time
+  // over the XCDs for the m-tiles of waves < s.
+  const int L = S.lag;
+  S.need[0] = 0;
   int loc = 0, w_next = 0;
   for (int e = 0; e < E_local; ++e) {
     while (w_next <= e / G && w_next < S.W) S.loc_pre[w_next++] = loc;
@@ -123,9 +136,10 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     int n = S.mt_pre[e + 1] - first;
     while (n > 0) {
       int x = 0;
-      for (int y = 1; y < kXcds; ++y) x = load[y] < load[x] ? y : x;
-      const int take = whole_experts ? (n > share ? share : n) : 1;
-      load[x] += take;
+      for (int y = 1; y < kXcds; ++y) x = room[y] > room[x] ? y : x;
+      const int take = whole_experts ? (n < room[x] ? n : room[x]) : 1;
+      room[x] -= take;
+      cnt[x] += take;
       if (x == xcd) {
         for (int q = 0; q < take; ++q) {
           if (loc < kSchedMaxLocal) S.loc_mt[loc] = first + q;
@@ -134,6 +148,14 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
       }
       first += take;
       n -= take;
+    }
+    if ((e + 1) % G == 0) {
+      int t = 0;
+      for (int y = 0; y < kXcds; ++y) {
+        const int ty = cnt[y] > 0 ? 2 * (cnt[y] + L < cap[y] ? cnt[y] + L : cap[y]) + cnt[y] : 0;
+        t = ty > t ? ty : t;
+      }
+      S.need[(e + 1) / G] = t;
     }
   }
   while (w_next <= S.W) S.loc_pre[w_next++] = loc;
@@ -145,9 +167,10 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     return;
   }
   // combine tasks of this XCD per slot, and the position of each slot
-  const int L = S.lag, npos = loc + L;  // positions 0 .. npos - 1
+  const int npos = loc + L;  // positions 0 .. npos - 1
   int cb = 0;
   for (int i = 0; i <= npos; ++i) S.cb_pos[i] = 0;
+  int p_time = 0;  // first position whose work reaches need[s] (need grows with s)
   for (int s = 0; s <= S.W; ++s) {
     S.cb_pre[s] = cb;
     const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
@@ -157,7 +180,15 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     // (slot s needs waves <= s - 1 of every XCD: two waves of slack for
     // XCDs that run behind this one)
     const int last = S.loc_pre[s + 2 < S.W ? s + 2 : S.W] - 1;
-    const int at = last >= 0 ? last + L : 0;
+    int at = last >= 0 ? last + L : 0;
+    // and not before this stream's own work reaches the time by which the
+    // slowest XCD ends the waves the slot waits for (an XCD carrying a hot
+    // expert ends them late; its partners run their later GEMM2 tiles first)
+    const int need = S.need[s < S.W ? s : S.W];
+    while (p_time < npos - 1 &&
+           2 * (p_time + 1 < loc ? p_time + 1 : loc) + (p_time + 1 - L > 0 ? p_time + 1 - L : 0) < need)
+      ++p_time;
+    at = at > p_time ? at : p_time;
     S.cb_pos[at + 1] += mine;  // counted from position at + 1 on
   }
   S.cb_pre[S.W + 1] = cb;

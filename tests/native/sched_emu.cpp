@@ -71,16 +71,18 @@ int main() {
         if (j > 0 && S[x].loc_mt[j - 1] >= mt) fail("local m-tiles not ascending", x, j);
         owner[mt] = x;
       }
-    const int share = (nmt + kXcds - 1) / kXcds;
-    int chunk_max = 0;
+    // every m-tile dealt; whole-expert deals split an expert only when an
+    // XCD fills up (each XCD fills once), so there are at most
+    // E_local + kXcds - 1 (expert, XCD) pieces
+    int pieces = 0;
     for (int e = 0; e < E_local; ++e) {
       const int a = S[0].mt_pre[e], b = S[0].mt_pre[e + 1];
-      for (int mt = a; mt < b; ++mt) if (owner[mt] < 0) fail("m-tile not dealt", e, mt);
-      if (whole && b - a <= share)
-        for (int mt = a; mt < b; ++mt) if (owner[mt] != owner[a]) fail("expert split over XCDs", e, mt);
-      const int c = whole ? (b - a < share ? b - a : share) : (b > a ? 1 : 0);
-      chunk_max = c > chunk_max ? c : chunk_max;
+      for (int mt = a; mt < b; ++mt) {
+        if (owner[mt] < 0) fail("m-tile not dealt", e, mt);
+        if (mt == a || owner[mt] != owner[mt - 1]) ++pieces;
+      }
     }
+    if (whole && pieces > E_local + kXcds - 1) fail("experts split more than XCD fills allow", pieces, E_local);
     int lo = 1 << 30, hi = -1;
     for (int x = 0; x < kXcds; ++x) {
       lo = S[x].n_local < lo ? S[x].n_local : lo;
@@ -90,7 +92,7 @@ int main() {
           if (S[0].mt_pre[w * G] > S[x].loc_mt[j] || S[x].loc_mt[j] >= S[0].mt_pre[(w + 1) * G])
             fail("local wave prefix", x, j);
     }
-    if (hi - lo > chunk_max) fail("XCD loads differ by more than one dealt chunk", lo, hi);
+    if (hi - lo > 1) fail("XCD loads differ by more than one m-tile", lo, hi);
   }
   for (int x = 0; x < kXcds; ++x)
     if (W + S[x].n_local > rw) fail("counter region too small", x, S[x].n_local);

@@ -2,7 +2,9 @@
 
 tests/native/sched_emu.cpp includes the same host+device schedule header the
 kernel uses (combine_wave_level_amd/csrc/wave_sched.h) and checks, for the
-given dispatch tables: every GEMM1 / GEMM2 tile and combine chunk has
+given dispatch tables: every m-tile is dealt once and the XCDs hold the
+same number of m-tiles to within one (whole-expert deals split an expert
+only when an XCD fills up), every GEMM1 / GEMM2 tile and combine chunk has
 exactly one ticket, every wait is on smaller tickets (no deadlock for any
 grid), and a multi-threaded emulated run reaches every wait target.
 """
@@ -112,8 +114,17 @@ def test_many_mtiles_per_xcd(emu):
 
 
 def test_hot_expert_dealt_in_chunks(emu):
-    # one expert holds most rows: it is split over XCDs in chunks of the
-    # share, every other expert stays whole on one XCD
+    # one expert holds most rows: it is split over the XCDs as they fill up
     counts = [30 * 128] + [128 * 2] * 15
     ready = [5, 40, 3, 9, 60]
     _run(emu, counts, ready, G=4, NT1=8, NT2=16, threads=3, seed=4, lag=4)
+
+
+def test_lumpy_experts_and_a_hot_one_stay_balanced(emu):
+    # the stress layer's shape: 64 experts of 5 to 7 m-tiles and one of 32
+    # (greedy whole-expert deals alone left XCDs 8 m-tiles apart)
+    rng = np.random.default_rng(12)
+    counts = [int(c) for c in rng.integers(5 * BT - 60, 7 * BT, size=64)]
+    counts[37] = 32 * BT
+    ready = [int(r) for r in rng.integers(0, 900, size=17)]
+    _run(emu, counts, ready, G=4, NT1=12, NT2=16, threads=2, seed=6, lag=64)
