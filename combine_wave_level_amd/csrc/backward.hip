@@ -51,6 +51,26 @@ using DhCfg13 = TileCfg<128, 128, 2, 2, 64, 3>;  // 128 packed rows = 64 (h1, h3
 using DhCfgG = TileCfg<64, 128, 2, 2, 64, 3>;    // 64 rows of W2 (as [I][d])
 static_assert(DhCfg13::BT == DhCfgG::BT, "same row tile");
 
+// LDS row strides (bf16 elements) of the transposing stages: rows of 128 and
+// 64 values plus 8, so that 16-byte reads stay aligned and the 2-byte
+// transposed writes of one instruction spread over the banks.
+constexpr int kStageRow = 136;
+constexpr int kGatherRow = 72;
+static_assert(192 * kStageRow * 2 <= DhCfg13::LDS_BYTES, "dH and w*a stages fit the tile's LDS");
+
+// seg[e] = first column of expert e in the transposed weight-gradient
+// operands: the routed rows of the experts before it, each rounded up to 64.
+__device__ __forceinline__ void build_seg_prefix(const int32_t* __restrict__ offsets, int E_local, int32_t* seg) {
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E_local; ++e) {
+      seg[e] = run;
+      run += (offsets[e + 1] - offsets[e] + 63) & ~63;
+    }
+    seg[E_local] = run;
+  }
+}
+
 // ---------------------------------------------------------------- stage 1
 
 // dwp: [P_max][I / 32] partial sums of the combine-weight gradient (wave wr
@@ -61,12 +81,20 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(
     const uint16_t* __restrict__ w13, const uint16_t* __restrict__ w2b,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d,
-    int I, int k, uint16_t* __restrict__ dh, uint16_t* __restrict__ aw, float* __restrict__ dwp) {
+    int I, int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht,
+    uint16_t* __restrict__ awt, float* __restrict__ dwp) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t seg[kMaxLocalExperts + 1];
   __shared__ float wrow[128];
   build_mtile_prefix(offsets, E_local, DhCfg13::BT, mt_pre);
+  build_seg_prefix(offsets, E_local, seg);
   __syncthreads();
+  // staging of the transposed outputs once the tile's products are done:
+  // [n][row] for the 128 (dH1, dH3) indices and [i][row] for w * a
+  uint16_t* sdh = lds;
+  uint16_t* saw = lds + 128 * kStageRow;
+  const bool trans = dht != nullptr;
   const int NT = I / 64, NQ = I / 32;
   const int total = uniform(mt_pre[E_local] * NT);
   const int lane = lane_id();
@@ -139,9 +167,16 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(
           const size_t o = static_cast<size_t>(row0 + tr) * 2 * I + i0;
           *reinterpret_cast<u32x2*>(dh + o) = u32x2{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
           *reinterpret_cast<u32x2*>(dh + o + I) = u32x2{pack_bf16x2(v3[0], v3[1]), pack_bf16x2(v3[2], v3[3])};
-          if (aw) {
-            const size_t oa = static_cast<size_t>(row0 + tr) * I + i0;
-            *reinterpret_cast<u32x2*>(aw + oa) = u32x2{pack_bf16x2(va[0], va[1]), pack_bf16x2(va[2], va[3])};
+        }
+        if (trans) {
+          // rows past count hold w = 0, hence zeros: the padding of the
+          // transposed operands
+          const int il = i0 - nt * 64;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sdh[(il + r) * kStageRow + tr] = f32_to_bf16(v1[r]);
+            sdh[(64 + il + r) * kStageRow + tr] = f32_to_bf16(v3[r]);
+            saw[(il + r) * kStageRow + tr] = f32_to_bf16(va[r]);
           }
         }
       }
@@ -153,7 +188,76 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(
         if (valid && lane < 16) dwp[static_cast<size_t>(row0 + tr) * NQ + nt * 2 + wr] = part;
       }
     }
-    __syncthreads();  // wrow reused by the next tile
+    if (trans) {
+      // the tile's rows are columns k0 .. k0 + 127 of the transposed
+      // operands; columns up to the expert's rows rounded to 64 are written
+      __syncthreads();
+      const int k0 = uniform(seg[e] + (mt - mt_pre[e]) * 128);
+      const int rows_pad = (count + 63) & ~63;
+      const int KB = P_pad / 32;
+      // (dH1 | dH3)^T fragments: 8 row blocks of 16 indices x rows_pad / 32 k blocks
+      for (int q = threadIdx.x; q < 8 * (rows_pad / 32) * 64; q += 256) {
+        const int frag = q / 64, slot = q % 64;
+        const int nl = (frag % 8) * 16 + slot % 16, kl = (frag / 8) * 32 + (slot / 16) * 8;
+        const int n = nl < 64 ? nt * 64 + nl : I + nt * 64 + (nl - 64);
+        st16(dht + frag_offset(n / 16, (k0 + kl) / 32, KB) + ((kl % 32) / 8 * 16 + n % 16) * 8,
+             ld16(sdh + nl * kStageRow + kl));
+      }
+      // (w * a)^T rows: 64 indices x rows_pad / 8 chunks of 8 columns
+      const int ng = rows_pad / 8;
+      for (int q = threadIdx.x; q < 64 * ng; q += 256) {
+        const int il = q / ng, g = q % ng;
+        st16(awt + static_cast<size_t>(nt * 64 + il) * P_pad + k0 + g * 8, ld16(saw + il * kStageRow + g * 8));
+      }
+    }
+    __syncthreads();  // wrow and the staging reused by the next tile
+  }
+}
+
+// ---------------------------------------------------------------- transposed x, dout
+
+// x and dout of the routed rows, transposed: xst [d][P_pad] (rows) and dst
+// [d][P_pad] (fragment layout), column k = routed row (expert segments
+// padded to 64 with zeros).  blockIdx.x: 64-column block, blockIdx.y:
+// 64-feature block; blocks past the last segment exit.
+__global__ __launch_bounds__(256) void bwd_gather_t_kernel(
+    const uint16_t* __restrict__ xb, const uint16_t* __restrict__ dout,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token, int E_local,
+    int d, int P_pad, uint16_t* __restrict__ xst, uint16_t* __restrict__ dst) {
+  __shared__ int32_t seg[kMaxLocalExperts + 1];
+  __shared__ __align__(16) uint16_t sx[64 * kGatherRow];
+  __shared__ __align__(16) uint16_t sd[64 * kGatherRow];
+  build_seg_prefix(offsets, E_local, seg);
+  __syncthreads();
+  const int k0 = blockIdx.x * 64;
+  if (k0 >= seg[E_local]) return;
+  const int e = expert_of_mtile(seg, 0, E_local, k0);
+  const int r0 = offsets[e] + (k0 - seg[e]), rend = offsets[e + 1];
+  const int f0 = blockIdx.y * 64;
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int r = q / 8, c = q % 8;
+    u32x4 vx = u32x4{0u, 0u, 0u, 0u}, vd = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + r < rend) {
+      const size_t t = static_cast<size_t>(sorted_token[r0 + r]);
+      vx = ld16(xb + t * d + f0 + c * 8);
+      vd = ld16(dout + t * d + f0 + c * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh = (j & 1) * 16;
+      sx[(c * 8 + j) * kGatherRow + r] = static_cast<uint16_t>(vx[j / 2] >> sh);
+      sd[(c * 8 + j) * kGatherRow + r] = static_cast<uint16_t>(vd[j / 2] >> sh);
+    }
+  }
+  __syncthreads();
+  const int KB = P_pad / 32;
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int f = q / 8, g = q % 8;
+    st16(xst + static_cast<size_t>(f0 + f) * P_pad + k0 + g * 8, ld16(sx + f * kGatherRow + g * 8));
+    const int frag = q / 64, slot = q % 64;
+    const int fl = (frag % 4) * 16 + slot % 16, kl = (frag / 4) * 32 + (slot / 16) * 8;
+    st16(dst + frag_offset((f0 + fl) / 16, (k0 + kl) / 32, KB) + ((kl % 32) / 8 * 16 + (f0 + fl) % 16) * 8,
+         ld16(sd + fl * kGatherRow + kl));
   }
 }
 
@@ -469,23 +573,38 @@ __device__ __forceinline__ int n_chunks(int rows) {
   return rows <= kWgradChunkRows ? 1 : (rows + kWgradChunkRows - 1) / kWgradChunkRows;
 }
 
-__global__ __launch_bounds__(256) void wgrad_w_kernel(
-    const uint16_t* __restrict__ xb, const uint16_t* __restrict__ dout,
-    const uint16_t* __restrict__ dh, const uint16_t* __restrict__ aw, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_token, int E_local, int d, int I, float* __restrict__ dW1,
-    float* __restrict__ dW3, float* __restrict__ dW2, float* __restrict__ partial) {
+// dW1 | dW3 and dW2 of one (expert, row chunk) per task, with the tile
+// product of the forward: D[n][t] = sum over the chunk's routed rows k of
+// A[n][k] B[t][k], K walked in ascending order.
+//   dW1 | dW3: A = (dH1 | dH3)^T fragments (n over 2I), B = x^T rows (t over d),
+//              D[n][t] = dW1[t][n] (n < I) or dW3[t][n - I];
+//   dW2:       A = dout^T fragments (n over d), B = (w * a)^T rows (t over I),
+//              D[n][t] = dW2[t][n].
+// Chunk c of expert e covers its routed rows c * kWgradChunkRows .. (padded
+// to 64 with zero columns); chunk 0 writes dW, chunk c >= 1 its own partial
+// slot.  An expert without rows has one empty chunk: its dW is written zero.
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void bwd_wgrad_kernel(
+    const uint16_t* __restrict__ dht, const uint16_t* __restrict__ awt,
+    const uint16_t* __restrict__ xst, const uint16_t* __restrict__ dst,
+    const int32_t* __restrict__ offsets, int E_local, int d, int I, int P_pad,
+    float* __restrict__ dW1, float* __restrict__ dW3, float* __restrict__ dW2,
+    float* __restrict__ partial) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t task_pre[kMaxLocalExperts + 1];
   __shared__ int32_t slot_pre[kMaxLocalExperts + 1];
-  const int tI = (I + 127) / 128, tD = (d + 127) / 128;
-  const int tpm = tI * tD;  // tiles per matrix (dW1/dW3: u = i, v = f; dW2: u = n, v = i)
+  __shared__ int32_t seg[kMaxLocalExperts + 1];
+  const int n13 = 2 * I / C::BW, t13 = (d + C::BT - 1) / C::BT;
+  const int n2 = d / C::BW, t2 = (I + C::BT - 1) / C::BT;
+  const int per_chunk = n13 * t13 + n2 * t2;
+  build_seg_prefix(offsets, E_local, seg);
   if (threadIdx.x == 0) {
     int run = 0, srun = 0;
     for (int e = 0; e < E_local; ++e) {
       const int nc = n_chunks(offsets[e + 1] - offsets[e]);
       task_pre[e] = run;
       slot_pre[e] = srun;
-      run += nc * 3 * tpm;
+      run += nc * per_chunk;
       srun += nc - 1;
     }
     task_pre[E_local] = run;
@@ -493,29 +612,55 @@ __global__ __launch_bounds__(256) void wgrad_w_kernel(
   }
   __syncthreads();
   const size_t mat = static_cast<size_t>(d) * I;
+  const int KB = P_pad / 32;
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
   const int total = uniform(task_pre[E_local]);
   for (int task = blockIdx.x; task < total; task += gridDim.x) {
     const int e = uniform(expert_of_mtile(task_pre, 0, E_local, task));
     int rel = task - uniform(task_pre[e]);
-    const int c = rel / (3 * tpm);
-    rel %= 3 * tpm;
-    const int m = rel / tpm, t = rel % tpm;
-    const int r0 = uniform(offsets[e]), rows = uniform(offsets[e + 1]) - r0;
-    const int rbeg = r0 + c * kWgradChunkRows;
-    const int rend = r0 + min(rows, (c + 1) * kWgradChunkRows);
-    float* base;
-    if (c == 0) {
-      base = (m == 0 ? dW1 : m == 1 ? dW3 : dW2) + e * mat;
-    } else {
-      base = partial + (static_cast<size_t>(uniform(slot_pre[e]) + c - 1) * 3 + m) * mat;
+    const int c = rel / per_chunk;
+    rel %= per_chunk;
+    const bool m13 = rel < n13 * t13;
+    if (!m13) rel -= n13 * t13;
+    const int nt = m13 ? rel % n13 : rel % n2, tt = m13 ? rel / n13 : rel / n2;
+    const int padded = uniform((offsets[e + 1] - offsets[e] + 63) & ~63);
+    const int kbeg = uniform(seg[e] + c * kWgradChunkRows);
+    const int kend = uniform(seg[e] + min(padded, (c + 1) * kWgradChunkRows));
+    const int nk = uniform((kend - kbeg) / C::BK);
+    const int Tdim = m13 ? d : I;
+    const uint16_t* A = (m13 ? dht : dst) + frag_offset(nt * (C::BW / 16), kbeg / 32, KB);
+    const uint16_t* Bm = m13 ? xst : awt;
+    TokRows<C> trow;
+#pragma unroll
+    for (int i = 0; i < C::LT; ++i) {
+      const int t = min(tt * C::BT + trow_index<C>(i), Tdim - 1);
+      trow.p[i] = Bm + static_cast<size_t>(t) * P_pad + kbeg;
     }
-    if (m < 2) {
-      const int ut = t % tI, vt = t / tI;
-      wgrad_tile(m == 0 ? dh : dh + I, false, 2 * I, I, xb, true, d, d, sorted_token, rbeg, rend, ut, vt,
-                 base, lds);
+    TileAcc<C> acc;
+    tile_mma<C>(A, KB, nk, trow, lds, acc, min(C::BT, Tdim - tt * C::BT));
+    float* base[3];
+    if (c == 0) {
+      base[0] = dW1 + e * mat;
+      base[1] = dW3 + e * mat;
+      base[2] = dW2 + e * mat;
     } else {
-      const int ut = t % tD, vt = t / tD;
-      wgrad_tile(dout, true, d, d, aw, false, I, I, sorted_token, rbeg, rend, ut, vt, base, lds);
+      float* slot = partial + static_cast<size_t>(uniform(slot_pre[e]) + c - 1) * 3 * mat;
+      base[0] = slot;
+      base[1] = slot + mat;
+      base[2] = slot + 2 * mat;
+    }
+#pragma unroll
+    for (int aa = 0; aa < C::AW; ++aa) {
+      const int n = nt * C::BW + (wr * C::AW + aa) * 16 + 4 * (lane / 16);
+#pragma unroll
+      for (int b = 0; b < C::AT; ++b) {
+        const int t = tt * C::BT + (wt * C::AT + b) * 16 + (lane & 15);
+        if (t >= Tdim) continue;
+        float* o = m13 ? (n < I ? base[0] + static_cast<size_t>(t) * I + n : base[1] + static_cast<size_t>(t) * I + (n - I))
+                       : base[2] + static_cast<size_t>(t) * d + n;
+        *reinterpret_cast<f32x4*>(o) = acc.v[aa][b];
+      }
     }
   }
 }
@@ -571,6 +716,20 @@ hipError_t launch_dx_gemm(const moe_problem_t& p, const uint16_t* dh, const uint
   return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const uint16_t* dht, const uint16_t* awt,
+                        const uint16_t* xst, const uint16_t* dst, const BackwardArgs& a, float* partial, int cus,
+                        hipStream_t s) {
+  int per_cu = 0;
+  hipError_t e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_wgrad_kernel<C>, C::NTHREADS,
+                                                        C::LDS_BYTES)) != hipSuccess)
+    return e;
+  bwd_wgrad_kernel<C><<<max(1, per_cu) * cus, C::NTHREADS, C::LDS_BYTES, s>>>(
+      dht, awt, xst, dst, a.offsets, p.E_local, p.d, p.I, L.P_pad, a.dW1, a.dW3, a.dW2, partial);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, char* ws,
@@ -583,7 +742,10 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
   const bool want_data = a.dx != nullptr;
   const bool xbf = p.x_dtype == MOE_BF16;
   uint16_t* dh = reinterpret_cast<uint16_t*>(ws + L.bwd_dh);
-  uint16_t* aw = want_dw ? reinterpret_cast<uint16_t*>(ws + L.bwd_aw) : nullptr;
+  uint16_t* dht = want_dw ? reinterpret_cast<uint16_t*>(ws + L.bwd_dht) : nullptr;
+  uint16_t* awt = reinterpret_cast<uint16_t*>(ws + L.bwd_awt);
+  uint16_t* xst = reinterpret_cast<uint16_t*>(ws + L.bwd_xst);
+  uint16_t* dst = reinterpret_cast<uint16_t*>(ws + L.bwd_dst);
   float* dwp = want_data ? reinterpret_cast<float*>(ws + L.bwd_dwp) : nullptr;
   float* dlc = reinterpret_cast<float*>(ws + L.bwd_dlc);
   uint16_t* dld = (want_data && a.dWg && xbf) ? reinterpret_cast<uint16_t*>(ws + L.bwd_dld) : nullptr;
@@ -610,7 +772,7 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
   const size_t lds13 = DhCfg13::LDS_BYTES > DhCfgG::LDS_BYTES ? DhCfg13::LDS_BYTES : DhCfgG::LDS_BYTES;
   bwd_dh_kernel<<<cus * 2, 256, lds13, s>>>(xb, static_cast<const uint16_t*>(a.dout), w13, w2b, a.offsets,
                                             a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k,
-                                            dh, aw, dwp);
+                                            L.P_pad, dh, dht, awt, dwp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (want_data) {
     const PackedBwdLayout BL = packed_bwd_layout(p);
@@ -654,11 +816,14 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     }
   }
   if (!want_dw) return hipSuccess;
-  using C = TileCfg<128, 128, 2, 2, 64, 2>;
-  wgrad_w_kernel<<<cus * 2, 256, C::LDS_BYTES, s>>>(xb, static_cast<const uint16_t*>(a.dout), dh, aw,
-                                                    a.offsets, a.sorted_token, p.E_local, p.d, p.I, a.dW1,
-                                                    a.dW3, a.dW2, partial);
+  bwd_gather_t_kernel<<<dim3(L.P_pad / 64, p.d / 64), 256, 0, s>>>(
+      xb, static_cast<const uint16_t*>(a.dout), a.offsets, a.sorted_token, p.E_local, p.d, L.P_pad, xst, dst);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((2 * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G1::BW == 0)
+    e = launch_wgrad<FfnLarge::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s);
+  else
+    e = launch_wgrad<FfnMid::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s);
+  if (e != hipSuccess) return e;
   wgrad_reduce_kernel<<<cus * 4, 256, 0, s>>>(a.offsets, p.E_local, static_cast<size_t>(p.d) * p.I, a.dW1,
                                               a.dW3, a.dW2, partial);
   return hipGetLastError();

@@ -55,7 +55,12 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.sync = take(L.sync_words * 4);
   const bool xbf = p.x_dtype == MOE_BF16;
   L.bwd_dh = take(static_cast<size_t>(L.P_max) * 2 * p.I * 2);
-  L.bwd_aw = take(static_cast<size_t>(L.P_max) * p.I * 2);
+  L.P_pad = static_cast<int>(align_up(static_cast<size_t>(L.P_max) + 64 * static_cast<size_t>(p.E_local), 64));
+  const size_t ppad = static_cast<size_t>(L.P_pad);
+  L.bwd_dht = take(ppad * 2 * p.I * 2);
+  L.bwd_awt = take(ppad * p.I * 2);
+  L.bwd_xst = take(ppad * p.d * 2);
+  L.bwd_dst = take(ppad * p.d * 2);
   L.wgrad = take(L.wgrad_bytes);
   L.bwd_dwp = take(static_cast<size_t>(L.P_max) * (p.I / 32) * 4);
   L.bwd_dlc = take(static_cast<size_t>(p.T) * p.k * 4);

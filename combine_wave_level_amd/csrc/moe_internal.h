@@ -28,7 +28,15 @@ namespace moe {
 //   act        bf16 [P_max][I]: a = silu(h1) * h3, sorted-row order
 //   sync       int32 counters of the persistent expert-wave kernel
 //   bwd_dh     bf16 [P_max][2I]: dH1 | dH3 per routed row (backward)
-//   bwd_aw     bf16 [P_max][I]: w * a per routed row (weight gradient)
+//   The weight gradient's operands, transposed so that the reduction index
+//   (the routed rows) is contiguous; column k of these [.][P_pad] matrices
+//   is a routed row, each expert's rows starting at a multiple of 64
+//   (seg_e = sum over e' < e of its row count rounded up to 64), the
+//   columns past an expert's rows zero:
+//   bwd_dht    bf16 [2I][P_pad] (dH1 | dH3)^T, MFMA fragment layout
+//   bwd_awt    bf16 [I][P_pad]  (w * a)^T, rows
+//   bwd_xst    bf16 [d][P_pad]  x^T of the routed rows, rows
+//   bwd_dst    bf16 [d][P_pad]  dout^T of the routed rows, fragment layout
 //   wgrad      fp32 isolated partial buffers of the weight gradient
 //   bwd_dwp    fp32 [P_max][I / 32]: partial sums of the combine-weight
 //              gradient of each routed row
@@ -38,9 +46,10 @@ namespace moe {
 //   bwd_dwg    fp32 [ceil(T / kDwgChunkRows)][d][Ep]: isolated partials of
 //              dWg (bf16 x only)
 struct WsLayout {
-  size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, bwd_dh, bwd_aw, wgrad,
-      bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, total;
+  size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, bwd_dh, bwd_dht, bwd_awt,
+      bwd_xst, bwd_dst, wgrad, bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, total;
   int nchunks, W, ngroups, P_max;
+  int P_pad;             // columns of the transposed weight-gradient operands
   int Ep;                // E_global rounded up to 64 (columns of the dense logits gradient)
   int ctr_region_words;  // per-XCD counter region of the persistent kernel
   size_t sync_words, wgrad_bytes;
