@@ -47,16 +47,19 @@
 namespace moe {
 namespace {
 
-using DhCfg13 = TileCfg<128, 128, 2, 2, 64, 3>;  // 128 packed rows = 64 (h1, h3) pairs
-using DhCfgG = TileCfg<64, 128, 2, 2, 64, 3>;    // 64 rows of W2 (as [I][d])
-static_assert(DhCfg13::BT == DhCfgG::BT, "same row tile");
+// The tile of the stage-1 products: the forward's mid GEMM1 tile (128 weight
+// rows x 256 routed rows, 8 wavefronts), for every problem shape.
+using BwdCfg = FfnMid::G1;
 
-// LDS row strides (bf16 elements) of the transposing stages: rows of 128 and
+// LDS row strides (bf16 elements) of the transposing stages: rows of 256 and
 // 64 values plus 8, so that 16-byte reads stay aligned and the 2-byte
 // transposed writes of one instruction spread over the banks.
-constexpr int kStageRow = 136;
+constexpr int kStageRow = BwdCfg::BT + 8;
 constexpr int kGatherRow = 72;
-static_assert(192 * kStageRow * 2 <= DhCfg13::LDS_BYTES, "dH and w*a stages fit the tile's LDS");
+constexpr int kBwdNI = BwdCfg::BW / 2;  // intermediate indices per stage-1 tile
+constexpr size_t kBwdStageBytes = static_cast<size_t>(3 * kBwdNI) * kStageRow * 2;
+constexpr size_t kBwdLds = kBwdStageBytes > BwdCfg::LDS_BYTES ? kBwdStageBytes : BwdCfg::LDS_BYTES;
+static_assert(kBwdLds <= 160 * 1024, "stage-1 LDS fits a CU");
 
 // seg[e] = first column of expert e in the transposed weight-gradient
 // operands: the routed rows of the experts before it, each rounded up to 64.
@@ -73,42 +76,90 @@ __device__ __forceinline__ void build_seg_prefix(const int32_t* __restrict__ off
 
 // ---------------------------------------------------------------- stage 1
 
-// dwp: [P_max][I / 32] partial sums of the combine-weight gradient (wave wr
-// of tile nt owns intermediate indices nt * 64 + wr * 32 .. + 31); aw and
-// dwp may be null.
-__global__ __launch_bounds__(256) void bwd_dh_kernel(
-    const uint16_t* __restrict__ xb, const uint16_t* __restrict__ dout,
-    const uint16_t* __restrict__ w13, const uint16_t* __restrict__ w2b,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
-    const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d,
-    int I, int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht,
-    uint16_t* __restrict__ awt, float* __restrict__ dwp) {
+// g = dout W2^T per routed row, fp32 [P][I]: BW intermediate indices x BT
+// routed rows per tile, K = d in ascending order (BwdCfg when I % 128 == 0,
+// else the 64-wide BwdCfgG; the shape does not change the bits).
+using BwdCfgG = TileCfg<64, 256, 1, 8, 64, 3>;
+
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
+    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ w2b,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token, int E_local, int d,
+    int I, float* __restrict__ g) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
-  __shared__ int32_t seg[kMaxLocalExperts + 1];
-  __shared__ float wrow[128];
-  build_mtile_prefix(offsets, E_local, DhCfg13::BT, mt_pre);
-  build_seg_prefix(offsets, E_local, seg);
+  build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   __syncthreads();
-  // staging of the transposed outputs once the tile's products are done:
-  // [n][row] for the 128 (dH1, dH3) indices and [i][row] for w * a
-  uint16_t* sdh = lds;
-  uint16_t* saw = lds + 128 * kStageRow;
-  const bool trans = dht != nullptr;
-  const int NT = I / 64, NQ = I / 32;
+  const int NT = I / C::BW;
   const int total = uniform(mt_pre[E_local] * NT);
-  const int lane = lane_id();
-  static_assert(DhCfg13::WR == 2 && DhCfg13::WT == 2 && DhCfgG::WR == 2 && DhCfgG::WT == 2, "epilogue below");
-  const int wr = tile_wr<DhCfg13>(), wt = tile_wt<DhCfg13>();
+  const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
-    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * 128);
-    const int count = uniform(min(128, offsets[e + 1] - row0));
-    {
-      // router weight of each row of the tile (threads 128..255 duplicate
-      // threads 0..127 and store the same value: no divergent branch here)
-      const int r = threadIdx.x & 127;
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
+    const int count = uniform(min(C::BT, offsets[e + 1] - row0));
+    TokRows<C> trow;
+#pragma unroll
+    for (int i = 0; i < C::LT; ++i) {
+      const int r = min(trow_index<C>(i), count - 1);
+      trow.p[i] = dout + static_cast<size_t>(sorted_token[row0 + r]) * d;
+    }
+    TileAcc<C> acc;
+    tile_mma<C>(w2b + static_cast<size_t>(e) * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
+                d / C::BK, trow, lds, acc, count);
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) {
+      const int t = (wt * C::AT + b) * 16 + (lane & 15);
+      if (t >= count) continue;
+#pragma unroll
+      for (int a = 0; a < C::AW; ++a) {
+        const int i = nt * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);
+        *reinterpret_cast<f32x4*>(g + static_cast<size_t>(row0 + t) * I + i) = acc.v[a][b];
+      }
+    }
+  }
+}
+
+// h1, h3 recomputed with the forward's GEMM1 arithmetic (BW packed rows =
+// BW/2 intermediate indices x BT routed rows per tile, K = d ascending; the
+// tile shape never changes the bits), then per element
+//   dA = w g, s = sigmoid(h1), silu = h1 s, a = silu h3,
+//   dH3 = dA silu, dH1 = dA h3 s (1 + h1 (1 - s)), aw = w a,
+// and the combine-weight gradient's partial sum_i g_i a_i over each block
+// of 16 intermediate indices (in-lane over 4 consecutive indices, then over
+// the block's 4 lane groups): dwp [P_max][I / 16] (null: skipped).
+// Outputs: dH rows [P][2I] (dH1 | dH3) for the dx product and, when dht is
+// not null, (dH1 | dH3)^T fragments and (w a)^T rows for the weight
+// gradient, transposed through an LDS stage.
+__global__ __launch_bounds__(BwdCfg::NTHREADS) void bwd_dh_kernel(
+    const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13, const float* __restrict__ g,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d, int I,
+    int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht, uint16_t* __restrict__ awt,
+    float* __restrict__ dwp) {
+  using C = BwdCfg;
+  static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
+  extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t seg[kMaxLocalExperts + 1];
+  __shared__ float wrow[C::BT];
+  build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  build_seg_prefix(offsets, E_local, seg);
+  __syncthreads();
+  constexpr int NI = kBwdNI;
+  uint16_t* sdh = lds;                       // [2 NI][kStageRow]: (dH1 | dH3)^T of the tile
+  uint16_t* saw = lds + 2 * NI * kStageRow;  // [NI][kStageRow]: (w a)^T
+  const bool trans = dht != nullptr;
+  const int NT = 2 * I / C::BW, NQ = I / 16;
+  const int total = uniform(mt_pre[E_local] * NT);
+  const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int mt = tile / NT, nt = tile % NT;
+    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+    const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
+    const int count = uniform(min(C::BT, offsets[e + 1] - row0));
+    // router weight of each row of the tile (0 past the valid rows)
+    for (int r = threadIdx.x; r < C::BT; r += C::NTHREADS) {
       const int row = row0 + min(r, count - 1), t = sorted_token[row];
       float w = 0.f;
       for (int j = 0; j < k; ++j) {
@@ -117,100 +168,88 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(
       }
       wrow[r] = r < count ? w : 0.f;
     }
-    // h1, h3: exactly the forward GEMM1 tile
-    TokRows<DhCfg13> trx;
-    TokRows<DhCfgG> trd;
+    TokRows<C> trow;
 #pragma unroll
-    for (int i = 0; i < DhCfg13::LT; ++i) {
-      const int r = min(trow_index<DhCfg13>(i), count - 1);
-      trx.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+    for (int i = 0; i < C::LT; ++i) {
+      const int r = min(trow_index<C>(i), count - 1);
+      trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
     }
+    TileAcc<C> acc;  // barriers inside order the wrow writes before the reads below
+    tile_mma<C>(w13 + static_cast<size_t>(e) * 2 * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
+                d / C::BK, trow, lds, acc, count);
+    // wave (wr, wt): row blocks a (W1) and a + 1 (W3) of intermediate block
+    // (wr * AW + a) / 2; lane l holds indices 4 (l / 16) + 0..3 of the block
+    // for tile row (wt * AT + b) * 16 + l % 16.  Rows past count compute
+    // zeros (w = 0): the padding of the transposed operands.
 #pragma unroll
-    for (int i = 0; i < DhCfgG::LT; ++i) {
-      const int r = min(trow_index<DhCfgG>(i), count - 1);
-      trd.p[i] = dout + static_cast<size_t>(sorted_token[row0 + r]) * d;
-    }
-    TileAcc<DhCfg13> acc13;
-    tile_mma<DhCfg13>(w13 + static_cast<size_t>(e) * 2 * I * d + frag_offset(nt * 8, 0, d / 32), d / 32,
-                      d / DhCfg13::BK, trx, lds, acc13);
-    TileAcc<DhCfgG> accg;
-    tile_mma<DhCfgG>(w2b + static_cast<size_t>(e) * I * d + frag_offset(nt * 4, 0, d / 32), d / 32,
-                     d / DhCfgG::BK, trd, lds, accg);
-    // wave (wr, wt): acc13 row blocks 4wr..4wr+3 = (h1, h3) pairs of
-    // intermediate blocks 2wr, 2wr+1 of this tile; accg row blocks 2wr, 2wr+1.
-    // Lane l holds intermediate indices 4 (l / 16) + 0..3 of each block for
-    // tile row (wt * 4 + b) * 16 + l % 16.
+    for (int b = 0; b < C::AT; ++b) {
+      const int t = (wt * C::AT + b) * 16 + (lane & 15);
+      const bool valid = t < count;
+      const float w = wrow[t];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int tr = (wt * 4 + b) * 16 + (lane & 15);
-      const bool valid = tr < count;
-      const float w = wrow[tr];
-      float part = 0.f;  // <g, a> over this lane's 8 indices, a-major then r
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int i0 = nt * 64 + (wr * 2 + a) * 16 + 4 * (lane / 16);
+      for (int a = 0; a < C::AW; a += 2) {
+        const int il = ((wr * C::AW + a) / 2) * 16 + 4 * (lane / 16);
+        const int i0 = nt * NI + il;
+        const f32x4 g4 = valid ? *reinterpret_cast<const f32x4*>(g + static_cast<size_t>(row0 + t) * I + i0)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
         float v1[4], v3[4], va[4];
+        float part = 0.f;  // <g, a> over the lane's 4 indices
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float h1 = acc13.v[2 * a][b][r], h3 = acc13.v[2 * a + 1][b][r];
-          const float g = accg.v[a][b][r];
-          const float dA = w * g;
+          const float h1 = acc.v[a][b][r], h3 = acc.v[a + 1][b][r];
+          const float dA = w * g4[r];
           const float s = 1.0f / (1.0f + expf(-h1));
           const float silu = h1 * s;
           const float act = silu * h3;
           v3[r] = dA * silu;
           v1[r] = ((dA * h3) * s) * (1.0f + h1 * (1.0f - s));
           va[r] = w * act;
-          part = fmaf(g, act, part);
+          part = fmaf(g4[r], act, part);
         }
+        // the block's four lane groups: a fixed butterfly (every lane ends
+        // with the same, commutatively equal sum)
+        part += __shfl_xor(part, 16, kWave);
+        part += __shfl_xor(part, 32, kWave);
+        if (dwp && valid && lane < 16) dwp[static_cast<size_t>(row0 + t) * NQ + i0 / 16] = part;
         if (valid) {
-          const size_t o = static_cast<size_t>(row0 + tr) * 2 * I + i0;
+          const size_t o = static_cast<size_t>(row0 + t) * 2 * I + i0;
           *reinterpret_cast<u32x2*>(dh + o) = u32x2{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
           *reinterpret_cast<u32x2*>(dh + o + I) = u32x2{pack_bf16x2(v3[0], v3[1]), pack_bf16x2(v3[2], v3[3])};
         }
         if (trans) {
-          // rows past count hold w = 0, hence zeros: the padding of the
-          // transposed operands
-          const int il = i0 - nt * 64;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sdh[(il + r) * kStageRow + tr] = f32_to_bf16(v1[r]);
-            sdh[(64 + il + r) * kStageRow + tr] = f32_to_bf16(v3[r]);
-            saw[(il + r) * kStageRow + tr] = f32_to_bf16(va[r]);
+            sdh[(il + r) * kStageRow + t] = f32_to_bf16(v1[r]);
+            sdh[(NI + il + r) * kStageRow + t] = f32_to_bf16(v3[r]);
+            saw[(il + r) * kStageRow + t] = f32_to_bf16(va[r]);
           }
         }
       }
-      if (dwp) {
-        // the four lane groups of one row: a fixed butterfly (every lane
-        // ends with the same, commutatively equal sum)
-        part += __shfl_xor(part, 16, kWave);
-        part += __shfl_xor(part, 32, kWave);
-        if (valid && lane < 16) dwp[static_cast<size_t>(row0 + tr) * NQ + nt * 2 + wr] = part;
-      }
     }
     if (trans) {
-      // the tile's rows are columns k0 .. k0 + 127 of the transposed
+      // the tile's rows are columns k0 .. k0 + BT - 1 of the transposed
       // operands; columns up to the expert's rows rounded to 64 are written
       __syncthreads();
-      const int k0 = uniform(seg[e] + (mt - mt_pre[e]) * 128);
+      const int k0 = uniform(seg[e] + (mt - mt_pre[e]) * C::BT);
       const int rows_pad = (count + 63) & ~63;
       const int KB = P_pad / 32;
-      // (dH1 | dH3)^T fragments: 8 row blocks of 16 indices x rows_pad / 32 k blocks
-      for (int q = threadIdx.x; q < 8 * (rows_pad / 32) * 64; q += 256) {
+      // (dH1 | dH3)^T fragments: 2 NI / 16 row blocks x rows_pad / 32 k blocks
+      constexpr int NB = 2 * NI / 16;
+      for (int q = threadIdx.x; q < NB * (rows_pad / 32) * 64; q += C::NTHREADS) {
         const int frag = q / 64, slot = q % 64;
-        const int nl = (frag % 8) * 16 + slot % 16, kl = (frag / 8) * 32 + (slot / 16) * 8;
-        const int n = nl < 64 ? nt * 64 + nl : I + nt * 64 + (nl - 64);
+        const int nl = (frag % NB) * 16 + slot % 16, kl = (frag / NB) * 32 + (slot / 16) * 8;
+        const int n = nl < NI ? nt * NI + nl : I + nt * NI + (nl - NI);
         st16(dht + frag_offset(n / 16, (k0 + kl) / 32, KB) + ((kl % 32) / 8 * 16 + n % 16) * 8,
              ld16(sdh + nl * kStageRow + kl));
       }
-      // (w * a)^T rows: 64 indices x rows_pad / 8 chunks of 8 columns
+      // (w a)^T rows: NI indices x rows_pad / 8 chunks of 8 columns
       const int ng = rows_pad / 8;
-      for (int q = threadIdx.x; q < 64 * ng; q += 256) {
-        const int il = q / ng, g = q % ng;
-        st16(awt + static_cast<size_t>(nt * 64 + il) * P_pad + k0 + g * 8, ld16(saw + il * kStageRow + g * 8));
+      for (int q = threadIdx.x; q < NI * ng; q += C::NTHREADS) {
+        const int il = q / ng, gq = q % ng;
+        st16(awt + static_cast<size_t>(nt * NI + il) * P_pad + k0 + gq * 8, ld16(saw + il * kStageRow + gq * 8));
       }
     }
-    __syncthreads();  // wrow and the staging reused by the next tile
+    __syncthreads();  // wrow and the stage reused by the next tile
   }
 }
 
@@ -717,6 +756,19 @@ hipError_t launch_dx_gemm(const moe_problem_t& p, const uint16_t* dh, const uint
 }
 
 template <class C>
+hipError_t launch_g(const moe_problem_t& p, const BackwardArgs& a, const uint16_t* w2b, float* g, int cus,
+                    hipStream_t s) {
+  int per_cu = 0;
+  hipError_t e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_g_kernel<C>, C::NTHREADS, C::LDS_BYTES)) !=
+      hipSuccess)
+    return e;
+  bwd_g_kernel<C><<<max(1, per_cu) * cus, C::NTHREADS, C::LDS_BYTES, s>>>(
+      static_cast<const uint16_t*>(a.dout), w2b, a.offsets, a.sorted_token, p.E_local, p.d, p.I, g);
+  return hipGetLastError();
+}
+
+template <class C>
 hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const uint16_t* dht, const uint16_t* awt,
                         const uint16_t* xst, const uint16_t* dst, const BackwardArgs& a, float* partial, int cus,
                         hipStream_t s) {
@@ -769,17 +821,26 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     if (a.dWg) return fill_zero(a.dWg, static_cast<size_t>(p.d) * p.E_global, s);
     return hipSuccess;
   }
-  const size_t lds13 = DhCfg13::LDS_BYTES > DhCfgG::LDS_BYTES ? DhCfg13::LDS_BYTES : DhCfgG::LDS_BYTES;
-  bwd_dh_kernel<<<cus * 2, 256, lds13, s>>>(xb, static_cast<const uint16_t*>(a.dout), w13, w2b, a.offsets,
-                                            a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k,
-                                            L.P_pad, dh, dht, awt, dwp);
+  float* g = reinterpret_cast<float*>(ws + L.bwd_g);
+  if (p.I % BwdCfg::BW == 0)
+    e = launch_g<BwdCfg>(p, a, w2b, g, cus, s);
+  else
+    e = launch_g<BwdCfgG>(p, a, w2b, g, cus, s);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel, BwdCfg::NTHREADS, kBwdLds)) !=
+      hipSuccess)
+    return e;
+  bwd_dh_kernel<<<max(1, per_cu) * cus, BwdCfg::NTHREADS, kBwdLds, s>>>(
+      xb, w13, g, a.offsets, a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh, dht,
+      awt, dwp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (want_data) {
     const PackedBwdLayout BL = packed_bwd_layout(p);
     const char* pb = static_cast<const char*>(a.packed_bwd);
     const uint16_t* w13t = reinterpret_cast<const uint16_t*>(pb + BL.w13t);
     const void* wgt = pb + BL.wgt;
-    bwd_gate_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(dwp, p.I / 32, a.pair_pos, a.topk_idx, a.topk_w, p.T, p.k,
+    bwd_gate_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(dwp, p.I / 16, a.pair_pos, a.topk_idx, a.topk_w, p.T, p.k,
                                                   p.E_global, L.Ep, a.dtopk_w, dlc, a.dlogits, dld);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (pick_dx_shape(p)) {

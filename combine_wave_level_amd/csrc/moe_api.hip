@@ -62,7 +62,8 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.bwd_xst = take(ppad * p.d * 2);
   L.bwd_dst = take(ppad * p.d * 2);
   L.wgrad = take(L.wgrad_bytes);
-  L.bwd_dwp = take(static_cast<size_t>(L.P_max) * (p.I / 32) * 4);
+  L.bwd_g = take(static_cast<size_t>(L.P_max) * p.I * 4);
+  L.bwd_dwp = take(static_cast<size_t>(L.P_max) * (p.I / 16) * 4);
   L.bwd_dlc = take(static_cast<size_t>(p.T) * p.k * 4);
   L.bwd_dld = take(xbf ? static_cast<size_t>(p.T) * L.Ep * 2 : 0);
   L.bwd_dxr = take(static_cast<size_t>(L.P_max) * p.d * 2);

@@ -38,8 +38,9 @@ namespace moe {
 //   bwd_xst    bf16 [d][P_pad]  x^T of the routed rows, rows
 //   bwd_dst    bf16 [d][P_pad]  dout^T of the routed rows, fragment layout
 //   wgrad      fp32 isolated partial buffers of the weight gradient
-//   bwd_dwp    fp32 [P_max][I / 32]: partial sums of the combine-weight
-//              gradient of each routed row
+//   bwd_g      fp32 [P_max][I]: dout W2^T per routed row
+//   bwd_dwp    fp32 [P_max][I / 16]: partial sums of the combine-weight
+//              gradient of each routed row, one per 16 intermediate indices
 //   bwd_dlc    fp32 [T][k]: gradient of the picked logits
 //   bwd_dld    bf16 [T][Ep]: dense logits gradient (bf16 x only)
 //   bwd_dxr    bf16 [P_max][d]: data gradient of each routed row
@@ -47,7 +48,7 @@ namespace moe {
 //              dWg (bf16 x only)
 struct WsLayout {
   size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, bwd_dh, bwd_dht, bwd_awt,
-      bwd_xst, bwd_dst, wgrad, bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, total;
+      bwd_xst, bwd_dst, wgrad, bwd_g, bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, total;
   int nchunks, W, ngroups, P_max;
   int P_pad;             // columns of the transposed weight-gradient operands
   int Ep;                // E_global rounded up to 64 (columns of the dense logits gradient)

@@ -18,7 +18,7 @@ import torch
 import oracle
 from combine_wave_level_amd import moe
 from helpers import OUT_TOL, Layer, dev, f64, host_f64, oracle_inputs, rel_err_rows
-from workloads import bf16_bits, make_inputs
+from workloads import Workload, bf16_bits, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +122,14 @@ def test_backward_v4_share_ragged_cut_full():
     no_local = nonlocal_pick.all(axis=1)
     assert no_local.any()
     assert rel_err_rows(host_f64(g["dx"])[no_local], ref["dx_router"][no_local]) <= OUT_TOL
+
+
+def test_backward_odd_intermediate_width_and_local_window():
+    """I = 192 (not a multiple of 128: the 64-wide stage-1 product), d = 384
+    (not a multiple of 256: the 128-wide tiles), a window of 3 local experts
+    of 7 starting at 2, k = 3, a ragged batch."""
+    wl = Workload("odd", T=157, d=384, I=192, E_global=7, E_local=3, k=3, G=1, e_begin=2, seed=11)
+    _compare_full(make_inputs(wl, need_dout=True))
 
 
 def test_backward_weight_gradient_matches_wgrad_entry_point():
