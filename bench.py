@@ -8,12 +8,13 @@ kernel (pull, GEMM1 + SwiGLU, GEMM2, fused combine), all inputs resident in
 HBM.  One JSON line is printed on stdout.
 
     python bench.py [--steps K] [--warmup W] [--workload mid|v4share|decode|stress]
-                    [--T T] [--no-cpu] [--serial] [--backward]
+                    [--T T] [--no-cpu] [--serial] [--no-backward]
 
---backward also times the layer's backward on the same batch (data gradient,
+The step is the forward (the metric's configuration is a forward).  The same
+run also times the layer's backward on the same batch (data gradient,
 combine-weight and logits gradients, dWg and the expert weight gradient, one
-moe_backward call) and reports it under "extra"; the headline value stays the
-forward step.
+moe_backward call) and reports it under "extra.backward" (--no-backward
+skips it).
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--serial", action="store_true", help="time the phase-by-phase path")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--backward", action="store_true", help="also time the backward")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     return ap.parse_args()
 
 
@@ -132,7 +133,7 @@ def main():
 
     wl = get(args.workload)
     T = args.T if args.T is not None else wl.T
-    inp = make_inputs(wl, T=T, need_dout=args.backward)
+    inp = make_inputs(wl, T=T, need_dout=not args.no_backward)
     dev = torch.device("cuda:0")
 
     def d(a):
@@ -245,7 +246,7 @@ def main():
         extra["serial_ffn_ms"] = round(s_ffn, 4)
         extra["overlap_speedup_ffn"] = round(s_ffn / ffn_ms, 3)
 
-    if args.backward:
+    if not args.no_backward:
         extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local)
 
     cpu = None

@@ -4,6 +4,11 @@
         A plain device-to-device copy of N MiB (R times): the reference whose
         FETCH_SIZE / WRITE_SIZE counters calibrate the traffic counters.
 
+    python -m combine_wave_level_amd.profiling stats --stats S.csv --title T
+        --command "..." --out-md X.md [--top N]
+        Writes a short markdown table of the kernel durations of a
+        --kernel-trace --stats run (the N longest by total time).
+
     python -m combine_wave_level_amd.profiling summarize --stats S.csv
         --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
         --kernel NAME --workload W --T T --command "..." --out-md X.md
@@ -146,12 +151,36 @@ def _summarize(a) -> None:
     print(json.dumps(rec))
 
 
+def _stats(a) -> None:
+    rows = _rows(a.stats)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]) if "TotalDurationNs" in r
+              else -float(r["AverageNs"]) * float(r["Calls"]))
+    lines = [f"# {a.title}", "",
+             "Commands (from /tmp on the GPU host, TMPDIR=/tmp; REPO = repository root, OUT = $REPO/gpurun_out/prof):", ""]
+    for c in a.command:
+        lines.append(f"    {c}")
+    lines += ["", "Kernel durations (--kernel-trace --stats):", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows[:a.top]:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines.append("")
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(prog="python -m combine_wave_level_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=3)
+    t = sub.add_parser("stats")
+    t.add_argument("--stats", required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", action="append", default=[])
+    t.add_argument("--out-md", required=True)
+    t.add_argument("--top", type=int, default=16)
     s = sub.add_parser("summarize")
     s.add_argument("--stats", required=True)
     s.add_argument("--fetch", required=True)
@@ -169,6 +198,8 @@ def main(argv=None) -> None:
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         _copy(a)
+    elif a.cmd == "stats":
+        _stats(a)
     else:
         _summarize(a)
 
