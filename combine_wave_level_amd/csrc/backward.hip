@@ -77,8 +77,9 @@ __device__ __forceinline__ void build_seg_prefix(const int32_t* __restrict__ off
 // ---------------------------------------------------------------- stage 1
 
 // g = dout W2^T per routed row, fp32 [P][I]: BW intermediate indices x BT
-// routed rows per tile, K = d in ascending order (BwdCfg when I % 128 == 0,
-// else the 64-wide BwdCfgG; the shape does not change the bits).
+// routed rows per tile, K = d in ascending order (256 wide when I % 256 ==
+// 0, BwdCfg when I % 128 == 0, else the 64-wide BwdCfgG; the shape does not
+// change the bits).
 using BwdCfgG = TileCfg<64, 256, 1, 8, 64, 3>;
 
 template <class C>
@@ -822,7 +823,9 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     return hipSuccess;
   }
   float* g = reinterpret_cast<float*>(ws + L.bwd_g);
-  if (p.I % BwdCfg::BW == 0)
+  if (p.I % FfnLarge::G1::BW == 0)
+    e = launch_g<FfnLarge::G1>(p, a, w2b, g, cus, s);
+  else if (p.I % BwdCfg::BW == 0)
     e = launch_g<BwdCfg>(p, a, w2b, g, cus, s);
   else
     e = launch_g<BwdCfgG>(p, a, w2b, g, cus, s);
