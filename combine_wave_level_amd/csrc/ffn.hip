@@ -216,19 +216,36 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   static_assert(C1::BT == C2::BT, "GEMM1 and GEMM2 share the m-tiles");
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ WaveSchedule S;
-  __shared__ int32_t s_off[kMaxLocalExperts + 1];  // expert row offsets
+  __shared__ int32_t s_off[kMaxLocalExperts + 1];    // expert row offsets
+  __shared__ int32_t s_ready[kSchedMaxWaves + 2];     // ready-slot starts in the ready list
   __shared__ int32_t s_ticket;
   const int xcd = uniform(xcc_id());
+  // the dispatch tables go to LDS first, in parallel: the schedule below is
+  // built by one thread, and reading them from global memory there costs a
+  // memory round trip per expert (tens of microseconds per launch)
+  for (int e = threadIdx.x; e <= A.E_local; e += F::NT) s_off[e] = A.offsets[e];
+  for (int w = threadIdx.x; w <= A.W + 1; w += F::NT) s_ready[w] = A.ready_off[w];
+  for (int i = threadIdx.x; i <= kSchedMaxLocal + kSchedMaxLag; i += F::NT) S.cb_pos[i] = 0;
+  __syncthreads();
   if (threadIdx.x == 0) {
     // GEMM2 lag: kSchedMaxLag m-tiles, i.e. an XCD runs the GEMM1 tiles of
     // (nearly) all its m-tiles before their GEMM2 tiles.  Interleaving the two
     // closer puts both operand sets (x and W1/W3, act and W2) through the
     // XCD's L2 at once; measured on the mid layer the short lags (2 to 4
     // m-tiles) cost 20% against 8 and more.
-    sched_build(S, A.offsets, A.ready_off, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
-                A.out != nullptr ? A.cb_parts : 0, xcd, kSchedMaxLag, F::WHOLE_EXPERTS);
+    sched_build_tables(S, s_off, s_ready, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
+                       A.out != nullptr ? A.cb_parts : 0, xcd, kSchedMaxLag, F::WHOLE_EXPERTS, true);
   }
-  for (int e = threadIdx.x; e <= A.E_local; e += F::NT) s_off[e] = A.offsets[e];
+  __syncthreads();
+  // the schedule's prefix sums in parallel (one thread takes tens of
+  // microseconds over them: a dependent LDS access per position)
+  if (uniform(S.err) == 0) {
+    if (wave_uniform() == 0) sched_scan_cb_pos_wave(S);
+    __syncthreads();
+    const int npos = uniform(S.n_local + S.lag);
+    for (int i = threadIdx.x; i <= npos; i += F::NT) S.pos[i] = sched_pos_of(S, i);
+    if (threadIdx.x == 0) S.total = sched_pos_of(S, npos);
+  }
   __syncthreads();
   if (uniform(S.err) != 0) {
     // more m-tiles on this XCD than the schedule holds (the host bounds this)
@@ -289,8 +306,8 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
         poll_geq(A.ctr + sched_g2all_index(S, rw, w), uniform(sched_g2_all(S, w)), A.timeout_ticks, A.err);
       __syncthreads();
       const int parts = A.cb_parts;
-      const int base = uniform(A.ready_off[t.slot] + (t.chunk / parts) * kCombineTokens);
-      const int end = uniform(min(base + kCombineTokens, A.ready_off[t.slot + 1]));
+      const int base = uniform(s_ready[t.slot] + (t.chunk / parts) * kCombineTokens);
+      const int end = uniform(min(base + kCombineTokens, s_ready[t.slot + 1]));
       int cb, ce;
       combine_cols(A.d, parts, t.chunk % parts, cb, ce);
       for (int i = base + wave_uniform(); i < end; i += F::NT / kWave)

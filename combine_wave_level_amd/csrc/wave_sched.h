@@ -97,11 +97,19 @@ __host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, in
 // combine).  lag = L (1 .. kSchedMaxLag).  whole_experts: deal experts whole
 // (else single m-tiles).  S.err = 1 if the XCD holds more than
 // kSchedMaxLocal m-tiles (the schedule is then empty).
-__host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offsets,
-                                            const int32_t* ready_off, int E_local, int G, int BT,
-                                            int NT1, int NT2, int cb_parts, int xcd, int lag,
-                                            bool whole_experts) {
+// sched_build = sched_build_tables (dealing, combine placement; leaves in
+// cb_pos[i + 1] the combine tasks placed at position i) + sched_build_positions
+// (prefix sums into cb_pos and the first ticket of every position).  The
+// kernel runs the tables on one thread and the positions on a wavefront
+// (sched_scan_cb_pos_wave, then sched_pos_of per position); the prefix sums
+// are exact integer sums, so both give the same schedule.  cb_pos_zeroed:
+// cb_pos[0 .. kSchedMaxLocal + kSchedMaxLag] already holds zeros.
+__host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_t* offsets,
+                                                   const int32_t* ready_off, int E_local, int G, int BT,
+                                                   int NT1, int NT2, int cb_parts, int xcd, int lag,
+                                                   bool whole_experts, bool cb_pos_zeroed) {
   S.W = E_local / G;
+  const int W = S.W;  // loop bounds in registers (stores into S may alias its fields)
   S.lag = lag < 1 ? 1 : (lag > kSchedMaxLag ? kSchedMaxLag : lag);
   S.G = G;
   S.NT1 = NT1;
@@ -130,8 +138,9 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
   const int L = S.lag;
   S.need[0] = 0;
   int loc = 0, w_next = 0;
+  int w_e = 0, in_wave = 0;  // wave of expert e and its rank in the wave (no integer division)
   for (int e = 0; e < E_local; ++e) {
-    while (w_next <= e / G && w_next < S.W) S.loc_pre[w_next++] = loc;
+    while (w_next <= w_e && w_next < W) S.loc_pre[w_next++] = loc;
     int first = S.mt_pre[e];
     int n = S.mt_pre[e + 1] - first;
     while (n > 0) {
@@ -149,16 +158,17 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
       first += take;
       n -= take;
     }
-    if ((e + 1) % G == 0) {
+    if (++in_wave == G) {
       int t = 0;
       for (int y = 0; y < kXcds; ++y) {
         const int ty = cnt[y] > 0 ? 2 * (cnt[y] + L < cap[y] ? cnt[y] + L : cap[y]) + cnt[y] : 0;
         t = ty > t ? ty : t;
       }
-      S.need[(e + 1) / G] = t;
+      S.need[++w_e] = t;
+      in_wave = 0;
     }
   }
-  while (w_next <= S.W) S.loc_pre[w_next++] = loc;
+  while (w_next <= W) S.loc_pre[w_next++] = loc;
   S.n_local = loc;
   if (loc > kSchedMaxLocal) {
     S.err = 1;
@@ -169,9 +179,10 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
   // combine tasks of this XCD per slot, and the position of each slot
   const int npos = loc + L;  // positions 0 .. npos - 1
   int cb = 0;
-  for (int i = 0; i <= npos; ++i) S.cb_pos[i] = 0;
+  if (!cb_pos_zeroed)
+    for (int i = 0; i <= npos; ++i) S.cb_pos[i] = 0;
   int p_time = 0;  // first position whose work reaches need[s] (need grows with s)
-  for (int s = 0; s <= S.W; ++s) {
+  for (int s = 0; s <= W; ++s) {
     S.cb_pre[s] = cb;
     const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     const int mine = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
@@ -179,30 +190,64 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
     // position of the GEMM2 tiles of the last m-tile of a wave <= s + 1
     // (slot s needs waves <= s - 1 of every XCD: two waves of slack for
     // XCDs that run behind this one)
-    const int last = S.loc_pre[s + 2 < S.W ? s + 2 : S.W] - 1;
+    const int last = S.loc_pre[s + 2 < W ? s + 2 : W] - 1;
     int at = last >= 0 ? last + L : 0;
     // and not before this stream's own work reaches the time by which the
     // slowest XCD ends the waves the slot waits for (an XCD carrying a hot
     // expert ends them late; its partners run their later GEMM2 tiles first)
-    const int need = S.need[s < S.W ? s : S.W];
+    const int need = S.need[s < W ? s : W];
     while (p_time < npos - 1 &&
            2 * (p_time + 1 < loc ? p_time + 1 : loc) + (p_time + 1 - L > 0 ? p_time + 1 - L : 0) < need)
       ++p_time;
     at = at > p_time ? at : p_time;
     S.cb_pos[at + 1] += mine;  // counted from position at + 1 on
   }
-  S.cb_pre[S.W + 1] = cb;
-  // cb_pos[i] = combine tasks at positions < i (prefix of the per-position counts)
+  S.cb_pre[W + 1] = cb;
+}
+
+// First ticket of position i, once cb_pos[i] = combine tasks at positions
+// < i: every position j < i holds NT1 GEMM1 tiles when j < n, NT2 GEMM2
+// tiles when j >= L, and its combine tasks.
+__host__ __device__ inline int sched_pos_of(const WaveSchedule& S, int i) {
+  const int n = S.n_local, L = S.lag;
+  return S.NT1 * (i < n ? i : n) + S.NT2 * (i > L ? i - L : 0) + S.cb_pos[i];
+}
+
+__host__ __device__ inline void sched_build_positions(WaveSchedule& S) {
+  const int npos = S.n_local + S.lag;
   for (int i = 1; i <= npos; ++i) S.cb_pos[i] += S.cb_pos[i - 1];
-  run = 0;
-  for (int i = 0; i < npos; ++i) {
-    S.pos[i] = run;
-    if (i < loc) run += NT1;
-    if (i >= L) run += NT2;
-    run += S.cb_pos[i + 1] - S.cb_pos[i];
+  for (int i = 0; i <= npos; ++i) S.pos[i] = sched_pos_of(S, i);
+  S.total = S.pos[npos];
+}
+
+__host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offsets,
+                                            const int32_t* ready_off, int E_local, int G, int BT,
+                                            int NT1, int NT2, int cb_parts, int xcd, int lag,
+                                            bool whole_experts) {
+  sched_build_tables(S, offsets, ready_off, E_local, G, BT, NT1, NT2, cb_parts, xcd, lag, whole_experts, false);
+  if (S.err == 0) sched_build_positions(S);
+}
+
+// The prefix of sched_build_positions by one wavefront (all 64 lanes of the
+// calling wave; lane l sums a contiguous chunk, the chunk sums are scanned
+// across lanes, then each lane writes its chunk's running sums).
+__device__ inline void sched_scan_cb_pos_wave(WaveSchedule& S) {
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int len = S.n_local + S.lag + 1;
+  const int per = (len + 63) / 64;
+  const int b = lane * per, e = b + per < len ? b + per : len;
+  int sum = 0;
+  for (int i = b; i < e; ++i) sum += S.cb_pos[i];
+  int incl = sum;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  S.pos[npos] = run;
-  S.total = run;
+  int run = incl - sum;
+  for (int i = b; i < e; ++i) {
+    run += S.cb_pos[i];
+    S.cb_pos[i] = run;
+  }
 }
 
 // GEMM2 tiles of wave w on this XCD.
