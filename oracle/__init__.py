@@ -16,4 +16,7 @@ from .moe_oracle import (  # noqa: F401
     wgrad,
     backward,
     backward_tokens,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_fp8_per_token,
 )

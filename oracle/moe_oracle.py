@@ -35,6 +35,12 @@ notes of this repository):
   exactly once;
 * the oracle computes everything in float64 from the exact input values
   (bf16 inputs decoded exactly); it rounds no intermediate;
+* FP8 dispatch (the "FP8 scatter" of [V4-TH] §1.4): the token rows the
+  experts pull are OCP e4m3 values with one power-of-two scale per token,
+  the smallest one that brings the row's largest magnitude to at most 448
+  (the pages name neither the format details nor the scale granularity);
+  e4m3 values times a power of two are exact in bf16, so the experts see
+  exactly the dequantized rows; the router keeps the unquantized x;
 * the backward holds the routing fixed: the top-k selection is piecewise
   constant in the logits, so gradients flow only through the k renormalised
   weights; on an expert-parallel share (some picks owned by other GPUs) the
@@ -60,6 +66,9 @@ __all__ = [
     "wgrad",
     "backward",
     "backward_tokens",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_fp8_per_token",
 ]
 
 
@@ -421,3 +430,76 @@ def backward_tokens(x_rows, x_ffn_rows, idx_rows, w_rows, dout_rows, Wg, W1, W3,
         for j in range(k):
             dx[i] += dl[i, j] * Wg64[:, int(idx_rows[i, j])]
     return dx, dw, dl
+
+
+# ---------------------------------------------------------------- FP8 dispatch
+
+_E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8), float64.
+
+    1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+    holds subnormals m * 2^-9; S.1111.111 is NaN (there is no infinity), so
+    the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of float64 values with |v| <= 448, ties to the even
+    code (the spacing is 2^-9 below 2^-6 and 2^(e-3) in the binade
+    [2^e, 2^(e+1)); rounding up out of a binade lands on its next power of
+    two, which is representable)."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.abs(v) > _E4M3_MAX) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode expects finite values with |v| <= 448")
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a >= 2.0 ** -6, e, -6.0)          # subnormal range shares the 2^-9 spacing
+    q = 2.0 ** (e - 3)
+    n = a / q                                        # exact: a power-of-two division
+    r = np.floor(n)
+    frac = n - r
+    r = r + ((frac > 0.5) | ((frac == 0.5) & (r % 2 == 1)))
+    mag = r * q
+    # encode mag (now exactly representable) back to bits
+    codes = np.zeros(v.shape, dtype=np.int64)
+    nz = mag > 0
+    me = np.floor(np.log2(np.where(nz, mag, 1.0)))
+    normal = nz & (me >= -6)
+    sub = nz & ~normal
+    codes = np.where(normal, ((me + 7).astype(np.int64) << 3) | ((mag / 2.0 ** me - 1.0) * 8).astype(np.int64), codes)
+    codes = np.where(sub, (mag / 2.0 ** -9).astype(np.int64), codes)
+    codes = np.where(np.signbit(v), codes | 0x80, codes)  # a negative value that rounds to zero is -0
+    return codes.astype(np.uint8)
+
+
+def quantize_fp8_per_token(x: np.ndarray):
+    """Per-token FP8 copy of x [T, d] (float64 values): scale_t = 2^k_t with
+    k_t the smallest integer for which max_i |x[t, i]| <= 448 * 2^k_t (scale
+    1 for an all-zero row), codes = e4m3_encode(x[t] / scale_t).
+    Returns (codes uint8 [T, d], scale float64 [T], dequantized float64 [T, d])."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0])
+    k = np.zeros(x.shape[0], dtype=np.int64)
+    for t in range(x.shape[0]):
+        if amax[t] > 0:
+            kk = int(np.ceil(np.log2(amax[t] / _E4M3_MAX)))
+            # guard the floating log2 against an off-by-one at exact powers
+            while amax[t] > _E4M3_MAX * 2.0 ** kk:
+                kk += 1
+            while amax[t] <= _E4M3_MAX * 2.0 ** (kk - 1):
+                kk -= 1
+            k[t] = kk
+    scale = np.exp2(k.astype(np.float64))
+    codes = e4m3_encode(x / scale[:, None])
+    deq = e4m3_decode(codes) * scale[:, None]
+    return codes, scale, deq

@@ -510,6 +510,57 @@ def test_backward_tokens_matches_backward():
                                rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- FP8 dispatch
+
+def test_e4m3_decode_known_codes():
+    # OCP 8-bit floating point specification, E4M3: bias 7, 3 mantissa bits,
+    # subnormals, no infinities, S.1111.111 = NaN
+    codes = np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x39, 0x7E, 0xFE, 0x3F], dtype=np.uint8)
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 448.0, -448.0, 1.875]
+    got = oracle.e4m3_decode(codes)
+    assert got.tolist() == want and np.signbit(got[1])
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert (oracle.e4m3_encode(oracle.e4m3_decode(codes)) == codes).all()
+
+
+def test_e4m3_encode_is_the_nearest_code_ties_to_even_by_brute_force():
+    finite = np.array([c for c in range(128) if c != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_decode(finite)                     # ascending, 0 .. 448
+    rng = np.random.default_rng(40)
+    mids = (vals[1:] + vals[:-1]) / 2                     # every tie
+    xs = np.concatenate([rng.uniform(0, 448, 4000), 2.0 ** rng.uniform(-14, 8.8, 4000), mids,
+                         np.nextafter(mids, 0), np.nextafter(mids, 1000)])
+    xs = xs[xs <= 448]
+    got = oracle.e4m3_encode(xs)
+    for x, g in zip(xs, got):
+        dist = np.abs(vals - x)
+        best = np.nonzero(dist == dist.min())[0]
+        want = finite[best[0]] if len(best) == 1 else [finite[b] for b in best if finite[b] % 2 == 0][0]
+        assert g == want, (x, g, want)
+    assert (oracle.e4m3_encode(-xs) == (got | 0x80)).all()
+
+
+def test_quantize_fp8_per_token_scale_and_error():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((9, 64)) * np.exp2(rng.integers(-20, 20, size=(9, 1)))
+    x[3] = 0.0
+    codes, scale, deq = oracle.quantize_fp8_per_token(x)
+    assert scale[3] == 1.0 and (deq[3] == 0).all()
+    k = np.log2(scale)
+    assert (k == np.round(k)).all()                       # powers of two
+    amax = np.abs(x).max(axis=1)
+    live = amax > 0
+    assert ((amax[live] / scale[live] <= 448) & (amax[live] / scale[live] > 224)).all()
+    # normal-range elements keep 3 mantissa bits: relative error <= 2^-4
+    big = np.abs(x) >= 2.0 ** -6 * scale[:, None]
+    assert (np.abs(deq - x)[big] <= 2.0 ** -4 * np.abs(x)[big]).all()
+    assert (oracle.e4m3_decode(codes) * scale[:, None] == deq).all()
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_bf16_rounding_is_rne():
