@@ -55,7 +55,7 @@ template <class F>
 __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
-    uint16_t* __restrict__ act, int E_local, int d, int I) {
+    uint16_t* __restrict__ act, int E_local, int d, int I, const float* __restrict__ xscale) {
   using C = typename F::G1;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
@@ -68,7 +68,8 @@ __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
-    gemm1_tile<C>(xb, w13 + static_cast<size_t>(e) * 2 * I * d, sorted_token, act, row0, count, nt, d, I, lds);
+    gemm1_tile<C>(xb, w13 + static_cast<size_t>(e) * 2 * I * d, sorted_token, act, row0, count, nt, d, I, lds,
+                  xscale);
   }
 }
 
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 constexpr long long kWaitTimeoutSeconds = 2;
 
 struct WaveArgs {
-  const uint16_t* xb;
+  const uint16_t* xb;        // token-order staging buffer (bf16, or e4m3 bytes for FP8 dispatch)
+  const float* xscale;       // FP8 dispatch: per-token scales (else unused)
   const uint16_t* w13;
   const uint16_t* w2;
   const int32_t* offsets;
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
       const int row0 = uniform(s_off[t.expert] + (t.mt - S.mt_pre[t.expert]) * C1::BT);
       const int count = uniform(min(C1::BT, s_off[t.expert + 1] - row0));
       gemm1_tile<C1>(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token,
-                     A.act, row0, count, t.nt, A.d, A.I, lds);
+                     A.act, row0, count, t.nt, A.d, A.I, lds, A.xscale);
       local_signal(A.ctr + sched_g1done_index(S, rw, t.loc));
     } else if (t.kind == kTaskGemm2) {
       // GEMM2 tile, once every GEMM1 tile of its m-tile is done (same XCD)
@@ -341,7 +343,7 @@ FfnShape pick_ffn_shape(const moe_problem_t& p) {
 }
 
 template <class F>
-hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint16_t* xb,
+hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint16_t* xb, const float* xscale,
                           const uint16_t* w13, const uint16_t* w2, const int32_t* offsets,
                           const int32_t* sorted_token, const int32_t* pair_pos, const float* topk_w,
                           void* y, void* out, uint32_t flags, char* ws, hipStream_t s) {
@@ -360,7 +362,7 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel<F>, F::NT, l1)) != hipSuccess)
       return e;
     gemm1_phase_kernel<F><<<max(1, per_cu) * cus, F::NT, l1, s>>>(xb, w13, offsets, sorted_token, act,
-                                                                 p.E_local, p.d, p.I);
+                                                                 p.E_local, p.d, p.I, xscale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm2_phase_kernel<F>, F::NT, l2)) != hipSuccess)
       return e;
@@ -374,6 +376,7 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   if ((e = fill_zero(ctr, L.sync_words, s)) != hipSuccess) return e;
   WaveArgs A;
   A.xb = xb;
+  A.xscale = xscale;
   A.w13 = w13;
   A.w2 = w2;
   A.offsets = offsets;
@@ -438,17 +441,40 @@ hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, 
   if ((e = stage_x_bf16(p, L, x, ws, s, &xb)) != hipSuccess) return e;
   switch (pick_ffn_shape(p)) {
     case FfnShape::Small:
-      return launch_ffn_cfg<FfnSmall>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+      return launch_ffn_cfg<FfnSmall>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
                                       out, flags, ws, s);
     case FfnShape::Small64:
-      return launch_ffn_cfg<FfnSmall64>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+      return launch_ffn_cfg<FfnSmall64>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
                                          out, flags, ws, s);
     case FfnShape::Large:
-      return launch_ffn_cfg<FfnLarge>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+      return launch_ffn_cfg<FfnLarge>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
                                       out, flags, ws, s);
     default:
-      return launch_ffn_cfg<FfnMid>(p, L, xb, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+      return launch_ffn_cfg<FfnMid>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
                                     out, flags, ws, s);
+  }
+}
+
+hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8_t* x8, const float* xscale,
+                          const void* packed, const int32_t* offsets, const int32_t* sorted_token,
+                          const int32_t* pair_pos, const float* topk_w, void* y, void* out, uint32_t flags,
+                          char* ws, hipStream_t s) {
+  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
+  const char* pk = static_cast<const char*>(packed);
+  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
+  const uint16_t* w2 = reinterpret_cast<const uint16_t*>(pk + PL.w2);
+  // the fp8 tiles take the bytes through the bf16 tiles' row pointers
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x8);
+  switch (pick_ffn_shape(p)) {
+    case FfnShape::Small:
+      return launch_ffn_cfg<FfnSmallF8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+                                        out, flags, ws, s);
+    case FfnShape::Small64:
+      return launch_ffn_cfg<FfnSmall64F8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w,
+                                          y, out, flags, ws, s);
+    default:  // large and mid batches
+      return launch_ffn_cfg<FfnMidF8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+                                      out, flags, ws, s);
   }
 }
 

@@ -49,6 +49,31 @@ struct FfnSmall64 {
   static constexpr bool WHOLE_EXPERTS = false;
 };
 
+// FP8 dispatch: the same shapes with the GEMM1 token operand in e4m3 (the
+// GEMM2 tiles are unchanged).  An fp8 token fragment holds 64 k, so the
+// GEMM1 K step is 64 (128 for the 32-row tile, whose two token blocks must
+// give each of its four wavefronts one load per step).  The 256 x 256 tile
+// with a 64-wide K step and the conversions does not fit the register file,
+// so large batches use the 128 x 256 tile (same bits).
+struct FfnMidF8 {
+  using G1 = TileCfg<128, 256, 2, 4, 64, 3, false, true>;
+  using G2 = FfnMid::G2;
+  static constexpr int NT = 512;
+  static constexpr bool WHOLE_EXPERTS = true;
+};
+struct FfnSmallF8 {
+  using G1 = TileCfg<128, 32, 4, 1, 128, 4, true, true>;
+  using G2 = FfnSmall::G2;
+  static constexpr int NT = 256;
+  static constexpr bool WHOLE_EXPERTS = false;
+};
+struct FfnSmall64F8 {
+  using G1 = TileCfg<128, 64, 4, 1, 64, 6, true, true>;
+  using G2 = FfnSmall64::G2;
+  static constexpr int NT = 256;
+  static constexpr bool WHOLE_EXPERTS = false;
+};
+
 template <class F>
 constexpr size_t ffn_lds_bytes() {
   static_assert(F::G1::NTHREADS == F::NT && F::G2::NTHREADS == F::NT, "one workgroup size per shape");
@@ -128,25 +153,38 @@ __device__ __forceinline__ void out_flush(const uint16_t* lds, uint16_t* __restr
 // intermediate indices [nt * BW/2, nt * BW/2 + BW/2).  The operand rows are
 // pulled straight from the token-order staging buffer xb by sorted_token:
 // the dispatch pull lands in LDS.
+// FP8T tiles: xb is the e4m3 staging buffer (d bytes per token) and xscale
+// the tokens' scales.
 template <class C>
 __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            const uint16_t* __restrict__ w13e,
                                            const int32_t* __restrict__ sorted_token,
                                            uint16_t* __restrict__ act, int row0, int count, int nt,
-                                           int d, int I, uint16_t* lds) {
+                                           int d, int I, uint16_t* lds,
+                                           const float* __restrict__ xscale = nullptr) {
   static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   constexpr int COLS = C::BW / 2;
   static_assert(static_cast<size_t>(C::BT) * COLS * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
   TokRows<C> trow;
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
     const int r = min(trow_index<C>(i), count - 1);
-    trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+    const size_t tok = static_cast<size_t>(sorted_token[row0 + r]);
+    if constexpr (C::FP8T)
+      trow.p[i] = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(xb) + tok * d);
+    else
+      trow.p[i] = xb + tok * d;
+  }
+  TokScale<C> tsc;
+  if constexpr (C::FP8T) {
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b)
+      tsc.s[b] = xscale[sorted_token[row0 + min((wt * C::AT + b) * 16 + (lane & 15), count - 1)]];
   }
   TileAcc<C> acc;
-  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc, count);
-  const int lane = lane_id();
-  const int wr = tile_wr<C>(), wt = tile_wt<C>();
+  tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc, count, &tsc);
 #pragma unroll
   for (int b = 0; b < C::AT; ++b) {
     if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones

@@ -26,13 +26,21 @@
 
 namespace moe {
 
-template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_, bool SKIPB_ = false>
+template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_, bool SKIPB_ = false, bool FP8T_ = false>
 struct TileCfg {
   static constexpr int BW = BW_, BT = BT_, WR = WR_, WT = WT_, BK = BK_, NST = NST_;
   // SKIPB: skip the MFMA work of every 16-row token block past the valid
   // rows (for tall token tiles that are mostly empty, as in small batches);
   // otherwise only a wave whose token rows are all invalid skips its work.
   static constexpr bool SKIPB = SKIPB_;
+  // FP8T: the token rows are OCP e4m3 bytes with one scale per row (FP8
+  // dispatch).  They go to LDS as bytes, 1 KiB = 16 rows x 64 k per wave
+  // load, and each lane converts its 8 bytes to bf16 (times the row's scale)
+  // right before the MFMA; K is still walked in the same ascending 32-wide
+  // slices, so the products equal those of the bf16 rows of the dequantized
+  // values, bit for bit.
+  static constexpr bool FP8T = FP8T_;
+  static_assert(!FP8T || BK % 64 == 0, "fp8 token fragments hold 64 k");
   static constexpr int NW = WR * WT;            // wavefronts per workgroup
   static constexpr int NTHREADS = 64 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts per workgroup");
@@ -40,8 +48,9 @@ struct TileCfg {
   static_assert(BK % 32 == 0 && BK >= 32, "K step is whole MFMA k-slices");
   static_assert(BW % (16 * WR) == 0 && BT % (16 * WT) == 0, "wave tile must hold whole MFMA blocks");
   static constexpr int KS = BK / 32;            // MFMA k-slices per K step
+  static constexpr int TKS = FP8T ? KS / 2 : KS;  // token fragments per 16-row block per K step
   static constexpr int NFW = BW / 16 * KS;      // weight fragments per K step
-  static constexpr int NFT = BT / 16 * KS;      // token fragments per K step
+  static constexpr int NFT = BT / 16 * TKS;     // token fragments per K step
   static_assert(NFW % NW == 0 && NFT % NW == 0, "fragments split evenly over the wavefronts");
   static constexpr int LW = NFW / NW;           // weight fragments each wave loads per step
   static constexpr int LT = NFT / NW;           // token fragments each wave loads per step
@@ -83,9 +92,16 @@ struct TokRows {
 // Token fragment i of this wave (i < C::LT) covers token block tb and k-slice
 // kc of the step; its rows in the tile are tb * 16 + (lane % 16).
 template <class C>
-__device__ __forceinline__ int tok_frag_block(int i) { return (C::NW * i + wave_id()) / C::KS; }
+__device__ __forceinline__ int tok_frag_block(int i) { return (C::NW * i + wave_id()) / C::TKS; }
 template <class C>
-__device__ __forceinline__ int tok_frag_slice(int i) { return (C::NW * i + wave_id()) % C::KS; }
+__device__ __forceinline__ int tok_frag_slice(int i) { return (C::NW * i + wave_id()) % C::TKS; }
+
+// Scales of this lane's token rows (FP8T only): s[b] for token block
+// wt * AT + b.
+template <class C>
+struct TokScale {
+  float s[C::FP8T ? C::AT : 1];
+};
 
 // Row index (0..BT-1) inside the tile of the token fragment i this lane loads.
 template <class C>
@@ -130,9 +146,31 @@ __device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, i
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
     const int f = C::NW * i + wave;  // token fragment of the step
-    const int kc = f % C::KS;
-    lds_dma16(trow.p[i] + kt * C::BK + kc * 32 + (lane >> 4) * 8, st + (C::NFW + f) * 512);
+    const int kc = f % C::TKS;
+    if constexpr (C::FP8T) {
+      // row bytes kt * BK + 64 kc .. + 63: lane l takes 16 of them
+      const char* row = reinterpret_cast<const char*>(trow.p[i]);
+      lds_dma16(row + kt * C::BK + kc * 64 + (lane >> 4) * 16, st + (C::NFW + f) * 512);
+    } else {
+      lds_dma16(trow.p[i] + kt * C::BK + kc * 32 + (lane >> 4) * 8, st + (C::NFW + f) * 512);
+    }
   }
+}
+
+// The MFMA operand of k-slice ks (0 .. KS-1 of a K step) of token block tb
+// from an fp8 fragment in LDS: lane l needs row l % 16, k = 32 ks + 8 (l / 16)
+// .. + 7, i.e. 8 bytes of the 1 KiB fragment that holds 64 k of the block
+// (slot = 16 (k / 16) + row, 16 bytes each), converted to bf16 times scale.
+template <class C>
+__device__ __forceinline__ u32x4 fp8_token_frag(const uint16_t* st, int tb, int ks, float scale) {
+  const int lane = lane_id();
+  const int frag = tb * C::TKS + ks / 2, kin = (ks % 2) * 32 + 8 * (lane >> 4);
+  const char* base = reinterpret_cast<const char*>(st + (C::NFW + frag) * 512);
+  const u32x2 raw = *reinterpret_cast<const u32x2*>(base + ((kin / 16) * 16 + (lane & 15)) * 16 + (kin % 16));
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, true))};
 }
 
 // MFMA operands of one 32-wide k-slice for one wave.
@@ -148,7 +186,8 @@ struct TileFrags {
 // nbv (C::SKIPB only, wave-uniform): token blocks of this wave that hold
 // valid rows; blocks b >= nbv are neither read nor multiplied.
 template <class C, bool ACT>
-__device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, TileFrags<C>& f, int nbv) {
+__device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, TileFrags<C>& f, int nbv,
+                                                const TokScale<C>& tsc) {
   if constexpr (!ACT) return;
   const int lane = lane_id();
   const int wr = tile_wr<C>(), wt = tile_wt<C>();
@@ -156,7 +195,12 @@ __device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, Tile
   for (int a = 0; a < C::AW; ++a) f.a[a] = ld16(st + ((wr * C::AW + a) * C::KS + ks) * 512 + lane * 8);
 #pragma unroll
   for (int b = 0; b < C::AT; ++b)
-    if (!C::SKIPB || b < nbv) f.b[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
+    if (!C::SKIPB || b < nbv) {
+      if constexpr (C::FP8T)
+        f.b[b] = fp8_token_frag<C>(st, wt * C::AT + b, ks, tsc.s[b]);
+      else
+        f.b[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
+    }
 }
 
 template <class C, bool ACT>
@@ -195,7 +239,7 @@ __device__ __forceinline__ void wait_steps_left(int later) {
 template <class C, int PAR, bool ACT>
 __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, int KB, int nk, int kt,
                                           const TokRows<C>& trow, uint16_t* lds, TileFrags<C>& f0,
-                                          TileFrags<C>& f1, TileAcc<C>& acc, int nbv) {
+                                          TileFrags<C>& f1, TileAcc<C>& acc, int nbv, const TokScale<C>& tsc) {
   const uint16_t* st = lds + (kt % C::NST) * C::STAGE;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
@@ -206,12 +250,12 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, in
     // on those as well
     wait_lgkm0();
     if (ks + 1 < C::KS) {
-      tile_read_frags<C, ACT>(st, ks + 1, nxt, nbv);
+      tile_read_frags<C, ACT>(st, ks + 1, nxt, nbv, tsc);
     } else if (kt + 1 < nk) {
       wait_steps_left<C>(min(C::NST - 2, nk - 2 - kt));
       raw_barrier();
       if (kt + C::NST < nk) tile_issue<C>(wtile, KB, trow, lds, kt + C::NST);
-      tile_read_frags<C, ACT>(lds + ((kt + 1) % C::NST) * C::STAGE, 0, nxt, nbv);
+      tile_read_frags<C, ACT>(lds + ((kt + 1) % C::NST) * C::STAGE, 0, nxt, nbv, tsc);
     }
     __builtin_amdgcn_sched_barrier(0);
     tile_mfma<C, ACT>(cur, acc, nbv);
@@ -222,7 +266,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, in
 template <class C, bool ACT>
 __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile, int KB, int nk,
                                              const TokRows<C>& trow, uint16_t* lds, TileAcc<C>& acc,
-                                             int nbv) {
+                                             int nbv, const TokScale<C>& tsc) {
 
   if constexpr (!C::DBUF) {
     // single operand set: steps 0 .. NST-2 in flight; step kt waits for its
@@ -239,7 +283,7 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         TileFrags<C> f;
-        tile_read_frags<C, ACT>(st, ks, f, nbv);
+        tile_read_frags<C, ACT>(st, ks, f, nbv, tsc);
         tile_mfma<C, ACT>(f, acc, nbv);
       }
     }
@@ -256,15 +300,15 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
   if (C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, C::NST - 1);
   raw_barrier();
   TileFrags<C> f0, f1;
-  tile_read_frags<C, ACT>(lds, 0, f0, nbv);
+  tile_read_frags<C, ACT>(lds, 0, f0, nbv, tsc);
 
   constexpr int P1 = C::KS & 1;  // register-set parity of the step after an even step
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv);
-    tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc, nbv);
+    tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv, tsc);
+    tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc, nbv, tsc);
   }
-  if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv);
+  if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv, tsc);
   // all LDS reads of this tile done before anyone refills the stages
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   raw_barrier();
@@ -283,13 +327,17 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
 //           MFMA work on token rows past them is skipped (whole waves, or
 //           whole 16-row blocks with C::SKIPB), and the accumulators of
 //           skipped rows hold no meaningful values
+//   tsc   : C::FP8T only: the scales of this lane's token rows (trow then
+//           points at rows of e4m3 bytes)
 // All C::NTHREADS threads must call it.  On entry no direct-to-LDS load of this
 // workgroup may be in flight; on exit none is, and a barrier has passed, so
 // the caller may reuse lds right away.
 template <class C>
 __device__ __forceinline__ void tile_mma(const uint16_t* __restrict__ wtile, int KB, int nk,
                                          const TokRows<C>& trow, uint16_t* lds,
-                                         TileAcc<C>& acc, int tvalid = C::BT) {
+                                         TileAcc<C>& acc, int tvalid = C::BT, const TokScale<C>* tsc = nullptr) {
+  TokScale<C> sc{};
+  if constexpr (C::FP8T) sc = *tsc;
 #pragma unroll
   for (int a = 0; a < C::AW; ++a)
 #pragma unroll
@@ -298,9 +346,9 @@ __device__ __forceinline__ void tile_mma(const uint16_t* __restrict__ wtile, int
   const int first = uniform(tile_wt<C>() * C::AT * 16);
   const int nbv = C::SKIPB ? min(C::AT, (tvalid - first + 15) / 16) : C::AT;
   if (first < tvalid)
-    tile_mma_run<C, true>(wtile, KB, nk, trow, lds, acc, nbv);
+    tile_mma_run<C, true>(wtile, KB, nk, trow, lds, acc, nbv, sc);
   else
-    tile_mma_run<C, false>(wtile, KB, nk, trow, lds, acc, nbv);
+    tile_mma_run<C, false>(wtile, KB, nk, trow, lds, acc, nbv, sc);
 }
 
 }  // namespace moe

@@ -168,6 +168,37 @@ moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const v
                                static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_quantize_fp8(const moe_problem_t* p, const void* x, uint8_t* x_fp8, float* x_scale,
+                              moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!x || !x_fp8 || !x_scale)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (x_fp8 && !aligned16(x_fp8))) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_fp8(*p, x, x_fp8, x_scale, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_ffn_waved_fp8(const moe_problem_t* p, const uint8_t* x_fp8, const float* x_scale,
+                                      const void* packed, const int32_t* expert_offsets,
+                                      const int32_t* sorted_token, const int32_t* pair_pos,
+                                      const float* topk_w, const int32_t* token_ready_wave, void* y,
+                                      void* out, uint32_t flags, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (flags & ~MOE_FLAG_SERIAL) return MOE_ERR_INVALID_ARG;
+  if (!packed || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x_fp8 || !x_scale || !sorted_token || !y)) return MOE_ERR_INVALID_ARG;
+  if (out && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if ((x_fp8 && !aligned16(x_fp8)) || !aligned16(packed) || (y && !aligned16(y)) || (out && !aligned16(out)))
+    return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  (void)token_ready_wave;
+  return hip_status(launch_ffn_fp8(*p, L, x_fp8, x_scale, packed, expert_offsets, sorted_token, pair_pos,
+                                   topk_w, y, out, flags, static_cast<char*>(ws),
+                                   static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* pair_pos,
                          const float* topk_w, void* out, moe_stream_t stream) {
   moe_status_t st = check_problem(p);

@@ -140,6 +140,14 @@ hipError_t stage_x_bf16(const moe_problem_t& p, const WsLayout& L, const void* x
 // capture the stream into a graph).
 hipError_t fill_zero(void* p, size_t n, hipStream_t s);
 
+// FP8 dispatch: per-token e4m3 codes and power-of-two scales of x, and the
+// expert FFN on them (same schedule and GEMM2, GEMM1 pulling the codes).
+hipError_t launch_quantize_fp8(const moe_problem_t& p, const void* x, uint8_t* x8, float* xscale, hipStream_t s);
+hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8_t* x8, const float* xscale,
+                          const void* packed, const int32_t* offsets, const int32_t* sorted_token,
+                          const int32_t* pair_pos, const float* topk_w, void* y, void* out, uint32_t flags,
+                          char* ws, hipStream_t s);
+
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s);
 

@@ -28,7 +28,8 @@ MOE_FLAG_SERIAL = 0x1
 EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
-    "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward",
+    "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
+    "moe_expert_ffn_waved_fp8",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
             "moe_pack_weights_bwd": (st, [P, vp, vp, vp, vp, vp]),
             "moe_backward": (st, [P, vp, vp, vp, i32p, f32p, i32p, i32p, i32p, vp, vp, f32p, f32p, f32p,
                                   f32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
+            "moe_quantize_fp8": (st, [P, vp, vp, f32p, vp]),
+            "moe_expert_ffn_waved_fp8": (st, [P, vp, f32p, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
+                                              ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
             "moe_check_error": (st, [vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_version": (ctypes.c_char_p, []),
@@ -200,6 +204,30 @@ def ffn_waved(p: Problem, x, packed, disp: Dispatch, topk_w, ws, fused_combine=T
         _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y),
         _p(out) if fused_combine else None, flags, _p(ws), ws.numel(), _stream()),
         "moe_expert_ffn_waved")
+    return y, (out if fused_combine else None)
+
+
+def quantize_fp8(p: Problem, x):
+    """Per-token e4m3 codes (uint8 [T, d]) and power-of-two scales (fp32 [T]) of x."""
+    x8 = torch.empty((p.T, p.d), dtype=torch.uint8, device=x.device)
+    scale = torch.empty(p.T, dtype=torch.float32, device=x.device)
+    _check(lib().moe_quantize_fp8(ctypes.byref(p), _p(x), _p(x8), _p(scale), _stream()), "moe_quantize_fp8")
+    return x8, scale
+
+
+def ffn_waved_fp8(p: Problem, x8, x_scale, packed, disp: Dispatch, topk_w, ws, fused_combine=True,
+                  serial=False, y=None, out=None):
+    """moe_expert_ffn_waved with the staging buffer in FP8 (from quantize_fp8)."""
+    dev = x8.device
+    if y is None:
+        y = torch.empty((max(1, p_max(p)), p.d), dtype=torch.bfloat16, device=dev)
+    if fused_combine and out is None:
+        out = torch.empty((p.T, p.d), dtype=_out_dtype(p), device=dev)
+    flags = MOE_FLAG_SERIAL if serial else 0
+    _check(lib().moe_expert_ffn_waved_fp8(
+        ctypes.byref(p), _p(x8), _p(x_scale), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
+        _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y), _p(out) if fused_combine else None,
+        flags, _p(ws), ws.numel(), _stream()), "moe_expert_ffn_waved_fp8")
     return y, (out if fused_combine else None)
 
 

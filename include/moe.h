@@ -170,6 +170,30 @@ moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const v
                                   uint32_t flags, void* ws, size_t ws_bytes,
                                   moe_stream_t stream);
 
+/* FP8 dispatch (digest section 1.4, compute/communication bullet: tokens go
+ * to the experts in FP8, results come back in BF16).  Per token t:
+ * scale[t] = 2^k, k the smallest integer with max_i |x[t, i]| <= 448 * 2^k
+ * (1 for an all-zero row), and x_fp8[t, i] = the OCP E4M3 code nearest to
+ * x[t, i] / scale[t] (ties to even; a negative value that rounds to zero
+ * gives -0).  The scale granularity and the format details are not on the
+ * pages; an e4m3 value times a power of two is exact in bf16.
+ *   x [T, d] in x_dtype.  Out: x_fp8 [T, d] bytes, x_scale [T] fp32. */
+moe_status_t moe_quantize_fp8(const moe_problem_t* p, const void* x, uint8_t* x_fp8, float* x_scale,
+                              moe_stream_t stream);
+
+/* moe_expert_ffn_waved with the token-order staging buffer in FP8: the
+ * GEMM1 tiles pull the e4m3 rows (d bytes per routed pair instead of 2d)
+ * and convert them to bf16 times the token's scale in registers; results are
+ * bit-identical to moe_expert_ffn_waved run on the dequantized rows
+ * (x_fp8 * x_scale, exact in bf16).  Arguments as for moe_expert_ffn_waved,
+ * with x replaced by x_fp8 [T, d] and x_scale [T] from moe_quantize_fp8. */
+moe_status_t moe_expert_ffn_waved_fp8(const moe_problem_t* p, const uint8_t* x_fp8, const float* x_scale,
+                                      const void* packed, const int32_t* expert_offsets,
+                                      const int32_t* sorted_token, const int32_t* pair_pos,
+                                      const float* topk_w, const int32_t* token_ready_wave, void* y,
+                                      void* out, uint32_t flags, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream);
+
 /* Combine (digest section 1.1; 10100.com deterministic operators): for each
  * token, out[t] = sum over ranks j = 0..k-1 with pair_pos[t, j] >= 0 of
  * topk_w[t, j] * y[pair_pos[t, j]], accumulated in fp32 with fused

@@ -20,7 +20,7 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -152,6 +152,20 @@ def test_backward_rejects_before_launch(L):
     assert L.moe_packed_bwd_size(ctypes.byref(_p(d=96))) == 0
     # Wg^T (E_global x d bf16) + [W1 | W3]^T per local expert (d x 2I bf16)
     assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2
+
+
+def test_fp8_dispatch_rejects_before_launch(L):
+    p = _p()
+    assert L.moe_quantize_fp8(ctypes.byref(p), FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(ctypes.byref(p), FAKE, ctypes.c_void_p(0x10008), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(ctypes.byref(_p(d=96)), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    f = L.moe_expert_ffn_waved_fp8
+    assert f(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30,
+             None) == moe.MOE_ERR_INVALID_ARG                         # no scales
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0x4, FAKE, 1 << 30,
+             None) == moe.MOE_ERR_INVALID_ARG                         # unknown flag
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64,
+             None) == moe.MOE_ERR_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
