@@ -14,7 +14,8 @@ The step is the forward (the metric's configuration is a forward).  The same
 run also times the layer's backward on the same batch (data gradient,
 combine-weight and logits gradients, dWg and the expert weight gradient, one
 moe_backward call) and reports it under "extra.backward" (--no-backward
-skips it).
+skips it), and the forward with FP8 dispatch (per-token e4m3 staging, then
+the expert FFN pulling it) under "extra.fp8_dispatch" (--no-fp8 skips it).
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -46,6 +47,7 @@ def parse():
     ap.add_argument("--serial", action="store_true", help="time the phase-by-phase path")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
+    ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8-dispatch forward")
     return ap.parse_args()
 
 
@@ -82,6 +84,42 @@ def cpu_baseline(inp, wl, target_s):
     return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {done} tokens of the {wl.name} batch, float64 numpy oracle "
                       f"(route, dispatch, expert FFN, combine), {dt:.1f} s for the last run"}
+
+
+def time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y, L, P, check, pp, sp, nws, T):
+    """Times the forward with FP8 dispatch: router, dispatch, the per-token
+    e4m3 quantization of x and the expert-wave kernel pulling it."""
+    import torch
+
+    from combine_wave_level_amd import moe
+
+    x8 = torch.empty((p.T, p.d), dtype=torch.uint8, device=x.device)
+    sc = torch.empty(p.T, dtype=torch.float32, device=x.device)
+
+    def step():
+        check(L.moe_route(pp, P(x), P(packed), P(bias), P(idx), P(w), None, P(ws), nws, sp), "route")
+        check(L.moe_dispatch(pp, P(idx), P(disp.counts), P(disp.offsets), P(disp.sorted_token),
+                             P(disp.pair_pos), P(disp.ready_wave), P(ws), nws, sp), "dispatch")
+        check(L.moe_quantize_fp8(pp, P(x), P(x8), P(sc), sp), "quantize")
+        check(L.moe_expert_ffn_waved_fp8(pp, P(x8), P(sc), P(packed), P(disp.offsets), P(disp.sorted_token),
+                                         P(disp.pair_pos), P(w), P(disp.ready_wave), P(y), P(out), 0,
+                                         P(ws), nws, sp), "ffn_fp8")
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(3, args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(n):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    moe.check_error(ws)
+    ms = t0.elapsed_time(t1) / n
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "pulled_bytes_per_pair": p.d, "pulled_bytes_per_pair_bf16": 2 * p.d}
 
 
 def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local):
@@ -246,6 +284,9 @@ def main():
         extra["serial_ffn_ms"] = round(s_ffn, 4)
         extra["overlap_speedup_ffn"] = round(s_ffn / ffn_ms, 3)
 
+    if not args.no_fp8:
+        extra["fp8_dispatch"] = time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y, L,
+                                                  P, check, pp, sp, nws, T)
     if not args.no_backward:
         extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local)
 
