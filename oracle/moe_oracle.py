@@ -192,19 +192,29 @@ def _silu(h: np.ndarray) -> np.ndarray:
     return h / (1.0 + np.exp(-h))
 
 
-def expert_ffn(X: np.ndarray, W1e: np.ndarray, W3e: np.ndarray, W2e: np.ndarray):
-    """One expert's SwiGLU FFN on the rows X [M, d], float64.
+def expert_ffn(X: np.ndarray, W1e: np.ndarray, W3e: np.ndarray, W2e: np.ndarray, activation: str = "swiglu"):
+    """One expert's FFN on the rows X [M, d], float64.
 
     [V4-TH] §1.4 (compute/communication bullet): each token-expert pair costs
     the gating, up and down projections.  With the workload formula:
       h1 = X W1, h3 = X W3, a = silu(h1) * h3, y = a W2,
     silu(h) = h / (1 + exp(-h)).
+    activation "relu2": the cheap element-wise activation of [V4-TH] §1.4
+    (activation-function bullet: no exponential, no division, no gating
+    projection; the function is not named there, the reading is squared
+    ReLU): a = max(h1, 0)^2, W3 unused (h3 is returned as None).
     Returns (y [M, d], h1, h3, a).
     """
     X = np.asarray(X, dtype=np.float64)
     h1 = X @ np.asarray(W1e, dtype=np.float64)
-    h3 = X @ np.asarray(W3e, dtype=np.float64)
-    a = _silu(h1) * h3
+    if activation == "relu2":
+        a = np.maximum(h1, 0.0) ** 2
+        h3 = None
+    elif activation == "swiglu":
+        h3 = X @ np.asarray(W3e, dtype=np.float64)
+        a = _silu(h1) * h3
+    else:
+        raise ValueError(f"unknown activation {activation!r}")
     y = a @ np.asarray(W2e, dtype=np.float64)
     return y, h1, h3, a
 
@@ -226,7 +236,7 @@ def combine(y_rows: np.ndarray, pair_pos: np.ndarray, w: np.ndarray, d: int) -> 
     return out
 
 
-def forward(x, Wg, bias, W1, W3, W2, k, e_begin, E_local, G, x_ffn=None):
+def forward(x, Wg, bias, W1, W3, W2, k, e_begin, E_local, G, x_ffn=None, activation="swiglu"):
     """Whole layer share: route -> dispatch -> expert FFN per expert -> combine.
 
     ``x`` feeds the router; ``x_ffn`` (default ``x``) feeds the experts.
@@ -250,12 +260,12 @@ def forward(x, Wg, bias, W1, W3, W2, k, e_begin, E_local, G, x_ffn=None):
         r0, r1 = int(off[le]), int(off[le + 1])
         if r1 > r0:
             rows = meta["sorted_token"][r0:r1]
-            y[r0:r1] = expert_ffn(xf[rows], W1[le], W3[le], W2[le])[0]
+            y[r0:r1] = expert_ffn(xf[rows], W1[le], None if W3 is None else W3[le], W2[le], activation)[0]
     out = combine(y, meta["pair_pos"], w, d)
     return {"logits": logits, "idx": idx, "w": w, "p": p, "meta": meta, "y": y, "out": out}
 
 
-def forward_tokens(x_ffn_rows, idx_rows, w_rows, W1, W3, W2, e_begin, E_local):
+def forward_tokens(x_ffn_rows, idx_rows, w_rows, W1, W3, W2, e_begin, E_local, activation="swiglu"):
     """Layer output for a subset of tokens, one token at a time.
 
     out[t] depends only on token t's own row, its picks and its weights
@@ -270,7 +280,7 @@ def forward_tokens(x_ffn_rows, idx_rows, w_rows, W1, W3, W2, e_begin, E_local):
         for j in range(idx_rows.shape[1]):
             le = int(idx_rows[i, j]) - e_begin
             if 0 <= le < E_local:
-                y = expert_ffn(xs[i:i + 1], W1[le], W3[le], W2[le])[0][0]
+                y = expert_ffn(xs[i:i + 1], W1[le], None if W3 is None else W3[le], W2[le], activation)[0][0]
                 out[i] += w_rows[i, j] * y
     return out
 

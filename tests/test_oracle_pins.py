@@ -510,6 +510,43 @@ def test_backward_tokens_matches_backward():
                                rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- cheap activation
+
+def test_relu2_expert_ffn_closed_form_and_torch():
+    X = np.array([[1.0, -2.0], [0.5, 0.25]])
+    W1 = np.array([[1.0, -1.0, 2.0], [0.5, 1.0, -1.0]])     # h1 = [[0, -3, 4], [0.625, -0.25, 0.75]]
+    W2 = np.arange(6.0).reshape(3, 2)
+    y, h1, h3, a = oracle.expert_ffn(X, W1, None, W2, "relu2")
+    assert h3 is None
+    np.testing.assert_array_equal(a, [[0.0, 0.0, 16.0], [0.390625, 0.0, 0.5625]])
+    np.testing.assert_array_equal(y, a @ W2)
+    rng = np.random.default_rng(50)
+    X, W1, W2 = rng.standard_normal((9, 12)), rng.standard_normal((12, 7)), rng.standard_normal((7, 12))
+    ref = (torch.relu(torch.from_numpy(X) @ torch.from_numpy(W1)) ** 2 @ torch.from_numpy(W2)).numpy()
+    np.testing.assert_allclose(oracle.expert_ffn(X, W1, None, W2, "relu2")[0], ref, rtol=1e-13, atol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.expert_ffn(X, W1, None, W2, "gelu")
+
+
+def test_relu2_forward_vs_dense_and_identical_experts():
+    x, Wg, b, W1, _, W2 = _tiny_layer(51, E=5, k=2, bias=True)
+    res = oracle.forward(x, Wg, b, W1, None, W2, 2, 0, 5, 5, activation="relu2")
+    dense = [(np.maximum(x @ W1[e], 0) ** 2) @ W2[e] for e in range(5)]
+    ref = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        for j in range(2):
+            ref[t] += res["w"][t, j] * dense[res["idx"][t, j]][t]
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-12, atol=1e-13)
+    W1[:] = W1[0]
+    W2[:] = W2[0]
+    same = oracle.forward(x, Wg, b, W1, None, W2, 2, 0, 5, 5, activation="relu2")
+    # one FFN shared by all experts: the renormalised weights sum to 1, so routing drops out
+    np.testing.assert_allclose(same["out"], (np.maximum(x @ W1[0], 0) ** 2) @ W2[0], rtol=1e-12, atol=1e-13)
+    toks = oracle.forward_tokens(x[[3, 0]], res["idx"][[3, 0]], res["w"][[3, 0]], W1, None, W2, 0, 5,
+                                 activation="relu2")
+    np.testing.assert_allclose(toks, same["out"][[3, 0]], rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- FP8 dispatch
 
 def test_e4m3_decode_known_codes():
