@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8-dispatch forward")
+    ap.add_argument("--no-ungated", action="store_true",
+                    help="skip timing the layer with the ungated squared-ReLU expert")
     return ap.parse_args()
 
 
@@ -120,6 +122,65 @@ def time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y
     ms = t0.elapsed_time(t1) / n
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
             "pulled_bytes_per_pair": p.d, "pulled_bytes_per_pair_bf16": 2 * p.d}
+
+
+def time_ungated(args, wl, T, d, stream):
+    """Times the forward of the same layer with the ungated squared-ReLU
+    expert at about the same parameter count (intermediate size 3I/2):
+    router, dispatch and the expert-wave kernel on its own buffers."""
+    import torch
+
+    from combine_wave_level_amd import moe
+    from workloads import make_inputs, ungated
+
+    uw = ungated(wl)
+    inp = make_inputs(uw, T=T)
+    xdt = moe.MOE_F32 if uw.dtype == "f32" else moe.MOE_BF16
+    p = moe.problem(T=T, d=uw.d, I=uw.I, E_global=uw.E_global, k=uw.k, e_begin=uw.e_begin,
+                    E_local=uw.E_local, experts_per_wave=uw.G, x_dtype=xdt, w_dtype=xdt, out_dtype=xdt,
+                    activation=moe.MOE_ACT_RELU2)
+    x = d(inp["x"])
+    bias = d(inp["bias"]) if inp.get("bias") is not None else None
+    packed = moe.pack_weights(p, d(inp["Wg"]), d(inp["W1"]), None, d(inp["W2"]))
+    ws = moe.workspace(p)
+    del inp
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    y = torch.empty((max(1, moe.p_max(p)), p.d), dtype=torch.bfloat16, device=x.device)
+    out = torch.empty((T, p.d), dtype=x.dtype, device=x.device)
+
+    def step(timed_ffn=False):
+        idx, w, _ = moe.route(p, x, packed, ws, bias=bias)
+        disp = moe.dispatch(p, idx, ws)
+        if timed_ffn:
+            ev[2].record(stream)
+        moe.ffn_waved(p, x, packed, disp, w, ws, y=y, out=out)
+        if timed_ffn:
+            ev[3].record(stream)
+        return disp
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(3, args.steps)
+    ffn = 0.0
+    ev[0].record(stream)
+    for _ in range(n):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / n
+    for _ in range(n):
+        disp = step(timed_ffn=True)
+        torch.cuda.synchronize()
+        ffn += ev[2].elapsed_time(ev[3])
+    moe.check_error(ws)
+    ffn /= n
+    P_local = int(disp.offsets[-1].item())
+    tflops = 4.0 * uw.d * uw.I * P_local / (ffn * 1e-3) / 1e12
+    return {"activation": "relu2", "I": uw.I, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "ffn_ms": round(ffn, 4), "grouped_gemm_tflops": round(tflops, 2),
+            "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
 def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local):
@@ -287,6 +348,8 @@ def main():
     if not args.no_fp8:
         extra["fp8_dispatch"] = time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y, L,
                                                   P, check, pp, sp, nws, T)
+    if not args.no_ungated:
+        extra["relu2_same_params"] = time_ungated(args, wl, T, d, stream)
     if not args.no_backward:
         extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local)
 

@@ -787,7 +787,7 @@ hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const uint16_
 
 hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, char* ws,
                            hipStream_t s) {
-  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
+  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16, gate_rows(p));
   const char* pk = static_cast<const char*>(a.packed);
   const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
   const uint16_t* w2b = reinterpret_cast<const uint16_t*>(pk + PL.w2b);

@@ -51,25 +51,27 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, size_t n) {
 
 // ---------------------------------------------------------------- phase kernels
 
-template <class F>
+// GATED: W13 holds W1 and W3 (SwiGLU); else W1 only (squared ReLU).
+template <class F, bool GATED>
 __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     uint16_t* __restrict__ act, int E_local, int d, int I, const float* __restrict__ xscale) {
+  constexpr int gr = GATED ? 2 : 1;  // packed W13 rows per intermediate index
   using C = typename F::G1;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   __syncthreads();
-  const int NT = 2 * I / C::BW;
+  const int NT = gr * I / C::BW;
   const int total = uniform(mt_pre[E_local] * NT);
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
-    gemm1_tile<C>(xb, w13 + static_cast<size_t>(e) * 2 * I * d, sorted_token, act, row0, count, nt, d, I, lds,
-                  xscale);
+    gemm1_tile<C, GATED>(xb, w13 + static_cast<size_t>(e) * gr * I * d, sorted_token, act, row0, count, nt, d,
+                         I, lds, xscale);
   }
 }
 
@@ -211,7 +213,7 @@ __device__ __forceinline__ void local_wait(const int32_t* p, int target, long lo
   asm volatile("buffer_inv sc0" ::: "memory");
 }
 
-template <class F, bool OUT_BF16>
+template <class F, bool OUT_BF16, bool GATED>
 __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   using C1 = typename F::G1;
   using C2 = typename F::G2;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
     // closer puts both operand sets (x and W1/W3, act and W2) through the
     // XCD's L2 at once; measured on the mid layer the short lags (2 to 4
     // m-tiles) cost 20% against 8 and more.
-    sched_build_tables(S, s_off, s_ready, A.E_local, A.G, C1::BT, 2 * A.I / C1::BW, A.d / C2::BW,
+    sched_build_tables(S, s_off, s_ready, A.E_local, A.G, C1::BT, (GATED ? 2 : 1) * A.I / C1::BW, A.d / C2::BW,
                        A.out != nullptr ? A.cb_parts : 0, xcd, kSchedMaxLag, F::WHOLE_EXPERTS, true);
   }
   __syncthreads();
@@ -280,8 +282,8 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
       // GEMM1 + SwiGLU tile (its operand rows pulled from the staging x)
       const int row0 = uniform(s_off[t.expert] + (t.mt - S.mt_pre[t.expert]) * C1::BT);
       const int count = uniform(min(C1::BT, s_off[t.expert + 1] - row0));
-      gemm1_tile<C1>(A.xb, A.w13 + static_cast<size_t>(t.expert) * 2 * A.I * A.d, A.sorted_token,
-                     A.act, row0, count, t.nt, A.d, A.I, lds, A.xscale);
+      gemm1_tile<C1, GATED>(A.xb, A.w13 + static_cast<size_t>(t.expert) * (GATED ? 2 : 1) * A.I * A.d,
+                            A.sorted_token, A.act, row0, count, t.nt, A.d, A.I, lds, A.xscale);
       local_signal(A.ctr + sched_g1done_index(S, rw, t.loc));
     } else if (t.kind == kTaskGemm2) {
       // GEMM2 tile, once every GEMM1 tile of its m-tile is done (same XCD)
@@ -328,7 +330,7 @@ enum class FfnShape { Small, Small64, Large, Mid };
 
 template <class F>
 bool ffn_shape_fits(const moe_problem_t& p) {
-  return p.d % F::G1::BK == 0 && p.I % F::G2::BK == 0 && (2 * p.I) % F::G1::BW == 0 &&
+  return p.d % F::G1::BK == 0 && p.I % F::G2::BK == 0 && (gate_rows(p) * p.I) % F::G1::BW == 0 &&
          p.d % F::G2::BW == 0;
 }
 
@@ -359,10 +361,9 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   if (mt_bound / kXcds + L.W + 1 > kSchedMaxLocal) flags |= MOE_FLAG_SERIAL;
   if (flags & MOE_FLAG_SERIAL) {
     constexpr size_t l1 = F::G1::LDS_BYTES, l2 = F::G2::LDS_BYTES;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm1_phase_kernel<F>, F::NT, l1)) != hipSuccess)
-      return e;
-    gemm1_phase_kernel<F><<<max(1, per_cu) * cus, F::NT, l1, s>>>(xb, w13, offsets, sorted_token, act,
-                                                                 p.E_local, p.d, p.I, xscale);
+    auto g1 = gate_rows(p) == 2 ? gemm1_phase_kernel<F, true> : gemm1_phase_kernel<F, false>;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g1, F::NT, l1)) != hipSuccess) return e;
+    g1<<<max(1, per_cu) * cus, F::NT, l1, s>>>(xb, w13, offsets, sorted_token, act, p.E_local, p.d, p.I, xscale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm2_phase_kernel<F>, F::NT, l2)) != hipSuccess)
       return e;
@@ -401,7 +402,9 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   int wall_khz = 0;
   if ((e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
   A.timeout_ticks = static_cast<long long>(max(wall_khz, 1)) * 1000ll * kWaitTimeoutSeconds;
-  auto kern = out_bf16 ? ffn_waved_kernel<F, true> : ffn_waved_kernel<F, false>;
+  const bool gated = gate_rows(p) == 2;
+  auto kern = out_bf16 ? (gated ? ffn_waved_kernel<F, true, true> : ffn_waved_kernel<F, true, false>)
+                       : (gated ? ffn_waved_kernel<F, false, true> : ffn_waved_kernel<F, false, false>);
   constexpr size_t lds = ffn_lds_bytes<F>();
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, F::NT, lds)) != hipSuccess) return e;
   kern<<<max(1, per_cu) * cus, F::NT, lds, s>>>(A);
@@ -432,7 +435,7 @@ hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, 
                       const float* topk_w, const int32_t* ready_wave, void* y, void* out,
                       uint32_t flags, char* ws, hipStream_t s) {
   (void)ready_wave;
-  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
+  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16, gate_rows(p));
   const char* pk = static_cast<const char*>(packed);
   const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
   const uint16_t* w2 = reinterpret_cast<const uint16_t*>(pk + PL.w2);
@@ -459,7 +462,7 @@ hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8
                           const void* packed, const int32_t* offsets, const int32_t* sorted_token,
                           const int32_t* pair_pos, const float* topk_w, void* y, void* out, uint32_t flags,
                           char* ws, hipStream_t s) {
-  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16);
+  const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16, gate_rows(p));
   const char* pk = static_cast<const char*>(packed);
   const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
   const uint16_t* w2 = reinterpret_cast<const uint16_t*>(pk + PL.w2);

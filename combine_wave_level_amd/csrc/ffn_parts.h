@@ -112,6 +112,12 @@ __device__ __forceinline__ float silu_mul(float h1, float h3) {
   return (h1 / (1.0f + expf(-h1))) * h3;
 }
 
+// The ungated activation: max(h, 0)^2 (no exponential, no division).
+__device__ __forceinline__ float relu_sq(float h) {
+  const float r = fmaxf(h, 0.0f);
+  return r * r;
+}
+
 // Output staging through LDS.  A tile's BT x COLS bf16 results are written
 // to LDS as [row][16-byte chunk] with the chunk index XOR-swizzled by the
 // row (the 8-byte writes of a lane group's 16 rows then hit distinct banks),
@@ -150,19 +156,20 @@ __device__ __forceinline__ void out_flush(const uint16_t* lds, uint16_t* __restr
 
 // GEMM1 tile: rows [row0, row0 + BT) of expert e's segment (count rows
 // valid), BW packed rows of W13 starting at row block nt * BW / 16, i.e.
-// intermediate indices [nt * BW/2, nt * BW/2 + BW/2).  The operand rows are
+// intermediate indices [nt * BW/2, nt * BW/2 + BW/2) (gated = false: W13
+// holds W1 only and the tile covers indices [nt * BW, nt * BW + BW)).  The operand rows are
 // pulled straight from the token-order staging buffer xb by sorted_token:
 // the dispatch pull lands in LDS.
 // FP8T tiles: xb is the e4m3 staging buffer (d bytes per token) and xscale
 // the tokens' scales.
-template <class C>
+template <class C, bool GATED = true>
 __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            const uint16_t* __restrict__ w13e,
                                            const int32_t* __restrict__ sorted_token,
                                            uint16_t* __restrict__ act, int row0, int count, int nt,
                                            int d, int I, uint16_t* lds,
                                            const float* __restrict__ xscale = nullptr) {
-  static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
+  static_assert(!GATED || C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   constexpr int COLS = C::BW / 2;
   static_assert(static_cast<size_t>(C::BT) * COLS * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
   const int lane = lane_id();
@@ -185,6 +192,26 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
   }
   TileAcc<C> acc;
   tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc, count, &tsc);
+  if constexpr (!GATED) {
+    // ungated: every row block is W1; a = max(h, 0)^2 for BW intermediate
+    // indices per tile
+    static_assert(static_cast<size_t>(C::BT) * C::BW * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) {
+      if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones
+      const int t = (wt * C::AT + b) * 16 + (lane & 15);
+#pragma unroll
+      for (int a = 0; a < C::AW; ++a) {
+        const int n = (wr * C::AW + a) * 16 + 4 * (lane / 16);
+        const f32x4 h = acc.v[a][b];
+        u32x2 pk;
+        pk.x = pack_bf16x2(relu_sq(h[0]), relu_sq(h[1]));
+        pk.y = pack_bf16x2(relu_sq(h[2]), relu_sq(h[3]));
+        out_put<C::BW>(lds, t, n, pk);
+      }
+    }
+    out_flush<C::BW, C::NW>(lds, act + static_cast<size_t>(row0) * I + nt * C::BW, I, count);
+  } else {
 #pragma unroll
   for (int b = 0; b < C::AT; ++b) {
     if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones
@@ -201,6 +228,7 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
     }
   }
   out_flush<COLS, C::NW>(lds, act + static_cast<size_t>(row0) * I + nt * COLS, I, count);
+  }
 }
 
 // GEMM2 tile: y[row0 .. row0 + count) x features [nt * BW, nt * BW + BW).

@@ -21,7 +21,10 @@ static moe_status_t check_problem(const moe_problem_t* p) {
   if (p->E_local % p->experts_per_wave != 0) return MOE_ERR_INVALID_ARG;
   const auto dt_ok = [](int32_t t) { return t == MOE_F32 || t == MOE_BF16; };
   if (!dt_ok(p->x_dtype) || !dt_ok(p->w_dtype) || !dt_ok(p->out_dtype)) return MOE_ERR_INVALID_ARG;
+  if (p->activation != MOE_ACT_SWIGLU && p->activation != MOE_ACT_RELU2) return MOE_ERR_INVALID_ARG;
   if (p->d % 128 != 0 || p->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  // an ungated GEMM1 tile spans 128 intermediate indices (a gated one 64)
+  if (p->activation == MOE_ACT_RELU2 && p->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (p->E_global > 256 || p->k > 64) return MOE_ERR_UNSUPPORTED;
   if (p->T > (1 << 24) || p->d > (1 << 16) || p->I > (1 << 16)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -88,7 +91,7 @@ extern "C" {
 
 size_t moe_packed_weights_size(const moe_problem_t* p) {
   if (check_problem(p) != MOE_OK) return 0;
-  return packed_layout(p->d, p->I, p->E_global, p->E_local, p->x_dtype == MOE_BF16).total;
+  return packed_layout(p->d, p->I, p->E_global, p->E_local, p->x_dtype == MOE_BF16, gate_rows(*p)).total;
 }
 
 size_t moe_workspace_size(const moe_problem_t* p) {
@@ -97,7 +100,7 @@ size_t moe_workspace_size(const moe_problem_t* p) {
 }
 
 size_t moe_packed_bwd_size(const moe_problem_t* p) {
-  if (check_problem(p) != MOE_OK) return 0;
+  if (check_problem(p) != MOE_OK || p->activation != MOE_ACT_SWIGLU) return 0;
   return packed_bwd_layout(*p).total;
 }
 
@@ -105,6 +108,7 @@ moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const 
                                   void* packed_bwd, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (!Wg || !W1 || !W3 || !packed_bwd) return MOE_ERR_INVALID_ARG;
   if (!aligned16(packed_bwd) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3)) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_pack_bwd(*p, Wg, W1, W3, packed_bwd, static_cast<hipStream_t>(stream)));
@@ -114,8 +118,9 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void
                               const void* W3, const void* W2, void* packed, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (!Wg || !W1 || !W3 || !W2 || !packed) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(packed) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2))
+  const bool need_w3 = p->activation == MOE_ACT_SWIGLU;
+  if (!Wg || !W1 || (need_w3 && !W3) || !W2 || !packed) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(Wg) || !aligned16(W1) || (W3 && !aligned16(W3)) || !aligned16(W2))
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_pack(*p, Wg, W1, W3, W2, packed, static_cast<hipStream_t>(stream)));
 }
@@ -215,6 +220,7 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
                               moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (!packed || !expert_offsets || !dW1 || !dW3 || !dW2) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !sorted_token || !pair_pos || !topk_w || !dout)) return MOE_ERR_INVALID_ARG;
   if ((x && !aligned16(x)) || (dout && !aligned16(dout)) || !aligned16(dW1) || !aligned16(dW3) ||
@@ -244,6 +250,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
                           size_t ws_bytes, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (!packed || !packed_bwd || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !topk_idx || !topk_w || !sorted_token || !pair_pos || !dout || !dx))
     return MOE_ERR_INVALID_ARG;

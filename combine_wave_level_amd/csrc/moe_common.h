@@ -72,7 +72,8 @@ __host__ __device__ __forceinline__ size_t frag_offset(int nb, int kb, int KB) {
 //   W13      : per local expert, [2I][d] fragment layout; row block 2b holds
 //              W1 columns 16b .. 16b+15 and row block 2b+1 the W3 columns
 //              with the same indices, so gate and up values of one
-//              intermediate index meet in the same lane.
+//              intermediate index meet in the same lane (ungated
+//              activation: W1^T only, [I][d]).
 //   W2       : per local expert, W2^T as [d][I] in fragment layout.
 //   W2b      : per local expert, W2 as [I][d] in fragment layout (K = d), the
 //              operand of dA = dy W2^T in the weight gradient.
@@ -83,15 +84,17 @@ struct PackedLayout {
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// gate_rows: 2 when W13 holds W1 and W3 (SwiGLU), 1 when it holds W1 only
+// (an ungated activation).
 __host__ __device__ inline PackedLayout packed_layout(int d, int I, int E_global, int E_local,
-                                                      int x_is_bf16) {
+                                                      int x_is_bf16, int gate_rows = 2) {
   PackedLayout L;
   L.Epad = static_cast<int>(align_up(static_cast<size_t>(E_global), 128));
   size_t off = 0;
   L.router = off;
   off += align_up(static_cast<size_t>(L.Epad) * d * (x_is_bf16 ? 2 : 4), 256);
   L.w13 = off;
-  off += align_up(static_cast<size_t>(E_local) * 2 * I * d * 2, 256);
+  off += align_up(static_cast<size_t>(E_local) * gate_rows * I * d * 2, 256);
   L.w2 = off;
   off += align_up(static_cast<size_t>(E_local) * d * I * 2, 256);
   L.w2b = off;

@@ -58,6 +58,10 @@ struct WsLayout {
 
 WsLayout ws_layout(const moe_problem_t& p);
 
+// Packed W13 rows per intermediate index: 2 (W1 and W3) for SwiGLU, 1 (W1)
+// for the ungated activation.
+inline int gate_rows(const moe_problem_t& p) { return p.activation == MOE_ACT_SWIGLU ? 2 : 1; }
+
 // Rows of the weight-gradient split along the routed rows of one expert:
 // each chunk of this many rows reduces into its own partial slot.
 constexpr int kWgradChunkRows = 2048;

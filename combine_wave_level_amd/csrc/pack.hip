@@ -121,7 +121,7 @@ hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, c
                        const void* W2, void* packed, hipStream_t s) {
   const bool xbf = p.x_dtype == MOE_BF16;
   const bool wbf = p.w_dtype == MOE_BF16;
-  const PackedLayout L = packed_layout(p.d, p.I, p.E_global, p.E_local, xbf);
+  const PackedLayout L = packed_layout(p.d, p.I, p.E_global, p.E_local, xbf, gate_rows(p));
   char* base = static_cast<char*>(packed);
   const int threads = 256;
   // router
@@ -139,8 +139,18 @@ hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.E_local == 0) return hipSuccess;
-  // W13: [2I][d] per expert, K = d
-  {
+  if (p.activation != MOE_ACT_SWIGLU) {
+    // ungated: W1^T as [I][d] per expert, K = d
+    const size_t slots = static_cast<size_t>(p.I) * (p.d / 8);
+    dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
+    const size_t stride = static_cast<size_t>(p.d) * p.I;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(base + L.w13);
+    if (wbf)
+      pack_frag_kernel<true, 0><<<grid, threads, 0, s>>>(W1, nullptr, dst, p.d, p.I, p.I, stride, stride);
+    else
+      pack_frag_kernel<false, 0><<<grid, threads, 0, s>>>(W1, nullptr, dst, p.d, p.I, p.I, stride, stride);
+  } else {
+    // W13: [2I][d] per expert, K = d
     const size_t slots = static_cast<size_t>(2 * p.I) * (p.d / 8);
     dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
     const size_t src_stride = static_cast<size_t>(p.d) * p.I;

@@ -176,7 +176,7 @@ hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packe
                         float* partial, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   const bool xbf = p.x_dtype == MOE_BF16;
-  const PackedLayout L = packed_layout(p.d, p.I, p.E_global, p.E_local, xbf);
+  const PackedLayout L = packed_layout(p.d, p.I, p.E_global, p.E_local, xbf, gate_rows(p));
   const char* base = static_cast<const char*>(packed);
   const int splits = router_splits(p.d, p.E_global, xbf);
   hipError_t e;

@@ -24,6 +24,8 @@ MOE_ERR_TIMEOUT = -5
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_SERIAL = 0x1
+MOE_ACT_SWIGLU = 0
+MOE_ACT_RELU2 = 1
 
 EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
@@ -37,7 +39,7 @@ EXPORTED = (
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d", "I", "E_global", "k", "e_begin", "E_local", "experts_per_wave",
-        "x_dtype", "w_dtype", "out_dtype")]
+        "x_dtype", "w_dtype", "out_dtype", "activation")]
 
     def replace(self, **kw) -> "Problem":
         q = Problem()
@@ -117,10 +119,11 @@ def _stream():
 
 
 def problem(T, d, I, E_global, k, e_begin=0, E_local=None, experts_per_wave=4,
-            x_dtype=MOE_BF16, w_dtype=MOE_BF16, out_dtype=MOE_BF16) -> Problem:
+            x_dtype=MOE_BF16, w_dtype=MOE_BF16, out_dtype=MOE_BF16,
+            activation=MOE_ACT_SWIGLU) -> Problem:
     E_local = E_global if E_local is None else E_local
     return Problem(T, d, I, E_global, k, e_begin, E_local, experts_per_wave,
-                   x_dtype, w_dtype, out_dtype)
+                   x_dtype, w_dtype, out_dtype, activation)
 
 
 def workspace_size(p: Problem) -> int:

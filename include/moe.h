@@ -55,13 +55,24 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Expert activation.  SWIGLU: a = silu(x W1) * (x W3) (the layer of the
+ * workloads).  RELU2: the cheap element-wise activation the DeepSeek-V4
+ * launch digest (section 1.4, activation-function bullet) recommends instead
+ * of SwiGLU, with no exponential, no division and no gating projection; the
+ * pages do not name the function, the reading here is squared ReLU,
+ * a = max(x W1, 0)^2, and W3 is not used.  The backward entry points
+ * support SWIGLU only. */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_activation_t;
+
 /* Shape of one layer share.  Limits checked by every call:
  *   T >= 0; d, I > 0 with d % 128 == 0 and I % 64 == 0 (MOE_ERR_UNSUPPORTED
  *   otherwise); 1 <= k <= E_global; E_global <= 256 and k <= 64
  *   (MOE_ERR_UNSUPPORTED beyond); E_local >= 1; 0 <= e_begin,
  *   e_begin + E_local <= E_global;
  *   1 <= experts_per_wave, E_local % experts_per_wave == 0;
- *   x_dtype in {F32, BF16}; out_dtype in {F32, BF16}. */
+ *   x_dtype in {F32, BF16}; out_dtype in {F32, BF16};
+ *   activation in {SWIGLU, RELU2}; RELU2 needs I % 128 == 0
+ *   (MOE_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   int32_t T;                /* tokens in the batch                         */
   int32_t d;                /* hidden size                                 */
@@ -74,6 +85,7 @@ typedef struct {
   int32_t x_dtype;          /* moe_dtype_t of x and the router weights     */
   int32_t w_dtype;          /* moe_dtype_t of the unpacked expert weights  */
   int32_t out_dtype;        /* moe_dtype_t of the layer output             */
+  int32_t activation;       /* moe_activation_t of the experts             */
 } moe_problem_t;
 
 /* Flags for moe_expert_ffn_waved. */
@@ -97,7 +109,7 @@ size_t moe_workspace_size(const moe_problem_t* p);
  * layout (not part of the per-batch path; weights are parameters).
  *   Wg [d, E_global] in x_dtype (router), W1, W3 [E_local, d, I] and
  *   W2 [E_local, I, d] in w_dtype, all row-major in math layout
- *   (h1 = x W1, h3 = x W3, y = a W2).
+ *   (h1 = x W1, h3 = x W3, y = a W2); W3 may be NULL for RELU2.
  *   packed: moe_packed_weights_size(p) bytes, written entirely.
  * Expert weights are rounded to bf16 (RNE) when w_dtype is F32. */
 moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void* W1,
@@ -105,7 +117,7 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void
                               moe_stream_t stream);
 
 /* Bytes of the backward weight buffer moe_pack_weights_bwd writes. 0 on a
- * bad shape. */
+ * bad shape or an activation other than SWIGLU. */
 size_t moe_packed_bwd_size(const moe_problem_t* p);
 
 /* One-time re-layout of the weights the data gradient reads (weights are

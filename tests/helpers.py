@@ -50,7 +50,7 @@ def problem_for(wl: Workload, T: int, G: int | None = None, **kw) -> moe.Problem
     return moe.problem(T=T, d=wl.d, I=wl.I, E_global=wl.E_global, k=kw.get("k", wl.k),
                        e_begin=kw.get("e_begin", wl.e_begin), E_local=kw.get("E_local", wl.E_local),
                        experts_per_wave=wl.G if G is None else G, x_dtype=xdt, w_dtype=xdt,
-                       out_dtype=xdt)
+                       out_dtype=xdt, activation=kw.get("activation", moe.MOE_ACT_SWIGLU))
 
 
 class Layer:
@@ -64,7 +64,8 @@ class Layer:
         self.x = dev(inp["x"])
         self.Wg = dev(inp["Wg"])
         self.bias = dev(inp["bias"]) if inp.get("bias") is not None else None
-        self.packed = moe.pack_weights(self.p, self.Wg, dev(inp["W1"]), dev(inp["W3"]), dev(inp["W2"]))
+        W3 = dev(inp["W3"]) if self.p.activation == moe.MOE_ACT_SWIGLU else None
+        self.packed = moe.pack_weights(self.p, self.Wg, dev(inp["W1"]), W3, dev(inp["W2"]))
         self.ws = moe.workspace(self.p)
         torch.cuda.synchronize()
 

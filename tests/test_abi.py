@@ -45,7 +45,7 @@ def test_status_strings_and_version(L):
 
 def _p(**kw):
     base = dict(T=64, d=256, I=128, E_global=8, k=2, e_begin=0, E_local=8, experts_per_wave=4,
-                x_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16, out_dtype=moe.MOE_BF16)
+                x_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16, out_dtype=moe.MOE_BF16, activation=moe.MOE_ACT_SWIGLU)
     base.update(kw)
     return moe.Problem(*[base[n] for n, _ in moe.Problem._fields_])
 
@@ -63,6 +63,9 @@ def _p(**kw):
     ({"E_global": 512, "E_local": 8}, False),  # router width limit
     ({"x_dtype": 7}, False),
     ({"T": -1}, False),
+    ({"activation": moe.MOE_ACT_RELU2}, True),
+    ({"activation": 2}, False),
+    ({"activation": moe.MOE_ACT_RELU2, "I": 192}, False),   # ungated: I % 128
 ])
 def test_sizes_accept_and_reject(L, kw, ok):
     p = _p(**kw)
@@ -152,6 +155,26 @@ def test_backward_rejects_before_launch(L):
     assert L.moe_packed_bwd_size(ctypes.byref(_p(d=96))) == 0
     # Wg^T (E_global x d bf16) + [W1 | W3]^T per local expert (d x 2I bf16)
     assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2
+
+
+def test_ungated_activation_sizes_and_backward_rejection(L):
+    """RELU2 packs W1 alone (no gating projection, W3 may be NULL) and has no
+    backward: its entry points return UNSUPPORTED before touching memory."""
+    g, u = _p(), _p(activation=moe.MOE_ACT_RELU2)
+    router = 128 * 256 * 2                       # Epad x d bf16
+    w2 = 2 * 8 * 128 * 256 * 2                   # W2^T and W2, E_local x d x I bf16
+    assert moe.packed_weights_size(g) == router + 8 * 2 * 128 * 256 * 2 + w2
+    assert moe.packed_weights_size(u) == router + 8 * 128 * 256 * 2 + w2
+    assert moe.workspace_size(u) > 0
+    assert L.moe_packed_bwd_size(ctypes.byref(u)) == 0
+    assert L.moe_pack_weights_bwd(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    args = [FAKE] * 9
+    assert L.moe_backward(ctypes.byref(u), *args, FAKE, None, None, None, None, None, None, FAKE, 1 << 30,
+                          None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_wgrad(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+    # W3 is required for SWIGLU only
+    assert L.moe_pack_weights(ctypes.byref(g), FAKE, FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_fp8_dispatch_rejects_before_launch(L):

@@ -18,6 +18,11 @@ Workloads (sizes as stated for the benchmark configurations):
                 top-6, one hot expert chosen by about half the tokens,
                 256 fixed probe tokens at random positions, dout ~ N(0, 1).
 
+``ungated(wl)`` is the same layer with an ungated expert (one input
+projection W1 instead of W1 and W3) at the same expert parameter count:
+intermediate size 3I/2, so that d * 3I/2 * 2 = 3 d I, rounded up to a
+multiple of 128 (only the tiny layer's 192 moves, to 256).
+
 Random streams: numpy ``SeedSequence(seed).spawn`` in the fixed order
 x, Wg, W1, W3, W2, bias/hot-direction, probes, positions, dout.  Values are
 drawn as float32 and, for bf16 workloads, rounded to bf16 (RNE).
@@ -28,7 +33,7 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "bf16_bits", "bf16_value"]
+__all__ = ["Workload", "WORKLOADS", "get", "ungated", "make_inputs", "bf16_bits", "bf16_value"]
 
 
 @dataclass(frozen=True)
@@ -72,6 +77,17 @@ HOT_SCALE = 100.0
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def ungated(wl: Workload | str) -> Workload:
+    """The workload's layer with an ungated expert at (about) the same
+    parameter count: W1 [d, I'] and W2 [I', d] with I' = 3I/2 rounded up to
+    a multiple of 128.  The generator still draws a W3, which such a layer
+    does not read."""
+    if isinstance(wl, str):
+        wl = get(wl)
+    I = -(-(3 * wl.I // 2) // 128) * 128
+    return replace(wl, name=wl.name + "_ungated", I=I)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
