@@ -224,27 +224,41 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   __shared__ int32_t s_ready[kSchedMaxWaves + 2];     // ready-slot starts in the ready list
   __shared__ int32_t s_ticket;
   const int xcd = uniform(xcc_id());
-  // the dispatch tables go to LDS first, in parallel: the schedule below is
-  // built by one thread, and reading them from global memory there costs a
-  // memory round trip per expert (tens of microseconds per launch)
+  // The schedule (the steps of sched_build, spread over the workgroup).
+  // The dispatch tables go to LDS first, in parallel; the m-tile prefix,
+  // the single-m-tile dealing, the combine placement and the prefix sums
+  // run on many threads (one thread takes tens of microseconds over them:
+  // a wave issues a dependent scalar instruction every few cycles at best).
   for (int e = threadIdx.x; e <= A.E_local; e += F::NT) s_off[e] = A.offsets[e];
   for (int w = threadIdx.x; w <= A.W + 1; w += F::NT) s_ready[w] = A.ready_off[w];
   for (int i = threadIdx.x; i <= kSchedMaxLocal + kSchedMaxLag; i += F::NT) S.cb_pos[i] = 0;
-  __syncthreads();
+  for (int e = threadIdx.x; e < A.E_local; e += F::NT) S.mt_pre[e + 1] = sched_mtiles(A.offsets, e, C1::BT);
   if (threadIdx.x == 0) {
     // GEMM2 lag: kSchedMaxLag m-tiles, i.e. an XCD runs the GEMM1 tiles of
     // (nearly) all its m-tiles before their GEMM2 tiles.  Interleaving the two
     // closer puts both operand sets (x and W1/W3, act and W2) through the
     // XCD's L2 at once; measured on the mid layer the short lags (2 to 4
     // m-tiles) cost 20% against 8 and more.
-    sched_build_tables(S, s_off, s_ready, A.E_local, A.G, C1::BT, (GATED ? 2 : 1) * A.I / C1::BW, A.d / C2::BW,
-                       A.out != nullptr ? A.cb_parts : 0, xcd, kSchedMaxLag, F::WHOLE_EXPERTS, true);
+    sched_init(S, A.E_local, A.G, (GATED ? 2 : 1) * A.I / C1::BW, A.d / C2::BW, xcd, kSchedMaxLag);
+    S.mt_pre[0] = 0;
+    S.cb_pre[0] = 0;
   }
   __syncthreads();
-  // the schedule's prefix sums in parallel (one thread takes tens of
-  // microseconds over them: a dependent LDS access per position)
+  if (wave_uniform() == 0) sched_scan_wave(S.mt_pre, A.E_local + 1);
+  __syncthreads();
+  if (F::WHOLE_EXPERTS) {
+    if (threadIdx.x == 0) sched_deal_whole(S, A.E_local);
+  } else {
+    sched_deal_single(S, A.E_local, threadIdx.x, F::NT);
+  }
+  __syncthreads();
   if (uniform(S.err) == 0) {
-    if (wave_uniform() == 0) sched_scan_cb_pos_wave(S);
+    sched_place(S, s_ready, A.out != nullptr ? A.cb_parts : 0, threadIdx.x, F::NT,
+                [](int32_t* p, int v) { atomicAdd(p, v); });
+    __syncthreads();
+    // the two prefix sums on two wavefronts
+    if (wave_uniform() == 0) sched_scan_wave(S.cb_pos, S.n_local + S.lag + 1);
+    if (wave_uniform() == 1) sched_scan_wave(S.cb_pre, S.W + 2);
     __syncthreads();
     const int npos = uniform(S.n_local + S.lag);
     for (int i = threadIdx.x; i <= npos; i += F::NT) S.pos[i] = sched_pos_of(S, i);

@@ -97,45 +97,64 @@ __host__ __device__ inline int sched_expert_of(const int32_t* mt_pre, int lo, in
 // combine).  lag = L (1 .. kSchedMaxLag).  whole_experts: deal experts whole
 // (else single m-tiles).  S.err = 1 if the XCD holds more than
 // kSchedMaxLocal m-tiles (the schedule is then empty).
-// sched_build = sched_build_tables (dealing, combine placement; leaves in
-// cb_pos[i + 1] the combine tasks placed at position i) + sched_build_positions
-// (prefix sums into cb_pos and the first ticket of every position).  The
-// kernel runs the tables on one thread and the positions on a wavefront
-// (sched_scan_cb_pos_wave, then sched_pos_of per position); the prefix sums
-// are exact integer sums, so both give the same schedule.  cb_pos_zeroed:
-// cb_pos[0 .. kSchedMaxLocal + kSchedMaxLag] already holds zeros.
-__host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_t* offsets,
-                                                   const int32_t* ready_off, int E_local, int G, int BT,
-                                                   int NT1, int NT2, int cb_parts, int xcd, int lag,
-                                                   bool whole_experts, bool cb_pos_zeroed) {
+//
+// The build is cut into steps that the kernel runs in parallel where it can
+// (sched_build runs them in order on the host):
+//   sched_init              header fields
+//   sched_mtiles            m-tiles of one expert (the kernel's wavefront
+//                           takes their prefix sum into mt_pre)
+//   sched_deal_whole        whole-expert dealing, sequential (one thread)
+//   sched_deal_single       single-m-tile dealing in closed form, any
+//                           index range (every thread a share)
+//   sched_place             combine placement, one slot at a time, any
+//                           range; leaves the slot's task count in
+//                           cb_pre[s + 1] and adds it to cb_pos[at + 1]
+//   exclusive prefix of cb_pre, then sched_build_positions.
+// Every step is exact integer arithmetic, so the order of the threads never
+// changes the schedule.
+
+__host__ __device__ inline void sched_init(WaveSchedule& S, int E_local, int G, int NT1, int NT2, int xcd,
+                                           int lag) {
   S.W = E_local / G;
-  const int W = S.W;  // loop bounds in registers (stores into S may alias its fields)
   S.lag = lag < 1 ? 1 : (lag > kSchedMaxLag ? kSchedMaxLag : lag);
   S.G = G;
   S.NT1 = NT1;
   S.NT2 = NT2;
   S.xcd = xcd;
   S.err = 0;
-  int run = 0;
-  for (int e = 0; e < E_local; ++e) {
-    S.mt_pre[e] = run;
-    run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
-  }
-  S.mt_pre[E_local] = run;
-  // deal the m-tiles to the XCD with the most room (lowest id on ties): as
-  // much of the expert as fits, or single m-tiles; the rooms sum to the
-  // m-tiles still to deal, so every deal finds room
+}
+
+__host__ __device__ inline int sched_mtiles(const int32_t* offsets, int e, int BT) {
+  return (offsets[e + 1] - offsets[e] + BT - 1) / BT;
+}
+
+// Rooms of the XCDs: the first n % 8 take floor(n / 8) + 1 m-tiles, the
+// others floor(n / 8).
+__host__ __device__ inline int sched_cap(int n, int y) { return n / kXcds + (y < n % kXcds ? 1 : 0); }
+
+// Work model for placing the combine (an m-tile's GEMM1 tiles cost 2 units:
+// K = d over 2I features; its GEMM2 tiles 1 unit: K = I over d features):
+// XCD y's stream ends the GEMM2 tiles of its first c of cap m-tiles after
+// 2 min(c + L, cap) + c units; need[s] = the largest such time over the
+// XCDs for the m-tiles of waves < s.
+__host__ __device__ inline int sched_work_of(int c, int cap, int L) {
+  return c > 0 ? 2 * (c + L < cap ? c + L : cap) + c : 0;
+}
+
+// Whole-expert dealing: each deal goes to the XCD with the most room
+// (lowest id on ties) and takes as much of the expert as fits; the rooms
+// sum to the m-tiles still to deal, so every deal finds room.  Needs the
+// header and mt_pre; writes loc_mt, loc_pre, need, n_local (err on
+// overflow).
+__host__ __device__ inline void sched_deal_whole(WaveSchedule& S, int E_local) {
+  const int W = S.W, G = S.G, L = S.lag, xcd = S.xcd;  // in registers: stores into S may alias
+  const int run = S.mt_pre[E_local];
   int room[kXcds], cap[kXcds], cnt[kXcds];
+#pragma unroll
   for (int y = 0; y < kXcds; ++y) {
-    cap[y] = room[y] = run / kXcds + (y < run % kXcds ? 1 : 0);
+    cap[y] = room[y] = sched_cap(run, y);
     cnt[y] = 0;
   }
-  // Work model for placing the combine (an m-tile's GEMM1 tiles cost 2
-  // units: K = d over 2I features; its GEMM2 tiles 1 unit: K = I over d
-  // features): XCD y's stream ends the GEMM2 tiles of its first c m-tiles
-  // after 2 min(c + L, cap_y) + c units.  need[s] = the largest such time
-  // over the XCDs for the m-tiles of waves < s.
-  const int L = S.lag;
   S.need[0] = 0;
   int loc = 0, w_next = 0;
   int w_e = 0, in_wave = 0;  // wave of expert e and its rank in the wave (no integer division)
@@ -144,11 +163,24 @@ __host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_
     int first = S.mt_pre[e];
     int n = S.mt_pre[e + 1] - first;
     while (n > 0) {
-      int x = 0;
-      for (int y = 1; y < kXcds; ++y) x = room[y] > room[x] ? y : x;
-      const int take = whole_experts ? (n < room[x] ? n : room[x]) : 1;
-      room[x] -= take;
-      cnt[x] += take;
+      // the argmax and the update index the arrays with constants only (an
+      // index held in a register makes every access a chain of selects)
+      int x = 0, rx = room[0];
+#pragma unroll
+      for (int y = 1; y < kXcds; ++y) {
+        if (room[y] > rx) {
+          rx = room[y];
+          x = y;
+        }
+      }
+      const int take = n < rx ? n : rx;
+#pragma unroll
+      for (int y = 0; y < kXcds; ++y) {
+        if (y == x) {
+          room[y] -= take;
+          cnt[y] += take;
+        }
+      }
       if (x == xcd) {
         for (int q = 0; q < take; ++q) {
           if (loc < kSchedMaxLocal) S.loc_mt[loc] = first + q;
@@ -160,8 +192,9 @@ __host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_
     }
     if (++in_wave == G) {
       int t = 0;
+#pragma unroll
       for (int y = 0; y < kXcds; ++y) {
-        const int ty = cnt[y] > 0 ? 2 * (cnt[y] + L < cap[y] ? cnt[y] + L : cap[y]) + cnt[y] : 0;
+        const int ty = sched_work_of(cnt[y], cap[y], L);
         t = ty > t ? ty : t;
       }
       S.need[++w_e] = t;
@@ -174,35 +207,118 @@ __host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_
     S.err = 1;
     S.n_local = 0;
     S.total = 0;
+  }
+}
+
+// Single-m-tile dealing in closed form.  Dealing one m-tile at a time to the
+// XCD with the most room (lowest id on ties), from rooms floor(n/8) + 1 for
+// the first r = n % 8 XCDs and floor(n/8) for the others, sends m-tile j to
+// XCD j for j < r and to XCD (j - r) % 8 after (the first r deals level the
+// rooms, then the deals go round the XCDs in id order).
+//   Deals to XCD x among the first M m-tiles:
+__host__ __device__ inline int sched_single_count(int x, int M, int r) {
+  return (x < r && x < M ? 1 : 0) + (M > r + x ? (M - r - x + kXcds - 1) / kXcds : 0);
+}
+//   Global index of XCD x's i-th m-tile:
+__host__ __device__ inline int sched_single_local(int x, int i, int r) {
+  return x < r ? (i == 0 ? x : r + x + kXcds * (i - 1)) : r + x + kXcds * i;
+}
+
+// The thread's share (indices begin, begin + step, ...) of loc_mt, loc_pre
+// and need for single-m-tile dealing.  Needs the header and mt_pre; every
+// thread sets the same n_local and err.
+__host__ __device__ inline void sched_deal_single(WaveSchedule& S, int E_local, int begin, int step) {
+  const int W = S.W, G = S.G, L = S.lag, xcd = S.xcd;
+  const int run = S.mt_pre[E_local], r = run % kXcds;
+  const int n = sched_cap(run, xcd);
+  if (n > kSchedMaxLocal) {
+    S.err = 1;
+    S.n_local = 0;
+    S.total = 0;
     return;
   }
-  // combine tasks of this XCD per slot, and the position of each slot
-  const int npos = loc + L;  // positions 0 .. npos - 1
-  int cb = 0;
-  if (!cb_pos_zeroed)
-    for (int i = 0; i <= npos; ++i) S.cb_pos[i] = 0;
-  int p_time = 0;  // first position whose work reaches need[s] (need grows with s)
-  for (int s = 0; s <= W; ++s) {
-    S.cb_pre[s] = cb;
+  S.n_local = n;
+  for (int i = begin; i < n; i += step) S.loc_mt[i] = sched_single_local(xcd, i, r);
+  for (int w = begin; w <= W; w += step) {
+    const int M = S.mt_pre[w * G];
+    S.loc_pre[w] = w == W ? n : sched_single_count(xcd, M, r);
+    int t = 0;
+    if (w > 0) {
+#pragma unroll
+      for (int y = 0; y < kXcds; ++y) {
+        const int ty = sched_work_of(sched_single_count(y, M, r), sched_cap(run, y), L);
+        t = ty > t ? ty : t;
+      }
+    }
+    S.need[w] = t;
+  }
+}
+
+// Work of this XCD's stream through position q: 2 units per m-tile of
+// GEMM1 (q <= n of them), 1 per m-tile of GEMM2 (positions >= L).
+__host__ __device__ inline int sched_stream_work(int q, int n, int L) {
+  return 2 * (q < n ? q : n) + (q - L > 0 ? q - L : 0);
+}
+
+// First position p in [0, npos - 1] whose next position's work reaches
+// need (npos - 1 if none does); sched_stream_work grows with q.
+__host__ __device__ inline int sched_p_time(int need, int n, int L, int npos) {
+  int lo = 0, hi = npos - 1;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (sched_stream_work(mid + 1, n, L) >= need) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Combine placement of slots begin, begin + step, ... <= W (tokens whose
+// last local wave is s - 1): this XCD's share of the slot's chunks sits at
+// the position of the GEMM2 tiles of its last m-tile of a wave <= s + 1
+// (slot s needs waves <= s - 1 of every XCD: two waves of slack for XCDs
+// that run behind this one), and not before this stream's own work reaches
+// need[s], the time by which the slowest XCD ends those waves (an XCD
+// carrying a hot expert ends them late; its partners run their later GEMM2
+// tiles first).  need grows with s, so the positions do too.  Writes the
+// slot's task count to cb_pre[s + 1] and adds it to cb_pos[at + 1] with
+// add(), which must be atomic when threads share the work.
+template <class Add>
+__host__ __device__ inline void sched_place(WaveSchedule& S, const int32_t* ready_off, int cb_parts, int begin,
+                                            int step, Add add) {
+  const int W = S.W, L = S.lag, xcd = S.xcd, n = S.n_local;
+  const int npos = n + L;  // positions 0 .. npos - 1
+  for (int s = begin; s <= W; s += step) {
     const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     const int mine = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
-    cb += mine;
-    // position of the GEMM2 tiles of the last m-tile of a wave <= s + 1
-    // (slot s needs waves <= s - 1 of every XCD: two waves of slack for
-    // XCDs that run behind this one)
     const int last = S.loc_pre[s + 2 < W ? s + 2 : W] - 1;
     int at = last >= 0 ? last + L : 0;
-    // and not before this stream's own work reaches the time by which the
-    // slowest XCD ends the waves the slot waits for (an XCD carrying a hot
-    // expert ends them late; its partners run their later GEMM2 tiles first)
-    const int need = S.need[s < W ? s : W];
-    while (p_time < npos - 1 &&
-           2 * (p_time + 1 < loc ? p_time + 1 : loc) + (p_time + 1 - L > 0 ? p_time + 1 - L : 0) < need)
-      ++p_time;
+    const int p_time = sched_p_time(S.need[s < W ? s : W], n, L, npos);
     at = at > p_time ? at : p_time;
-    S.cb_pos[at + 1] += mine;  // counted from position at + 1 on
+    S.cb_pre[s + 1] = mine;
+    if (mine > 0) add(&S.cb_pos[at + 1], mine);
   }
-  S.cb_pre[W + 1] = cb;
+}
+
+// The host composition of the steps (cb_pos must hold zeros).
+__host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_t* offsets,
+                                                   const int32_t* ready_off, int E_local, int G, int BT,
+                                                   int NT1, int NT2, int cb_parts, int xcd, int lag,
+                                                   bool whole_experts) {
+  sched_init(S, E_local, G, NT1, NT2, xcd, lag);
+  int run = 0;
+  for (int e = 0; e < E_local; ++e) {
+    S.mt_pre[e] = run;
+    run += sched_mtiles(offsets, e, BT);
+  }
+  S.mt_pre[E_local] = run;
+  if (whole_experts)
+    sched_deal_whole(S, E_local);
+  else
+    sched_deal_single(S, E_local, 0, 1);
+  if (S.err) return;
+  for (int i = 0; i <= S.n_local + S.lag; ++i) S.cb_pos[i] = 0;
+  sched_place(S, ready_off, cb_parts, 0, 1, [](int32_t* p, int v) { *p += v; });
+  S.cb_pre[0] = 0;
+  for (int s = 1; s <= S.W + 1; ++s) S.cb_pre[s] += S.cb_pre[s - 1];
 }
 
 // First ticket of position i, once cb_pos[i] = combine tasks at positions
@@ -224,20 +340,20 @@ __host__ __device__ inline void sched_build(WaveSchedule& S, const int32_t* offs
                                             const int32_t* ready_off, int E_local, int G, int BT,
                                             int NT1, int NT2, int cb_parts, int xcd, int lag,
                                             bool whole_experts) {
-  sched_build_tables(S, offsets, ready_off, E_local, G, BT, NT1, NT2, cb_parts, xcd, lag, whole_experts, false);
+  sched_build_tables(S, offsets, ready_off, E_local, G, BT, NT1, NT2, cb_parts, xcd, lag, whole_experts);
   if (S.err == 0) sched_build_positions(S);
 }
 
-// The prefix of sched_build_positions by one wavefront (all 64 lanes of the
-// calling wave; lane l sums a contiguous chunk, the chunk sums are scanned
-// across lanes, then each lane writes its chunk's running sums).
-__device__ inline void sched_scan_cb_pos_wave(WaveSchedule& S) {
+// In-place inclusive prefix sum of a[0 .. len) by one wavefront (all 64
+// lanes of the calling wave; lane l sums a contiguous chunk, the chunk sums
+// are scanned across lanes, then each lane writes its chunk's running sums).
+// The kernel's form of the host loops over mt_pre, cb_pre and cb_pos.
+__device__ inline void sched_scan_wave(int32_t* a, int len) {
   const int lane = static_cast<int>(threadIdx.x) & 63;
-  const int len = S.n_local + S.lag + 1;
   const int per = (len + 63) / 64;
   const int b = lane * per, e = b + per < len ? b + per : len;
   int sum = 0;
-  for (int i = b; i < e; ++i) sum += S.cb_pos[i];
+  for (int i = b; i < e; ++i) sum += a[i];
   int incl = sum;
   for (int off = 1; off < 64; off <<= 1) {
     const int v = __shfl_up(incl, off, 64);
@@ -245,8 +361,8 @@ __device__ inline void sched_scan_cb_pos_wave(WaveSchedule& S) {
   }
   int run = incl - sum;
   for (int i = b; i < e; ++i) {
-    run += S.cb_pos[i];
-    S.cb_pos[i] = run;
+    run += a[i];
+    a[i] = run;
   }
 }
 

@@ -17,7 +17,13 @@
 //   2. every GEMM2 tile waits only on smaller tickets of its own stream, and
 //      every combine task of slot s comes after all of its stream's GEMM2
 //      tiles of waves < s (no stream can block on its own later tickets);
-//   3. an emulated run completes and every counter ends at its target.
+//   3. an emulated run completes and every counter ends at its target;
+//   4. the schedule equals the one a plain sequential greedy builds (the
+//      definition: every deal to the XCD with the most room, lowest id on
+//      ties, the combine placed by walking the positions), and the kernel's
+//      split of the build over threads (strided index ranges taken in any
+//      order) gives the same schedule.
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cstdio>
@@ -36,6 +42,147 @@ static int fail(const char* msg, long a = 0, long b = 0) {
   std::exit(1);
 }
 
+// The sequential definition of the dealing and the combine placement, one
+// m-tile or expert piece and one position at a time.
+static void reference_tables(WaveSchedule& S, const int32_t* offsets, const int32_t* ready_off, int E_local, int G,
+                             int BT, int NT1, int NT2, int cb_parts, int xcd, int lag, bool whole_experts) {
+  const bool cb_pos_zeroed = false;
+  S.W = E_local / G;
+  const int W = S.W;  // loop bounds in registers (stores into S may alias its fields)
+  S.lag = lag < 1 ? 1 : (lag > kSchedMaxLag ? kSchedMaxLag : lag);
+  S.G = G;
+  S.NT1 = NT1;
+  S.NT2 = NT2;
+  S.xcd = xcd;
+  S.err = 0;
+  int run = 0;
+  for (int e = 0; e < E_local; ++e) {
+    S.mt_pre[e] = run;
+    run += (offsets[e + 1] - offsets[e] + BT - 1) / BT;
+  }
+  S.mt_pre[E_local] = run;
+  // deal the m-tiles to the XCD with the most room (lowest id on ties): as
+  // much of the expert as fits, or single m-tiles; the rooms sum to the
+  // m-tiles still to deal, so every deal finds room
+  int room[kXcds], cap[kXcds], cnt[kXcds];
+  for (int y = 0; y < kXcds; ++y) {
+    cap[y] = room[y] = run / kXcds + (y < run % kXcds ? 1 : 0);
+    cnt[y] = 0;
+  }
+  // Work model for placing the combine (an m-tile's GEMM1 tiles cost 2
+  // units: K = d over 2I features; its GEMM2 tiles 1 unit: K = I over d
+  // features): XCD y's stream ends the GEMM2 tiles of its first c m-tiles
+  // after 2 min(c + L, cap_y) + c units.  need[s] = the largest such time
+  // over the XCDs for the m-tiles of waves < s.
+  const int L = S.lag;
+  S.need[0] = 0;
+  int loc = 0, w_next = 0;
+  int w_e = 0, in_wave = 0;  // wave of expert e and its rank in the wave (no integer division)
+  for (int e = 0; e < E_local; ++e) {
+    while (w_next <= w_e && w_next < W) S.loc_pre[w_next++] = loc;
+    int first = S.mt_pre[e];
+    int n = S.mt_pre[e + 1] - first;
+    while (n > 0) {
+      int x = 0;
+      for (int y = 1; y < kXcds; ++y) x = room[y] > room[x] ? y : x;
+      const int take = whole_experts ? (n < room[x] ? n : room[x]) : 1;
+      room[x] -= take;
+      cnt[x] += take;
+      if (x == xcd) {
+        for (int q = 0; q < take; ++q) {
+          if (loc < kSchedMaxLocal) S.loc_mt[loc] = first + q;
+          ++loc;
+        }
+      }
+      first += take;
+      n -= take;
+    }
+    if (++in_wave == G) {
+      int t = 0;
+      for (int y = 0; y < kXcds; ++y) {
+        const int ty = cnt[y] > 0 ? 2 * (cnt[y] + L < cap[y] ? cnt[y] + L : cap[y]) + cnt[y] : 0;
+        t = ty > t ? ty : t;
+      }
+      S.need[++w_e] = t;
+      in_wave = 0;
+    }
+  }
+  while (w_next <= W) S.loc_pre[w_next++] = loc;
+  S.n_local = loc;
+  if (loc > kSchedMaxLocal) {
+    S.err = 1;
+    S.n_local = 0;
+    S.total = 0;
+    return;
+  }
+  // combine tasks of this XCD per slot, and the position of each slot
+  const int npos = loc + L;  // positions 0 .. npos - 1
+  int cb = 0;
+  if (!cb_pos_zeroed)
+    for (int i = 0; i <= npos; ++i) S.cb_pos[i] = 0;
+  int p_time = 0;  // first position whose work reaches need[s] (need grows with s)
+  for (int s = 0; s <= W; ++s) {
+    S.cb_pre[s] = cb;
+    const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
+    const int mine = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
+    cb += mine;
+    // position of the GEMM2 tiles of the last m-tile of a wave <= s + 1
+    // (slot s needs waves <= s - 1 of every XCD: two waves of slack for
+    // XCDs that run behind this one)
+    const int last = S.loc_pre[s + 2 < W ? s + 2 : W] - 1;
+    int at = last >= 0 ? last + L : 0;
+    // and not before this stream's own work reaches the time by which the
+    // slowest XCD ends the waves the slot waits for (an XCD carrying a hot
+    // expert ends them late; its partners run their later GEMM2 tiles first)
+    const int need = S.need[s < W ? s : W];
+    while (p_time < npos - 1 &&
+           2 * (p_time + 1 < loc ? p_time + 1 : loc) + (p_time + 1 - L > 0 ? p_time + 1 - L : 0) < need)
+      ++p_time;
+    at = at > p_time ? at : p_time;
+    S.cb_pos[at + 1] += mine;  // counted from position at + 1 on
+  }
+  S.cb_pre[W + 1] = cb;
+}
+
+
+// The build as the kernel splits it: strided ranges of the parallel steps,
+// the ranges taken in a shuffled order.
+static void strided_tables(WaveSchedule& S, const int32_t* offsets, const int32_t* ready_off, int E_local, int G,
+                           int BT, int NT1, int NT2, int cb_parts, int xcd, int lag, bool whole, int step,
+                           std::mt19937& rng) {
+  sched_init(S, E_local, G, NT1, NT2, xcd, lag);
+  S.mt_pre[0] = 0;
+  for (int e = 0; e < E_local; ++e) S.mt_pre[e + 1] = sched_mtiles(offsets, e, BT);
+  for (int e = 1; e <= E_local; ++e) S.mt_pre[e] += S.mt_pre[e - 1];
+  std::vector<int> order(step);
+  for (int b = 0; b < step; ++b) order[b] = b;
+  std::shuffle(order.begin(), order.end(), rng);
+  if (whole)
+    sched_deal_whole(S, E_local);
+  else
+    for (int b : order) sched_deal_single(S, E_local, b, step);
+  if (S.err) return;
+  for (int i = 0; i <= kSchedMaxLocal + kSchedMaxLag; ++i) S.cb_pos[i] = 0;
+  S.cb_pre[0] = 0;
+  std::shuffle(order.begin(), order.end(), rng);
+  for (int b : order) sched_place(S, ready_off, cb_parts, b, step, [](int32_t* p, int v) { *p += v; });
+  for (int s = 1; s <= S.W + 1; ++s) S.cb_pre[s] += S.cb_pre[s - 1];
+  sched_build_positions(S);
+}
+
+static void same_schedule(const WaveSchedule& a, const WaveSchedule& b, int E_local, const char* what, int x) {
+  if (a.err != b.err) fail(what, x, 0);
+  if (a.err) return;
+  bool ok = a.W == b.W && a.G == b.G && a.NT1 == b.NT1 && a.NT2 == b.NT2 && a.lag == b.lag &&
+            a.n_local == b.n_local && a.total == b.total;
+  for (int e = 0; ok && e <= E_local; ++e) ok = a.mt_pre[e] == b.mt_pre[e];
+  for (int j = 0; ok && j < a.n_local; ++j) ok = a.loc_mt[j] == b.loc_mt[j];
+  for (int w = 0; ok && w <= a.W; ++w) ok = a.loc_pre[w] == b.loc_pre[w] && a.need[w] == b.need[w];
+  for (int s = 0; ok && s <= a.W + 1; ++s) ok = a.cb_pre[s] == b.cb_pre[s];
+  for (int i = 0; ok && i <= a.n_local + a.lag; ++i) ok = a.cb_pos[i] == b.cb_pos[i] && a.pos[i] == b.pos[i];
+  if (!ok) fail(what, x, 1);
+}
+
 int main() {
   int E_local, G, BT, NT1, NT2, cb_parts, per_xcd, lag, whole;
   unsigned seed;
@@ -50,6 +197,21 @@ int main() {
     sched_build(S[x], offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag, whole != 0);
   for (int x = 0; x < kXcds; ++x)
     if (S[x].err) fail("schedule overflow", x, S[x].n_local);
+  {
+    // ---- 4. the sequential definition and the kernel's split of the build
+    static WaveSchedule R, P;
+    std::mt19937 rng(seed);
+    for (int x = 0; x < kXcds; ++x) {
+      reference_tables(R, offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag, whole != 0);
+      if (R.err == 0) sched_build_positions(R);
+      same_schedule(R, S[x], E_local, "schedule differs from the sequential definition", x);
+      for (int step : {1, 3, 64, 256}) {
+        strided_tables(P, offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag, whole != 0,
+                       step, rng);
+        same_schedule(R, P, E_local, "strided build differs", x);
+      }
+    }
+  }
   const int nmt = S[0].mt_pre[E_local];
   const int rw = sched_region_words(W);
 
