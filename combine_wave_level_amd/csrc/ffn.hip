@@ -202,6 +202,22 @@ __device__ __forceinline__ void local_signal(int32_t* p) {
   if (wave_uniform() == 0) wave0_atomic_add(p, 1);
 }
 
+// Spread schedules: the hand-off of an m-tile crosses XCDs.  Every tile's
+// stores reach the L2 before the XCD's counter moves; the XCD's last tile of
+// the m-tile writes the L2 back (agent-scope release) and adds the XCD's
+// tiles to the device-wide counter.
+__device__ __forceinline__ void spread_signal(int32_t* local, int32_t* all, int mine) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (wave_uniform() == 0) {
+    const int done = wave0_atomic_add(local, 1) + 1;
+    if (done == mine) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      wave0_atomic_add(all, mine);
+    }
+  }
+}
+
 // XCD-local consumer side: bounded poll of the counter (device-scope loads,
 // which skip the CU's L1; a workgroup-scope load may keep returning the L1
 // line it first read), then drop this CU's L1 lines so the following loads
@@ -224,6 +240,11 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   __shared__ int32_t s_ready[kSchedMaxWaves + 2];     // ready-slot starts in the ready list
   __shared__ int32_t s_ticket;
   const int xcd = uniform(xcc_id());
+  int32_t* ticket = A.ctr + sched_ticket_index(xcd);
+  // the first ticket is claimed now: the atomic's round trip overlaps the
+  // schedule build (which waits on no other workgroup)
+  int claim = 0;
+  if (wave_uniform() == 0) claim = claim_issue(ticket);
   // The schedule (the steps of sched_build, spread over the workgroup).
   // The dispatch tables go to LDS first, in parallel; the m-tile prefix,
   // the single-m-tile dealing, the combine placement and the prefix sums
@@ -273,14 +294,12 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   }
   const int total = uniform(S.total);
   const int NT1 = uniform(S.NT1);
+  const int spread = F::WHOLE_EXPERTS ? 0 : uniform(S.spread);
   const int rw = A.region_words;
-  int32_t* ticket = A.ctr + sched_ticket_index(xcd);
 
   // Every value that steers this loop is made wave-uniform explicitly (the
   // ticket and the decoded task come from LDS), so all waves run the same
   // iterations between barriers.
-  int claim = 0;
-  if (wave_uniform() == 0) claim = claim_issue(ticket);
   for (int tk = claim_finish(claim, &s_ticket); tk < total; tk = claim_finish(claim, &s_ticket)) {
     if (wave_uniform() == 0) claim = claim_issue(ticket);
     Task t = sched_decode(S, tk);
@@ -298,14 +317,28 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
       const int count = uniform(min(C1::BT, s_off[t.expert + 1] - row0));
       gemm1_tile<C1, GATED>(A.xb, A.w13 + static_cast<size_t>(t.expert) * (GATED ? 2 : 1) * A.I * A.d,
                             A.sorted_token, A.act, row0, count, t.nt, A.d, A.I, lds, A.xscale);
-      local_signal(A.ctr + sched_g1done_index(S, rw, t.loc));
+      if (spread)
+        spread_signal(A.ctr + sched_g1done_index(S, rw, t.loc), A.ctr + sched_g1all_index(S, rw, t.loc), NT1);
+      else
+        local_signal(A.ctr + sched_g1done_index(S, rw, t.loc));
     } else if (t.kind == kTaskGemm2) {
       // GEMM2 tile, once every GEMM1 tile of its m-tile is done (same XCD)
       const int row0 = uniform(s_off[t.expert] + (t.mt - S.mt_pre[t.expert]) * C2::BT);
       const int count = uniform(min(C2::BT, s_off[t.expert + 1] - row0));
-      local_wait(A.ctr + sched_g1done_index(S, rw, t.loc), NT1, A.timeout_ticks, A.err);
-      gemm2_tile<C2>(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count,
-                     t.nt, A.d, A.I, lds);
+      if constexpr (!F::WHOLE_EXPERTS) {
+        if (spread) {
+          // every XCD's GEMM1 tiles of the m-tile; the activations are read
+          // with device-coherent loads
+          local_wait(A.ctr + sched_g1all_index(S, rw, t.loc), uniform(S.NT1_all), A.timeout_ticks, A.err);
+          gemm2_tile<TokCoherent<C2>>(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count,
+                                      t.nt, A.d, A.I, lds);
+        }
+      }
+      if (!spread) {
+        local_wait(A.ctr + sched_g1done_index(S, rw, t.loc), NT1, A.timeout_ticks, A.err);
+        gemm2_tile<C2>(A.act, A.w2 + static_cast<size_t>(t.expert) * A.d * A.I, A.y, row0, count,
+                       t.nt, A.d, A.I, lds);
+      }
       wait_vmcnt<0>();
       __syncthreads();
       if (wave_uniform() == 0) {

@@ -26,7 +26,8 @@
 
 namespace moe {
 
-template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_, bool SKIPB_ = false, bool FP8T_ = false>
+template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_, bool SKIPB_ = false, bool FP8T_ = false,
+          bool TCOH_ = false>
 struct TileCfg {
   static constexpr int BW = BW_, BT = BT_, WR = WR_, WT = WT_, BK = BK_, NST = NST_;
   // SKIPB: skip the MFMA work of every 16-row token block past the valid
@@ -41,6 +42,9 @@ struct TileCfg {
   // values, bit for bit.
   static constexpr bool FP8T = FP8T_;
   static_assert(!FP8T || BK % 64 == 0, "fp8 token fragments hold 64 k");
+  // TCOH: the token rows are read with device-coherent loads (rows another
+  // XCD wrote during the same kernel and wrote back from its L2).
+  static constexpr bool TCOH = TCOH_;
   static constexpr int NW = WR * WT;            // wavefronts per workgroup
   static constexpr int NTHREADS = 64 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts per workgroup");
@@ -131,6 +135,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The same tile with device-coherent token-row loads.
+template <class C>
+using TokCoherent = TileCfg<C::BW, C::BT, C::WR, C::WT, C::BK, C::NST, C::SKIPB, C::FP8T, true>;
+
 // Issues this wave's direct-to-LDS loads of K step kt into stage kt % NST.
 template <class C>
 __device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, int KB,
@@ -151,6 +159,8 @@ __device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, i
       // row bytes kt * BK + 64 kc .. + 63: lane l takes 16 of them
       const char* row = reinterpret_cast<const char*>(trow.p[i]);
       lds_dma16(row + kt * C::BK + kc * 64 + (lane >> 4) * 16, st + (C::NFW + f) * 512);
+    } else if constexpr (C::TCOH) {
+      lds_dma16_coherent(trow.p[i] + kt * C::BK + kc * 32 + (lane >> 4) * 8, st + (C::NFW + f) * 512);
     } else {
       lds_dma16(trow.p[i] + kt * C::BK + kc * 32 + (lane >> 4) * 8, st + (C::NFW + f) * 512);
     }

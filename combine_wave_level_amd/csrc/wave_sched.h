@@ -18,6 +18,10 @@
 // ticket stream, so GEMM1 -> GEMM2 dependencies never leave an XCD's L2;
 // only the combine, which reads y rows of every XCD, crosses XCDs.
 //
+// When the m-tiles of a weight-streaming shape do not divide evenly over the
+// XCDs, each XCD instead takes an eighth of the output tiles of every m-tile
+// ("spread", see sched_spreads).
+//
 // Inside one XCD's stream the XCD's m-tiles are taken in wave order,
 // m_0 .. m_{n-1}, and the tickets run through positions i = 0 .. n+L-1:
 //   the GEMM1 tiles of m_i (i < n; their operand loads are the dispatch
@@ -52,6 +56,10 @@ constexpr int kCtrPad = 64;             // int32 words (256 B) between counters 
 
 struct WaveSchedule {
   int W, G, NT1, NT2, total, xcd, n_local, lag, err;
+  // spread: every m-tile's output tiles are split over the 8 XCDs (NT1 / NT2
+  // = this stream's share per m-tile, starting at nt1_base / nt2_base of the
+  // NT1_all / NT2_all tiles); else an m-tile lives on one XCD
+  int spread, nt1_base, nt2_base, NT1_all, NT2_all;
   int32_t mt_pre[kSchedMaxExperts + 1];  // first m-tile of each local expert
   int32_t loc_mt[kSchedMaxLocal];        // global m-tile of this XCD's j-th m-tile (ascending)
   int32_t loc_pre[kSchedMaxWaves + 1];   // this XCD's m-tiles in waves < w (loc_pre[W] = n_local)
@@ -118,8 +126,9 @@ __host__ __device__ inline void sched_init(WaveSchedule& S, int E_local, int G, 
   S.W = E_local / G;
   S.lag = lag < 1 ? 1 : (lag > kSchedMaxLag ? kSchedMaxLag : lag);
   S.G = G;
-  S.NT1 = NT1;
-  S.NT2 = NT2;
+  S.NT1 = S.NT1_all = NT1;
+  S.NT2 = S.NT2_all = NT2;
+  S.spread = S.nt1_base = S.nt2_base = 0;
   S.xcd = xcd;
   S.err = 0;
 }
@@ -224,12 +233,39 @@ __host__ __device__ inline int sched_single_local(int x, int i, int r) {
   return x < r ? (i == 0 ? x : r + x + kXcds * (i - 1)) : r + x + kXcds * i;
 }
 
+// Spreading: when the m-tiles do not divide evenly over the XCDs (r != 0)
+// and both GEMMs' output tiles do, every XCD takes an eighth of every
+// m-tile's GEMM1 and GEMM2 tiles instead, so that the weight-streaming
+// shapes load every XCD equally.  The GEMM1 -> GEMM2 hand-off of an m-tile
+// then crosses XCDs (a device-wide counter per m-tile; the kernel writes the
+// L2 back before publishing and reads the activations with device-coherent
+// loads).  Each stream holds every m-tile, in order.
+__host__ __device__ inline bool sched_spreads(int run, int NT1_all, int NT2_all) {
+  return run % kXcds != 0 && NT1_all % kXcds == 0 && NT2_all % kXcds == 0 && run <= kSchedMaxLocal;
+}
+
 // The thread's share (indices begin, begin + step, ...) of loc_mt, loc_pre
-// and need for single-m-tile dealing.  Needs the header and mt_pre; every
-// thread sets the same n_local and err.
+// and need for single-m-tile dealing (or spreading).  Needs the header and
+// mt_pre; every thread sets the same header fields, n_local and err.
 __host__ __device__ inline void sched_deal_single(WaveSchedule& S, int E_local, int begin, int step) {
   const int W = S.W, G = S.G, L = S.lag, xcd = S.xcd;
   const int run = S.mt_pre[E_local], r = run % kXcds;
+  if (sched_spreads(run, S.NT1_all, S.NT2_all)) {
+    const int nt1 = S.NT1_all / kXcds, nt2 = S.NT2_all / kXcds;
+    S.spread = 1;
+    S.NT1 = nt1;
+    S.NT2 = nt2;
+    S.nt1_base = xcd * nt1;
+    S.nt2_base = xcd * nt2;
+    S.n_local = run;
+    for (int i = begin; i < run; i += step) S.loc_mt[i] = i;
+    for (int w = begin; w <= W; w += step) {
+      const int M = S.mt_pre[w * G];
+      S.loc_pre[w] = M;
+      S.need[w] = w > 0 ? sched_work_of(M, run, L) : 0;
+    }
+    return;
+  }
   const int n = sched_cap(run, xcd);
   if (n > kSchedMaxLocal) {
     S.err = 1;
@@ -372,7 +408,7 @@ __host__ __device__ inline int sched_g2_of_wave(const WaveSchedule& S, int w) {
 }
 // GEMM2 tiles of wave w over all XCDs.
 __host__ __device__ inline int sched_g2_all(const WaveSchedule& S, int w) {
-  return (S.mt_pre[(w + 1) * S.G] - S.mt_pre[w * S.G]) * S.NT2;
+  return (S.mt_pre[(w + 1) * S.G] - S.mt_pre[w * S.G]) * S.NT2_all;
 }
 
 // Fills the m-tile fields of t for this XCD's m-tile j.
@@ -395,7 +431,7 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   if (i < n) {
     if (o < S.NT1) {
       t.kind = kTaskGemm1;
-      t.nt = o;
+      t.nt = S.nt1_base + o;
       sched_local_mtile(S, i, t);
       return t;
     }
@@ -404,7 +440,7 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   if (i >= L) {
     if (o < S.NT2) {
       t.kind = kTaskGemm2;
-      t.nt = o;
+      t.nt = S.nt2_base + o;
       sched_local_mtile(S, i - L, t);
       return t;
     }
@@ -427,12 +463,16 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
 //     region(x) + w                 GEMM2 tiles of wave w finished on XCD x
 //     region(x) + W + j             GEMM1 tiles finished of XCD x's m-tile j
 //   kXcds * (kCtrPad + region_words) + w   GEMM2 tiles of wave w finished, all XCDs
-// region_words >= W + kSchedMaxLocal, rounded up to kCtrPad.
+//   that + pad(W) + j               spread schedules: GEMM1 tiles of m-tile j
+//                                   finished, all XCDs
+// region_words >= W + kSchedMaxLocal, rounded up to kCtrPad (pad).
 __host__ __device__ inline int sched_region_words(int W) {
   return ((W + kSchedMaxLocal + kCtrPad - 1) / kCtrPad) * kCtrPad;
 }
+__host__ __device__ inline int sched_pad_words(int n) { return ((n + kCtrPad - 1) / kCtrPad) * kCtrPad; }
 __host__ __device__ inline size_t sched_counter_words(int W) {
-  return static_cast<size_t>(kXcds) * (kCtrPad + sched_region_words(W)) + W + kCtrPad;
+  return static_cast<size_t>(kXcds) * (kCtrPad + sched_region_words(W)) + sched_pad_words(W) + kSchedMaxLocal +
+         kCtrPad;
 }
 __host__ __device__ inline int sched_ticket_index(int xcd) { return xcd * kCtrPad; }
 __host__ __device__ inline int sched_g2local_index(const WaveSchedule& S, int rw, int w) {
@@ -443,6 +483,10 @@ __host__ __device__ inline int sched_g1done_index(const WaveSchedule& S, int rw,
 }
 __host__ __device__ inline int sched_g2all_index(const WaveSchedule& S, int rw, int w) {
   return kXcds * (kCtrPad + rw) + w;
+}
+// spread schedules: GEMM1 tiles of m-tile j finished, all XCDs
+__host__ __device__ inline int sched_g1all_index(const WaveSchedule& S, int rw, int j) {
+  return kXcds * (kCtrPad + rw) + sched_pad_words(S.W) + j;
 }
 
 }  // namespace moe

@@ -7,7 +7,8 @@
 // stdin: E_local G BT NT1 NT2 cb_parts threads_per_xcd seed lag whole_experts   (cb_parts 0: no combine)
 //        offsets[E_local + 1]  ready_off[W + 2]
 // Checks (exit status 0 = all hold):
-//   1. structure: every expert with at most an eighth of all m-tiles lives
+//   1. structure (spread schedules: every stream holds every m-tile and an
+//      eighth of its output tiles; otherwise:) every expert with at most an eighth of all m-tiles lives
 //      on one XCD, the XCDs' m-tile counts differ by at most the largest
 //      dealt chunk; over the 8 streams every GEMM1 / GEMM2 tile (m-tile x
 //      output tile) and every combine chunk has exactly one ticket; both
@@ -53,6 +54,9 @@ static void reference_tables(WaveSchedule& S, const int32_t* offsets, const int3
   S.G = G;
   S.NT1 = NT1;
   S.NT2 = NT2;
+  S.NT1_all = NT1;
+  S.NT2_all = NT2;
+  S.spread = S.nt1_base = S.nt2_base = 0;
   S.xcd = xcd;
   S.err = 0;
   int run = 0;
@@ -174,7 +178,8 @@ static void same_schedule(const WaveSchedule& a, const WaveSchedule& b, int E_lo
   if (a.err != b.err) fail(what, x, 0);
   if (a.err) return;
   bool ok = a.W == b.W && a.G == b.G && a.NT1 == b.NT1 && a.NT2 == b.NT2 && a.lag == b.lag &&
-            a.n_local == b.n_local && a.total == b.total;
+            a.n_local == b.n_local && a.total == b.total && a.spread == b.spread && a.nt1_base == b.nt1_base &&
+            a.nt2_base == b.nt2_base && a.NT1_all == b.NT1_all && a.NT2_all == b.NT2_all;
   for (int e = 0; ok && e <= E_local; ++e) ok = a.mt_pre[e] == b.mt_pre[e];
   for (int j = 0; ok && j < a.n_local; ++j) ok = a.loc_mt[j] == b.loc_mt[j];
   for (int w = 0; ok && w <= a.W; ++w) ok = a.loc_pre[w] == b.loc_pre[w] && a.need[w] == b.need[w];
@@ -202,8 +207,22 @@ int main() {
     static WaveSchedule R, P;
     std::mt19937 rng(seed);
     for (int x = 0; x < kXcds; ++x) {
-      reference_tables(R, offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag, whole != 0);
-      if (R.err == 0) sched_build_positions(R);
+      if (S[x].spread) {
+        // spreading replaces the deal: every m-tile in order, an eighth of
+        // its output tiles, the same work model on every XCD
+        const int run = S[x].mt_pre[E_local];
+        if (whole || !sched_spreads(run, NT1, NT2) || S[x].n_local != run || S[x].NT1 * kXcds != NT1 ||
+            S[x].NT2 * kXcds != NT2 || S[x].nt1_base != x * S[x].NT1 || S[x].nt2_base != x * S[x].NT2)
+          fail("spread header", x, run);
+        for (int j = 0; j < run; ++j)
+          if (S[x].loc_mt[j] != j) fail("spread local m-tiles", x, j);
+        R = S[x];
+      } else {
+        if (!whole && sched_spreads(S[x].mt_pre[E_local], NT1, NT2)) fail("should spread", x, 0);
+        reference_tables(R, offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag,
+                         whole != 0);
+        if (R.err == 0) sched_build_positions(R);
+      }
       same_schedule(R, S[x], E_local, "schedule differs from the sequential definition", x);
       for (int step : {1, 3, 64, 256}) {
         strided_tables(P, offsets.data(), ready_off.data(), E_local, G, BT, NT1, NT2, cb_parts, x, lag, whole != 0,
@@ -223,7 +242,10 @@ int main() {
     const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     cb_seen[s].assign(chunks, 0);
   }
-  {
+  const bool spread = S[0].spread != 0;
+  for (int x = 1; x < kXcds; ++x)
+    if ((S[x].spread != 0) != spread) fail("spread differs between XCDs", x);
+  if (!spread) {
     // owner XCD of every m-tile, from the local lists
     std::vector<int> owner(nmt, -1);
     for (int x = 0; x < kXcds; ++x)
@@ -298,15 +320,29 @@ int main() {
   for (int v : g2_owner) if (v < 0) fail("GEMM2 tile without ticket");
   for (int s = 0; s <= W; ++s)
     for (int c : cb_seen[s]) if (c != 1) fail("combine chunk not covered once", s);
-  for (int mt = 0; mt < nmt; ++mt)
-    for (int nt = 0; nt < NT2; ++nt) {
-      const size_t i2 = static_cast<size_t>(mt) * NT2 + nt;
-      for (int n1 = 0; n1 < NT1; ++n1) {
-        const size_t i1 = static_cast<size_t>(mt) * NT1 + n1;
-        if (g1_owner[i1] != g2_owner[i2]) fail("GEMM1 and GEMM2 of an m-tile on different XCDs", mt);
-        if (g1_ticket[i1] >= g2_ticket[i2]) fail("GEMM2 waits on a later ticket", mt, nt);
+  if (!spread) {
+    for (int mt = 0; mt < nmt; ++mt)
+      for (int nt = 0; nt < NT2; ++nt) {
+        const size_t i2 = static_cast<size_t>(mt) * NT2 + nt;
+        for (int n1 = 0; n1 < NT1; ++n1) {
+          const size_t i1 = static_cast<size_t>(mt) * NT1 + n1;
+          if (g1_owner[i1] != g2_owner[i2]) fail("GEMM1 and GEMM2 of an m-tile on different XCDs", mt);
+          if (g1_ticket[i1] >= g2_ticket[i2]) fail("GEMM2 waits on a later ticket", mt, nt);
+        }
+      }
+  } else {
+    // a GEMM2 tile waits on every stream's GEMM1 tiles of its m-tile: they
+    // sit at an earlier position (m-tile j at position j, its GEMM2 at
+    // j + L) in every stream, and GEMM1 tiles wait on nothing
+    for (int x = 0; x < kXcds; ++x) {
+      std::vector<int> g1_last(nmt, -1);
+      for (int tk = 0; tk < S[x].total; ++tk) {
+        const Task t = sched_decode(S[x], tk);
+        if (t.kind == kTaskGemm1) g1_last[t.mt] = tk;
+        if (t.kind == kTaskGemm2 && g1_last[t.mt] < 0) fail("spread GEMM2 before its stream's GEMM1 tiles", x, tk);
       }
     }
+  }
 
   // ---- 3. emulated run
   const size_t nctr = sched_counter_words(W);
@@ -329,9 +365,13 @@ int main() {
       const Task t = sched_decode(s, tk);
       if (rng() % 4 == 0) std::this_thread::sleep_for(std::chrono::microseconds(rng() % 200));
       if (t.kind == kTaskGemm1) {
-        ctr[sched_g1done_index(s, rw, t.loc)].fetch_add(1, std::memory_order_release);
+        const int done = ctr[sched_g1done_index(s, rw, t.loc)].fetch_add(1, std::memory_order_release) + 1;
+        if (s.spread && done == s.NT1) ctr[sched_g1all_index(s, rw, t.loc)].fetch_add(s.NT1);
       } else if (t.kind == kTaskGemm2) {
-        wait_geq(sched_g1done_index(s, rw, t.loc), s.NT1);
+        if (s.spread)
+          wait_geq(sched_g1all_index(s, rw, t.loc), s.NT1_all);
+        else
+          wait_geq(sched_g1done_index(s, rw, t.loc), s.NT1);
         const int done = ctr[sched_g2local_index(s, rw, t.wave)].fetch_add(1) + 1;
         if (done == sched_g2_of_wave(s, t.wave)) ctr[sched_g2all_index(s, rw, t.wave)].fetch_add(done);
       } else {
@@ -349,9 +389,12 @@ int main() {
   if (done_tasks.load() != total) fail("tasks done", done_tasks.load(), total);
   for (int x = 0; x < kXcds; ++x)
     for (int j = 0; j < S[x].n_local; ++j)
-      if (ctr[sched_g1done_index(S[x], rw, j)].load() != NT1) fail("g1done count", x, j);
+      if (ctr[sched_g1done_index(S[x], rw, j)].load() != S[x].NT1) fail("g1done count", x, j);
+  if (spread)
+    for (int j = 0; j < nmt; ++j)
+      if (ctr[sched_g1all_index(S[0], rw, j)].load() != NT1) fail("g1all count", j);
   for (int w = 0; w < W; ++w)
     if (ctr[sched_g2all_index(S[0], rw, w)].load() != sched_g2_all(S[0], w)) fail("g2 all count", w);
-  std::printf("OK total=%d W=%d mtiles=%d\n", total, W, nmt);
+  std::printf("OK total=%d W=%d mtiles=%d spread=%d\n", total, W, nmt, spread ? 1 : 0);
   return 0;
 }

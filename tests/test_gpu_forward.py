@@ -117,6 +117,21 @@ def test_persistent_equals_serial_and_standalone_combine():
     assert torch.equal(c, a["out"])
 
 
+@pytest.mark.parametrize("T", [8, 32, 100, 128])
+def test_small_batch_persistent_equals_serial_over_runs(T):
+    """Decode shapes: m-tiles that do not divide evenly over the 8 XCDs
+    make the persistent kernel spread every m-tile's output tiles over all
+    XCDs (the GEMM1 -> GEMM2 hand-off then crosses XCDs); its bits equal
+    the phase-by-phase path's on every one of several runs."""
+    L = Layer(inputs("decode", T=T))
+    b = L.forward(serial=True)
+    P = int(b["disp"].offsets[-1])
+    for _ in range(5):
+        a = L.forward(serial=False)
+        assert torch.equal(a["out"], b["out"])
+        assert torch.equal(a["y"][:P], b["y"][:P])
+
+
 @pytest.mark.parametrize("G", [1, 2, 8, 16])
 def test_output_bits_do_not_depend_on_wave_size(G):
     inp = inputs("mid", T=500)

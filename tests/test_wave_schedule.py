@@ -6,7 +6,11 @@ given dispatch tables: every m-tile is dealt once and the XCDs hold the
 same number of m-tiles to within one (whole-expert deals split an expert
 only when an XCD fills up), every GEMM1 / GEMM2 tile and combine chunk has
 exactly one ticket, every wait is on smaller tickets (no deadlock for any
-grid), and a multi-threaded emulated run reaches every wait target.
+grid), and a multi-threaded emulated run reaches every wait target.  The
+schedule also equals the plain sequential greedy's, and the kernel's split
+of the build over threads gives the same schedule.  Weight-streaming shapes
+whose m-tiles do not divide evenly over the XCDs spread every m-tile's
+output tiles over all of them instead.
 """
 import os
 import subprocess
@@ -128,3 +132,29 @@ def test_lumpy_experts_and_a_hot_one_stay_balanced(emu):
     counts[37] = 32 * BT
     ready = [int(r) for r in rng.integers(0, 900, size=17)]
     _run(emu, counts, ready, G=4, NT1=12, NT2=16, threads=2, seed=6, lag=64)
+
+
+@pytest.mark.parametrize("counts,spread", [
+    ([40, 0, 3, 17, 64, 0, 0, 9, 31, 2, 5, 64, 0, 1, 7, 12], True),     # 13 m-tiles: 13 % 8 != 0
+    ([1] * 8 + [0] * 8, False),                                         # 8 m-tiles: dealt one per XCD
+])
+def test_small_batch_spread_and_dealt(emu, counts, spread):
+    # decode-like: every expert at most one m-tile (BT = 128 rows)
+    rng = np.random.default_rng(21)
+    ready = [int(r) for r in rng.integers(0, 9, size=5)]
+    for threads in (1, 3):
+        out = _run(emu, counts, ready, G=4, NT1=32, NT2=56, cb_parts=14, threads=threads, seed=threads, lag=64,
+                   whole=0)
+        assert f"spread={int(spread)}" in out
+
+
+def test_spread_needs_tiles_divisible_by_xcds(emu):
+    # NT2 = 54 is not a multiple of 8: single m-tile dealing
+    rng = np.random.default_rng(22)
+    counts = list(rng.integers(0, 300, size=32))
+    ready = list(rng.integers(0, 20, size=9))
+    n_mt = sum((c + BT - 1) // BT for c in counts)
+    assert n_mt % 8 != 0
+    assert "spread=0" in _run(emu, counts, ready, G=4, NT1=32, NT2=54, cb_parts=3, threads=2, seed=3, lag=64, whole=0)
+    # the same tables with NT2 = 56 spread, also with a lag shorter than the m-tile count
+    assert "spread=1" in _run(emu, counts, ready, G=4, NT1=32, NT2=56, cb_parts=3, threads=2, seed=3, lag=5, whole=0)
