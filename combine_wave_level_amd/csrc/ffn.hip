@@ -515,17 +515,25 @@ hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8
   const uint16_t* w2 = reinterpret_cast<const uint16_t*>(pk + PL.w2);
   // the fp8 tiles take the bytes through the bf16 tiles' row pointers
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x8);
-  switch (pick_ffn_shape(p)) {
-    case FfnShape::Small:
-      return launch_ffn_cfg<FfnSmallF8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
+  const FfnShape shape = pick_ffn_shape(p);
+  if (shape == FfnShape::Small)
+    return launch_ffn_cfg<FfnSmallF8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
+                                      flags, ws, s);
+  if (shape == FfnShape::Small64)
+    return launch_ffn_cfg<FfnSmall64F8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
                                         out, flags, ws, s);
-    case FfnShape::Small64:
-      return launch_ffn_cfg<FfnSmall64F8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w,
-                                          y, out, flags, ws, s);
-    default:  // large and mid batches
-      return launch_ffn_cfg<FfnMidF8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
-                                      out, flags, ws, s);
-  }
+  // Large and mid batches are compute-bound: the rows are dequantized once
+  // on arrival (T x d bytes read, 2 T x d written, exact in bf16) and the
+  // bf16 tiles run on them; the conversions inside the GEMM1 tile would
+  // cost the 256 x 256 tile its register budget.
+  uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xbf);
+  hipError_t e = launch_dequant_fp8(p, x8, xscale, xs, s);
+  if (e != hipSuccess) return e;
+  if (shape == FfnShape::Large)
+    return launch_ffn_cfg<FfnLarge>(p, L, xs, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
+                                    flags, ws, s);
+  return launch_ffn_cfg<FfnMid>(p, L, xs, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out, flags,
+                                ws, s);
 }
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,

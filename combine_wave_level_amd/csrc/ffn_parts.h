@@ -49,18 +49,11 @@ struct FfnSmall64 {
   static constexpr bool WHOLE_EXPERTS = false;
 };
 
-// FP8 dispatch: the same shapes with the GEMM1 token operand in e4m3 (the
-// GEMM2 tiles are unchanged).  An fp8 token fragment holds 64 k, so the
-// GEMM1 K step is 64 (128 for the 32-row tile, whose two token blocks must
-// give each of its four wavefronts one load per step).  The 256 x 256 tile
-// with a 64-wide K step and the conversions does not fit the register file,
-// so large batches use the 128 x 256 tile (same bits).
-struct FfnMidF8 {
-  using G1 = TileCfg<128, 256, 2, 4, 64, 3, false, true>;
-  using G2 = FfnMid::G2;
-  static constexpr int NT = 512;
-  static constexpr bool WHOLE_EXPERTS = true;
-};
+// FP8 dispatch on the weight-streaming shapes: the GEMM1 token operand in
+// e4m3 (the GEMM2 tiles are unchanged).  An fp8 token fragment holds 64 k,
+// so the GEMM1 K step is 64 (128 for the 32-row tile, whose two token blocks
+// must give each of its four wavefronts one load per step).  (The large
+// shapes dequantize the rows first and run the bf16 tiles.)
 struct FfnSmallF8 {
   using G1 = TileCfg<128, 32, 4, 1, 128, 4, true, true>;
   using G2 = FfnSmall::G2;

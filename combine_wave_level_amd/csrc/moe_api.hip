@@ -53,7 +53,7 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.group_off = take(static_cast<size_t>(L.ngroups + 2) * 4);
   L.ready_list = take(static_cast<size_t>(p.T) * 4);
   L.logits = take(static_cast<size_t>(router_splits(p.d, p.E_global, p.x_dtype == MOE_BF16)) * p.T * p.E_global * 4);
-  L.xbf = take(p.x_dtype == MOE_F32 ? static_cast<size_t>(p.T) * p.d * 2 : 0);
+  L.xbf = take(static_cast<size_t>(p.T) * p.d * 2);
   L.act = take(static_cast<size_t>(L.P_max) * p.I * 2);
   L.sync = take(L.sync_words * 4);
   const bool xbf = p.x_dtype == MOE_BF16;

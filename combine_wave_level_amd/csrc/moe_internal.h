@@ -24,7 +24,8 @@ namespace moe {
 //   ready_list int32 [T]: tokens ordered by ready wave, ascending token id
 //              inside a wave
 //   logits     fp32 [splits][T][E_global] partial router logits (K split)
-//   xbf        bf16 [T][d] (only when x is fp32): x rounded for the FFN
+//   xbf        bf16 [T][d]: x rounded for the FFN (fp32 x), or the
+//              dequantized FP8 rows (FP8 dispatch on the large shapes)
 //   act        bf16 [P_max][I]: a = silu(h1) * h3, sorted-row order
 //   sync       int32 counters of the persistent expert-wave kernel
 //   bwd_dh     bf16 [P_max][2I]: dH1 | dH3 per routed row (backward)
@@ -147,6 +148,9 @@ hipError_t fill_zero(void* p, size_t n, hipStream_t s);
 // FP8 dispatch: per-token e4m3 codes and power-of-two scales of x, and the
 // expert FFN on them (same schedule and GEMM2, GEMM1 pulling the codes).
 hipError_t launch_quantize_fp8(const moe_problem_t& p, const void* x, uint8_t* x8, float* xscale, hipStream_t s);
+// The dequantized bf16 rows of the FP8 staging buffer (T x d).
+hipError_t launch_dequant_fp8(const moe_problem_t& p, const uint8_t* x8, const float* xscale, uint16_t* xb,
+                              hipStream_t s);
 hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8_t* x8, const float* xscale,
                           const void* packed, const int32_t* offsets, const int32_t* sorted_token,
                           const int32_t* pair_pos, const float* topk_w, void* y, void* out, uint32_t flags,

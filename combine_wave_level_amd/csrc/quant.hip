@@ -75,7 +75,33 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* __restric
   if (lane == 0) xscale[t] = ldexpf(1.0f, k);
 }
 
+// The dequantized rows as bf16: 8 codes per thread, each pair through the
+// same scaled conversion the fp8 GEMM tiles apply in registers (an e4m3
+// value times a power of two is exact in bf16).
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t* __restrict__ x8,
+                                                          const float* __restrict__ xscale, int d, size_t n8,
+                                                          uint16_t* __restrict__ xb) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const size_t t = i * 8 / d;
+  const float sc = xscale[t];
+  const u32x2 raw = *reinterpret_cast<const u32x2*>(x8 + i * 8);
+  const u32x4 o{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, sc, true)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, sc, true))};
+  st16(xb + i * 8, o);
+}
+
 }  // namespace
+
+hipError_t launch_dequant_fp8(const moe_problem_t& p, const uint8_t* x8, const float* xscale, uint16_t* xb,
+                              hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const size_t n8 = static_cast<size_t>(p.T) * p.d / 8;
+  dequant_fp8_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, s>>>(x8, xscale, p.d, n8, xb);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const moe_problem_t& p, const void* x, uint8_t* x8, float* xscale, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
