@@ -21,6 +21,10 @@
 //   GEMM1 -> GEMM2 of one m-tile stay on one XCD.  The producer waits for
 //   its stores to reach the L2 (vmcnt) and bumps a counter; the consumer
 //   polls it and drops its CU's L1 copies.  No L2 write-back or invalidate.
+//   Spread schedules (small batches whose m-tiles do not divide evenly over
+//   the XCDs) split every m-tile's tiles over all XCDs: there the XCD's last
+//   GEMM1 tile of the m-tile writes the L2 back and publishes device-wide,
+//   and GEMM2 reads the activations with device-coherent loads.
 //   GEMM2 -> combine crosses XCDs.  The last GEMM2 tile of a wave on an XCD
 //   writes that L2 back once (agent-scope release) and adds the XCD's tile
 //   count to a device-wide counter; combine tasks wait for the device-wide
