@@ -110,7 +110,7 @@ def _short(name: str) -> str:
 def _summarize(a) -> None:
     stats = _rows(a.stats)
     lines = [f"# {a.kernel}: {a.workload}, T={a.T}", "",
-             "Commands (from /tmp on the GPU host, TMPDIR=/tmp; REPO = repository root, OUT = $REPO/gpurun_out/prof):", ""]
+             "Commands (run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = the profiler output folder):", ""]
     for c in a.command:
         lines.append(f"    {c}")
     lines += ["", "Kernel durations (--kernel-trace --stats):", "",
@@ -156,7 +156,7 @@ def _stats(a) -> None:
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]) if "TotalDurationNs" in r
               else -float(r["AverageNs"]) * float(r["Calls"]))
     lines = [f"# {a.title}", "",
-             "Commands (from /tmp on the GPU host, TMPDIR=/tmp; REPO = repository root, OUT = $REPO/gpurun_out/prof):", ""]
+             "Commands (run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = the profiler output folder):", ""]
     for c in a.command:
         lines.append(f"    {c}")
     lines += ["", "Kernel durations (--kernel-trace --stats):", "",
