@@ -312,6 +312,24 @@ def main():
     ms, route_ms, disp_ms, ffn_ms = timed(args.steps, flags)
     moe.check_error(ws)
 
+    # host side of the C ABI (side metric): wall time to validate and enqueue
+    # one step's three calls, ctypes marshalling included, and of a call that
+    # validation rejects before any launch
+    n_host = max(10, args.steps)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for _ in range(n_host):
+        step()
+    h1 = time.perf_counter()
+    torch.cuda.synchronize()
+    bad = ctypes.c_void_p(out.data_ptr() + 8)  # misaligned out: rejected by validation
+    h2 = time.perf_counter()
+    for _ in range(1000):
+        L.moe_combine(pp, P(y), P(disp.pair_pos), P(w), bad, sp)
+    h3 = time.perf_counter()
+    host_us_per_call = (h1 - h0) / (3 * n_host) * 1e6
+    host_us_rejected = (h3 - h2) / 1000 * 1e6
+
     counts = disp.counts.cpu().numpy().astype(np.int64)
     P_local = int(counts.sum())
     flops_ffn = 6.0 * wl.d * wl.I * P_local
@@ -338,7 +356,8 @@ def main():
 
     extra = {"route_ms": round(route_ms, 4), "dispatch_ms": round(disp_ms, 4), "ffn_ms": round(ffn_ms, 4),
              "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-             "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched}
+             "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched,
+             "host_us_per_abi_call": round(host_us_per_call, 2), "host_us_rejected_call": round(host_us_rejected, 2)}
     if not args.serial:
         s_ms, _, _, s_ffn = timed(max(3, args.steps // 4), moe.MOE_FLAG_SERIAL)
         extra["serial_ms_per_step"] = round(s_ms, 4)
