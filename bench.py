@@ -222,7 +222,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X, no collectives)", file=sys.stderr)
+              "(one process drives one MI355X; there are no collectives)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
