@@ -47,19 +47,32 @@
 namespace moe {
 namespace {
 
-// The tile of the stage-1 products: the forward's mid GEMM1 tile (128 weight
-// rows x 256 routed rows, 8 wavefronts), for every problem shape.
+// The tiles of the recompute: the forward's GEMM1 tiles, 256 weight rows
+// (128 intermediate indices) when 2I allows, else 128 (the mid tile); 256
+// routed rows, 8 wavefronts.  The shape does not change the bits.
 using BwdCfg = FfnMid::G1;
+using BwdCfgL = FfnLarge::G1;
 
 // LDS row strides (bf16 elements) of the transposing stages: rows of 256 and
 // 64 values plus 8, so that 16-byte reads stay aligned and the 2-byte
 // transposed writes of one instruction spread over the banks.
 constexpr int kStageRow = BwdCfg::BT + 8;
+static_assert(BwdCfgL::BT == BwdCfg::BT, "one stage row length");
 constexpr int kGatherRow = 72;
-constexpr int kBwdNI = BwdCfg::BW / 2;  // intermediate indices per stage-1 tile
-constexpr size_t kBwdStageBytes = static_cast<size_t>(3 * kBwdNI) * kStageRow * 2;
-constexpr size_t kBwdLds = kBwdStageBytes > BwdCfg::LDS_BYTES ? kBwdStageBytes : BwdCfg::LDS_BYTES;
-static_assert(kBwdLds <= 160 * 1024, "stage-1 LDS fits a CU");
+
+// The recompute's epilogue stages (dH1 | dH3)^T and (w a)^T of the tile in
+// LDS for the transposed weight-gradient operands: in one pass when the
+// three fit, else (the 256-wide tile) dH first and w a in a second pass.
+template <class C>
+struct BwdDh {
+  static constexpr int NI = C::BW / 2;  // intermediate indices per tile
+  static constexpr size_t DH_BYTES = static_cast<size_t>(2 * NI) * kStageRow * 2;
+  static constexpr size_t AW_BYTES = static_cast<size_t>(NI) * kStageRow * 2;
+  static constexpr bool ONE_PASS = DH_BYTES + AW_BYTES <= 160 * 1024 - 8 * 1024;
+  static constexpr size_t STAGE = ONE_PASS ? DH_BYTES + AW_BYTES : DH_BYTES;
+  static constexpr size_t LDS = STAGE > C::LDS_BYTES ? STAGE : C::LDS_BYTES;
+  static_assert(LDS <= 160 * 1024 - 8 * 1024, "recompute LDS (with the static tables) fits a CU");
+};
 
 // seg[e] = first column of expert e in the transposed weight-gradient
 // operands: the routed rows of the experts before it, each rounded up to 64.
@@ -132,13 +145,14 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
 // Outputs: dH rows [P][2I] (dH1 | dH3) for the dx product and, when dht is
 // not null, (dH1 | dH3)^T fragments and (w a)^T rows for the weight
 // gradient, transposed through an LDS stage.
-__global__ __launch_bounds__(BwdCfg::NTHREADS) void bwd_dh_kernel(
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13, const float* __restrict__ g,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d, int I,
     int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht, uint16_t* __restrict__ awt,
     float* __restrict__ dwp) {
-  using C = BwdCfg;
+  using D = BwdDh<C>;
   static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
@@ -147,9 +161,10 @@ __global__ __launch_bounds__(BwdCfg::NTHREADS) void bwd_dh_kernel(
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   build_seg_prefix(offsets, E_local, seg);
   __syncthreads();
-  constexpr int NI = kBwdNI;
-  uint16_t* sdh = lds;                       // [2 NI][kStageRow]: (dH1 | dH3)^T of the tile
-  uint16_t* saw = lds + 2 * NI * kStageRow;  // [NI][kStageRow]: (w a)^T
+  constexpr int NI = D::NI;
+  uint16_t* sdh = lds;  // [2 NI][kStageRow]: (dH1 | dH3)^T of the tile
+  // [NI][kStageRow]: (w a)^T, after sdh, or over it in the second pass
+  uint16_t* saw = D::ONE_PASS ? lds + 2 * NI * kStageRow : lds;
   const bool trans = dht != nullptr;
   const int NT = 2 * I / C::BW, NQ = I / 16;
   const int total = uniform(mt_pre[E_local] * NT);
@@ -178,6 +193,9 @@ __global__ __launch_bounds__(BwdCfg::NTHREADS) void bwd_dh_kernel(
     TileAcc<C> acc;  // barriers inside order the wrow writes before the reads below
     tile_mma<C>(w13 + static_cast<size_t>(e) * 2 * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
                 d / C::BK, trow, lds, acc, count);
+    // second-pass staging keeps the tile's w a values as bf16 pairs (not the
+    // accumulators) across the read-out of the first stage
+    uint32_t vaw[D::ONE_PASS ? 1 : C::AT][D::ONE_PASS ? 1 : C::AW / 2][2];
     // wave (wr, wt): row blocks a (W1) and a + 1 (W3) of intermediate block
     // (wr * AW + a) / 2; lane l holds indices 4 (l / 16) + 0..3 of the block
     // for tile row (wt * AT + b) * 16 + l % 16.  Rows past count compute
@@ -222,8 +240,14 @@ __global__ __launch_bounds__(BwdCfg::NTHREADS) void bwd_dh_kernel(
           for (int r = 0; r < 4; ++r) {
             sdh[(il + r) * kStageRow + t] = f32_to_bf16(v1[r]);
             sdh[(NI + il + r) * kStageRow + t] = f32_to_bf16(v3[r]);
-            saw[(il + r) * kStageRow + t] = f32_to_bf16(va[r]);
+            if constexpr (D::ONE_PASS) saw[(il + r) * kStageRow + t] = f32_to_bf16(va[r]);
           }
+        }
+        if constexpr (!D::ONE_PASS) {
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            vaw[b][a / 2][r] = static_cast<uint32_t>(f32_to_bf16(va[2 * r])) |
+                               (static_cast<uint32_t>(f32_to_bf16(va[2 * r + 1])) << 16);
         }
       }
     }
@@ -242,6 +266,22 @@ __global__ __launch_bounds__(BwdCfg::NTHREADS) void bwd_dh_kernel(
         const int n = nl < NI ? nt * NI + nl : I + nt * NI + (nl - NI);
         st16(dht + frag_offset(n / 16, (k0 + kl) / 32, KB) + ((kl % 32) / 8 * 16 + n % 16) * 8,
              ld16(sdh + nl * kStageRow + kl));
+      }
+      if constexpr (!D::ONE_PASS) {
+        // second pass: the kept w a values, staged over the read-out sdh
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < C::AT; ++b) {
+          const int t = (wt * C::AT + b) * 16 + (lane & 15);
+#pragma unroll
+          for (int a = 0; a < C::AW; a += 2) {
+            const int il = ((wr * C::AW + a) / 2) * 16 + 4 * (lane / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              saw[(il + r) * kStageRow + t] = static_cast<uint16_t>(vaw[b][a / 2][r / 2] >> (16 * (r % 2)));
+          }
+        }
+        __syncthreads();
       }
       // (w a)^T rows: NI indices x rows_pad / 8 chunks of 8 columns
       const int ng = rows_pad / 8;
@@ -783,6 +823,22 @@ hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const uint16_
   return hipGetLastError();
 }
 
+// The recompute with the gradient epilogue on tile C.
+template <class C>
+hipError_t launch_dh(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, const uint16_t* xb,
+                     const uint16_t* w13, const float* g, uint16_t* dh, uint16_t* dht, uint16_t* awt, float* dwp,
+                     int cus, hipStream_t s) {
+  constexpr size_t lds = BwdDh<C>::LDS;
+  int per_cu = 0;
+  hipError_t e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel<C>, C::NTHREADS, lds)) != hipSuccess)
+    return e;
+  bwd_dh_kernel<C><<<max(1, per_cu) * cus, C::NTHREADS, lds, s>>>(xb, w13, g, a.offsets, a.sorted_token, a.pair_pos,
+                                                                  a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh,
+                                                                  dht, awt, dwp);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, char* ws,
@@ -830,14 +886,11 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
   else
     e = launch_g<BwdCfgG>(p, a, w2b, g, cus, s);
   if (e != hipSuccess) return e;
-  int per_cu = 0;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel, BwdCfg::NTHREADS, kBwdLds)) !=
-      hipSuccess)
-    return e;
-  bwd_dh_kernel<<<max(1, per_cu) * cus, BwdCfg::NTHREADS, kBwdLds, s>>>(
-      xb, w13, g, a.offsets, a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh, dht,
-      awt, dwp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((2 * p.I) % BwdCfgL::BW == 0)
+    e = launch_dh<BwdCfgL>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
+  else
+    e = launch_dh<BwdCfg>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
+  if (e != hipSuccess) return e;
   if (want_data) {
     const PackedBwdLayout BL = packed_bwd_layout(p);
     const char* pb = static_cast<const char*>(a.packed_bwd);
