@@ -289,6 +289,8 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    step_stats = {}
+
     def timed(nsteps, fl):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
         torch.cuda.synchronize()
@@ -300,6 +302,8 @@ def main():
         t1.record(stream)
         torch.cuda.synchronize()
         total = t0.elapsed_time(t1)
+        per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
+        step_stats.update(median=per_step[len(per_step) // 2], lo=per_step[0], hi=per_step[-1])
         route = sum(e[0].elapsed_time(e[1]) for e in evs) / nsteps
         disp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / nsteps
         ffn = sum(e[2].elapsed_time(e[3]) for e in evs) / nsteps
@@ -311,6 +315,7 @@ def main():
     moe.check_error(ws)
     ms, route_ms, disp_ms, ffn_ms = timed(args.steps, flags)
     moe.check_error(ws)
+    step_ms = {k: round(v, 4) for k, v in step_stats.items()}
 
     # host side of the C ABI (side metric): wall time to validate and enqueue
     # one step's three calls, ctypes marshalling included, and of a call that
@@ -357,7 +362,8 @@ def main():
     extra = {"route_ms": round(route_ms, 4), "dispatch_ms": round(disp_ms, 4), "ffn_ms": round(ffn_ms, 4),
              "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
              "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched,
-             "host_us_per_abi_call": round(host_us_per_call, 2), "host_us_rejected_call": round(host_us_rejected, 2)}
+             "host_us_per_abi_call": round(host_us_per_call, 2), "host_us_rejected_call": round(host_us_rejected, 2),
+             "step_ms_median": step_ms["median"], "step_ms_min": step_ms["lo"], "step_ms_max": step_ms["hi"]}
     if not args.serial:
         s_ms, _, _, s_ffn = timed(max(3, args.steps // 4), moe.MOE_FLAG_SERIAL)
         extra["serial_ms_per_step"] = round(s_ms, 4)
