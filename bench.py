@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="mid")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -289,33 +289,60 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    step_stats = {}
-
     def timed(nsteps, fl):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
-        torch.cuda.synchronize()
+        """Wall time of nsteps whole steps between one event pair on the
+        launch stream: nothing else is recorded inside the region."""
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0.record(stream)
-        for i in range(nsteps):
-            step(evs[i], fl)
+        for _ in range(nsteps):
+            step(None, fl)
         t1.record(stream)
         torch.cuda.synchronize()
-        total = t0.elapsed_time(t1)
+        return t0.elapsed_time(t1) / nsteps
+
+    def ffn_launches(nsteps, fl):
+        """Average duration of the expert-FFN call (the dominant kernel),
+        nsteps launches back to back on the last step's routing, between one
+        event pair on the launch stream."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(nsteps):
+            check(L.moe_expert_ffn_waved(pp, P(x), P(packed), P(disp.offsets), P(disp.sorted_token),
+                                         P(disp.pair_pos), P(w), P(disp.ready_wave), P(y), P(out), fl,
+                                         P(ws), nws, sp), "ffn")
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / nsteps
+
+    def instrumented(nsteps, fl):
+        """Per-step breakdown from a separate pass with events between the
+        calls (the events themselves add to these steps)."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+        torch.cuda.synchronize()
+        for i in range(nsteps):
+            step(evs[i], fl)
+        torch.cuda.synchronize()
         per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
-        step_stats.update(median=per_step[len(per_step) // 2], lo=per_step[0], hi=per_step[-1])
-        route = sum(e[0].elapsed_time(e[1]) for e in evs) / nsteps
-        disp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / nsteps
-        ffn = sum(e[2].elapsed_time(e[3]) for e in evs) / nsteps
-        return total / nsteps, route, disp_ms, ffn
+        return {"route_ms": sum(e[0].elapsed_time(e[1]) for e in evs) / nsteps,
+                "dispatch_ms": sum(e[1].elapsed_time(e[2]) for e in evs) / nsteps,
+                "ffn_ms": sum(e[2].elapsed_time(e[3]) for e in evs) / nsteps,
+                "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
+                "step_ms_max": per_step[-1]}
 
     for _ in range(max(0, args.warmup)):
         step()
     torch.cuda.synchronize()
     moe.check_error(ws)
-    ms, route_ms, disp_ms, ffn_ms = timed(args.steps, flags)
+    ms = timed(args.steps, flags)
     moe.check_error(ws)
-    step_ms = {k: round(v, 4) for k, v in step_stats.items()}
+    ffn_ms = ffn_launches(args.steps, flags)
+    moe.check_error(ws)
+    inst = {k: round(v, 4) for k, v in instrumented(args.steps, flags).items()}
+    moe.check_error(ws)
 
     # host side of the C ABI (side metric): wall time to validate and enqueue
     # one step's three calls, ctypes marshalling included, and of a call that
@@ -359,14 +386,15 @@ def main():
         os.path.join(ROOT, "profiles", f"traffic_ffn_waved_kernel_{wl.name}_T{T}.json"), wl.name, T)
     roof["traffic"] = trec["traffic_bytes"] if trec else None
 
-    extra = {"route_ms": round(route_ms, 4), "dispatch_ms": round(disp_ms, 4), "ffn_ms": round(ffn_ms, 4),
+    extra = {"ffn_ms": round(ffn_ms, 4),
              "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
              "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched,
              "host_us_per_abi_call": round(host_us_per_call, 2), "host_us_rejected_call": round(host_us_rejected, 2),
-             "step_ms_median": step_ms["median"], "step_ms_min": step_ms["lo"], "step_ms_max": step_ms["hi"]}
+             "instrumented_pass": inst}
     if not args.serial:
-        s_ms, _, _, s_ffn = timed(max(3, args.steps // 4), moe.MOE_FLAG_SERIAL)
-        extra["serial_ms_per_step"] = round(s_ms, 4)
+        n_s = max(3, args.steps // 4)
+        extra["serial_ms_per_step"] = round(timed(n_s, moe.MOE_FLAG_SERIAL), 4)
+        s_ffn = ffn_launches(n_s, moe.MOE_FLAG_SERIAL)
         extra["serial_ffn_ms"] = round(s_ffn, 4)
         extra["overlap_speedup_ffn"] = round(s_ffn / ffn_ms, 3)
 
