@@ -57,9 +57,12 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const unsigned long long* __restrict__ masks, int nchunks, int ngroups, int E_local,
     int32_t* __restrict__ bases, int32_t* __restrict__ group_off, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ err) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ err, int32_t* __restrict__ ctr, int n_ctr) {
   extern __shared__ int32_t stot[];  // [ngroups]
   if (threadIdx.x == 0) *err = 0;  // a new layer call starts with a clean error word
+  // the expert-wave kernel's counters start the layer call at zero (that
+  // kernel clears them again when it ends, for back-to-back FFN calls)
+  for (int i = threadIdx.x; i < n_ctr; i += blockDim.x) ctr[i] = 0;
   // one wavefront per group: lanes take 64 chunks at a time, an exclusive
   // prefix sum of their popcounts (shuffles) gives the chunks' bases, and
   // the running total carries over to the next 64 chunks
@@ -145,7 +148,8 @@ hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int3
   }
   dispatch_scan_kernel<<<1, 1024, L.ngroups * sizeof(int32_t), s>>>(
       masks, L.nchunks, L.ngroups, p.E_local, bases, group_off, counts, offsets,
-      reinterpret_cast<int32_t*>(ws + L.err));
+      reinterpret_cast<int32_t*>(ws + L.err), reinterpret_cast<int32_t*>(ws + L.sync),
+      static_cast<int>(L.sync_words));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.T == 0) return e;
   dispatch_scatter_kernel<<<(p.T + 255) / 256, 256, 0, s>>>(

@@ -130,8 +130,9 @@ struct WaveArgs {
   uint16_t* act;
   uint16_t* y;
   void* out;                 // nullptr: no fused combine
-  int32_t* ctr;              // counters, layout in wave_sched.h
+  int32_t* ctr;              // counters, layout in wave_sched.h, then the exit count
   int32_t* err;
+  int ctr_words;             // counter words including the exit count (the last one)
   int E_local, G, W, d, I, k;
   int region_words;
   int cb_parts;              // column parts of a combine task
@@ -234,7 +235,7 @@ __device__ __forceinline__ void local_wait(const int32_t* p, int target, long lo
 }
 
 template <class F, bool OUT_BF16, bool GATED>
-__global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
+__device__ __forceinline__ void ffn_waved_run(const WaveArgs& A) {
   using C1 = typename F::G1;
   using C2 = typename F::G2;
   static_assert(C1::BT == C2::BT, "GEMM1 and GEMM2 share the m-tiles");
@@ -372,6 +373,29 @@ __global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
   }
 }
 
+// The kernel: the task loop, then the exit count.  The last workgroup to
+// leave clears every counter (the exit count included), so the next launch
+// on this workspace starts from zero without a fill of its own.  Every
+// workgroup makes its counter atomics complete (agent-scope release by every
+// thread) before it is counted, so no counter is touched after the clear.
+template <class F, bool OUT_BF16, bool GATED>
+__global__ __launch_bounds__(F::NT) void ffn_waved_kernel(WaveArgs A) {
+  __shared__ int32_t s_last;
+  ffn_waved_run<F, OUT_BF16, GATED>(A);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (wave_uniform() == 0) {
+    const int prev = wave0_atomic_add(A.ctr + A.ctr_words - 1, 1);
+    if (lane_id() == 0) s_last = prev == static_cast<int>(gridDim.x) - 1;
+  }
+  __syncthreads();
+  if (s_last) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int i = threadIdx.x; i < A.ctr_words; i += F::NT)
+      __hip_atomic_store(A.ctr + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Tile shape of the expert GEMMs.  The shape never changes result bits.
 //   small batches (mean routed rows per expert under 96, assuming uniform
 //   routing): token tiles of 32 rows for T <= 32 (all rows of an expert: a
@@ -424,8 +448,9 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
     if (out && p.T > 0) return launch_combine(p, y, pair_pos, topk_w, out, s);
     return hipSuccess;
   }
+  // the counters are zero: moe_dispatch clears them and every launch of the
+  // kernel clears them again as it ends
   int32_t* ctr = reinterpret_cast<int32_t*>(ws + L.sync);
-  if ((e = fill_zero(ctr, L.sync_words, s)) != hipSuccess) return e;
   WaveArgs A;
   A.xb = xb;
   A.xscale = xscale;
@@ -449,6 +474,7 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   A.I = p.I;
   A.k = p.k;
   A.region_words = L.ctr_region_words;
+  A.ctr_words = static_cast<int>(L.sync_words);
   A.cb_parts = combine_parts(p.T, p.d);
   int wall_khz = 0;
   if ((e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;

@@ -132,6 +132,33 @@ def test_small_batch_persistent_equals_serial_over_runs(T):
         assert torch.equal(a["y"][:P], b["y"][:P])
 
 
+@pytest.mark.parametrize("name,T", [("mid", 777), ("decode", 1), ("decode", 128)])
+def test_persistent_back_to_back_on_one_dispatch(name, T):
+    """The persistent kernel's tickets and hand-off counters need no fill of
+    their own: moe_dispatch clears them and every launch clears them as it
+    ends.  On a workspace poisoned before the dispatch, repeated persistent
+    calls on one dispatch (outputs poisoned before each call) all give the
+    phase-by-phase path's bits."""
+    L = Layer(inputs(name, T=T))
+    L.ws.fill_(0xA5)
+    idx, w, _ = moe.route(L.p, L.x, L.packed, L.ws, bias=L.bias)
+    disp = moe.dispatch(L.p, idx, L.ws)
+    y_ref, out_ref = moe.ffn_waved(L.p, L.x, L.packed, disp, w, L.ws, serial=True)
+    torch.cuda.synchronize()
+    moe.check_error(L.ws)
+    P = int(disp.offsets[-1])
+    y = torch.empty_like(y_ref)
+    out = torch.empty_like(out_ref)
+    for _ in range(4):
+        y.view(torch.int16).fill_(0x7F7F)
+        out.view(torch.int16).fill_(0x7F7F)
+        moe.ffn_waved(L.p, L.x, L.packed, disp, w, L.ws, y=y, out=out)
+        torch.cuda.synchronize()
+        moe.check_error(L.ws)
+        assert torch.equal(out, out_ref)
+        assert torch.equal(y[:P], y_ref[:P])
+
+
 @pytest.mark.parametrize("G", [1, 2, 8, 16])
 def test_output_bits_do_not_depend_on_wave_size(G):
     inp = inputs("mid", T=500)
