@@ -279,6 +279,7 @@ __device__ __forceinline__ void ffn_waved_run(const WaveArgs& A) {
   }
   __syncthreads();
   if (uniform(S.err) == 0) {
+    sched_groups(S, threadIdx.x, F::NT);
     sched_place(S, s_ready, A.out != nullptr ? A.cb_parts : 0, threadIdx.x, F::NT,
                 [](int32_t* p, int v) { atomicAdd(p, v); });
     __syncthreads();

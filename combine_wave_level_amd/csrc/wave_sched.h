@@ -31,6 +31,15 @@
 //   position is i (tokens whose last local wave is s-1; slot 0 = tokens with
 //   no local pick): the position of the GEMM2 tiles of the XCD's last m-tile
 //   of a wave <= s + 1.
+// The GEMM2 tiles of consecutive m-tiles of one expert are dealt in groups
+// of up to min(kSchedGroup, L) m-tiles (a group never crosses an expert, so
+// never a wave, and starts at a multiple of that size or at the expert's
+// first local m-tile): the group's tiles fill the positions of its m-tiles
+// in output-tile-major order, (m_a, n), (m_a+1, n), ..., (m_a, n+1), ...,
+// so an XCD runs every m-tile's use of a W2 tile at about the same time and
+// the tile is read from HBM once into the L2.  A group of g <= L m-tiles
+// starting at m_a has its GEMM2 tiles at positions >= a + L > a + g - 1,
+// after the GEMM1 tiles of all its m-tiles.
 // GEMM2 of an m-tile thus trails its GEMM1 by L m-tiles (the kernel uses a
 // long lag: an XCD's GEMM1 tiles mostly run before its GEMM2 tiles, which
 // keeps the two operand sets from sharing the XCD's L2 at the same time).  A GEMM2 tile waits for its m-tile's
@@ -53,6 +62,7 @@ constexpr int kSchedMaxLocal = 512;     // m-tiles of one XCD
 constexpr int kSchedMaxLag = 64;       // GEMM2 lag, in m-tiles
 constexpr int kCombineTokens = 8;       // tokens per combine task
 constexpr int kCtrPad = 64;             // int32 words (256 B) between counters of different XCDs
+constexpr int kSchedGroup = 8;          // m-tiles whose GEMM2 tiles interleave (at most the lag)
 
 struct WaveSchedule {
   int W, G, NT1, NT2, total, xcd, n_local, lag, err;
@@ -62,6 +72,7 @@ struct WaveSchedule {
   int spread, nt1_base, nt2_base, NT1_all, NT2_all;
   int32_t mt_pre[kSchedMaxExperts + 1];  // first m-tile of each local expert
   int32_t loc_mt[kSchedMaxLocal];        // global m-tile of this XCD's j-th m-tile (ascending)
+  int32_t grp[kSchedMaxLocal];           // GEMM2 group of local m-tile j: first | size << 16
   int32_t loc_pre[kSchedMaxWaves + 1];   // this XCD's m-tiles in waves < w (loc_pre[W] = n_local)
   int32_t cb_pre[kSchedMaxWaves + 2];    // this XCD's combine tasks of slots < s
   int32_t need[kSchedMaxWaves + 1];      // work units by which every XCD ends waves < s (see sched_build)
@@ -290,6 +301,26 @@ __host__ __device__ inline void sched_deal_single(WaveSchedule& S, int E_local, 
   }
 }
 
+// GEMM2 groups of local m-tiles begin, begin + step, ... (needs the dealt
+// tables: loc_mt, mt_pre, n_local).  Local m-tiles j - 1 and j share a group
+// when they are consecutive m-tiles of one expert and j is not a multiple
+// of the group size.
+__host__ __device__ inline bool sched_same_run(const WaveSchedule& S, int j) {
+  if (j <= 0 || S.loc_mt[j] != S.loc_mt[j - 1] + 1) return false;
+  const int E = S.W * S.G;
+  return sched_expert_of(S.mt_pre, 0, E, S.loc_mt[j]) == sched_expert_of(S.mt_pre, 0, E, S.loc_mt[j - 1]);
+}
+__host__ __device__ inline void sched_groups(WaveSchedule& S, int begin, int step) {
+  const int C = kSchedGroup < S.lag ? kSchedGroup : S.lag, n = S.n_local;
+  for (int j = begin; j < n; j += step) {
+    const int a0 = (j / C) * C, a1 = a0 + C < n ? a0 + C : n;
+    int c0 = j, c1 = j + 1;
+    while (c0 > a0 && sched_same_run(S, c0)) --c0;
+    while (c1 < a1 && sched_same_run(S, c1)) ++c1;
+    S.grp[j] = c0 | ((c1 - c0) << 16);
+  }
+}
+
 // Work of this XCD's stream through position q: 2 units per m-tile of
 // GEMM1 (q <= n of them), 1 per m-tile of GEMM2 (positions >= L).
 __host__ __device__ inline int sched_stream_work(int q, int n, int L) {
@@ -351,6 +382,7 @@ __host__ __device__ inline void sched_build_tables(WaveSchedule& S, const int32_
   else
     sched_deal_single(S, E_local, 0, 1);
   if (S.err) return;
+  sched_groups(S, 0, 1);
   for (int i = 0; i <= S.n_local + S.lag; ++i) S.cb_pos[i] = 0;
   sched_place(S, ready_off, cb_parts, 0, 1, [](int32_t* p, int v) { *p += v; });
   S.cb_pre[0] = 0;
@@ -439,9 +471,12 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   }
   if (i >= L) {
     if (o < S.NT2) {
+      // position i's share of its m-tile's group, output-tile-major
+      const int j = i - L, c0 = S.grp[j] & 0xffff, cs = S.grp[j] >> 16;
+      const int g = (j - c0) * S.NT2 + o;
       t.kind = kTaskGemm2;
-      t.nt = S.nt2_base + o;
-      sched_local_mtile(S, i - L, t);
+      t.nt = S.nt2_base + g / cs;
+      sched_local_mtile(S, c0 + g % cs, t);
       return t;
     }
     o -= S.NT2;

@@ -119,6 +119,26 @@ static void reference_tables(WaveSchedule& S, const int32_t* offsets, const int3
     S.total = 0;
     return;
   }
+  // GEMM2 groups, in one pass: a group ends at an expert change, a break in
+  // the global m-tile numbering, or when it holds min(kSchedGroup, L) m-tiles
+  // counted from a multiple of that size
+  {
+    const int C = kSchedGroup < L ? kSchedGroup : L;
+    auto expert_of = [&](int mt) {
+      int e = 0;
+      while (S.mt_pre[e + 1] <= mt) ++e;
+      return e;
+    };
+    int start = 0;
+    for (int j = 0; j <= loc; ++j) {
+      const bool cut = j == loc || j % C == 0 || S.loc_mt[j] != S.loc_mt[j - 1] + 1 ||
+                       expert_of(S.loc_mt[j]) != expert_of(S.loc_mt[j - 1]);
+      if (cut && j > start) {
+        for (int q = start; q < j; ++q) S.grp[q] = start | ((j - start) << 16);
+        start = j;
+      }
+    }
+  }
   // combine tasks of this XCD per slot, and the position of each slot
   const int npos = loc + L;  // positions 0 .. npos - 1
   int cb = 0;
@@ -166,6 +186,8 @@ static void strided_tables(WaveSchedule& S, const int32_t* offsets, const int32_
   else
     for (int b : order) sched_deal_single(S, E_local, b, step);
   if (S.err) return;
+  std::shuffle(order.begin(), order.end(), rng);
+  for (int b : order) sched_groups(S, b, step);
   for (int i = 0; i <= kSchedMaxLocal + kSchedMaxLag; ++i) S.cb_pos[i] = 0;
   S.cb_pre[0] = 0;
   std::shuffle(order.begin(), order.end(), rng);
@@ -181,7 +203,7 @@ static void same_schedule(const WaveSchedule& a, const WaveSchedule& b, int E_lo
             a.n_local == b.n_local && a.total == b.total && a.spread == b.spread && a.nt1_base == b.nt1_base &&
             a.nt2_base == b.nt2_base && a.NT1_all == b.NT1_all && a.NT2_all == b.NT2_all;
   for (int e = 0; ok && e <= E_local; ++e) ok = a.mt_pre[e] == b.mt_pre[e];
-  for (int j = 0; ok && j < a.n_local; ++j) ok = a.loc_mt[j] == b.loc_mt[j];
+  for (int j = 0; ok && j < a.n_local; ++j) ok = a.loc_mt[j] == b.loc_mt[j] && a.grp[j] == b.grp[j];
   for (int w = 0; ok && w <= a.W; ++w) ok = a.loc_pre[w] == b.loc_pre[w] && a.need[w] == b.need[w];
   for (int s = 0; ok && s <= a.W + 1; ++s) ok = a.cb_pre[s] == b.cb_pre[s];
   for (int i = 0; ok && i <= a.n_local + a.lag; ++i) ok = a.cb_pos[i] == b.cb_pos[i] && a.pos[i] == b.pos[i];
