@@ -22,7 +22,7 @@ namespace moe {
 //   small : a handful of rows per expert (weight streaming, HBM bound):
 //           token tiles of 32 or 64 rows (empty 16-row blocks skipped) and
 //           6 to 7 LDS stages, so that each workgroup keeps 80 to 96 KiB of
-//           weights in flight
+//           weights in flight, loaded with the non-temporal hint
 // GEMM1 and GEMM2 of one shape use the same workgroup size (NT threads).
 struct FfnLarge {
   using G1 = TileCfg<256, 256, 2, 4, 32, 4>;
@@ -37,14 +37,14 @@ struct FfnMid {
   static constexpr bool WHOLE_EXPERTS = true;
 };
 struct FfnSmall {
-  using G1 = TileCfg<128, 32, 4, 1, 64, 7, true>;
-  using G2 = TileCfg<128, 32, 4, 1, 64, 7, true>;
+  using G1 = TileCfg<128, 32, 4, 1, 64, 7, true, false, false, true>;
+  using G2 = TileCfg<128, 32, 4, 1, 64, 7, true, false, false, true>;
   static constexpr int NT = 256;
   static constexpr bool WHOLE_EXPERTS = false;  // deal single m-tiles: balance
 };
 struct FfnSmall64 {
-  using G1 = TileCfg<128, 64, 4, 1, 64, 6, true>;
-  using G2 = TileCfg<128, 64, 4, 1, 64, 6, true>;
+  using G1 = TileCfg<128, 64, 4, 1, 64, 6, true, false, false, true>;
+  using G2 = TileCfg<128, 64, 4, 1, 64, 6, true, false, false, true>;
   static constexpr int NT = 256;
   static constexpr bool WHOLE_EXPERTS = false;
 };
@@ -55,13 +55,13 @@ struct FfnSmall64 {
 // must give each of its four wavefronts one load per step).  (The large
 // shapes dequantize the rows first and run the bf16 tiles.)
 struct FfnSmallF8 {
-  using G1 = TileCfg<128, 32, 4, 1, 128, 4, true, true>;
+  using G1 = TileCfg<128, 32, 4, 1, 128, 4, true, true, false, true>;
   using G2 = FfnSmall::G2;
   static constexpr int NT = 256;
   static constexpr bool WHOLE_EXPERTS = false;
 };
 struct FfnSmall64F8 {
-  using G1 = TileCfg<128, 64, 4, 1, 64, 6, true, true>;
+  using G1 = TileCfg<128, 64, 4, 1, 64, 6, true, true, false, true>;
   using G2 = FfnSmall64::G2;
   static constexpr int NT = 256;
   static constexpr bool WHOLE_EXPERTS = false;

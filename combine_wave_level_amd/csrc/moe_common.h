@@ -123,6 +123,11 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
+// The same load with the non-temporal hint (cache policy nt): data read
+// once, which the caches should not keep in preference to reused lines.
+__device__ __forceinline__ void lds_dma16_nt(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 2);
+}
 // The same load at device scope (cache policy sc1): coherent with stores
 // that another XCD wrote back from its L2.
 __device__ __forceinline__ void lds_dma16_coherent(const void* g, void* l) {
