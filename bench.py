@@ -61,11 +61,10 @@ def cpu_baseline(inp, wl, target_s):
 
     import oracle
 
-    x = oracle.decode_bf16(inp["x"]) if inp["x"].dtype == np.uint16 else inp["x"].astype(np.float64)
-    Wg = oracle.decode_bf16(inp["Wg"]) if inp["Wg"].dtype == np.uint16 else inp["Wg"].astype(np.float64)
-    W1 = oracle.decode_bf16(inp["W1"])
-    W3 = oracle.decode_bf16(inp["W3"])
-    W2 = oracle.decode_bf16(inp["W2"])
+    def f64(a):
+        return oracle.decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    x, Wg, W1, W3, W2 = (f64(inp[n]) for n in ("x", "Wg", "W1", "W3", "W2"))
     bias = inp.get("bias")
     n, spent, done = 32, 0.0, 0
     while True:
@@ -78,6 +77,17 @@ def cpu_baseline(inp, wl, target_s):
         if spent >= target_s or n == x.shape[0]:
             break
         n = int(min(x.shape[0], max(2 * n, n * (target_s - spent) / max(dt, 1e-3))))
+    # when the whole batch takes less than the budget, repeat it and report
+    # the mean over the repetitions
+    reps, total = 1, dt
+    while n == x.shape[0] and spent < target_s:
+        t0 = time.perf_counter()
+        oracle.forward(x[:n], Wg, bias, W1, W3, W2, wl.k, wl.e_begin, wl.E_local, wl.G)
+        d1 = time.perf_counter() - t0
+        spent += d1
+        total += d1
+        reps += 1
+    dt = total / reps
     try:
         from threadpoolctl import threadpool_info
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
@@ -85,7 +95,7 @@ def cpu_baseline(inp, wl, target_s):
         cores = os.cpu_count()
     return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {done} tokens of the {wl.name} batch, float64 numpy oracle "
-                      f"(route, dispatch, expert FFN, combine), {dt:.1f} s for the last run"}
+                      f"(route, dispatch, expert FFN, combine), {dt:.2f} s per run, mean of {reps}"}
 
 
 def time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y, L, P, check, pp, sp, nws, T):
