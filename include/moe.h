@@ -174,7 +174,11 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx,
  *   kernel (tokens with no local pick get zeros).
  * Each GEMM accumulates in fp32 over K in one fixed ascending order with one
  * MFMA shape, never split; a is rounded to bf16 before the second GEMM and y
- * is rounded to bf16.  flags: MOE_FLAG_SERIAL or 0. */
+ * is rounded to bf16.  flags: MOE_FLAG_SERIAL or 0.
+ * After one moe_dispatch the call may be repeated on the same workspace any
+ * number of times: moe_dispatch zeroes the persistent kernel's tickets and
+ * counters, and every launch zeroes them again as it ends.  Calls that
+ * overlap on one workspace race. */
 moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const void* packed,
                                   const int32_t* expert_offsets, const int32_t* sorted_token,
                                   const int32_t* pair_pos, const float* topk_w,
