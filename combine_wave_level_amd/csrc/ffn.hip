@@ -244,6 +244,7 @@ __device__ __forceinline__ void ffn_waved_run(const WaveArgs& A) {
   __shared__ int32_t s_off[kMaxLocalExperts + 1];    // expert row offsets
   __shared__ int32_t s_ready[kSchedMaxWaves + 2];     // ready-slot starts in the ready list
   __shared__ int32_t s_ticket;
+  __shared__ int32_t s_wdone;  // waves 0 .. s_wdone - 1 seen finished on every XCD
   const int xcd = uniform(xcc_id());
   int32_t* ticket = A.ctr + sched_ticket_index(xcd);
   // the first ticket is claimed now: the atomic's round trip overlaps the
@@ -268,6 +269,7 @@ __device__ __forceinline__ void ffn_waved_run(const WaveArgs& A) {
     sched_init(S, A.E_local, A.G, (GATED ? 2 : 1) * A.I / C1::BW, A.d / C2::BW, xcd, kSchedMaxLag);
     S.mt_pre[0] = 0;
     S.cb_pre[0] = 0;
+    s_wdone = 0;
   }
   __syncthreads();
   if (wave_uniform() == 0) sched_scan_wave(S.mt_pre, A.E_local + 1);
@@ -358,10 +360,12 @@ __device__ __forceinline__ void ffn_waved_run(const WaveArgs& A) {
         }
       }
     } else {
-      // combine of tokens whose last local wave is t.slot - 1
-      for (int w = 0; w <= t.slot - 1; ++w)
+      // combine of tokens whose last local wave is t.slot - 1; waves this
+      // workgroup already saw finished are not polled again
+      for (int w = uniform(s_wdone); w <= t.slot - 1; ++w)
         poll_geq(A.ctr + sched_g2all_index(S, rw, w), uniform(sched_g2_all(S, w)), A.timeout_ticks, A.err);
       __syncthreads();
+      if (threadIdx.x == 0 && t.slot > s_wdone) s_wdone = t.slot;
       const int parts = A.cb_parts;
       const int base = uniform(s_ready[t.slot] + (t.chunk / parts) * kCombineTokens);
       const int end = uniform(min(base + kCombineTokens, s_ready[t.slot + 1]));
