@@ -417,6 +417,9 @@ int main() {
       if (ctr[sched_g1all_index(S[0], rw, j)].load() != NT1) fail("g1all count", j);
   for (int w = 0; w < W; ++w)
     if (ctr[sched_g2all_index(S[0], rw, w)].load() != sched_g2_all(S[0], w)) fail("g2 all count", w);
-  std::printf("OK total=%d W=%d mtiles=%d spread=%d\n", total, W, nmt, spread ? 1 : 0);
+  int max_group = 0;
+  for (int x = 0; x < kXcds; ++x)
+    for (int j = 0; j < S[x].n_local; ++j) max_group = std::max(max_group, S[x].grp[j] >> 16);
+  std::printf("OK total=%d W=%d mtiles=%d spread=%d max_group=%d\n", total, W, nmt, spread ? 1 : 0, max_group);
   return 0;
 }

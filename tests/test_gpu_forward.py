@@ -132,6 +132,28 @@ def test_small_batch_persistent_equals_serial_over_runs(T):
         assert torch.equal(a["y"][:P], b["y"][:P])
 
 
+@pytest.mark.parametrize("T", [1024, 1025])
+def test_dispatch_exact_on_both_sides_of_the_one_workgroup_path(T):
+    """moe_dispatch runs its count, scan and scatter in one workgroup for
+    T <= 1024 and as three kernels above: on the mid layer's routing at
+    T = 1024 and 1025 both give the oracle's permutation exactly, and the
+    persistent and phase-by-phase FFNs on them the same bits."""
+    inp = inputs("mid", T=T)
+    wl = inp["workload"]
+    L = Layer(inp)
+    o = oracle_inputs(inp)
+    l64 = oracle.router_logits(o["x"], o["Wg"], o["bias"])
+    idx_o, w_o, _ = oracle.route(l64, wl.k)
+    meta = oracle.dispatch(idx_o, wl.e_begin, L.p.E_local, L.p.experts_per_wave)
+    disp, y, out, _ = L.ffn_from_routing(idx_o, w_o)
+    check_dispatch_exact(disp, meta, T)
+    disp_s, y_s, out_s, _ = L.ffn_from_routing(idx_o, w_o, serial=True)
+    check_dispatch_exact(disp_s, meta, T)
+    P = int(meta["offsets"][-1])
+    assert torch.equal(out, out_s)
+    assert torch.equal(y[:P], y_s[:P])
+
+
 @pytest.mark.parametrize("name,T", [("mid", 777), ("decode", 1), ("decode", 128)])
 def test_persistent_back_to_back_on_one_dispatch(name, T):
     """The persistent kernel's tickets and hand-off counters need no fill of

@@ -121,7 +121,18 @@ def test_hot_expert_dealt_in_chunks(emu):
     # one expert holds most rows: it is split over the XCDs as they fill up
     counts = [30 * 128] + [128 * 2] * 15
     ready = [5, 40, 3, 9, 60]
-    _run(emu, counts, ready, G=4, NT1=8, NT2=16, threads=3, seed=4, lag=4)
+    out = _run(emu, counts, ready, G=4, NT1=8, NT2=16, threads=3, seed=4, lag=4)
+    # GEMM2 groups are capped by the lag (4 here)
+    assert "max_group=4" in out
+
+
+def test_gemm2_groups_span_an_experts_mtiles(emu):
+    # experts of 1 to 12 m-tiles under the long lag: groups of up to 8 m-tiles
+    rng = np.random.default_rng(31)
+    counts = [int(c) for c in rng.integers(1, 12 * BT, size=16)]
+    ready = [int(r) for r in rng.integers(0, 300, size=5)]
+    out = _run(emu, counts, ready, G=4, NT1=8, NT2=16, threads=2, seed=8, lag=64)
+    assert "max_group=8" in out
 
 
 def test_lumpy_experts_and_a_hot_one_stay_balanced(emu):
