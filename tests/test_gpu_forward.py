@@ -28,9 +28,10 @@ def inputs(name, T=None):
     return _cache[key]
 
 
-def _full_compare(inp, G=None, sample=None, seed=0):
+def _full_compare(inp, G=None, sample=None, seed=0, extra=()):
     """Runs the layer on the GPU and compares every stage with the oracle.
-    sample: number of tokens whose output rows are compared (None = all)."""
+    sample: number of tokens whose output rows are compared (None = all);
+    extra: tokens compared in addition to the sample."""
     wl = inp["workload"]
     L = Layer(inp, G=G)
     o = oracle_inputs(inp)
@@ -51,6 +52,7 @@ def _full_compare(inp, G=None, sample=None, seed=0):
     w32 = w_d.cpu().numpy().astype(np.float64)   # the weights the GPU was given
     rng = np.random.default_rng(seed)
     toks = np.arange(T) if sample is None or sample >= T else np.sort(rng.choice(T, sample, replace=False))
+    toks = np.unique(np.concatenate([toks, np.asarray(extra, dtype=np.int64)]))
     ref = oracle.forward_tokens(o["x"][toks], idx_o[toks], w32[toks], o["W1"], o["W3"], o["W2"],
                                 wl.e_begin, L.p.E_local)
     got = host_f64(out)[toks]
@@ -102,6 +104,51 @@ def test_v4_scale_share_sampled():
     none = ~((idx >= 0) & (idx < 32)).any(axis=1)
     assert none.any()
     assert (host_f64(r["out"])[none] == 0).all()
+
+
+def test_stress_layer_full_size_sampled():
+    """The stress layer at its largest batch (T = 16384; one expert chosen
+    by about half of the tokens, so the whole-expert deal splits it over
+    XCDs): routing and dispatch in full, output rows of 32 sampled tokens
+    plus token 0, token T - 1 and 8 tokens that pick the hot expert, and y
+    rows of their pairs."""
+    inp = inputs("stress", T=16384)
+    wl = inp["workload"]
+    o = oracle_inputs(inp)
+    idx_o, _, _ = oracle.route(oracle.router_logits(o["x"], o["Wg"], o["bias"]), wl.k)
+    hot_toks = np.nonzero((idx_o == inp["hot_expert"]).any(axis=1))[0]
+    assert hot_toks.size > 0.3 * wl.T
+    pick = np.random.default_rng(7).choice(hot_toks, 8, replace=False)
+    _full_compare(inp, sample=32, seed=1, extra=np.concatenate([[0, 16383], pick]))
+
+
+@pytest.mark.parametrize("name,T", [("mid", 777), ("decode", 8)])
+def test_forward_stays_inside_the_forward_workspace(name, T):
+    """A workspace of exactly the forward size (moe_workspace_size with no
+    flags) followed by guard bytes: route, dispatch, the expert FFN
+    (persistent and phases) and the FP8-dispatch FFN write nothing past it,
+    and give the same bits as on a backward-sized workspace."""
+    inp = inputs(name, T=T)
+    L = Layer(inp)
+    print(f"[case] forward-only workspace {name} T={T}", flush=True)
+    n = moe.workspace_size(L.p)
+    assert n == L.ws.numel() and n < moe.workspace_size(L.p, backward=True)
+    buf = torch.full((n + 65536,), 0xA5, dtype=torch.uint8, device="cuda")
+    buf[:n].zero_()
+    ws = buf[:n]
+    big = moe.workspace(L.p, backward=True)
+    for serial in (False, True):
+        a = moe.forward(L.p, L.x, L.packed, ws, bias=L.bias, serial=serial)
+        b = moe.forward(L.p, L.x, L.packed, big, bias=L.bias, serial=serial)
+        torch.cuda.synchronize()
+        moe.check_error(ws)
+        moe.check_error(big)
+        assert torch.equal(a["out"], b["out"]) and torch.equal(a["idx"], b["idx"])
+        x8, sc = moe.quantize_fp8(L.p, L.x)
+        moe.ffn_waved_fp8(L.p, x8, sc, L.packed, a["disp"], a["w"], ws, serial=serial)
+        torch.cuda.synchronize()
+        moe.check_error(ws)
+    assert (buf[n:] == 0xA5).all()
 
 
 def test_persistent_equals_serial_and_standalone_combine():
