@@ -846,7 +846,9 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
   const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16, gate_rows(p));
   const char* pk = static_cast<const char*>(a.packed);
   const uint16_t* w13 = reinterpret_cast<const uint16_t*>(pk + PL.w13);
-  const uint16_t* w2b = reinterpret_cast<const uint16_t*>(pk + PL.w2b);
+  const PackedBwdLayout BL = packed_bwd_layout(p);
+  const char* pb = static_cast<const char*>(a.packed_bwd);
+  const uint16_t* w2b = reinterpret_cast<const uint16_t*>(pb + BL.w2b);
   const bool want_dw = a.dW1 != nullptr;
   const bool want_data = a.dx != nullptr;
   const bool xbf = p.x_dtype == MOE_BF16;
@@ -892,8 +894,6 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     e = launch_dh<BwdCfg>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
   if (e != hipSuccess) return e;
   if (want_data) {
-    const PackedBwdLayout BL = packed_bwd_layout(p);
-    const char* pb = static_cast<const char*>(a.packed_bwd);
     const uint16_t* w13t = reinterpret_cast<const uint16_t*>(pb + BL.w13t);
     const void* wgt = pb + BL.wgt;
     bwd_gate_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(dwp, p.I / 16, a.pair_pos, a.topk_idx, a.topk_w, p.T, p.k,

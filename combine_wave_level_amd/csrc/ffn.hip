@@ -424,6 +424,16 @@ FfnShape pick_ffn_shape(const moe_problem_t& p) {
   return FfnShape::Mid;
 }
 
+// m-tile rows of the shape a problem runs (GEMM1 and GEMM2 share them).
+int ffn_mtile_rows(const moe_problem_t& p) {
+  switch (pick_ffn_shape(p)) {
+    case FfnShape::Small: return FfnSmall::G1::BT;
+    case FfnShape::Small64: return FfnSmall64::G1::BT;
+    case FfnShape::Large: return FfnLarge::G1::BT;
+    default: return FfnMid::G1::BT;
+  }
+}
+
 template <class F>
 hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint16_t* xb, const float* xscale,
                           const uint16_t* w13, const uint16_t* w2, const int32_t* offsets,
@@ -435,11 +445,7 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   const bool out_bf16 = p.out_dtype == MOE_BF16;
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
-  // the persistent schedule holds at most kSchedMaxLocal m-tiles per XCD;
-  // larger problems run the phase-by-phase path (same kernels, same bits)
-  const long long mt_bound = static_cast<long long>(L.P_max) / F::G1::BT + p.E_local + 1;
-  if (mt_bound / kXcds + L.W + 1 > kSchedMaxLocal) flags |= MOE_FLAG_SERIAL;
-  if (flags & MOE_FLAG_SERIAL) {
+  if (!ffn_uses_persistent(p, cus, flags)) {
     constexpr size_t l1 = F::G1::LDS_BYTES, l2 = F::G2::LDS_BYTES;
     auto g1 = gate_rows(p) == 2 ? gemm1_phase_kernel<F, true> : gemm1_phase_kernel<F, false>;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g1, F::NT, l1)) != hipSuccess) return e;
@@ -494,6 +500,18 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
 }
 
 }  // namespace
+
+bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags) {
+  if (flags & MOE_FLAG_SERIAL) return false;
+  // every per-XCD ticket stream needs workgroups: the whole device
+  if (cus != kXcds * kCusPerXcd) return false;
+  // the schedule holds at most kSchedMaxLocal m-tiles per XCD; larger
+  // problems run the phase-by-phase path (same kernels, same bits)
+  const int W = p.E_local / p.experts_per_wave;
+  const long long P_max = static_cast<long long>(p.T) * (p.k < p.E_local ? p.k : p.E_local);
+  const long long mt_bound = P_max / ffn_mtile_rows(p) + p.E_local + 1;
+  return mt_bound / kXcds + W + 1 <= kSchedMaxLocal;
+}
 
 hipError_t fill_zero(void* p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;

@@ -56,6 +56,7 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.xbf = take(static_cast<size_t>(p.T) * p.d * 2);
   L.act = take(static_cast<size_t>(L.P_max) * p.I * 2);
   L.sync = take(L.sync_words * 4);
+  L.fwd_total = off;
   const bool xbf = p.x_dtype == MOE_BF16;
   L.bwd_dh = take(static_cast<size_t>(L.P_max) * 2 * p.I * 2);
   L.P_pad = static_cast<int>(align_up(static_cast<size_t>(L.P_max) + 64 * static_cast<size_t>(p.E_local), 64));
@@ -75,9 +76,12 @@ WsLayout ws_layout(const moe_problem_t& p) {
   return L;
 }
 
-static moe_status_t check_ws(const moe_problem_t* p, const void* ws, size_t ws_bytes, WsLayout* L) {
+// bwd: the call uses the backward regions (the whole layout); otherwise the
+// forward prefix suffices.
+static moe_status_t check_ws(const moe_problem_t* p, const void* ws, size_t ws_bytes, WsLayout* L,
+                             bool bwd = false) {
   *L = ws_layout(*p);
-  if (!ws || !aligned16(ws) || ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  if (!ws || !aligned16(ws) || ws_bytes < (bwd ? L->total : L->fwd_total)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -94,9 +98,17 @@ size_t moe_packed_weights_size(const moe_problem_t* p) {
   return packed_layout(p->d, p->I, p->E_global, p->E_local, p->x_dtype == MOE_BF16, gate_rows(*p)).total;
 }
 
-size_t moe_workspace_size(const moe_problem_t* p) {
-  if (check_problem(p) != MOE_OK) return 0;
-  return ws_layout(*p).total;
+size_t moe_workspace_size(const moe_problem_t* p, uint32_t flags) {
+  if (check_problem(p) != MOE_OK || (flags & ~MOE_WS_BACKWARD)) return 0;
+  const WsLayout L = ws_layout(*p);
+  return (flags & MOE_WS_BACKWARD) ? L.total : L.fwd_total;
+}
+
+int32_t moe_ffn_path(const moe_problem_t* p, int32_t num_cus, uint32_t flags) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (num_cus <= 0 || (flags & ~MOE_FLAG_SERIAL)) return MOE_ERR_INVALID_ARG;
+  return ffn_uses_persistent(*p, num_cus, flags) ? MOE_PATH_PERSISTENT : MOE_PATH_PHASES;
 }
 
 size_t moe_packed_bwd_size(const moe_problem_t* p) {
@@ -105,13 +117,14 @@ size_t moe_packed_bwd_size(const moe_problem_t* p) {
 }
 
 moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const void* W1, const void* W3,
-                                  void* packed_bwd, moe_stream_t stream) {
+                                  const void* W2, void* packed_bwd, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
-  if (!Wg || !W1 || !W3 || !packed_bwd) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(packed_bwd) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3)) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_pack_bwd(*p, Wg, W1, W3, packed_bwd, static_cast<hipStream_t>(stream)));
+  if (!Wg || !W1 || !W3 || !W2 || !packed_bwd) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed_bwd) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_bwd(*p, Wg, W1, W3, W2, packed_bwd, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void* W1,
@@ -214,23 +227,24 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* p
 }
 
 moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void* packed,
-                              const int32_t* expert_offsets, const int32_t* sorted_token,
+                              const void* packed_bwd, const int32_t* expert_offsets, const int32_t* sorted_token,
                               const int32_t* pair_pos, const float* topk_w, const void* dout,
                               float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
                               moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
-  if (!packed || !expert_offsets || !dW1 || !dW3 || !dW2) return MOE_ERR_INVALID_ARG;
+  if (!packed || !packed_bwd || !expert_offsets || !dW1 || !dW3 || !dW2) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !sorted_token || !pair_pos || !topk_w || !dout)) return MOE_ERR_INVALID_ARG;
-  if ((x && !aligned16(x)) || (dout && !aligned16(dout)) || !aligned16(dW1) || !aligned16(dW3) ||
-      !aligned16(dW2))
+  if ((x && !aligned16(x)) || (dout && !aligned16(dout)) || !aligned16(packed) || !aligned16(packed_bwd) ||
+      !aligned16(dW1) || !aligned16(dW3) || !aligned16(dW2))
     return MOE_ERR_INVALID_ARG;
   WsLayout L;
-  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if ((st = check_ws(p, ws, ws_bytes, &L, true)) != MOE_OK) return st;
   BackwardArgs a{};
   a.x = x;
   a.packed = packed;
+  a.packed_bwd = packed_bwd;
   a.topk_w = topk_w;
   a.offsets = expert_offsets;
   a.sorted_token = sorted_token;
@@ -261,7 +275,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
       (dW2 && !aligned16(dW2)))
     return MOE_ERR_INVALID_ARG;
   WsLayout L;
-  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  if ((st = check_ws(p, ws, ws_bytes, &L, true)) != MOE_OK) return st;
   BackwardArgs a{};
   a.x = x;
   a.packed = packed;

@@ -75,10 +75,11 @@ __host__ __device__ __forceinline__ size_t frag_offset(int nb, int kb, int KB) {
 //              intermediate index meet in the same lane (ungated
 //              activation: W1^T only, [I][d]).
 //   W2       : per local expert, W2^T as [d][I] in fragment layout.
-//   W2b      : per local expert, W2 as [I][d] in fragment layout (K = d), the
-//              operand of dA = dy W2^T in the weight gradient.
+// (The copies of the weights that only the gradients read live in the
+// backward buffer, moe_pack_weights_bwd, so a forward-only caller holds each
+// expert weight once.)
 struct PackedLayout {
-  size_t router, w13, w2, w2b, total;
+  size_t router, w13, w2, total;
   int Epad;
 };
 
@@ -96,8 +97,6 @@ __host__ __device__ inline PackedLayout packed_layout(int d, int I, int E_global
   L.w13 = off;
   off += align_up(static_cast<size_t>(E_local) * gate_rows * I * d * 2, 256);
   L.w2 = off;
-  off += align_up(static_cast<size_t>(E_local) * d * I * 2, 256);
-  L.w2b = off;
   off += align_up(static_cast<size_t>(E_local) * d * I * 2, 256);
   L.total = off;
   return L;

@@ -47,9 +47,12 @@ namespace moe {
 //   bwd_dxr    bf16 [P_max][d]: data gradient of each routed row
 //   bwd_dwg    fp32 [ceil(T / kDwgChunkRows)][d][Ep]: isolated partials of
 //              dWg (bf16 x only)
+//   The forward regions (err .. sync) come first: fwd_total bytes hold them,
+//   and a workspace of that size serves every forward entry point; the
+//   backward regions follow (total).
 struct WsLayout {
   size_t err, masks, bases, group_off, ready_list, logits, xbf, act, sync, bwd_dh, bwd_dht, bwd_awt,
-      bwd_xst, bwd_dst, wgrad, bwd_g, bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, total;
+      bwd_xst, bwd_dst, wgrad, bwd_g, bwd_dwp, bwd_dlc, bwd_dld, bwd_dxr, bwd_dwg, fwd_total, total;
   int nchunks, W, ngroups, P_max;
   int P_pad;             // columns of the transposed weight-gradient operands
   int Ep;                // E_global rounded up to 64 (columns of the dense logits gradient)
@@ -74,9 +77,11 @@ constexpr int kDwgChunkRows = 1024;
 //          for the router's share of dx);
 //   w13t : per local expert, [W1 | W3]^T as [d][2I] in fragment layout
 //          (K = 2I: the W1 columns, then the W3 columns), the weights of
-//          dx = dH1 W1^T + dH3 W3^T.
+//          dx = dH1 W1^T + dH3 W3^T;
+//   w2b  : per local expert, W2 as [I][d] in fragment layout (K = d), the
+//          operand of dA = dy W2^T.
 struct PackedBwdLayout {
-  size_t wgt, w13t, total;
+  size_t wgt, w13t, w2b, total;
 };
 
 inline PackedBwdLayout packed_bwd_layout(const moe_problem_t& p) {
@@ -86,6 +91,8 @@ inline PackedBwdLayout packed_bwd_layout(const moe_problem_t& p) {
   off += align_up(static_cast<size_t>(p.E_global) * p.d * (p.x_dtype == MOE_BF16 ? 2 : 4), 256);
   L.w13t = off;
   off += align_up(static_cast<size_t>(p.E_local) * p.d * 2 * p.I * 2, 256);
+  L.w2b = off;
+  off += align_up(static_cast<size_t>(p.E_local) * p.d * p.I * 2, 256);
   L.total = off;
   return L;
 }
@@ -118,7 +125,7 @@ struct BackwardArgs {
 hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
                        const void* W2, void* packed, hipStream_t s);
 hipError_t launch_pack_bwd(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
-                           void* packed_bwd, hipStream_t s);
+                           const void* W2, void* packed_bwd, hipStream_t s);
 
 hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packed,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
@@ -130,6 +137,15 @@ int router_splits(int d, int E_global, bool x_bf16);
 hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* sorted_token,
                            int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s);
+
+// Whether moe_expert_ffn_waved runs the persistent expert-wave kernel
+// (true) or the phase-by-phase kernels (false) on a device with `cus`
+// compute units, for flags as passed.  The persistent kernel deals its
+// tickets to kXcds per-XCD streams and a workgroup serves the stream of the
+// XCD it runs on, so it needs the whole gfx950 device (kXcds XCDs of
+// kCusPerXcd CUs; a partitioned or harvested device leaves streams without
+// workgroups) and a schedule that fits its tables.
+bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags);
 
 hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
                       const int32_t* offsets, const int32_t* sorted_token, const int32_t* pair_pos,

@@ -90,7 +90,7 @@ __global__ void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
 }  // namespace
 
 hipError_t launch_pack_bwd(const moe_problem_t& p, const void* Wg, const void* W1, const void* W3,
-                           void* packed_bwd, hipStream_t s) {
+                           const void* W2, void* packed_bwd, hipStream_t s) {
   const PackedBwdLayout L = packed_bwd_layout(p);
   char* base = static_cast<char*>(packed_bwd);
   const int threads = 256;
@@ -114,6 +114,18 @@ hipError_t launch_pack_bwd(const moe_problem_t& p, const void* Wg, const void* W
     pack_frag_kernel<true, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
   else
     pack_frag_kernel<false, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // W2 as [I][d] (K = d) for dA = dy W2^T
+  {
+    const size_t slots2 = static_cast<size_t>(p.I) * (p.d / 8);
+    dim3 grid2(static_cast<unsigned>((slots2 + threads - 1) / threads), p.E_local);
+    const size_t stride = static_cast<size_t>(p.d) * p.I;
+    uint16_t* dst2 = reinterpret_cast<uint16_t*>(base + L.w2b);
+    if (p.w_dtype == MOE_BF16)
+      pack_frag_kernel<true, 2><<<grid2, threads, 0, s>>>(W2, nullptr, dst2, p.d, p.I, p.I, stride, stride);
+    else
+      pack_frag_kernel<false, 2><<<grid2, threads, 0, s>>>(W2, nullptr, dst2, p.d, p.I, p.I, stride, stride);
+  }
   return hipGetLastError();
 }
 
@@ -173,19 +185,6 @@ hipError_t launch_pack(const moe_problem_t& p, const void* Wg, const void* W1, c
       pack_frag_kernel<true, 0><<<grid, threads, 0, s>>>(W2, nullptr, dst, p.I, p.d, p.d, stride, stride);
     else
       pack_frag_kernel<false, 0><<<grid, threads, 0, s>>>(W2, nullptr, dst, p.I, p.d, p.d, stride, stride);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // W2 as [I][d] (K = d) for the weight gradient's dA = dy W2^T
-  {
-    const size_t slots = static_cast<size_t>(p.I) * (p.d / 8);
-    dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
-    const size_t stride = static_cast<size_t>(p.d) * p.I;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(base + L.w2b);
-    if (wbf)
-      pack_frag_kernel<true, 2><<<grid, threads, 0, s>>>(W2, nullptr, dst, p.d, p.I, p.I, stride, stride);
-    else
-      pack_frag_kernel<false, 2><<<grid, threads, 0, s>>>(W2, nullptr, dst, p.d, p.I, p.I, stride, stride);
   }
   return hipGetLastError();
 }

@@ -56,6 +56,7 @@
 namespace moe {
 
 constexpr int kXcds = 8;                // XCDs of an MI355X
+constexpr int kCusPerXcd = 32;          // compute units of one XCD
 constexpr int kSchedMaxExperts = 256;
 constexpr int kSchedMaxWaves = 256;
 constexpr int kSchedMaxLocal = 512;     // m-tiles of one XCD

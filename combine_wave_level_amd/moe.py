@@ -26,12 +26,15 @@ MOE_BF16 = 1
 MOE_FLAG_SERIAL = 0x1
 MOE_ACT_SWIGLU = 0
 MOE_ACT_RELU2 = 1
+MOE_WS_BACKWARD = 0x1
+MOE_PATH_PERSISTENT = 0
+MOE_PATH_PHASES = 1
 
 EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
     "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
-    "moe_expert_ffn_waved_fp8",
+    "moe_expert_ffn_waved_fp8", "moe_ffn_path",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -73,17 +76,18 @@ def lib() -> ctypes.CDLL:
         st = ctypes.c_int
         sig = {
             "moe_packed_weights_size": (ctypes.c_size_t, [P]),
-            "moe_workspace_size": (ctypes.c_size_t, [P]),
+            "moe_workspace_size": (ctypes.c_size_t, [P, ctypes.c_uint32]),
+            "moe_ffn_path": (ctypes.c_int32, [P, ctypes.c_int32, ctypes.c_uint32]),
             "moe_pack_weights": (st, [P, vp, vp, vp, vp, vp, vp]),
             "moe_route": (st, [P, vp, vp, f32p, i32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
             "moe_dispatch": (st, [P, i32p, i32p, i32p, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]),
             "moe_expert_ffn_waved": (st, [P, vp, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
                                           ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
             "moe_combine": (st, [P, vp, i32p, f32p, vp, vp]),
-            "moe_expert_wgrad": (st, [P, vp, vp, i32p, i32p, i32p, f32p, vp, f32p, f32p, f32p,
+            "moe_expert_wgrad": (st, [P, vp, vp, vp, i32p, i32p, i32p, f32p, vp, f32p, f32p, f32p,
                                       vp, ctypes.c_size_t, vp]),
             "moe_packed_bwd_size": (ctypes.c_size_t, [P]),
-            "moe_pack_weights_bwd": (st, [P, vp, vp, vp, vp, vp]),
+            "moe_pack_weights_bwd": (st, [P, vp, vp, vp, vp, vp, vp]),
             "moe_backward": (st, [P, vp, vp, vp, i32p, f32p, i32p, i32p, i32p, vp, vp, f32p, f32p, f32p,
                                   f32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
             "moe_quantize_fp8": (st, [P, vp, vp, f32p, vp]),
@@ -126,16 +130,27 @@ def problem(T, d, I, E_global, k, e_begin=0, E_local=None, experts_per_wave=4,
                    x_dtype, w_dtype, out_dtype, activation)
 
 
-def workspace_size(p: Problem) -> int:
-    return int(lib().moe_workspace_size(ctypes.byref(p)))
+def workspace_size(p: Problem, backward: bool = False) -> int:
+    """Workspace bytes: the forward entry points' size, or with backward=True
+    the size every entry point (moe_expert_wgrad, moe_backward) needs."""
+    return int(lib().moe_workspace_size(ctypes.byref(p), MOE_WS_BACKWARD if backward else 0))
+
+
+def ffn_path(p: Problem, num_cus: int, serial: bool = False) -> int:
+    """MOE_PATH_PERSISTENT or MOE_PATH_PHASES: the schedule the expert FFN
+    runs on a device with num_cus compute units."""
+    r = int(lib().moe_ffn_path(ctypes.byref(p), int(num_cus), MOE_FLAG_SERIAL if serial else 0))
+    if r < 0:
+        raise MoEError(r, "moe_ffn_path")
+    return r
 
 
 def packed_weights_size(p: Problem) -> int:
     return int(lib().moe_packed_weights_size(ctypes.byref(p)))
 
 
-def workspace(p: Problem, device="cuda") -> torch.Tensor:
-    n = workspace_size(p)
+def workspace(p: Problem, device="cuda", backward: bool = False) -> torch.Tensor:
+    n = workspace_size(p, backward)
     if n == 0:
         raise MoEError(MOE_ERR_INVALID_ARG, "workspace_size")
     # zero-filled once, so the device error word starts clean
@@ -242,14 +257,14 @@ def combine(p: Problem, y, pair_pos, topk_w, out=None):
     return out
 
 
-def wgrad(p: Problem, x, packed, disp: Dispatch, topk_w, dout, ws):
+def wgrad(p: Problem, x, packed, packed_bwd, disp: Dispatch, topk_w, dout, ws):
     dev = x.device
     shp13 = (p.E_local, p.d, p.I)
     dW1 = torch.empty(shp13, dtype=torch.float32, device=dev)
     dW3 = torch.empty(shp13, dtype=torch.float32, device=dev)
     dW2 = torch.empty((p.E_local, p.I, p.d), dtype=torch.float32, device=dev)
     _check(lib().moe_expert_wgrad(
-        ctypes.byref(p), _p(x), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
+        ctypes.byref(p), _p(x), _p(packed), _p(packed_bwd), _p(disp.offsets), _p(disp.sorted_token),
         _p(disp.pair_pos), _p(topk_w), _p(dout), _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(),
         _stream()), "moe_expert_wgrad")
     return dW1, dW3, dW2
@@ -259,13 +274,13 @@ def packed_bwd_size(p: Problem) -> int:
     return int(lib().moe_packed_bwd_size(ctypes.byref(p)))
 
 
-def pack_weights_bwd(p: Problem, Wg, W1, W3) -> torch.Tensor:
+def pack_weights_bwd(p: Problem, Wg, W1, W3, W2) -> torch.Tensor:
     n = packed_bwd_size(p)
     if n == 0:
         raise MoEError(MOE_ERR_INVALID_ARG, "packed_bwd_size")
     packed = torch.empty(n, dtype=torch.uint8, device=W1.device)
-    _check(lib().moe_pack_weights_bwd(ctypes.byref(p), _p(Wg), _p(W1), _p(W3), _p(packed), _stream()),
-           "moe_pack_weights_bwd")
+    _check(lib().moe_pack_weights_bwd(ctypes.byref(p), _p(Wg), _p(W1), _p(W3), _p(W2), _p(packed),
+                                      _stream()), "moe_pack_weights_bwd")
     return packed
 
 

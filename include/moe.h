@@ -98,10 +98,32 @@ typedef struct {
 /* Bytes of the packed weight buffer moe_pack_weights writes. 0 on bad shape. */
 size_t moe_packed_weights_size(const moe_problem_t* p);
 
-/* Bytes of workspace every entry point below needs for problem p.  One
- * workspace of this size serves all of them (not concurrently).  0 on a bad
- * shape. */
-size_t moe_workspace_size(const moe_problem_t* p);
+/* Flags for moe_workspace_size. */
+#define MOE_WS_BACKWARD 0x1u /* size for the backward entry points too     */
+
+/* Bytes of workspace for problem p.  flags = 0: what the forward entry
+ * points need (moe_route, moe_dispatch, moe_expert_ffn_waved,
+ * moe_expert_ffn_waved_fp8); MOE_WS_BACKWARD: what every entry point needs,
+ * moe_expert_wgrad and moe_backward included.  The forward regions sit at
+ * the same offsets in both layouts, so one workspace of the larger size
+ * serves every entry point (not concurrently).  A forward entry point never
+ * touches bytes past the forward size.  0 on a bad shape or unknown flag. */
+size_t moe_workspace_size(const moe_problem_t* p, uint32_t flags);
+
+/* Which schedule moe_expert_ffn_waved (and _fp8) runs for problem p with
+ * these flags on a device of num_cus compute units:
+ *   MOE_PATH_PERSISTENT: the persistent expert-wave kernel.  It hands out
+ *     tiles from one ticket stream per XCD and a workgroup serves the stream
+ *     of the XCD it runs on, so it needs the whole MI355X (8 XCDs of 32 CUs,
+ *     num_cus == 256; a partitioned or harvested device would leave streams
+ *     without workgroups) and at most 512 m-tiles per XCD;
+ *   MOE_PATH_PHASES: gather + GEMM1, GEMM2 and combine as grid-wide phases
+ *     (MOE_FLAG_SERIAL, or when the persistent kernel does not fit).
+ * Both give the same bits.  The library calls this with the current
+ * device's CU count.  Returns a moe_status_t (< 0) on a bad argument. */
+#define MOE_PATH_PERSISTENT 0
+#define MOE_PATH_PHASES 1
+int32_t moe_ffn_path(const moe_problem_t* p, int32_t num_cus, uint32_t flags);
 
 /* ------------------------------------------------------------ weights */
 
@@ -120,14 +142,16 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void
  * bad shape or an activation other than SWIGLU. */
 size_t moe_packed_bwd_size(const moe_problem_t* p);
 
-/* One-time re-layout of the weights the data gradient reads (weights are
+/* One-time re-layout of the weights the gradients read (weights are
  * parameters; forward-only callers never need this buffer): Wg^T in the
- * dtype of x, and per local expert [W1 | W3]^T in the MFMA fragment layout.
- *   Wg [d, E_global] in x_dtype; W1, W3 [E_local, d, I] in w_dtype (rounded
- *   to bf16 when F32).  packed_bwd: moe_packed_bwd_size(p) bytes, written
- *   entirely. */
+ * dtype of x, and per local expert [W1 | W3]^T and W2 (K = d) in the MFMA
+ * fragment layout.
+ *   Wg [d, E_global] in x_dtype; W1, W3 [E_local, d, I] and W2 [E_local, I,
+ *   d] in w_dtype (rounded to bf16 when F32).  packed_bwd:
+ *   moe_packed_bwd_size(p) bytes, written entirely. */
 moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const void* W1,
-                                  const void* W3, void* packed_bwd, moe_stream_t stream);
+                                  const void* W3, const void* W2, void* packed_bwd,
+                                  moe_stream_t stream);
 
 /* ------------------------------------------------------------ the path */
 
@@ -225,10 +249,13 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* p
  *   dA = dy W2_e^T,  dH3 = dA * silu(h1),
  *   dH1 = dA * h3 * s * (1 + h1 (1 - s)),  s = sigmoid(h1),
  * with h1, h3 recomputed exactly as the forward computes them.
+ *   packed, packed_bwd: from moe_pack_weights and moe_pack_weights_bwd.
  *   dout [T, d] bf16.  Out (fp32, math layout): dW1, dW3 [E_local, d, I],
- *   dW2 [E_local, I, d], every element written. */
+ *   dW2 [E_local, I, d], every element written.  ws: the MOE_WS_BACKWARD
+ *   size. */
 moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void* packed,
-                              const int32_t* expert_offsets, const int32_t* sorted_token,
+                              const void* packed_bwd, const int32_t* expert_offsets,
+                              const int32_t* sorted_token,
                               const int32_t* pair_pos, const float* topk_w, const void* dout,
                               float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
                               moe_stream_t stream);
@@ -257,8 +284,9 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
  * On an expert-parallel share these are this GPU's additive shares of the
  * layer's gradients (out is this GPU's partial sum).
  *   x, packed, topk_idx, topk_w, expert_offsets, sorted_token, pair_pos: as
- *   in the forward (same workspace after moe_dispatch); packed_bwd from
- *   moe_pack_weights_bwd; dout [T, d] bf16.
+ *   in the forward (same workspace after moe_dispatch, of the
+ *   MOE_WS_BACKWARD size); packed_bwd from moe_pack_weights_bwd; dout [T, d]
+ *   bf16.
  *   Out: dx [T, d] in x_dtype (required when T > 0); dtopk_w [T, k] fp32,
  *   dlogits [T, E_global] fp32 (dense, zeros off the picks), dWg
  *   [d, E_global] fp32: each optional (NULL = not computed); dW1, dW3 [E_local,

@@ -77,8 +77,51 @@ def test_sizes_accept_and_reject(L, kw, ok):
 def test_packed_size_matches_layout(L):
     p = _p(T=10, d=4096, I=1024, E_global=16, E_local=16, k=4)
     epad = 128
-    want = epad * 4096 * 2 + 16 * 2 * 1024 * 4096 * 2 + 2 * (16 * 4096 * 1024 * 2)
+    # router + W1|W3 + W2, each expert weight held once
+    want = epad * 4096 * 2 + 16 * 2 * 1024 * 4096 * 2 + 16 * 4096 * 1024 * 2
     assert moe.packed_weights_size(p) == want
+
+
+def _v4share(T=8192):
+    return moe.problem(T=T, d=7168, I=2048, E_global=256, k=8, E_local=32, experts_per_wave=4)
+
+
+def test_forward_workspace_and_pack_exclude_the_backward(L):
+    """A forward-only caller of the V3/V4-scale share needs under 1 GB of
+    workspace and holds each expert weight once; the backward layout extends
+    the forward one (same offsets), so its size is the larger."""
+    p = _v4share()
+    fwd, bwd = moe.workspace_size(p), moe.workspace_size(p, backward=True)
+    assert 0 < fwd < 1 << 30
+    assert bwd > fwd
+    # the forward regions: dispatch tables, partial router logits, x staging
+    # [T, d] bf16, the activations a [P_max, I] bf16 and the kernel counters
+    P_max = 8192 * 8
+    assert P_max * 2048 * 2 + 8192 * 7168 * 2 < fwd < P_max * 2048 * 2 + 8192 * 7168 * 2 + 64 * 2 ** 20
+    router = 256 * 7168 * 2
+    experts = 32 * 3 * 7168 * 2048 * 2
+    assert moe.packed_weights_size(p) == router + experts
+    # the backward buffer: Wg^T, [W1 | W3]^T and W2 (K = d)
+    assert L.moe_packed_bwd_size(ctypes.byref(p)) == 256 * 7168 * 2 + experts
+    assert L.moe_workspace_size(ctypes.byref(p), 0x80) == 0      # unknown flag
+
+
+def test_ffn_path_decision(L):
+    """The persistent kernel runs only on the whole 8-XCD device; any other
+    CU count (partition modes, harvested parts) and MOE_FLAG_SERIAL take the
+    phase kernels."""
+    p = _p(T=4096, d=4096, I=1024, E_global=16, E_local=16, k=4)
+    assert moe.ffn_path(p, 256) == moe.MOE_PATH_PERSISTENT
+    assert moe.ffn_path(p, 256, serial=True) == moe.MOE_PATH_PHASES
+    for cus in (32, 64, 128, 224, 240, 304):
+        assert moe.ffn_path(p, cus) == moe.MOE_PATH_PHASES, cus
+    assert moe.ffn_path(_p(T=1, d=7168, I=2048, E_global=32, E_local=32, k=8), 256) == moe.MOE_PATH_PERSISTENT
+    # more m-tiles per XCD than the schedule holds
+    big = _p(T=1 << 20, d=4096, I=1024, E_global=16, E_local=16, k=4)
+    assert moe.ffn_path(big, 256) == moe.MOE_PATH_PHASES
+    assert L.moe_ffn_path(ctypes.byref(p), 0, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_ffn_path(ctypes.byref(p), 256, 0x80) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_ffn_path(ctypes.byref(_p(d=100)), 256, 0) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_grows_with_tokens(L):
@@ -124,11 +167,22 @@ def test_dispatch_ffn_combine_wgrad_reject_before_launch(L):
     assert st == moe.MOE_ERR_INVALID_ARG
     st = L.moe_combine(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.c_void_p(0x10008), None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                             FAKE, 1 << 30, None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG                                 # no backward weights
+    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             FAKE, 1, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    # the forward-sized workspace is too small for the weight gradient
+    fwd = moe.workspace_size(p)
+    st = L.moe_expert_wgrad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, fwd, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_expert_ffn_waved(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                0, FAKE, fwd - 1, None)
     assert st == moe.MOE_ERR_WORKSPACE
     st = L.moe_pack_weights(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None)
     assert st == moe.MOE_ERR_INVALID_ARG
@@ -148,13 +202,16 @@ def test_backward_rejects_before_launch(L):
     assert call(dw=(FAKE, None, FAKE)) == moe.MOE_ERR_INVALID_ARG          # dW trio incomplete
     assert call(dx=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG    # misaligned dx
     assert call(nbytes=64) == moe.MOE_ERR_WORKSPACE
+    assert call(nbytes=moe.workspace_size(p)) == moe.MOE_ERR_WORKSPACE      # forward size only
     assert call(ws=None) == moe.MOE_ERR_WORKSPACE
-    assert L.moe_pack_weights_bwd(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_pack_weights_bwd(ctypes.byref(_p(d=96)), FAKE, FAKE, FAKE, FAKE, None) == \
+    assert L.moe_pack_weights_bwd(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights_bwd(ctypes.byref(_p(d=96)), FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
         moe.MOE_ERR_UNSUPPORTED
     assert L.moe_packed_bwd_size(ctypes.byref(_p(d=96))) == 0
-    # Wg^T (E_global x d bf16) + [W1 | W3]^T per local expert (d x 2I bf16)
-    assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2
+    # Wg^T (E_global x d bf16) + per local expert [W1 | W3]^T (d x 2I bf16)
+    # and W2 (I x d bf16)
+    assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2 + 8 * 128 * 256 * 2
 
 
 def test_ungated_activation_sizes_and_backward_rejection(L):
@@ -162,16 +219,16 @@ def test_ungated_activation_sizes_and_backward_rejection(L):
     backward: its entry points return UNSUPPORTED before touching memory."""
     g, u = _p(), _p(activation=moe.MOE_ACT_RELU2)
     router = 128 * 256 * 2                       # Epad x d bf16
-    w2 = 2 * 8 * 128 * 256 * 2                   # W2^T and W2, E_local x d x I bf16
+    w2 = 8 * 128 * 256 * 2                       # W2^T, E_local x d x I bf16
     assert moe.packed_weights_size(g) == router + 8 * 2 * 128 * 256 * 2 + w2
     assert moe.packed_weights_size(u) == router + 8 * 128 * 256 * 2 + w2
     assert moe.workspace_size(u) > 0
     assert L.moe_packed_bwd_size(ctypes.byref(u)) == 0
-    assert L.moe_pack_weights_bwd(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights_bwd(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     args = [FAKE] * 9
     assert L.moe_backward(ctypes.byref(u), *args, FAKE, None, None, None, None, None, None, FAKE, 1 << 30,
                           None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_wgrad(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert L.moe_expert_wgrad(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
     # W3 is required for SWIGLU only
     assert L.moe_pack_weights(ctypes.byref(g), FAKE, FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG

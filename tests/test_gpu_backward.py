@@ -26,9 +26,9 @@ pytestmark = pytest.mark.gpu
 def _setup(inp):
     """Layer on the GPU, backward weights, and the oracle's routing."""
     wl = inp["workload"]
-    L = Layer(inp)
+    L = Layer(inp, backward=True)
     o = oracle_inputs(inp)
-    packed_bwd = moe.pack_weights_bwd(L.p, L.Wg, dev(inp["W1"]), dev(inp["W3"]))
+    packed_bwd = moe.pack_weights_bwd(L.p, L.Wg, dev(inp["W1"]), dev(inp["W3"]), dev(inp["W2"]))
     l64 = oracle.router_logits(o["x"], o["Wg"], o["bias"])
     idx_o, w_o, _ = oracle.route(l64, wl.k)
     meta = oracle.dispatch(idx_o, wl.e_begin, wl.E_local, wl.G)
@@ -137,7 +137,7 @@ def test_backward_weight_gradient_matches_wgrad_entry_point():
     L, o, packed_bwd, idx_o, meta, idx_d, w_d, disp = _setup(inp)
     dout = dev(inp["dout"])
     g = _backward(L, packed_bwd, idx_d, w_d, disp, dout, want_dw=True)
-    ref = moe.wgrad(L.p, L.x, L.packed, disp, w_d, dout, L.ws)
+    ref = moe.wgrad(L.p, L.x, L.packed, packed_bwd, disp, w_d, dout, L.ws)
     torch.cuda.synchronize()
     for a, b in zip((g["dW1"], g["dW3"], g["dW2"]), ref):
         assert torch.equal(a, b)
@@ -217,8 +217,8 @@ def test_backward_batch_invariance_of_probe_tokens():
 
 def test_backward_edge_empty_batch():
     inp = make_inputs("mid", T=0, need_dout=True)
-    L = Layer(inp)
-    packed_bwd = moe.pack_weights_bwd(L.p, L.Wg, dev(inp["W1"]), dev(inp["W3"]))
+    L = Layer(inp, backward=True)
+    packed_bwd = moe.pack_weights_bwd(L.p, L.Wg, dev(inp["W1"]), dev(inp["W3"]), dev(inp["W2"]))
     idx = torch.zeros((0, L.p.k), dtype=torch.int32, device="cuda")
     w = torch.zeros((0, L.p.k), dtype=torch.float32, device="cuda")
     disp = moe.dispatch(L.p, idx, L.ws)
