@@ -64,12 +64,18 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* __restric
   int e = 0;
   const float f = frexpf(amax, &e);
   const int k = amax > 0.f ? e - 9 + (f > 0.875f ? 1 : 0) : 0;
-  const float inv = ldexpf(1.0f, -k);
+  // x / 2^k as two exact power-of-two products: 2^-k alone overflows fp32
+  // for rows whose largest magnitude is below about 2^-119 (k <= -128), and
+  // each factor here stays within fp32's normal range; a value the first
+  // product takes below fp32's normal range is far below half the smallest
+  // e4m3 step after the second, so its code (+-0) is the exact one
+  const float s1 = ldexpf(1.0f, (-k) / 2), s2 = ldexpf(1.0f, -k - (-k) / 2);
   for (int c = lane; c < nchunk; c += kWave) {
     float v[8];
     load8<XBF>(x, static_cast<size_t>(t), d, c, v);
-    const u32x2 o{pack_fp8x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
-                  pack_fp8x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv)};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (v[j] * s1) * s2;
+    const u32x2 o{pack_fp8x4(v[0], v[1], v[2], v[3]), pack_fp8x4(v[4], v[5], v[6], v[7])};
     *reinterpret_cast<u32x2*>(x8 + static_cast<size_t>(t) * d + c * 8) = o;
   }
   if (lane == 0) xscale[t] = ldexpf(1.0f, k);

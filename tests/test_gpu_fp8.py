@@ -44,10 +44,10 @@ def test_quantize_matches_oracle_on_workload_rows(name, T):
 
 
 def test_quantize_crafted_rounding_cases():
-    inp = make_inputs("mid", T=6)
+    inp = make_inputs("mid", T=7)
     L = Layer(inp)
     d = L.p.d
-    rows = np.zeros((6, d), dtype=np.float32)
+    rows = np.zeros((7, d), dtype=np.float32)
     rows[0, 0] = 448.0                                      # scale 1
     ties = [1 + 1 / 16, 1 + 3 / 16, 2.0 ** -10, 3 * 2.0 ** -10, 13 * 2.0 ** -10, 432.0, 200.0, 2.0 ** -7 * 1.0625]
     rows[0, 1:1 + len(ties)] = ties
@@ -59,12 +59,17 @@ def test_quantize_crafted_rounding_cases():
     rows[4, :] = np.linspace(-2, 2, d, dtype=np.float32)
     rows[5, 0] = 448.0 * 2 ** 5 * (1 + 2.0 ** -7)           # just above a power-of-two boundary
     rows[5, 1:9] = np.float32(448.0 * 2 ** 5) / np.arange(1, 9, dtype=np.float32)
+    # a row so small that 2^-k exceeds fp32's range (scale 2^-129): codes
+    # 256, -96, 10, 1.5 and a tie at 34 that rounds to 32
+    rows[6, :5] = [2.0 ** -121, -1.5 * 2.0 ** -123, 1.25 * 2.0 ** -126, 3 * 2.0 ** -130, 1.0625 * 2.0 ** -124]
     x = bf16_bits(rows)                                     # the values the layer receives
     # one bf16 step above four ties: they round up
     x[0, 41:45] = bf16_bits(np.array([2.0 ** -10, 1 + 1 / 16, 432.0, 3 * 2.0 ** -10], dtype=np.float32)) + 1
     print("[case] fp8 quantize crafted rows", flush=True)
     codes, scale = _check_codes(L, x)
     assert codes[0, 40] == 0x80 and scale[1] == 1.0 and (codes[1] == 0).all()
+    assert scale[6] == 2.0 ** -129
+    assert (oracle.e4m3_decode(codes[6, :5]) == [256.0, -96.0, 10.0, 1.5, 32.0]).all()
 
 
 def _ffn_compare(inp, serial):
