@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8-dispatch forward")
     ap.add_argument("--no-ungated", action="store_true",
                     help="skip timing the layer with the ungated squared-ReLU expert")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other workloads' rows (decode sweep, V3/V4-scale share, stress)")
+    ap.add_argument("--ramp-ms", type=float, default=200.0,
+                    help="untimed run of the layer before the warmup steps, in ms of wall time")
     return ap.parse_args()
 
 
@@ -193,15 +197,18 @@ def time_ungated(args, wl, T, d, stream):
             "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
-def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local):
-    """Times moe_backward (all outputs) on the forward's routing; returns the
-    figures reported under extra.backward."""
+def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, stream, P_local):
+    """Times moe_backward (all outputs) on the forward's routing, on a
+    workspace of the backward size; returns the figures reported under
+    extra.backward."""
     import torch
 
     from combine_wave_level_amd import moe
 
-    packed_bwd = moe.pack_weights_bwd(p, d(inp["Wg"]), d(inp["W1"]), d(inp["W3"]))
+    packed_bwd = moe.pack_weights_bwd(p, d(inp["Wg"]), d(inp["W1"]), d(inp["W3"]), d(inp["W2"]))
     dout = d(inp["dout"])
+    ws = moe.workspace(p, backward=True)
+    disp = moe.dispatch(p, idx, ws)
 
     def run():
         return moe.backward(p, x, packed, packed_bwd, idx, w, disp, dout, ws, want_dtopk_w=True,
@@ -226,6 +233,112 @@ def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "flops_per_step": flops, "tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+
+MALL_FLUSH_BYTES = 512 << 20   # twice the MI355X's 256 MB last-level cache
+
+# Other workloads, timed as rows of "extra.rows": the small-batch decode
+# sweep and the V3/V4-scale share stream their experts' weights (HBM bound;
+# the last-level cache is flushed before every timed step), the stress
+# layer at T = 4096 is compute bound.
+ROWS = (("decode", 1), ("decode", 8), ("decode", 32), ("decode", 128), ("v4share", 8192), ("stress", 4096))
+STREAMING = ("decode", "v4share")
+
+
+def roofline_of(d, I, T, counts):
+    """Algorithmic work of the expert FFN for one batch: FLOPs 6 d I per
+    routed pair; bytes = the touched experts' weights once + x read, y
+    written and read, out written."""
+    P_local = int(counts.sum())
+    flops = 6.0 * d * I * P_local
+    nbytes = int((counts > 0).sum()) * 3.0 * d * I * 2 + 2.0 * d * (2 * T + 2 * P_local)
+    mfma = flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
+    return flops, nbytes, mfma, P_local
+
+
+def time_rows(args, stream):
+    """Each row: the workload's router, dispatch and persistent expert-wave
+    kernel, timed per step between events (median of the steps), and the
+    expert FFN call alone the same way; for the weight-streaming rows a
+    512 MiB buffer is written before every timed step and call, outside the
+    events.  The expert weights are drawn on the device (seeded, N(0, 0.02),
+    bf16): only the routing depends on values, and x, Wg and the bias come
+    from the workload generator."""
+    import numpy as np
+    import torch
+
+    from combine_wave_level_amd import moe
+    from workloads import get, make_inputs
+
+    dev = torch.device("cuda:0")
+    flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    rows, weights = [], {}
+
+    def d(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    for name, T in ROWS:
+        wl = get(name)
+        inp = make_inputs(wl, T=T, weights=False)
+        p = moe.problem(T=T, d=wl.d, I=wl.I, E_global=wl.E_global, k=wl.k, e_begin=wl.e_begin,
+                        E_local=wl.E_local, experts_per_wave=wl.G)
+        if name not in weights:
+            weights.clear()
+            g = torch.Generator(device=dev)
+            g.manual_seed(1000 + len(rows))
+            W = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in
+                 ((wl.E_local, wl.d, wl.I), (wl.E_local, wl.d, wl.I), (wl.E_local, wl.I, wl.d))]
+            for w_ in W:
+                for e in range(w_.shape[0]):
+                    w_[e].copy_(torch.randn(w_.shape[1:], generator=g, device=dev) * 0.02)
+            weights[name] = W
+        W1, W3, W2 = weights[name]
+        x = d(inp["x"])
+        bias = d(inp["bias"]) if inp.get("bias") is not None else None
+        packed = moe.pack_weights(p, d(inp["Wg"]), W1, W3, W2)
+        ws = moe.workspace(p)
+        y = torch.empty((max(1, moe.p_max(p)), wl.d), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((T, wl.d), dtype=torch.bfloat16, device=dev)
+        cache = {}
+
+        def step(ffn_only=False):
+            if not ffn_only:
+                idx, w, _ = moe.route(p, x, packed, ws, bias=bias)
+                cache["disp"], cache["w"] = moe.dispatch(p, idx, ws), w
+            moe.ffn_waved(p, x, packed, cache["disp"], cache["w"], ws, y=y, out=out)
+
+        for _ in range(max(10, args.warmup // 5)):
+            step()
+        torch.cuda.synchronize()
+        stream_w = name in STREAMING
+        res = {}
+        for kind in ("step", "ffn"):
+            ts = []
+            for _ in range(max(10, args.steps)):
+                if stream_w:
+                    flush.fill_(len(ts) & 0xff)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step(ffn_only=kind == "ffn")
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            res[kind] = float(np.median(ts))
+        moe.check_error(ws)
+        counts = cache["disp"].counts.cpu().numpy().astype(np.int64)
+        flops, nbytes, mfma, P_local = roofline_of(wl.d, wl.I, T, counts)
+        row = {"workload": name, "T": T, "step_ms": round(res["step"], 4), "ffn_ms": round(res["ffn"], 4),
+               "tokens_per_s": round(T / (res["step"] * 1e-3), 1), "local_pairs": P_local,
+               "experts_touched": int((counts > 0).sum()), "bound": "mfma" if mfma else "hbm",
+               "mall_flushed": stream_w}
+        for lvl, ms in (("ffn", res["ffn"]), ("step", res["step"])):
+            row[f"{lvl}_hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            row[f"{lvl}_mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        rows.append(row)
+        del packed, ws, y, out, x
+    return rows
 
 
 def main():
@@ -343,6 +456,14 @@ def main():
                 "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
                 "step_ms_max": per_step[-1]}
 
+    # the clocks ramp up over the first ~10 ms of launches: run the layer
+    # untimed for --ramp-ms of wall time, then the W warmup steps
+    torch.cuda.synchronize()
+    r0 = time.perf_counter()
+    while (time.perf_counter() - r0) * 1e3 < args.ramp_ms:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
     for _ in range(max(0, args.warmup)):
         step()
     torch.cuda.synchronize()
@@ -414,7 +535,9 @@ def main():
     if not args.no_ungated:
         extra["relu2_same_params"] = time_ungated(args, wl, T, d, stream)
     if not args.no_backward:
-        extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, ws, stream, P_local)
+        extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, stream, P_local)
+    if not args.no_rows:
+        extra["rows"] = time_rows(args, stream)
 
     cpu = None
     if not args.no_cpu:
