@@ -152,6 +152,19 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* packed
                                  static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_route_noalloc(const moe_problem_t* p, const void* x, const void* packed, const float* bias,
+                               int32_t* topk_idx, float* topk_w, float* logits, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!x || !packed || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (packed && !aligned16(packed))) return MOE_ERR_INVALID_ARG;
+  // the partial logits must fit the fixed scratch array
+  if (noalloc_route_bytes(*p) > noalloc_scratch_bytes()) return MOE_ERR_UNSUPPORTED;
+  if (p->T == 0) return MOE_OK;
+  return hip_status(launch_route_noalloc(*p, x, packed, bias, topk_idx, topk_w, logits,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_counts,
                           int32_t* expert_offsets, int32_t* sorted_token, int32_t* pair_pos,
                           int32_t* token_ready_wave, void* ws, size_t ws_bytes, moe_stream_t stream) {

@@ -134,6 +134,13 @@ hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packe
 // depends on the layer only: d and E_global).
 int router_splits(int d, int E_global, bool x_bf16);
 
+// moe_route_noalloc: bytes of scratch a problem's router needs, the fixed
+// scratch size, and the launch on the fixed device array.
+size_t noalloc_route_bytes(const moe_problem_t& p);
+size_t noalloc_scratch_bytes();
+hipError_t launch_route_noalloc(const moe_problem_t& p, const void* x, const void* packed, const float* bias,
+                                int32_t* topk_idx, float* topk_w, float* logits, hipStream_t s);
+
 hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* sorted_token,
                            int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s);

@@ -34,7 +34,7 @@ EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
     "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
-    "moe_expert_ffn_waved_fp8", "moe_ffn_path",
+    "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "moe_ffn_path": (ctypes.c_int32, [P, ctypes.c_int32, ctypes.c_uint32]),
             "moe_pack_weights": (st, [P, vp, vp, vp, vp, vp, vp]),
             "moe_route": (st, [P, vp, vp, f32p, i32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
+            "moe_route_noalloc": (st, [P, vp, vp, f32p, i32p, f32p, f32p, vp]),
             "moe_dispatch": (st, [P, i32p, i32p, i32p, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]),
             "moe_expert_ffn_waved": (st, [P, vp, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
                                           ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
@@ -174,6 +175,25 @@ def route(p: Problem, x, packed, ws, bias=None, want_logits=False):
     logits = torch.empty((p.T, p.E_global), dtype=torch.float32, device=dev) if want_logits else None
     _check(lib().moe_route(ctypes.byref(p), _p(x), _p(packed), _p(bias), _p(idx), _p(w), _p(logits),
                            _p(ws), ws.numel(), _stream()), "moe_route")
+    return idx, w, logits
+
+
+ROUTE_NOALLOC_MAX_BYTES = 16 << 20
+
+
+def route_noalloc(p: Problem, x, packed, bias=None, want_logits=False, out=None):
+    """moe_route_noalloc: the router without a workspace (its scratch is the
+    library's fixed per-GPU array).  out: optional (idx, w, logits) tensors
+    to write into, so that the call itself allocates nothing."""
+    dev = x.device
+    if out is None:
+        idx = torch.empty((p.T, p.k), dtype=torch.int32, device=dev)
+        w = torch.empty((p.T, p.k), dtype=torch.float32, device=dev)
+        logits = torch.empty((p.T, p.E_global), dtype=torch.float32, device=dev) if want_logits else None
+    else:
+        idx, w, logits = out
+    _check(lib().moe_route_noalloc(ctypes.byref(p), _p(x), _p(packed), _p(bias), _p(idx), _p(w), _p(logits),
+                                   _stream()), "moe_route_noalloc")
     return idx, w, logits
 
 

@@ -172,6 +172,24 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* packed
                        const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
                        void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and the same results bit for bit, with the router's scratch
+ * (its partial logits, splits x T x E_global fp32, splits as described for
+ * moe_route; the fp32 router: T x E_global fp32) in a fixed device array of
+ * MOE_ROUTE_NOALLOC_MAX_BYTES that the library holds on every GPU it runs on
+ * until the process ends, instead of a caller workspace.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); the caller
+ * still passes inputs and outputs as for moe_route.  A problem whose scratch
+ * exceeds the array returns MOE_ERR_UNSUPPORTED before any launch.  Every
+ * call on a GPU uses that GPU's one array: calls that overlap on one GPU
+ * (different streams, threads or processes' graphs) race.  The first call
+ * on each device looks up the array's device address (thread safe). */
+#define MOE_ROUTE_NOALLOC_MAX_BYTES (16u << 20)
+moe_status_t moe_route_noalloc(const moe_problem_t* p, const void* x, const void* packed,
+                               const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                               moe_stream_t stream);
+
 /* Dispatch metadata: a deterministic counting sort of the routed pairs by
  * local expert (10100.com, deterministic operators: pre-sorting instead of
  * unordered atomics).  Inside an expert, pairs are in ascending token order.
