@@ -293,12 +293,14 @@ __host__ __device__ inline void combine_cols(int d, int parts, int part, int& cb
 
 // Combine of token t, 16-byte column chunks [cb, ce), by one wavefront:
 // out[t] = sum_j w[t, j] * y[pair_pos[t, j]] over local picks, fp32 fused
-// multiply-adds in ascending j, one rounding.  Each lane takes two chunks
-// at a time and the picks kCombineGroup at a time; all of a group's loads
-// are issued before its first multiply-add, so a lane keeps up to
-// 2 * kCombineGroup row reads in flight (the accumulation order stays
-// ascending j).
+// multiply-adds in ascending j, one rounding.  Each lane takes
+// kCombineChunks chunks at a time and the picks kCombineGroup at a time; all
+// of a group's loads are issued before its first multiply-add, so a lane
+// keeps up to kCombineChunks * kCombineGroup row reads in flight and a
+// token of d = 4096 with four picks takes two round trips to memory (the
+// accumulation order of every element stays ascending j).
 constexpr int kCombineGroup = 4;
+constexpr int kCombineChunks = 4;
 
 template <bool OUT_BF16>
 __device__ __forceinline__ void combine_store(void* __restrict__ out, int t, int d, int c, const float (&acc)[8]) {
@@ -330,32 +332,40 @@ __device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict_
   const int lane = lane_id();
   const int32_t* pp = pair_pos + static_cast<size_t>(t) * k;
   const float* pw = topk_w + static_cast<size_t>(t) * k;
-  for (int c0 = cb; c0 < ce; c0 += 2 * kWave) {
-    const int c1 = c0 + lane, c2 = c0 + kWave + lane;
-    const bool h1 = c1 < ce, h2 = c2 < ce;
-    float a1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float a2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c0 = cb; c0 < ce; c0 += kCombineChunks * kWave) {
+    int c[kCombineChunks];
+    bool h[kCombineChunks];
+    float acc[kCombineChunks][8];
+#pragma unroll
+    for (int q = 0; q < kCombineChunks; ++q) {
+      c[q] = c0 + q * kWave + lane;
+      h[q] = c[q] < ce;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+    }
     for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
       int r[kCombineGroup];
-      u32x4 v1[kCombineGroup], v2[kCombineGroup];
+      u32x4 v[kCombineGroup][kCombineChunks];
 #pragma unroll
-      for (int q = 0; q < kCombineGroup; ++q) {
-        r[q] = uniform(j0 + q < k ? pp[j0 + q] : -1);
-        if (r[q] >= 0) {
-          if (h1) v1[q] = load_y16<COHERENT>(y, r[q], d, c1 * 8);
-          if (h2) v2[q] = load_y16<COHERENT>(y, r[q], d, c2 * 8);
+      for (int g = 0; g < kCombineGroup; ++g) {
+        r[g] = uniform(j0 + g < k ? pp[j0 + g] : -1);
+        if (r[g] >= 0) {
+#pragma unroll
+          for (int q = 0; q < kCombineChunks; ++q)
+            if (h[q]) v[g][q] = load_y16<COHERENT>(y, r[g], d, c[q] * 8);
         }
       }
 #pragma unroll
-      for (int q = 0; q < kCombineGroup; ++q) {
-        if (r[q] < 0) continue;
-        const float w = pw[j0 + q];
-        combine_fma(w, v1[q], a1);
-        combine_fma(w, v2[q], a2);
+      for (int g = 0; g < kCombineGroup; ++g) {
+        if (r[g] < 0) continue;
+        const float w = pw[j0 + g];
+#pragma unroll
+        for (int q = 0; q < kCombineChunks; ++q) combine_fma(w, v[g][q], acc[q]);
       }
     }
-    if (h1) combine_store<OUT_BF16>(out, t, d, c1, a1);
-    if (h2) combine_store<OUT_BF16>(out, t, d, c2, a2);
+#pragma unroll
+    for (int q = 0; q < kCombineChunks; ++q)
+      if (h[q]) combine_store<OUT_BF16>(out, t, d, c[q], acc[q]);
   }
 }
 
