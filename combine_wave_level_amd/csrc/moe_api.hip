@@ -38,7 +38,8 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.P_max = p.T * (p.k < p.E_local ? p.k : p.E_local);
   L.Ep = static_cast<int>(align_up(static_cast<size_t>(p.E_global), 64));
   L.ctr_region_words = sched_region_words(L.W);
-  L.sync_words = sched_counter_words(L.W) + 1;  // + the persistent kernel's exit count
+  L.sync_words = sched_counter_words(L.W) + 1;  // + the persistent kernel's exit count (the per-XCD
+                                                 // pool counters sit in the last spans of the counters)
   const size_t wg_slots = static_cast<size_t>(L.P_max) / kWgradChunkRows;
   L.wgrad_bytes = wg_slots * 3 * static_cast<size_t>(p.d) * p.I * sizeof(float);
   size_t off = 0;

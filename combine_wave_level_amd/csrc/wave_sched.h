@@ -27,10 +27,17 @@
 //   the GEMM1 tiles of m_i (i < n; their operand loads are the dispatch
 //   pulls),
 //   the GEMM2 tiles of m_{i-L} (i >= L),
-//   the XCD's share of the combine chunks of every ready slot s whose
+//   the XCD's share of the combine chunks of every ready slot s < W whose
 //   position is i (tokens whose last local wave is s-1; slot 0 = tokens with
 //   no local pick): the position of the GEMM2 tiles of the XCD's last m-tile
 //   of a wave <= s + 1.
+// The last slot (W: tokens whose last local wave is the last one, most of
+// the tokens once k is a few waves' worth of experts) is in no stream: a
+// workgroup whose stream is exhausted takes chunks of that slot from its
+// XCD's pool counter (XCD x takes chunks x, x + 8, ...), waiting once for
+// every wave on every XCD before its first chunk, so every workgroup of the
+// chip works on it, each as soon as it is free.  One counter per XCD keeps
+// the claims of 256 workgroups off a single address.
 // The GEMM2 tiles of consecutive m-tiles of one expert are dealt in groups
 // of up to min(kSchedGroup, L) m-tiles (a group never crosses an expert, so
 // never a wave, and starts at a multiple of that size or at the expert's
@@ -355,7 +362,9 @@ __host__ __device__ inline void sched_place(WaveSchedule& S, const int32_t* read
   const int W = S.W, L = S.lag, xcd = S.xcd, n = S.n_local;
   const int npos = n + L;  // positions 0 .. npos - 1
   for (int s = begin; s <= W; s += step) {
-    const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
+    // the last slot is combined from the device-wide pool (no stream tasks)
+    const int chunks =
+        s == W ? 0 : cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     const int mine = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
     const int last = S.loc_pre[s + 2 < W ? s + 2 : W] - 1;
     int at = last >= 0 ? last + L : 0;
@@ -492,6 +501,18 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
   return t;
 }
 
+// The last ready slot's pool: column parts of a chunk (at least two, so
+// each wavefront's share of a token is one pass of its loads for d = 4096)
+// and chunks of kCombineTokens tokens x parts.
+__host__ __device__ inline int sched_pool_parts(int cb_parts) { return cb_parts > 2 ? cb_parts : 2; }
+__host__ __device__ inline int sched_pool_chunks(int ntok, int pparts) {
+  return pparts * ((ntok + kCombineTokens - 1) / kCombineTokens);
+}
+// Chunks of XCD x's share (chunks x, x + kXcds, ...).
+__host__ __device__ inline int sched_pool_share(int nchunks, int x) {
+  return nchunks > x ? (nchunks - x + kXcds - 1) / kXcds : 0;
+}
+
 // Counter layout (int32 words) of the persistent kernel.  Counters touched
 // by different XCDs never share a 256-byte span:
 //   [x * kCtrPad]                   ticket of XCD x
@@ -501,6 +522,8 @@ __host__ __device__ inline Task sched_decode(const WaveSchedule& S, int tk) {
 //   kXcds * (kCtrPad + region_words) + w   GEMM2 tiles of wave w finished, all XCDs
 //   that + pad(W) + j               spread schedules: GEMM1 tiles of m-tile j
 //                                   finished, all XCDs
+//   that + pad(W) + kSchedMaxLocal + x * kCtrPad   XCD x's pool counter of
+//                                   the last ready slot
 // region_words >= W + kSchedMaxLocal, rounded up to kCtrPad (pad).
 __host__ __device__ inline int sched_region_words(int W) {
   return ((W + kSchedMaxLocal + kCtrPad - 1) / kCtrPad) * kCtrPad;
@@ -508,7 +531,7 @@ __host__ __device__ inline int sched_region_words(int W) {
 __host__ __device__ inline int sched_pad_words(int n) { return ((n + kCtrPad - 1) / kCtrPad) * kCtrPad; }
 __host__ __device__ inline size_t sched_counter_words(int W) {
   return static_cast<size_t>(kXcds) * (kCtrPad + sched_region_words(W)) + sched_pad_words(W) + kSchedMaxLocal +
-         kCtrPad;
+         static_cast<size_t>(kXcds) * kCtrPad;
 }
 __host__ __device__ inline int sched_ticket_index(int xcd) { return xcd * kCtrPad; }
 __host__ __device__ inline int sched_g2local_index(const WaveSchedule& S, int rw, int w) {
@@ -523,6 +546,9 @@ __host__ __device__ inline int sched_g2all_index(const WaveSchedule& S, int rw, 
 // spread schedules: GEMM1 tiles of m-tile j finished, all XCDs
 __host__ __device__ inline int sched_g1all_index(const WaveSchedule& S, int rw, int j) {
   return kXcds * (kCtrPad + rw) + sched_pad_words(S.W) + j;
+}
+__host__ __device__ inline int sched_pool_index(int W, int xcd) {
+  return kXcds * (kCtrPad + sched_region_words(W)) + sched_pad_words(W) + kSchedMaxLocal + xcd * kCtrPad;
 }
 
 }  // namespace moe

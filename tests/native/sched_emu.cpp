@@ -11,14 +11,18 @@
 //      eighth of its output tiles; otherwise:) every expert with at most an eighth of all m-tiles lives
 //      on one XCD, the XCDs' m-tile counts differ by at most the largest
 //      dealt chunk; over the 8 streams every GEMM1 / GEMM2 tile (m-tile x
-//      output tile) and every combine chunk has exactly one ticket; both
+//      output tile) and every combine chunk of the slots before the last
+//      has exactly one ticket (the last slot is in no stream); both
 //      GEMM tiles of an m-tile live in the stream of the XCD owning it;
 //      decoded experts own their m-tiles and belong to the decoded wave;
 //      every XCD's counters fit its region;
 //   2. every GEMM2 tile waits only on smaller tickets of its own stream, and
 //      every combine task of slot s comes after all of its stream's GEMM2
 //      tiles of waves < s (no stream can block on its own later tickets);
-//   3. an emulated run completes and every counter ends at its target;
+//   3. an emulated run completes (a thread whose stream is exhausted then
+//      takes its XCD's share of the last slot's chunks from that XCD's pool
+//      counter once every wave of every XCD is done), every counter ends at
+//      its target and every pool chunk is combined once;
 //   4. the schedule equals the one a plain sequential greedy builds (the
 //      definition: every deal to the XCD with the most room, lowest id on
 //      ties, the combine placed by walking the positions), and the kernel's
@@ -147,7 +151,8 @@ static void reference_tables(WaveSchedule& S, const int32_t* offsets, const int3
   int p_time = 0;  // first position whose work reaches need[s] (need grows with s)
   for (int s = 0; s <= W; ++s) {
     S.cb_pre[s] = cb;
-    const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
+    // the last slot is combined from the device-wide pool, in no stream
+    const int chunks = s == W ? 0 : cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     const int mine = chunks > xcd ? (chunks - xcd + kXcds - 1) / kXcds : 0;
     cb += mine;
     // position of the GEMM2 tiles of the last m-tile of a wave <= s + 1
@@ -261,9 +266,13 @@ int main() {
   std::vector<int> g1_ticket(g1_owner.size(), -1), g2_ticket(g2_owner.size(), -1);
   std::vector<std::vector<int>> cb_seen(W + 1);
   for (int s = 0; s <= W; ++s) {
-    const int chunks = cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
+    const int chunks = s == W ? 0 : cb_parts * ((ready_off[s + 1] - ready_off[s] + kCombineTokens - 1) / kCombineTokens);
     cb_seen[s].assign(chunks, 0);
   }
+  // the last slot's pool chunks (only with a fused combine)
+  const int pool_chunks = cb_parts > 0 ? sched_pool_chunks(ready_off[W + 1] - ready_off[W], sched_pool_parts(cb_parts)) : 0;
+  std::vector<std::atomic<int>> pool_seen(pool_chunks);
+  for (auto& c : pool_seen) c.store(0);
   const bool spread = S[0].spread != 0;
   for (int x = 1; x < kXcds; ++x)
     if ((S[x].spread != 0) != spread) fail("spread differs between XCDs", x);
@@ -367,7 +376,16 @@ int main() {
   }
 
   // ---- 3. emulated run
-  const size_t nctr = sched_counter_words(W);
+  const size_t nctr = sched_counter_words(W) + 1;  // + the kernel's exit count
+  for (int x = 0; x < kXcds; ++x)
+    if (static_cast<size_t>(sched_pool_index(W, x)) >= nctr - 1) fail("pool counter outside the counters", x);
+  for (int x = 1; x < kXcds; ++x)
+    if (sched_pool_index(W, x) - sched_pool_index(W, x - 1) < kCtrPad) fail("pool counters share a span", x);
+  {
+    int sum = 0;
+    for (int x = 0; x < kXcds; ++x) sum += sched_pool_share(pool_chunks, x);
+    if (sum != pool_chunks) fail("pool shares do not cover the chunks", sum, pool_chunks);
+  }
   std::vector<std::atomic<int>> ctr(nctr);
   for (auto& c : ctr) c.store(0);
   std::atomic<int> done_tasks{0};
@@ -401,6 +419,21 @@ int main() {
       }
       done_tasks.fetch_add(1);
     }
+    // the stream is exhausted: the last slot from the pool (a thread that
+    // claims a chunk waits once for every wave of every XCD)
+    if (pool_chunks == 0) return;
+    bool waited = false;
+    const int mine = sched_pool_share(pool_chunks, x);
+    for (;;) {
+      const int j = ctr[sched_pool_index(W, x)].fetch_add(1, std::memory_order_relaxed);
+      if (j >= mine) break;
+      const int c = x + kXcds * j;
+      if (!waited)
+        for (int w = 0; w < W; ++w) wait_geq(sched_g2all_index(s, rw, w), sched_g2_all(s, w));
+      waited = true;
+      if (rng() % 4 == 0) std::this_thread::sleep_for(std::chrono::microseconds(rng() % 100));
+      pool_seen[c].fetch_add(1);
+    }
   };
   std::vector<std::thread> th;
   for (int x = 0; x < kXcds; ++x)
@@ -417,6 +450,8 @@ int main() {
       if (ctr[sched_g1all_index(S[0], rw, j)].load() != NT1) fail("g1all count", j);
   for (int w = 0; w < W; ++w)
     if (ctr[sched_g2all_index(S[0], rw, w)].load() != sched_g2_all(S[0], w)) fail("g2 all count", w);
+  for (int c = 0; c < pool_chunks; ++c)
+    if (pool_seen[c].load() != 1) fail("pool chunk not combined once", c);
   int max_group = 0;
   for (int x = 0; x < kXcds; ++x)
     for (int j = 0; j < S[x].n_local; ++j) max_group = std::max(max_group, S[x].grp[j] >> 16);
