@@ -3,12 +3,14 @@
 Default workload (the mid layer): T=4096 tokens, d=4096, I=1024, 16 experts,
 top-4, 4 experts per wave, bf16 with fp32 accumulation; synthetic seeded
 inputs (x ~ N(0,1), weights ~ N(0, 0.02)).  A step is one pass of the layer's
-hot path over the batch: router, dispatch, and the persistent expert-wave
-kernel (pull, GEMM1 + SwiGLU, GEMM2, fused combine), all inputs resident in
-HBM.  One JSON line is printed on stdout.
+hot path over the batch: router, dispatch, and the expert FFN in waves (pull,
+GEMM1 + SwiGLU, GEMM2, fused combine) on the schedule the library picks for
+the shape (the persistent expert-wave kernel on the mid layer; --serial and
+--persistent force the phase kernels or the persistent kernel), all inputs
+resident in HBM.  One JSON line is printed on stdout.
 
     python bench.py [--steps K] [--warmup W] [--workload mid|v4share|decode|stress]
-                    [--T T] [--no-cpu] [--serial] [--no-backward]
+                    [--T T] [--no-cpu] [--serial | --persistent] [--no-backward]
 
 The step is the forward (the metric's configuration is a forward).  The same
 run also times the layer's backward on the same batch (data gradient,
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--serial", action="store_true", help="time the phase-by-phase path")
+    ap.add_argument("--persistent", action="store_true",
+                    help="time the persistent expert-wave kernel wherever it fits")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8-dispatch forward")
@@ -257,9 +261,9 @@ def roofline_of(d, I, T, counts):
 
 
 def time_rows(args, stream):
-    """Each row: the workload's router, dispatch and persistent expert-wave
-    kernel, timed per step between events (median of the steps), and the
-    expert FFN call alone the same way; for the weight-streaming rows a
+    """Each row: the workload's router, dispatch and expert FFN (on the
+    schedule the library picks), timed per step between events (median of
+    the steps), and the expert FFN call alone the same way; for the weight-streaming rows a
     512 MiB buffer is written before every timed step and call, outside the
     events.  The expert weights are drawn on the device (seeded, N(0, 0.02),
     bf16): only the routing depends on values, and x, Wg and the bias come
@@ -329,7 +333,9 @@ def time_rows(args, stream):
         moe.check_error(ws)
         counts = cache["disp"].counts.cpu().numpy().astype(np.int64)
         flops, nbytes, mfma, P_local = roofline_of(wl.d, wl.I, T, counts)
-        row = {"workload": name, "T": T, "step_ms": round(res["step"], 4), "ffn_ms": round(res["ffn"], 4),
+        path = moe.ffn_path(p, torch.cuda.get_device_properties(dev).multi_processor_count)
+        row = {"workload": name, "T": T, "ffn_path": "persistent" if path == moe.MOE_PATH_PERSISTENT else "phases",
+               "step_ms": round(res["step"], 4), "ffn_ms": round(res["ffn"], 4),
                "tokens_per_s": round(T / (res["step"] * 1e-3), 1), "local_pairs": P_local,
                "experts_touched": int((counts > 0).sum()), "bound": "mfma" if mfma else "hbm",
                "mall_flushed": stream_w}
@@ -394,7 +400,12 @@ def main():
             raise moe.MoEError(st, where)
 
     nws = ws.numel()
-    flags = moe.MOE_FLAG_SERIAL if args.serial else 0
+    if args.serial and args.persistent:
+        raise SystemExit("--serial and --persistent exclude each other")
+    flags = moe.MOE_FLAG_SERIAL if args.serial else (moe.MOE_FLAG_PERSISTENT if args.persistent else 0)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    path = moe.ffn_path(p, cus, serial=args.serial, persistent=args.persistent)
+    persistent_path = path == moe.MOE_PATH_PERSISTENT
 
     def step(ev=None, fl=flags):
         if ev is not None:
@@ -508,26 +519,33 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["kernel"] = "ffn_waved_kernel" if not args.serial else "gemm1_phase_kernel+gemm2_phase_kernel+combine_kernel"
+    roof["kernel"] = ("ffn_waved_kernel" if persistent_path
+                      else "gemm1_phase_kernel+gemm2_phase_kernel+combine_kernel")
     # HBM bytes per launch from the committed rocprofv3 counter runs
     # (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy), reported only
     # while the kernel sources are the ones that were measured
     from combine_wave_level_amd import profiling
-    trec = None if args.serial else profiling.load_traffic(
+    trec = None if not persistent_path else profiling.load_traffic(
         os.path.join(ROOT, "profiles", f"traffic_ffn_waved_kernel_{wl.name}_T{T}.json"), wl.name, T)
     roof["traffic"] = trec["traffic_bytes"] if trec else None
 
-    extra = {"ffn_ms": round(ffn_ms, 4),
+    extra = {"ffn_path": "persistent" if persistent_path else "phases", "ffn_ms": round(ffn_ms, 4),
              "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
              "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched,
              "host_us_per_abi_call": round(host_us_per_call, 2), "host_us_rejected_call": round(host_us_rejected, 2),
              "instrumented_pass": inst}
-    if not args.serial:
+    if not args.serial and not args.persistent:
+        # both schedules forced (same bits): the phase kernels, and the
+        # persistent kernel wherever it fits
         n_s = max(3, args.steps // 4)
         extra["serial_ms_per_step"] = round(timed(n_s, moe.MOE_FLAG_SERIAL), 4)
         s_ffn = ffn_launches(n_s, moe.MOE_FLAG_SERIAL)
         extra["serial_ffn_ms"] = round(s_ffn, 4)
-        extra["overlap_speedup_ffn"] = round(s_ffn / ffn_ms, 3)
+        if moe.ffn_path(p, cus, persistent=True) == moe.MOE_PATH_PERSISTENT:
+            p_ffn = ffn_launches(n_s, moe.MOE_FLAG_PERSISTENT)
+            extra["persistent_ffn_ms"] = round(p_ffn, 4)
+            extra["overlap_speedup_ffn"] = round(s_ffn / p_ffn, 3)
+        extra["speedup_vs_phases_ffn"] = round(s_ffn / ffn_ms, 3)
 
     if not args.no_fp8:
         extra["fp8_dispatch"] = time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y, L,
@@ -558,7 +576,7 @@ def main():
         "data": "synthetic (seeded x ~ N(0,1), weights ~ N(0,0.02), random-init)",
         "config": {"workload": f"{wl.name}: T={T} d={wl.d} I={wl.I} experts {wl.E_local} local of "
                                f"{wl.E_global}, top-{wl.k}, {wl.G} experts per wave, "
-                               f"{'serial phases' if args.serial else 'persistent expert-wave kernel'}",
+                               f"{'persistent expert-wave kernel' if persistent_path else 'phase kernels'}",
                    "T": T, "d": wl.d, "I": wl.I, "E_global": wl.E_global, "E_local": wl.E_local,
                    "k": wl.k, "experts_per_wave": wl.G},
         "roofline": roof,

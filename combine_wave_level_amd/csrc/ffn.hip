@@ -537,6 +537,36 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
 
 }  // namespace
 
+// The schedule the library picks when the caller does not force one.  Both
+// give the same bits.  The persistent kernel hides the combine of finished
+// waves under later waves' GEMMs and has no phase boundaries, but it deals
+// the work to the XCDs in whole m-tiles (whole experts for the large tile
+// shapes) and keeps an m-tile's GEMM1 -> GEMM2 hand-off inside one XCD;
+// the phase kernels spread every phase's tiles over all 256 CUs.  Measured
+// on MI355X, FFN with the fused combine, persistent against phases:
+//   mid layer, T=4096, 16 experts, top-4 (1024 rows per expert):
+//     0.514 against 0.533 ms;
+//   stress layer, T=4096, 64 experts, top-6, one hot expert (384 rows per
+//     expert on average): 1.31 against 1.36 ms;
+//   V3/V4-scale share, T=8192, 32 of 256 experts, top-8 (256 rows per
+//     expert: about one m-tile each, so the XCDs' loads differ by whole
+//     m-tiles): 1.21 against 1.20 ms;
+//   stress layer, T=16384 (98304 local rows): 4.24 to 4.32 against 4.02 to
+//     4.07 ms;
+//   decode, T = 1, 32, 128 (small tile shapes, weight streaming): 7 to 12%
+//     slower (2.6% faster at T = 8).
+// Hence: the persistent kernel for the large tile shapes when the experts
+// average at least one and a half m-tiles and the share holds at most
+// 32768 expected local rows (uniform routing assumed, as for the tile
+// shape); the phases otherwise.
+bool ffn_prefers_persistent(const moe_problem_t& p) {
+  const FfnShape shape = pick_ffn_shape(p);
+  if (shape != FfnShape::Large && shape != FfnShape::Mid) return false;
+  const double rows_per_expert = static_cast<double>(p.T) * p.k / p.E_global;
+  const double local_rows = rows_per_expert * p.E_local;
+  return rows_per_expert >= 1.5 * ffn_mtile_rows(p) && local_rows <= 32768.0;
+}
+
 bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags) {
   if (flags & MOE_FLAG_SERIAL) return false;
   // every per-XCD ticket stream needs workgroups: the whole device
@@ -546,7 +576,8 @@ bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags) {
   const int W = p.E_local / p.experts_per_wave;
   const long long P_max = static_cast<long long>(p.T) * (p.k < p.E_local ? p.k : p.E_local);
   const long long mt_bound = P_max / ffn_mtile_rows(p) + p.E_local + 1;
-  return mt_bound / kXcds + W + 1 <= kSchedMaxLocal;
+  if (mt_bound / kXcds + W + 1 > kSchedMaxLocal) return false;
+  return (flags & MOE_FLAG_PERSISTENT) || ffn_prefers_persistent(p);
 }
 
 hipError_t fill_zero(void* p, size_t n, hipStream_t s) {

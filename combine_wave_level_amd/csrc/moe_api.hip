@@ -12,6 +12,12 @@ namespace moe {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// FFN flags: MOE_FLAG_SERIAL or MOE_FLAG_PERSISTENT, not both.
+static bool ffn_flags_ok(uint32_t flags) {
+  const uint32_t both = MOE_FLAG_SERIAL | MOE_FLAG_PERSISTENT;
+  return (flags & ~both) == 0 && (flags & both) != both;
+}
+
 static moe_status_t check_problem(const moe_problem_t* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
   if (p->T < 0 || p->d <= 0 || p->I <= 0 || p->E_global <= 0 || p->k <= 0 || p->E_local <= 0 ||
@@ -108,7 +114,7 @@ size_t moe_workspace_size(const moe_problem_t* p, uint32_t flags) {
 int32_t moe_ffn_path(const moe_problem_t* p, int32_t num_cus, uint32_t flags) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (num_cus <= 0 || (flags & ~MOE_FLAG_SERIAL)) return MOE_ERR_INVALID_ARG;
+  if (num_cus <= 0 || !ffn_flags_ok(flags)) return MOE_ERR_INVALID_ARG;
   return ffn_uses_persistent(*p, num_cus, flags) ? MOE_PATH_PERSISTENT : MOE_PATH_PHASES;
 }
 
@@ -187,7 +193,7 @@ moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const v
                                   uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (flags & ~MOE_FLAG_SERIAL) return MOE_ERR_INVALID_ARG;
+  if (!ffn_flags_ok(flags)) return MOE_ERR_INVALID_ARG;
   if (!packed || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !sorted_token || !y)) return MOE_ERR_INVALID_ARG;
   if (out && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
@@ -217,7 +223,7 @@ moe_status_t moe_expert_ffn_waved_fp8(const moe_problem_t* p, const uint8_t* x_f
                                       moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (flags & ~MOE_FLAG_SERIAL) return MOE_ERR_INVALID_ARG;
+  if (!ffn_flags_ok(flags)) return MOE_ERR_INVALID_ARG;
   if (!packed || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x_fp8 || !x_scale || !sorted_token || !y)) return MOE_ERR_INVALID_ARG;
   if (out && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARG;

@@ -24,6 +24,7 @@ MOE_ERR_TIMEOUT = -5
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_SERIAL = 0x1
+MOE_FLAG_PERSISTENT = 0x2
 MOE_ACT_SWIGLU = 0
 MOE_ACT_RELU2 = 1
 MOE_WS_BACKWARD = 0x1
@@ -137,10 +138,15 @@ def workspace_size(p: Problem, backward: bool = False) -> int:
     return int(lib().moe_workspace_size(ctypes.byref(p), MOE_WS_BACKWARD if backward else 0))
 
 
-def ffn_path(p: Problem, num_cus: int, serial: bool = False) -> int:
+def _ffn_flags(serial: bool, persistent: bool) -> int:
+    return (MOE_FLAG_SERIAL if serial else 0) | (MOE_FLAG_PERSISTENT if persistent else 0)
+
+
+def ffn_path(p: Problem, num_cus: int, serial: bool = False, persistent: bool = False) -> int:
     """MOE_PATH_PERSISTENT or MOE_PATH_PHASES: the schedule the expert FFN
-    runs on a device with num_cus compute units."""
-    r = int(lib().moe_ffn_path(ctypes.byref(p), int(num_cus), MOE_FLAG_SERIAL if serial else 0))
+    runs on a device with num_cus compute units (serial / persistent: the
+    flags MOE_FLAG_SERIAL / MOE_FLAG_PERSISTENT)."""
+    r = int(lib().moe_ffn_path(ctypes.byref(p), int(num_cus), _ffn_flags(serial, persistent)))
     if r < 0:
         raise MoEError(r, "moe_ffn_path")
     return r
@@ -230,13 +236,13 @@ def _out_dtype(p: Problem):
 
 
 def ffn_waved(p: Problem, x, packed, disp: Dispatch, topk_w, ws, fused_combine=True,
-              serial=False, y=None, out=None):
+              serial=False, y=None, out=None, persistent=False):
     dev = x.device
     if y is None:
         y = torch.empty((max(1, p_max(p)), p.d), dtype=torch.bfloat16, device=dev)
     if fused_combine and out is None:
         out = torch.empty((p.T, p.d), dtype=_out_dtype(p), device=dev)
-    flags = MOE_FLAG_SERIAL if serial else 0
+    flags = _ffn_flags(serial, persistent)
     _check(lib().moe_expert_ffn_waved(
         ctypes.byref(p), _p(x), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
         _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y),
@@ -254,14 +260,14 @@ def quantize_fp8(p: Problem, x):
 
 
 def ffn_waved_fp8(p: Problem, x8, x_scale, packed, disp: Dispatch, topk_w, ws, fused_combine=True,
-                  serial=False, y=None, out=None):
+                  serial=False, y=None, out=None, persistent=False):
     """moe_expert_ffn_waved with the staging buffer in FP8 (from quantize_fp8)."""
     dev = x8.device
     if y is None:
         y = torch.empty((max(1, p_max(p)), p.d), dtype=torch.bfloat16, device=dev)
     if fused_combine and out is None:
         out = torch.empty((p.T, p.d), dtype=_out_dtype(p), device=dev)
-    flags = MOE_FLAG_SERIAL if serial else 0
+    flags = _ffn_flags(serial, persistent)
     _check(lib().moe_expert_ffn_waved_fp8(
         ctypes.byref(p), _p(x8), _p(x_scale), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
         _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y), _p(out) if fused_combine else None,
@@ -330,9 +336,9 @@ def check_error(ws) -> None:
     _check(lib().moe_check_error(_p(ws), _stream()), "moe_check_error")
 
 
-def forward(p: Problem, x, packed, ws, bias=None, serial=False, want_logits=False):
+def forward(p: Problem, x, packed, ws, bias=None, serial=False, want_logits=False, persistent=False):
     """route -> dispatch -> waved expert FFN with fused combine."""
     idx, w, logits = route(p, x, packed, ws, bias=bias, want_logits=want_logits)
     disp = dispatch(p, idx, ws)
-    y, out = ffn_waved(p, x, packed, disp, w, ws, fused_combine=True, serial=serial)
+    y, out = ffn_waved(p, x, packed, disp, w, ws, fused_combine=True, serial=serial, persistent=persistent)
     return {"idx": idx, "w": w, "logits": logits, "disp": disp, "y": y, "out": out}

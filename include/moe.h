@@ -88,10 +88,14 @@ typedef struct {
   int32_t activation;       /* moe_activation_t of the experts             */
 } moe_problem_t;
 
-/* Flags for moe_expert_ffn_waved. */
+/* Flags for moe_expert_ffn_waved (at most one of the two).  With neither,
+ * the library picks the schedule (moe_ffn_path). */
 #define MOE_FLAG_SERIAL 0x1u /* run gather+GEMM1, GEMM2, combine as separate
                                 grid-wide phases instead of the persistent
                                 expert-wave kernel (same bits, no overlap)   */
+#define MOE_FLAG_PERSISTENT 0x2u /* run the persistent expert-wave kernel
+                                whenever it fits, also where the library
+                                would pick the phases (same bits)            */
 
 /* ------------------------------------------------------------ sizing */
 
@@ -119,8 +123,15 @@ size_t moe_workspace_size(const moe_problem_t* p, uint32_t flags);
  *     without workgroups) and at most 512 m-tiles per XCD;
  *   MOE_PATH_PHASES: gather + GEMM1, GEMM2 and combine as grid-wide phases
  *     (MOE_FLAG_SERIAL, or when the persistent kernel does not fit).
- * Both give the same bits.  The library calls this with the current
- * device's CU count.  Returns a moe_status_t (< 0) on a bad argument. */
+ * With neither flag the library picks: the persistent kernel for batches
+ * that run the large tile shapes (at least 96 routed rows per expert) when
+ * the experts average at least one and a half m-tiles and the share holds
+ * at most 32768 expected local rows (T k E_local / E_global), the phases
+ * otherwise (small-batch weight streaming, about one m-tile per expert, or
+ * very long batches), where they measured faster.  MOE_FLAG_PERSISTENT
+ * takes the persistent kernel whenever it fits.  Both schedules give the
+ * same bits.  The library calls this with the current device's CU count.
+ * Returns a moe_status_t (< 0) on a bad argument. */
 #define MOE_PATH_PERSISTENT 0
 #define MOE_PATH_PHASES 1
 int32_t moe_ffn_path(const moe_problem_t* p, int32_t num_cus, uint32_t flags);
@@ -216,7 +227,9 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx,
  *   kernel (tokens with no local pick get zeros).
  * Each GEMM accumulates in fp32 over K in one fixed ascending order with one
  * MFMA shape, never split; a is rounded to bf16 before the second GEMM and y
- * is rounded to bf16.  flags: MOE_FLAG_SERIAL or 0.
+ * is rounded to bf16.  flags: 0 (the library picks the schedule, see
+ * moe_ffn_path), MOE_FLAG_SERIAL or MOE_FLAG_PERSISTENT; any other value is
+ * MOE_ERR_INVALID_ARG.
  * After one moe_dispatch the call may be repeated on the same workspace any
  * number of times: moe_dispatch zeroes the persistent kernel's tickets and
  * counters, and every launch zeroes them again as it ends.  Calls that

@@ -87,8 +87,10 @@ class Layer:
         return other
 
     def forward(self, serial=False, want_logits=True):
+        """The layer on the phase kernels (serial) or the persistent kernel
+        (forced, whatever schedule the library would pick)."""
         r = moe.forward(self.p, self.x, self.packed, self.ws, bias=self.bias, serial=serial,
-                        want_logits=want_logits)
+                        want_logits=want_logits, persistent=not serial)
         torch.cuda.synchronize()
         moe.check_error(self.ws)
         return r
@@ -99,7 +101,7 @@ class Layer:
         w_d = torch.from_numpy(w.astype(np.float32)).cuda()
         disp = moe.dispatch(self.p, idx_d, self.ws)
         y, out = moe.ffn_waved(self.p, self.x, self.packed, disp, w_d, self.ws, fused_combine=fused,
-                               serial=serial)
+                               serial=serial, persistent=not serial)
         torch.cuda.synchronize()
         moe.check_error(self.ws)
         return disp, y, out, w_d

@@ -138,14 +138,14 @@ def test_forward_stays_inside_the_forward_workspace(name, T):
     ws = buf[:n]
     big = moe.workspace(L.p, backward=True)
     for serial in (False, True):
-        a = moe.forward(L.p, L.x, L.packed, ws, bias=L.bias, serial=serial)
-        b = moe.forward(L.p, L.x, L.packed, big, bias=L.bias, serial=serial)
+        a = moe.forward(L.p, L.x, L.packed, ws, bias=L.bias, serial=serial, persistent=not serial)
+        b = moe.forward(L.p, L.x, L.packed, big, bias=L.bias, serial=serial, persistent=not serial)
         torch.cuda.synchronize()
         moe.check_error(ws)
         moe.check_error(big)
         assert torch.equal(a["out"], b["out"]) and torch.equal(a["idx"], b["idx"])
         x8, sc = moe.quantize_fp8(L.p, L.x)
-        moe.ffn_waved_fp8(L.p, x8, sc, L.packed, a["disp"], a["w"], ws, serial=serial)
+        moe.ffn_waved_fp8(L.p, x8, sc, L.packed, a["disp"], a["w"], ws, serial=serial, persistent=not serial)
         torch.cuda.synchronize()
         moe.check_error(ws)
     assert (buf[n:] == 0xA5).all()
@@ -221,7 +221,7 @@ def test_persistent_back_to_back_on_one_dispatch(name, T):
     for _ in range(4):
         y.view(torch.int16).fill_(0x7F7F)
         out.view(torch.int16).fill_(0x7F7F)
-        moe.ffn_waved(L.p, L.x, L.packed, disp, w, L.ws, y=y, out=out)
+        moe.ffn_waved(L.p, L.x, L.packed, disp, w, L.ws, y=y, out=out, persistent=True)
         torch.cuda.synchronize()
         moe.check_error(L.ws)
         assert torch.equal(out, out_ref)
@@ -284,3 +284,26 @@ def test_edge_k_equals_E_and_single_expert():
     ref = oracle.forward_tokens(o["x"], idx1, w_d.cpu().numpy().astype(np.float64), sub["W1"].astype(np.float64),
                                 sub["W3"].astype(np.float64), sub["W2"].astype(np.float64), 2, 1)
     assert rel_err_rows(host_f64(out), ref) <= OUT_TOL
+
+
+@pytest.mark.parametrize("name,T,want", [("mid", 4096, "persistent"), ("stress", 4096, "persistent"),
+                                         ("decode", 1, "phases"), ("v4share", 2048, "phases")])
+def test_default_schedule_choice_gives_the_same_bits(name, T, want):
+    """With no flag the library picks the schedule (moe_ffn_path on the
+    device's CU count); the call gives the bits of both forced schedules."""
+    L = Layer(inputs(name, T=T))
+    print(f"[case] default schedule {name} T={T}", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    path = moe.ffn_path(L.p, cus)
+    if cus == 256:
+        assert path == (moe.MOE_PATH_PERSISTENT if want == "persistent" else moe.MOE_PATH_PHASES)
+    a = moe.forward(L.p, L.x, L.packed, L.ws, bias=L.bias)
+    torch.cuda.synchronize()
+    moe.check_error(L.ws)
+    P = int(a["disp"].offsets[-1])
+    for forced in ({"serial": True}, {"persistent": True}):
+        b = moe.forward(L.p, L.x, L.packed, L.ws, bias=L.bias, **forced)
+        torch.cuda.synchronize()
+        moe.check_error(L.ws)
+        assert torch.equal(a["out"], b["out"]), forced
+        assert torch.equal(a["y"][:P], b["y"][:P]), forced

@@ -85,13 +85,13 @@ def _ffn_compare(inp, serial):
     disp = moe.dispatch(L.p, idx_d, L.ws)
     x8 = torch.from_numpy(codes).cuda()
     sc = torch.from_numpy(scale.astype(np.float32)).cuda()
-    y8, out8 = moe.ffn_waved_fp8(L.p, x8, sc, L.packed, disp, w_d, L.ws, serial=serial)
+    y8, out8 = moe.ffn_waved_fp8(L.p, x8, sc, L.packed, disp, w_d, L.ws, serial=serial, persistent=not serial)
     torch.cuda.synchronize()
     moe.check_error(L.ws)
     # the bf16 path on the dequantized rows
     xq = x_deq.astype(np.float32) if inp["x"].dtype == np.float32 else bf16_bits(x_deq.astype(np.float32))
     assert (f64(xq) == x_deq).all()
-    yb, outb = moe.ffn_waved(L.p, dev(xq), L.packed, disp, w_d, L.ws, serial=serial)
+    yb, outb = moe.ffn_waved(L.p, dev(xq), L.packed, disp, w_d, L.ws, serial=serial, persistent=not serial)
     torch.cuda.synchronize()
     moe.check_error(L.ws)
     P = int(disp.offsets[-1].item())

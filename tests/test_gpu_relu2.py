@@ -160,11 +160,11 @@ def test_relu2_fp8_dispatch_equals_bf16_path_on_dequantized_rows(name, T, serial
     idx_d = torch.from_numpy(idx_o.astype(np.int32)).cuda()
     w_d = torch.from_numpy(w_o.astype(np.float32)).cuda()
     disp = moe.dispatch(L.p, idx_d, L.ws)
-    y8, out8 = moe.ffn_waved_fp8(L.p, x8, sc, L.packed, disp, w_d, L.ws, serial=serial)
+    y8, out8 = moe.ffn_waved_fp8(L.p, x8, sc, L.packed, disp, w_d, L.ws, serial=serial, persistent=not serial)
     torch.cuda.synchronize()
     moe.check_error(L.ws)
     xq = bf16_bits(x_deq.astype(np.float32))
-    yb, outb = moe.ffn_waved(L.p, dev(xq), L.packed, disp, w_d, L.ws, serial=serial)
+    yb, outb = moe.ffn_waved(L.p, dev(xq), L.packed, disp, w_d, L.ws, serial=serial, persistent=not serial)
     torch.cuda.synchronize()
     moe.check_error(L.ws)
     P = int(disp.offsets[-1].item())
