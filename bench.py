@@ -260,12 +260,52 @@ def roofline_of(d, I, T, counts):
     return flops, nbytes, mfma, P_local
 
 
+def time_graph_step(step, stream, flush, out, n):
+    """The row's whole step (route, dispatch, FFN) captured once in a HIP
+    graph and replayed n times, each replay timed alone between events on
+    the launch stream (after the cache flush when one is given); the replays'
+    output must equal the eager step's bits."""
+    import numpy as np
+    import torch
+
+    try:
+        step()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):   # warm the capture stream
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(i & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        if not torch.equal(out, ref):
+            return {"graph_error": "replayed output differs from the eager step"}
+        return {"step_ms_graph": round(float(np.median(ts)), 4)}
+    except RuntimeError as exc:   # capture refused: reported, the eager figures stand
+        return {"graph_error": str(exc)[:200]}
+
+
 def time_rows(args, stream):
     """Each row: the workload's router, dispatch and expert FFN (on the
     schedule the library picks), timed per step between events (median of
     the steps), and the expert FFN call alone the same way; for the weight-streaming rows a
     512 MiB buffer is written before every timed step and call, outside the
-    events.  The expert weights are drawn on the device (seeded, N(0, 0.02),
+    events.  The step is also captured in a HIP graph and its replays timed
+    the same way (step_ms_graph).  The expert weights are drawn on the device (seeded, N(0, 0.02),
     bf16): only the routing depends on values, and x, Wg and the bias come
     from the workload generator."""
     import numpy as np
@@ -332,13 +372,15 @@ def time_rows(args, stream):
             res[kind] = float(np.median(ts))
         moe.check_error(ws)
         counts = cache["disp"].counts.cpu().numpy().astype(np.int64)
+        graph = time_graph_step(step, stream, flush if stream_w else None, out, max(10, args.steps))
+        moe.check_error(ws)
         flops, nbytes, mfma, P_local = roofline_of(wl.d, wl.I, T, counts)
         path = moe.ffn_path(p, torch.cuda.get_device_properties(dev).multi_processor_count)
         row = {"workload": name, "T": T, "ffn_path": "persistent" if path == moe.MOE_PATH_PERSISTENT else "phases",
                "step_ms": round(res["step"], 4), "ffn_ms": round(res["ffn"], 4),
                "tokens_per_s": round(T / (res["step"] * 1e-3), 1), "local_pairs": P_local,
                "experts_touched": int((counts > 0).sum()), "bound": "mfma" if mfma else "hbm",
-               "mall_flushed": stream_w}
+               "mall_flushed": stream_w, **graph}
         for lvl, ms in (("ffn", res["ffn"]), ("step", res["step"])):
             row[f"{lvl}_hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
             row[f"{lvl}_mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
