@@ -41,6 +41,9 @@
 //     own partial slot; then dW_e += partial slots in ascending chunk order.
 // Every per-token result (dx, dw, dl) depends on the token's own rows only,
 // so it is batch invariant as the forward is.
+#include <mutex>
+#include <vector>
+
 #include "ffn_parts.h"
 #include "moe_internal.h"
 
@@ -839,6 +842,54 @@ hipError_t launch_dh(const moe_problem_t& p, const WsLayout& L, const BackwardAr
   return hipGetLastError();
 }
 
+// The weight gradient's branch (the transposed x and dout rows, then the
+// weight-gradient tiles and their reduction) shares no buffer with the data
+// gradient's branch (gate, dx rows, scatter, dWg) and runs on a second stream
+// of the device, forked from and joined back into the caller's stream with
+// events: the CUs one branch leaves idle at the tail of a kernel, or while
+// an HBM-bound kernel runs, take the other branch's tiles.  Every kernel
+// computes what it computed in order; only their overlap changes, never a
+// bit.  The stream is created once per device (default priority, not
+// blocking on the null stream) and kept; the events belong to one call.
+hipError_t side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static std::vector<hipStream_t> streams;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<size_t>(dev) >= streams.size()) streams.resize(dev + 1, nullptr);
+  if (!streams[dev] && (e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking)) != hipSuccess) {
+    streams[dev] = nullptr;
+    return e;
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+
+struct ForkEvents {
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  hipError_t create() {
+    for (auto& e : ev) {
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+  // destroying an event whose waits are enqueued is allowed: its resources
+  // are released once it completes
+  ~ForkEvents() {
+    for (auto e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
+
+// s2 continues after everything enqueued on s so far.
+hipError_t fork_to(hipStream_t s, hipStream_t s2, hipEvent_t ev) {
+  hipError_t e = hipEventRecord(ev, s);
+  return e != hipSuccess ? e : hipStreamWaitEvent(s2, ev, 0);
+}
+
 }  // namespace
 
 hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, char* ws,
@@ -880,6 +931,27 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     if (a.dWg) return fill_zero(a.dWg, static_cast<size_t>(p.d) * p.E_global, s);
     return hipSuccess;
   }
+  // the weight-gradient branch on s2: the transposes now (they need only x
+  // and dout), the tiles once the recompute below has run
+  hipStream_t s2 = s;
+  ForkEvents fk;
+  if (want_dw) {
+    if ((e = side_stream(&s2)) != hipSuccess) return e;
+    if ((e = fk.create()) != hipSuccess) return e;
+    if ((e = fork_to(s, s2, fk.ev[0])) != hipSuccess) return e;
+    bwd_gather_t_kernel<<<dim3(L.P_pad / 64, p.d / 64), 256, 0, s2>>>(
+        xb, static_cast<const uint16_t*>(a.dout), a.offsets, a.sorted_token, p.E_local, p.d, L.P_pad, xst, dst);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // joins s2 back into s (also after a failed launch, so that no work of
+  // this call is left behind on s2)
+  auto finish = [&](hipError_t r) {
+    if (want_dw) {
+      const hipError_t j = fork_to(s2, s, fk.ev[2]);
+      if (r == hipSuccess) r = j;
+    }
+    return r;
+  };
   float* g = reinterpret_cast<float*>(ws + L.bwd_g);
   if (p.I % FfnLarge::G1::BW == 0)
     e = launch_g<FfnLarge::G1>(p, a, w2b, g, cus, s);
@@ -887,25 +959,36 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     e = launch_g<BwdCfg>(p, a, w2b, g, cus, s);
   else
     e = launch_g<BwdCfgG>(p, a, w2b, g, cus, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) return finish(e);
   if ((2 * p.I) % BwdCfgL::BW == 0)
     e = launch_dh<BwdCfgL>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
   else
     e = launch_dh<BwdCfg>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) return finish(e);
+  if (want_dw) {
+    if ((e = fork_to(s, s2, fk.ev[1])) != hipSuccess) return finish(e);
+    if ((2 * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G1::BW == 0)
+      e = launch_wgrad<FfnLarge::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s2);
+    else
+      e = launch_wgrad<FfnMid::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s2);
+    if (e != hipSuccess) return finish(e);
+    wgrad_reduce_kernel<<<cus * 4, 256, 0, s2>>>(a.offsets, p.E_local, static_cast<size_t>(p.d) * p.I, a.dW1,
+                                                 a.dW3, a.dW2, partial);
+    if ((e = hipGetLastError()) != hipSuccess) return finish(e);
+  }
   if (want_data) {
     const uint16_t* w13t = reinterpret_cast<const uint16_t*>(pb + BL.w13t);
     const void* wgt = pb + BL.wgt;
     bwd_gate_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(dwp, p.I / 16, a.pair_pos, a.topk_idx, a.topk_w, p.T, p.k,
                                                   p.E_global, L.Ep, a.dtopk_w, dlc, a.dlogits, dld);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return finish(e);
     switch (pick_dx_shape(p)) {
       case DxShape::Small: e = launch_dx_gemm<FfnSmall>(p, dh, w13t, a.offsets, dxr, cus, s); break;
       case DxShape::Small64: e = launch_dx_gemm<FfnSmall64>(p, dh, w13t, a.offsets, dxr, cus, s); break;
       case DxShape::Large: e = launch_dx_gemm<FfnLarge>(p, dh, w13t, a.offsets, dxr, cus, s); break;
       default: e = launch_dx_gemm<FfnMid>(p, dh, w13t, a.offsets, dxr, cus, s); break;
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) return finish(e);
     const int parts = combine_parts(p.T, p.d);
     const dim3 grid((p.T + 3) / 4, parts);
     if (xbf)
@@ -914,7 +997,7 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     else
       bwd_dx_scatter_kernel<false><<<grid, 256, 0, s>>>(dxr, a.pair_pos, a.topk_idx, dlc, wgt, p.T, p.k, p.d,
                                                         p.E_global, parts, a.dx);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return finish(e);
     if (a.dWg) {
       const size_t n = static_cast<size_t>(p.d) * p.E_global;
       const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
@@ -922,28 +1005,17 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
         using C = TileCfg<128, 128, 2, 2, 64, 2>;
         float* part = reinterpret_cast<float*>(ws + L.bwd_dwg);
         bwd_dwg_kernel<<<cus * 2, 256, C::LDS_BYTES, s>>>(dld, xb, p.T, p.d, L.Ep, part);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return finish(e);
         bwd_dwg_reduce_kernel<<<blocks, 256, 0, s>>>(part, (p.T + kDwgChunkRows - 1) / kDwgChunkRows, p.d,
                                                      p.E_global, L.Ep, a.dWg);
       } else {
         bwd_dwg_f32_kernel<<<blocks, 256, 0, s>>>(static_cast<const float*>(a.x), a.topk_idx, dlc, p.T, p.k,
                                                   p.d, p.E_global, a.dWg);
       }
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipGetLastError()) != hipSuccess) return finish(e);
     }
   }
-  if (!want_dw) return hipSuccess;
-  bwd_gather_t_kernel<<<dim3(L.P_pad / 64, p.d / 64), 256, 0, s>>>(
-      xb, static_cast<const uint16_t*>(a.dout), a.offsets, a.sorted_token, p.E_local, p.d, L.P_pad, xst, dst);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((2 * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G1::BW == 0)
-    e = launch_wgrad<FfnLarge::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s);
-  else
-    e = launch_wgrad<FfnMid::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s);
-  if (e != hipSuccess) return e;
-  wgrad_reduce_kernel<<<cus * 4, 256, 0, s>>>(a.offsets, p.E_local, static_cast<size_t>(p.d) * p.I, a.dW1,
-                                              a.dW3, a.dW2, partial);
-  return hipGetLastError();
+  return finish(hipSuccess);
 }
 
 }  // namespace moe
