@@ -9,6 +9,12 @@
         Writes a short markdown table of the kernel durations of a
         --kernel-trace --stats run (the N longest by total time).
 
+    python -m combine_wave_level_amd.profiling steptraffic --fetch F.csv --write W.csv
+        --copy-fetch CF.csv --copy-write CW.csv --kernels K1 K2 ... --title T
+        --command "..." --out-md X.md
+        Writes the calibrated HBM bytes of one pass over kernels that each
+        run once per pass (the phase schedule's GEMM1, GEMM2 and combine).
+
     python -m combine_wave_level_amd.profiling summarize --stats S.csv
         --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
         --kernel NAME --workload W --T T --command "..." --out-md X.md
@@ -151,6 +157,37 @@ def _summarize(a) -> None:
     print(json.dumps(rec))
 
 
+def _step_traffic(a) -> None:
+    """HBM bytes of one pass over several kernels (each launched once per
+    pass): the sum over the kernels of their mean calibrated bytes per
+    dispatch."""
+    cf_kib, _ = _kernel_counter(a.copy_fetch, a.copy_kernel, "FETCH_SIZE")
+    cw_kib, _ = _kernel_counter(a.copy_write, a.copy_kernel, "WRITE_SIZE")
+    copy_bytes = a.copy_mib * (1 << 20)
+    f_fetch = cf_kib * 1024.0 / copy_bytes
+    f_write = cw_kib * 1024.0 / copy_bytes
+    lines = [f"# {a.title}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = the profiler output folder):", ""]
+    for c in a.command:
+        lines.append(f"    {c}")
+    lines += ["", f"Calibration: a plain {a.copy_mib} MiB copy reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE "
+              f"{cw_kib:.0f} KiB: factors {f_fetch:.3f} (fetch) and {f_write:.3f} (write) per byte moved.", "",
+              "| kernel | dispatches | read MB | written MB |", "|---|---|---|---|"]
+    tot_r = tot_w = 0.0
+    for k in a.kernels:
+        fk, nf = _kernel_counter(a.fetch, k, "FETCH_SIZE")
+        wk, nw = _kernel_counter(a.write, k, "WRITE_SIZE")
+        rb, wb = fk * 1024.0 / f_fetch, wk * 1024.0 / f_write
+        tot_r += rb
+        tot_w += wb
+        lines.append(f"| {k} | {nf} / {nw} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    lines += ["", f"One pass: {tot_r / 1e6:.1f} MB read + {tot_w / 1e6:.1f} MB written = "
+              f"{(tot_r + tot_w) / 1e6:.1f} MB.", ""]
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"read_bytes": round(tot_r), "write_bytes": round(tot_w)}))
+
+
 def _stats(a) -> None:
     rows = _rows(a.stats)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]) if "TotalDurationNs" in r
@@ -195,11 +232,24 @@ def main(argv=None) -> None:
     s.add_argument("--command", action="append", default=[])
     s.add_argument("--out-md", required=True)
     s.add_argument("--out-json", required=True)
+    st = sub.add_parser("steptraffic")
+    st.add_argument("--fetch", required=True)
+    st.add_argument("--write", required=True)
+    st.add_argument("--copy-fetch", required=True)
+    st.add_argument("--copy-write", required=True)
+    st.add_argument("--copy-mib", type=int, default=1024)
+    st.add_argument("--copy-kernel", default="copy|Copy")
+    st.add_argument("--kernels", nargs="+", required=True)
+    st.add_argument("--title", required=True)
+    st.add_argument("--command", action="append", default=[])
+    st.add_argument("--out-md", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         _copy(a)
     elif a.cmd == "stats":
         _stats(a)
+    elif a.cmd == "steptraffic":
+        _step_traffic(a)
     else:
         _summarize(a)
 
