@@ -287,7 +287,8 @@ def test_edge_k_equals_E_and_single_expert():
 
 
 @pytest.mark.parametrize("name,T,want", [("mid", 4096, "persistent"), ("stress", 4096, "persistent"),
-                                         ("decode", 1, "phases"), ("v4share", 2048, "phases")])
+                                         ("stress", 16384, "phases"), ("decode", 1, "phases"),
+                                         ("v4share", 2048, "phases")])
 def test_default_schedule_choice_gives_the_same_bits(name, T, want):
     """With no flag the library picks the schedule (moe_ffn_path on the
     device's CU count); the call gives the bits of both forced schedules."""
