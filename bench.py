@@ -260,6 +260,39 @@ def roofline_of(d, I, T, counts):
     return flops, nbytes, mfma, P_local
 
 
+def measure_peaks(stream):
+    """The roofline denominators measured on this device with the library's
+    probes: a matrix-core loop (bf16 16x16x32 MFMA on register operands, 8
+    wavefronts per CU) and a plain 1 GiB device copy, each launched 10 times
+    between one event pair on the launch stream after 3 untimed launches."""
+    import torch
+
+    from combine_wave_level_amd import moe
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    out, flops = moe.probe_mfma(4096)
+    t_mfma = timed(lambda: moe.probe_mfma(4096, out))
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=out.device)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: moe.probe_copy(dst, src))
+    del src, dst
+    return {"mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1), "copy_gbs": round(2.0 * nbytes / t_copy / 1e9, 1),
+            "mfma_probe": "8 wavefronts per CU, 16 independent 16x16x32 bf16 MFMAs per step, 4096 steps",
+            "copy_probe": "1 GiB device to device, read + written bytes"}
+
+
 def time_graph_step(step, stream, flush, out, n):
     """The row's whole step (route, dispatch, FFN) captured once in a HIP
     graph and replayed n times, each replay timed alone between events on
@@ -299,7 +332,7 @@ def time_graph_step(step, stream, flush, out, n):
         return {"graph_error": str(exc)[:200]}
 
 
-def time_rows(args, stream):
+def time_rows(args, stream, peaks=None):
     """Each row: the workload's router, dispatch and expert FFN (on the
     schedule the library picks), timed per step between events (median of
     the steps), and the expert FFN call alone the same way; for the weight-streaming rows a
@@ -384,6 +417,10 @@ def time_rows(args, stream):
         for lvl, ms in (("ffn", res["ffn"]), ("step", res["step"])):
             row[f"{lvl}_hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
             row[f"{lvl}_mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if peaks:
+            row["ffn_frac_of_measured_peak"] = round(
+                (flops / (res["ffn"] * 1e-3) / 1e12 / peaks["mfma_bf16_tflops"]) if mfma
+                else (nbytes / (res["ffn"] * 1e-3) / 1e9 / peaks["copy_gbs"]), 4)
         rows.append(row)
         del packed, ws, y, out, x
     return rows
@@ -570,8 +607,12 @@ def main():
     trec = None if not persistent_path else profiling.load_traffic(
         os.path.join(ROOT, "profiles", f"traffic_ffn_waved_kernel_{wl.name}_T{T}.json"), wl.name, T)
     roof["traffic"] = trec["traffic_bytes"] if trec else None
+    peaks = measure_peaks(stream)
+    meas = peaks["mfma_bf16_tflops"] if roof["bound"] == "mfma" else peaks["copy_gbs"]
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / meas, 4)
 
-    extra = {"ffn_path": "persistent" if persistent_path else "phases", "ffn_ms": round(ffn_ms, 4),
+    extra = {"measured_peaks": peaks,
+             "ffn_path": "persistent" if persistent_path else "phases", "ffn_ms": round(ffn_ms, 4),
              "grouped_gemm_tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
              "ffn_hbm_gbs_min_bytes": round(gbs, 1), "local_pairs": P_local, "experts_touched": touched,
              "host_us_per_abi_call": round(host_us_per_call, 2), "host_us_rejected_call": round(host_us_rejected, 2),
@@ -597,7 +638,7 @@ def main():
     if not args.no_backward:
         extra["backward"] = time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, stream, P_local)
     if not args.no_rows:
-        extra["rows"] = time_rows(args, stream)
+        extra["rows"] = time_rows(args, stream, peaks)
 
     cpu = None
     if not args.no_cpu:

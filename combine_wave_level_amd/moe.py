@@ -35,7 +35,7 @@ EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
     "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
-    "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc",
+    "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc", "moe_probe_mfma", "moe_probe_copy",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8": (st, [P, vp, vp, f32p, vp]),
             "moe_expert_ffn_waved_fp8": (st, [P, vp, f32p, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
                                               ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
+            "moe_probe_mfma": (st, [f32p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), vp]),
+            "moe_probe_copy": (st, [vp, vp, ctypes.c_size_t, vp]),
             "moe_check_error": (st, [vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_version": (ctypes.c_char_p, []),
@@ -330,6 +332,26 @@ def backward(p: Problem, x, packed, packed_bwd, topk_idx, topk_w, disp: Dispatch
         _p(disp.sorted_token), _p(disp.pair_pos), _p(dout), _p(dx), _p(dtw), _p(dlg), _p(dwg),
         _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(), _stream()), "moe_backward")
     return {"dx": dx, "dtopk_w": dtw, "dlogits": dlg, "dWg": dwg, "dW1": dW1, "dW3": dW3, "dW2": dW2}
+
+
+def probe_mfma(steps: int, out=None):
+    """One launch of the library's matrix-core loop on the current stream;
+    returns (out, FLOPs of the launch).  Time it with events on that stream."""
+    if out is None:
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    flops = ctypes.c_double(0.0)
+    _check(lib().moe_probe_mfma(_p(out), out.numel() * 4, int(steps), ctypes.byref(flops), _stream()),
+           "moe_probe_mfma")
+    return out, flops.value
+
+
+def probe_copy(dst, src) -> None:
+    """One launch of the library's plain copy (src -> dst, same byte size)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _check(lib().moe_probe_copy(_p(dst), _p(src), n, _stream()), "moe_probe_copy")
 
 
 def check_error(ws) -> None:

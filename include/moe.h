@@ -343,6 +343,23 @@ const char* moe_status_string(moe_status_t s);
 /* Library build identification (static string). */
 const char* moe_version(void);
 
+/* ------------------------------------------------------------ measurement probes
+ * Not part of the layer: they measure, on the running device, the two
+ * denominators the layer's kernels are compared against (the matrix-core
+ * rate and the HBM copy rate), next to the published peaks. */
+
+/* One launch of a matrix-core loop: every wavefront (8 per workgroup, one
+ * workgroup per CU) runs `steps` rounds of 16 independent
+ * v_mfma_f32_16x16x32_bf16 on register operands.  out: device, at least
+ * num_cus * 512 floats (one sum per thread keeps the work alive).  *flops
+ * receives the launch's FLOP count (num_cus * 8 * steps * 16 * 16384).
+ * steps in [1, 2^20]; MOE_ERR_INVALID_ARG otherwise or when out is too small. */
+moe_status_t moe_probe_mfma(float* out, size_t out_bytes, int32_t steps, double* flops, moe_stream_t stream);
+
+/* One launch of a plain device-to-device copy of `bytes` (a multiple of 16;
+ * src and dst 16-byte aligned and not overlapping): 2 * bytes of HBM traffic. */
+moe_status_t moe_probe_copy(void* dst, const void* src, size_t bytes, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -276,3 +276,18 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         moe.lib()
+
+
+def test_probes_reject_bad_arguments_before_any_launch(L):
+    """The measurement probes validate on the host: null or short output,
+    steps out of range, unaligned, ragged or overlapping copies."""
+    flops = ctypes.c_double(0.0)
+    assert L.moe_probe_mfma(None, 1 << 20, 16, ctypes.byref(flops), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_mfma(ctypes.c_void_p(256), 1 << 20, 0, ctypes.byref(flops), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_mfma(ctypes.c_void_p(256), 1 << 20, (1 << 20) + 1, ctypes.byref(flops),
+                            None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_mfma(ctypes.c_void_p(256), 1 << 20, 16, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_copy(ctypes.c_void_p(4096), ctypes.c_void_p(8192), 100, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_copy(ctypes.c_void_p(4100), ctypes.c_void_p(8192), 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_copy(ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 32), 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_probe_copy(None, ctypes.c_void_p(8192), 64, None) == moe.MOE_ERR_INVALID_ARG
