@@ -285,7 +285,7 @@ def forward_tokens(x_ffn_rows, idx_rows, w_rows, W1, W3, W2, e_begin, E_local, a
     return out
 
 
-def wgrad(x_ffn, W1, W3, W2, meta, w, dout, experts=None, cols=None):
+def wgrad(x_ffn, W1, W3, W2, meta, w, dout, experts=None, cols=None, activation="swiglu"):
     """Weight gradient of L = <dout, out> for the local experts, float64.
 
     For every routed row r = (t, j) of expert e (dy_r = w[t, j] * dout[t]):
@@ -294,6 +294,8 @@ def wgrad(x_ffn, W1, W3, W2, meta, w, dout, experts=None, cols=None):
       dH3 = dA * h1 s,
       dH1 = dA * h3 * s (1 + h1 (1 - s)),
       dW2_e += a^T dy_r, dW1_e += x_t^T dH1, dW3_e += x_t^T dH3.
+    activation "relu2" (a = max(h1, 0)^2, no W3): dH1 = dA * 2 max(h1, 0),
+    dW3 is not formed (the dict stays empty).
     Determinism ([ZH-10100], [V4-TH] §3) is a property of the GPU reduction
     order; the oracle sums in float64 with matmuls.
 
@@ -316,18 +318,23 @@ def wgrad(x_ffn, W1, W3, W2, meta, w, dout, experts=None, cols=None):
         X = xf[toks]                                   # [M, d]
         dY = w[toks, slots][:, None] * dout[toks]      # [M, d]
         W1c = np.asarray(W1[le], dtype=np.float64)[:, cols]
-        W3c = np.asarray(W3[le], dtype=np.float64)[:, cols]
         W2c = np.asarray(W2[le], dtype=np.float64)[cols, :]
         h1 = X @ W1c
-        h3 = X @ W3c
-        s = 1.0 / (1.0 + np.exp(-h1))
-        a = h1 * s * h3
         dA = dY @ W2c.T
-        dH3 = dA * h1 * s
-        dH1 = dA * h3 * s * (1.0 + h1 * (1.0 - s))
+        if activation == "relu2":
+            r = np.maximum(h1, 0.0)
+            a = r * r
+            dH1 = dA * 2.0 * r
+        else:
+            W3c = np.asarray(W3[le], dtype=np.float64)[:, cols]
+            h3 = X @ W3c
+            s = 1.0 / (1.0 + np.exp(-h1))
+            a = h1 * s * h3
+            dH3 = dA * h1 * s
+            dH1 = dA * h3 * s * (1.0 + h1 * (1.0 - s))
+            dW3[le] = X.T @ dH3
         dW2[le] = a.T @ dY
         dW1[le] = X.T @ dH1
-        dW3[le] = X.T @ dH3
     return dW1, dW3, dW2
 
 
@@ -340,7 +347,7 @@ def _gate_backward(w: np.ndarray, dw: np.ndarray) -> np.ndarray:
     return w * (dw - s)
 
 
-def backward(x, Wg, W1, W3, W2, idx, w, meta, dout, x_ffn=None):
+def backward(x, Wg, W1, W3, W2, idx, w, meta, dout, x_ffn=None, activation="swiglu"):
     """Data and router gradients of L = <dout, out>, float64.
 
     Chain rule through the layer of the workload definition ([V4-TH] §1.1
@@ -356,6 +363,9 @@ def backward(x, Wg, W1, W3, W2, idx, w, meta, dout, x_ffn=None):
       per token: dl[t, idx_j] = w_j (dw_j - sum_m w_m dw_m), 0 off the picks;
       router (l = x Wg + b): dWg = x^T dl, dx_router = dl Wg^T;
       dx = dx_router + dx_ffn.
+    activation "relu2" (a = max(h1, 0)^2, no W3): dH1 = dA * 2 max(h1, 0),
+    dx_ffn[t] += dH1 W1_e^T (the derivative of max(h, 0)^2 is 0 at h = 0
+    from both sides).
     ``x`` feeds the router and ``x_ffn`` (default ``x``) the experts; a cast
     between them passes the gradient through unchanged.  [ZH-10100]
     (deterministic operators): the GPU's fixed reduction orders are its own
@@ -381,20 +391,27 @@ def backward(x, Wg, W1, W3, W2, idx, w, meta, dout, x_ffn=None):
         toks = meta["sorted_token"][r0:r1]
         slots = meta["sorted_slot"][r0:r1]
         W1e = np.asarray(W1[le], dtype=np.float64)
-        W3e = np.asarray(W3[le], dtype=np.float64)
         W2e = np.asarray(W2[le], dtype=np.float64)
         X = xf[toks]
         h1 = X @ W1e
-        h3 = X @ W3e
-        s = 1.0 / (1.0 + np.exp(-h1))
-        a = h1 * s * h3
+        if activation == "relu2":
+            r = np.maximum(h1, 0.0)
+            a = r * r
+        else:
+            W3e = np.asarray(W3[le], dtype=np.float64)
+            h3 = X @ W3e
+            s = 1.0 / (1.0 + np.exp(-h1))
+            a = h1 * s * h3
         y = a @ W2e
         dw[toks, slots] = (dout[toks] * y).sum(axis=1)
         dA = (w[toks, slots][:, None] * dout[toks]) @ W2e.T
-        dH3 = dA * h1 * s
-        dH1 = dA * h3 * s * (1.0 + h1 * (1.0 - s))
         # a token picks an expert at most once: toks has no repeats here
-        dx_ffn[toks] += dH1 @ W1e.T + dH3 @ W3e.T
+        if activation == "relu2":
+            dx_ffn[toks] += (dA * 2.0 * r) @ W1e.T
+        else:
+            dH3 = dA * h1 * s
+            dH1 = dA * h3 * s * (1.0 + h1 * (1.0 - s))
+            dx_ffn[toks] += dH1 @ W1e.T + dH3 @ W3e.T
     dl_picks = _gate_backward(np.asarray(w, dtype=np.float64), dw)
     dl = np.zeros((T, E), dtype=np.float64)
     rows = np.repeat(np.arange(T), k)
@@ -405,7 +422,8 @@ def backward(x, Wg, W1, W3, W2, idx, w, meta, dout, x_ffn=None):
             "dx": dx_router + dx_ffn}
 
 
-def backward_tokens(x_rows, x_ffn_rows, idx_rows, w_rows, dout_rows, Wg, W1, W3, W2, e_begin, E_local):
+def backward_tokens(x_rows, x_ffn_rows, idx_rows, w_rows, dout_rows, Wg, W1, W3, W2, e_begin, E_local,
+                    activation="swiglu"):
     """dx, dw and the picked dl of a subset of tokens, one token at a time.
 
     A token's data gradient depends only on its own row, picks, weights and
@@ -427,13 +445,18 @@ def backward_tokens(x_rows, x_ffn_rows, idx_rows, w_rows, dout_rows, Wg, W1, W3,
             if not 0 <= le < E_local:
                 continue
             W1e = np.asarray(W1[le], dtype=np.float64)
-            W3e = np.asarray(W3[le], dtype=np.float64)
             W2e = np.asarray(W2[le], dtype=np.float64)
             h1 = xf[i] @ W1e
+            dA = W2e @ (w[i, j] * dout[i])
+            if activation == "relu2":
+                r = np.maximum(h1, 0.0)
+                dw[i, j] = dout[i] @ ((r * r) @ W2e)
+                dx[i] += W1e @ (dA * 2.0 * r)
+                continue
+            W3e = np.asarray(W3[le], dtype=np.float64)
             h3 = xf[i] @ W3e
             s = 1.0 / (1.0 + np.exp(-h1))
             dw[i, j] = dout[i] @ ((h1 * s * h3) @ W2e)
-            dA = W2e @ (w[i, j] * dout[i])
             dx[i] += W1e @ (dA * h3 * s * (1.0 + h1 * (1.0 - s))) + W3e @ (dA * h1 * s)
     dl = _gate_backward(w, dw)
     for i in range(n):

@@ -547,6 +547,94 @@ def test_relu2_forward_vs_dense_and_identical_experts():
     np.testing.assert_allclose(toks, same["out"][[3, 0]], rtol=1e-12, atol=1e-13)
 
 
+def _relu2_autograd(x, Wg, b, W1, W2, k, e_begin, E_local, dout):
+    """torch autograd (float64, CPU) through the dense per-token squared-ReLU
+    layer share, routing from torch.topk held fixed: dx, dWg, the logits and
+    combine-weight gradients and the expert weight gradients."""
+    xt = torch.from_numpy(x.copy()).requires_grad_()
+    wg = torch.from_numpy(Wg.copy()).requires_grad_()
+    logits = xt @ wg + (torch.from_numpy(b) if b is not None else 0)
+    logits.retain_grad()
+    p = torch.softmax(logits, dim=1)
+    top_p, top_i = torch.topk(p, k, dim=1, sorted=True)
+    wts = top_p / top_p.sum(dim=1, keepdim=True)
+    wts.retain_grad()
+    w1 = torch.from_numpy(W1.copy()).requires_grad_()
+    w2 = torch.from_numpy(W2.copy()).requires_grad_()
+    rows = []
+    for t in range(x.shape[0]):
+        acc = torch.zeros(x.shape[1], dtype=torch.float64)
+        for j in range(k):
+            le = int(top_i[t, j]) - e_begin
+            if 0 <= le < E_local:
+                acc = acc + wts[t, j] * ((torch.relu(xt[t] @ w1[le]) ** 2) @ w2[le])
+        rows.append(acc)
+    (torch.stack(rows) * torch.from_numpy(dout)).sum().backward()
+    return {"dx": xt.grad.numpy(), "dWg": wg.grad.numpy(), "dl": logits.grad.numpy(), "dw": wts.grad.numpy(),
+            "dW1": w1.grad.numpy(), "dW2": w2.grad.numpy(), "idx": top_i.numpy()}
+
+
+@pytest.mark.parametrize("e_begin,E_local,k,bias", [(0, 5, 2, False), (1, 3, 3, True)])
+def test_relu2_backward_and_wgrad_match_autograd(e_begin, E_local, k, bias):
+    x, Wg, b, W1, _, W2 = _tiny_layer(60 + e_begin, T=11, d=9, I=6, E=5, k=k, e_begin=e_begin,
+                                      E_local=E_local, bias=bias)
+    dout = np.random.default_rng(61).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, b, W1, None, W2, k, e_begin, E_local, 1, activation="relu2")
+    g = oracle.backward(x, Wg, W1, None, W2, res["idx"], res["w"], res["meta"], dout, activation="relu2")
+    dW1, dW3, dW2 = oracle.wgrad(x, W1, None, W2, res["meta"], res["w"], dout, activation="relu2")
+    ref = _relu2_autograd(x, Wg, b, W1, W2, k, e_begin, E_local, dout)
+    assert (ref["idx"] == res["idx"]).all() and dW3 == {}
+    for key in ("dx", "dWg", "dl", "dw"):
+        np.testing.assert_allclose(g[key], ref[key], rtol=1e-10, atol=1e-12)
+    for e in range(E_local):
+        np.testing.assert_allclose(dW1[e], ref["dW1"][e], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dW2[e], ref["dW2"][e], rtol=1e-10, atol=1e-12)
+
+
+def test_relu2_backward_central_finite_differences_and_tokens():
+    """dx and dW1, dW2 against central differences of L = <dout, out> away
+    from the kink (no h within 1e-3 of 0 in this draw); backward_tokens
+    equals backward on a token subset."""
+    x, Wg, b, W1, _, W2 = _tiny_layer(62, T=7, d=6, I=4, E=3, k=2)
+    dout = np.random.default_rng(63).standard_normal(x.shape)
+    res = oracle.forward(x, Wg, b, W1, None, W2, 2, 0, 3, 1, activation="relu2")
+    assert np.abs(np.einsum("td,edi->tei", x, W1)).min() > 1e-3
+    g = oracle.backward(x, Wg, W1, None, W2, res["idx"], res["w"], res["meta"], dout, x_ffn=x,
+                        activation="relu2")
+    dW1, _, dW2 = oracle.wgrad(x, W1, None, W2, res["meta"], res["w"], dout, activation="relu2")
+
+    def loss_ffn(xf, a1, a2):
+        # routing and weights held fixed: the experts' path only
+        return float((oracle.forward(x, Wg, b, a1, None, a2, 2, 0, 3, 1, x_ffn=xf,
+                                     activation="relu2")["out"] * dout).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(64)
+    for _ in range(10):
+        t, i = rng.integers(7), rng.integers(6)
+        A, B = x.copy(), x.copy()
+        A[t, i] += h
+        B[t, i] -= h
+        fd = (loss_ffn(A, W1, W2) - loss_ffn(B, W1, W2)) / (2 * h)
+        assert abs(fd - g["dx_ffn"][t, i]) <= 1e-6 * max(1.0, abs(fd))
+        e, j = rng.integers(3), rng.integers(4)
+        A1, B1 = W1.copy(), W1.copy()
+        A1[e, i, j] += h
+        B1[e, i, j] -= h
+        fd = (loss_ffn(x, A1, W2) - loss_ffn(x, B1, W2)) / (2 * h)
+        assert abs(fd - dW1[e][i, j]) <= 1e-6 * max(1.0, abs(fd))
+        A2, B2 = W2.copy(), W2.copy()
+        A2[e, j, i] += h
+        B2[e, j, i] -= h
+        fd = (loss_ffn(x, W1, A2) - loss_ffn(x, W1, B2)) / (2 * h)
+        assert abs(fd - dW2[e][j, i]) <= 1e-6 * max(1.0, abs(fd))
+    sel = np.array([5, 0, 3])
+    dx, dw, dl = oracle.backward_tokens(x[sel], x[sel], res["idx"][sel], res["w"][sel], dout[sel], Wg, W1, None,
+                                        W2, 0, 3, activation="relu2")
+    np.testing.assert_allclose(dx, g["dx"][sel], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dw, g["dw"][sel], rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- FP8 dispatch
 
 def test_e4m3_decode_known_codes():
