@@ -66,10 +66,11 @@ constexpr int kGatherRow = 72;
 // The recompute's epilogue stages (dH1 | dH3)^T and (w a)^T of the tile in
 // LDS for the transposed weight-gradient operands: in one pass when the
 // three fit, else (the 256-wide tile) dH first and w a in a second pass.
-template <class C>
+template <class C, bool GATED = true>
 struct BwdDh {
-  static constexpr int NI = C::BW / 2;  // intermediate indices per tile
-  static constexpr size_t DH_BYTES = static_cast<size_t>(2 * NI) * kStageRow * 2;
+  static constexpr int NI = GATED ? C::BW / 2 : C::BW;  // intermediate indices per tile
+  static constexpr int NH = GATED ? 2 * NI : NI;        // staged dH rows: (dH1 | dH3) or dH1
+  static constexpr size_t DH_BYTES = static_cast<size_t>(NH) * kStageRow * 2;
   static constexpr size_t AW_BYTES = static_cast<size_t>(NI) * kStageRow * 2;
   static constexpr bool ONE_PASS = DH_BYTES + AW_BYTES <= 160 * 1024 - 8 * 1024;
   static constexpr size_t STAGE = ONE_PASS ? DH_BYTES + AW_BYTES : DH_BYTES;
@@ -148,15 +149,16 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
 // Outputs: dH rows [P][2I] (dH1 | dH3) for the dx product and, when dht is
 // not null, (dH1 | dH3)^T fragments and (w a)^T rows for the weight
 // gradient, transposed through an LDS stage.
-template <class C>
+template <class C, bool GATED>
 __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13, const float* __restrict__ g,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d, int I,
     int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht, uint16_t* __restrict__ awt,
     float* __restrict__ dwp) {
-  using D = BwdDh<C>;
-  static_assert(C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
+  using D = BwdDh<C, GATED>;
+  static_assert(!GATED || C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
+  constexpr int GR = GATED ? 2 : 1;  // packed W13 rows per intermediate index
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
   __shared__ int32_t seg[kMaxLocalExperts + 1];
@@ -165,11 +167,11 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
   build_seg_prefix(offsets, E_local, seg);
   __syncthreads();
   constexpr int NI = D::NI;
-  uint16_t* sdh = lds;  // [2 NI][kStageRow]: (dH1 | dH3)^T of the tile
+  uint16_t* sdh = lds;  // [NH][kStageRow]: (dH1 | dH3)^T (or dH1^T) of the tile
   // [NI][kStageRow]: (w a)^T, after sdh, or over it in the second pass
-  uint16_t* saw = D::ONE_PASS ? lds + 2 * NI * kStageRow : lds;
+  uint16_t* saw = D::ONE_PASS ? lds + D::NH * kStageRow : lds;
   const bool trans = dht != nullptr;
-  const int NT = 2 * I / C::BW, NQ = I / 16;
+  const int NT = GR * I / C::BW, NQ = I / 16;
   const int total = uniform(mt_pre[E_local] * NT);
   const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -194,15 +196,59 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
       trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
     }
     TileAcc<C> acc;  // barriers inside order the wrow writes before the reads below
-    tile_mma<C>(w13 + static_cast<size_t>(e) * 2 * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
+    tile_mma<C>(w13 + static_cast<size_t>(e) * GR * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
                 d / C::BK, trow, lds, acc, count);
     // second-pass staging keeps the tile's w a values as bf16 pairs (not the
-    // accumulators) across the read-out of the first stage
-    uint32_t vaw[D::ONE_PASS ? 1 : C::AT][D::ONE_PASS ? 1 : C::AW / 2][2];
+    // accumulators) across the read-out of the first stage (gated; the
+    // ungated epilogue recomputes w a from the accumulators instead)
+    uint32_t vaw[(D::ONE_PASS || !GATED) ? 1 : C::AT][(D::ONE_PASS || !GATED) ? 1 : C::AW / 2][2];
+
     // wave (wr, wt): row blocks a (W1) and a + 1 (W3) of intermediate block
     // (wr * AW + a) / 2; lane l holds indices 4 (l / 16) + 0..3 of the block
     // for tile row (wt * AT + b) * 16 + l % 16.  Rows past count compute
     // zeros (w = 0): the padding of the transposed operands.
+    if constexpr (!GATED) {
+      // ungated: row block a is intermediate block wr * AW + a; per element
+      // r = max(h, 0), a = r^2, dA = w g, dH = (2 dA) r, aw = w a
+#pragma unroll
+      for (int b = 0; b < C::AT; ++b) {
+        const int t = (wt * C::AT + b) * 16 + (lane & 15);
+        const bool valid = t < count;
+        const float w = wrow[t];
+#pragma unroll
+        for (int a = 0; a < C::AW; ++a) {
+          const int il = (wr * C::AW + a) * 16 + 4 * (lane / 16);
+          const int i0 = nt * NI + il;
+          const f32x4 g4 = valid ? *reinterpret_cast<const f32x4*>(g + static_cast<size_t>(row0 + t) * I + i0)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+          float v1[4], va[4];
+          float part = 0.f;  // <g, a> over the lane's 4 indices
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float rl = fmaxf(acc.v[a][b][r], 0.0f);
+            const float act = rl * rl;
+            const float dA = w * g4[r];
+            v1[r] = (dA * 2.0f) * rl;
+            va[r] = w * act;
+            part = fmaf(g4[r], act, part);
+          }
+          part += __shfl_xor(part, 16, kWave);
+          part += __shfl_xor(part, 32, kWave);
+          if (dwp && valid && lane < 16) dwp[static_cast<size_t>(row0 + t) * NQ + i0 / 16] = part;
+          if (valid) {
+            const size_t o = static_cast<size_t>(row0 + t) * I + i0;
+            *reinterpret_cast<u32x2*>(dh + o) = u32x2{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+          }
+          if (trans) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sdh[(il + r) * kStageRow + t] = f32_to_bf16(v1[r]);
+              if constexpr (D::ONE_PASS) saw[(il + r) * kStageRow + t] = f32_to_bf16(va[r]);
+            }
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int b = 0; b < C::AT; ++b) {
       const int t = (wt * C::AT + b) * 16 + (lane & 15);
@@ -254,6 +300,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
         }
       }
     }
+    }
     if (trans) {
       // the tile's rows are columns k0 .. k0 + BT - 1 of the transposed
       // operands; columns up to the expert's rows rounded to 64 are written
@@ -261,27 +308,42 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
       const int k0 = uniform(seg[e] + (mt - mt_pre[e]) * C::BT);
       const int rows_pad = (count + 63) & ~63;
       const int KB = P_pad / 32;
-      // (dH1 | dH3)^T fragments: 2 NI / 16 row blocks x rows_pad / 32 k blocks
-      constexpr int NB = 2 * NI / 16;
+      // (dH1 | dH3)^T (or dH1^T) fragments: NH / 16 row blocks x rows_pad / 32 k blocks
+      constexpr int NB = D::NH / 16;
       for (int q = threadIdx.x; q < NB * (rows_pad / 32) * 64; q += C::NTHREADS) {
         const int frag = q / 64, slot = q % 64;
         const int nl = (frag % NB) * 16 + slot % 16, kl = (frag / NB) * 32 + (slot / 16) * 8;
-        const int n = nl < NI ? nt * NI + nl : I + nt * NI + (nl - NI);
+        const int n = nl < NI ? nt * NI + nl : I + nt * NI + (nl - NI);  // nl < NI always when ungated
         st16(dht + frag_offset(n / 16, (k0 + kl) / 32, KB) + ((kl % 32) / 8 * 16 + n % 16) * 8,
              ld16(sdh + nl * kStageRow + kl));
       }
       if constexpr (!D::ONE_PASS) {
-        // second pass: the kept w a values, staged over the read-out sdh
+        // second pass: the w a values (kept as bf16 pairs when gated,
+        // recomputed from the accumulators when ungated), staged over the
+        // read-out sdh
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < C::AT; ++b) {
           const int t = (wt * C::AT + b) * 16 + (lane & 15);
+          if constexpr (GATED) {
 #pragma unroll
-          for (int a = 0; a < C::AW; a += 2) {
-            const int il = ((wr * C::AW + a) / 2) * 16 + 4 * (lane / 16);
+            for (int a = 0; a < C::AW; a += 2) {
+              const int il = ((wr * C::AW + a) / 2) * 16 + 4 * (lane / 16);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              saw[(il + r) * kStageRow + t] = static_cast<uint16_t>(vaw[b][a / 2][r / 2] >> (16 * (r % 2)));
+              for (int r = 0; r < 4; ++r)
+                saw[(il + r) * kStageRow + t] = static_cast<uint16_t>(vaw[b][a / 2][r / 2] >> (16 * (r % 2)));
+            }
+          } else {
+            const float w = wrow[t];
+#pragma unroll
+            for (int a = 0; a < C::AW; ++a) {
+              const int il = (wr * C::AW + a) * 16 + 4 * (lane / 16);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float rl = fmaxf(acc.v[a][b][r], 0.0f);
+                saw[(il + r) * kStageRow + t] = f32_to_bf16(w * (rl * rl));
+              }
+            }
           }
         }
         __syncthreads();
@@ -402,7 +464,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(
 template <class F>
 __global__ __launch_bounds__(F::NT) void bwd_dx_gemm_kernel(
     const uint16_t* __restrict__ dh, const uint16_t* __restrict__ w13t,
-    const int32_t* __restrict__ offsets, uint16_t* __restrict__ dxr, int E_local, int d, int I) {
+    const int32_t* __restrict__ offsets, uint16_t* __restrict__ dxr, int E_local, int d, int K2) {
   using C = typename F::G2;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
@@ -415,7 +477,7 @@ __global__ __launch_bounds__(F::NT) void bwd_dx_gemm_kernel(
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
-    gemm2_tile<C>(dh, w13t + static_cast<size_t>(e) * d * 2 * I, dxr, row0, count, nt, d, 2 * I, lds);
+    gemm2_tile<C>(dh, w13t + static_cast<size_t>(e) * d * K2, dxr, row0, count, nt, d, K2, lds);
   }
 }
 
@@ -670,14 +732,15 @@ template <class C>
 __global__ __launch_bounds__(C::NTHREADS) void bwd_wgrad_kernel(
     const uint16_t* __restrict__ dht, const uint16_t* __restrict__ awt,
     const uint16_t* __restrict__ xst, const uint16_t* __restrict__ dst,
-    const int32_t* __restrict__ offsets, int E_local, int d, int I, int P_pad,
+    const int32_t* __restrict__ offsets, int E_local, int d, int I, int gr, int P_pad,
     float* __restrict__ dW1, float* __restrict__ dW3, float* __restrict__ dW2,
     float* __restrict__ partial) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t task_pre[kMaxLocalExperts + 1];
   __shared__ int32_t slot_pre[kMaxLocalExperts + 1];
   __shared__ int32_t seg[kMaxLocalExperts + 1];
-  const int n13 = 2 * I / C::BW, t13 = (d + C::BT - 1) / C::BT;
+  // gr = 2: the (dH1 | dH3)^T rows give dW1 (n < I) and dW3; gr = 1: dW1 only
+  const int n13 = gr * I / C::BW, t13 = (d + C::BT - 1) / C::BT;
   const int n2 = d / C::BW, t2 = (I + C::BT - 1) / C::BT;
   const int per_chunk = n13 * t13 + n2 * t2;
   build_seg_prefix(offsets, E_local, seg);
@@ -725,7 +788,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_wgrad_kernel(
     float* base[3];
     if (c == 0) {
       base[0] = dW1 + e * mat;
-      base[1] = dW3 + e * mat;
+      base[1] = dW3 ? dW3 + e * mat : nullptr;  // no dW3 when ungated (never written then)
       base[2] = dW2 + e * mat;
     } else {
       float* slot = partial + static_cast<size_t>(uniform(slot_pre[e]) + c - 1) * 3 * mat;
@@ -748,9 +811,10 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_wgrad_kernel(
   }
 }
 
-// dW_e += partial slots of chunks 1 .. n-1 in ascending order.
+// dW_e += partial slots of chunks 1 .. n-1 in ascending order (dW3 only
+// when gr = 2).
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int32_t* __restrict__ offsets,
-                                                           int E_local, size_t mat,
+                                                           int E_local, size_t mat, int gr,
                                                            float* __restrict__ dW1,
                                                            float* __restrict__ dW3,
                                                            float* __restrict__ dW2,
@@ -762,6 +826,7 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int32_t* __rest
       for (size_t i = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < 3 * mat;
            i += static_cast<size_t>(gridDim.x) * blockDim.x * 4) {
         const int m = static_cast<int>(i / mat);
+        if (m == 1 && gr == 1) continue;
         const size_t o = i % mat;
         float* dst = (m == 0 ? dW1 : m == 1 ? dW3 : dW2) + e * mat + o;
         f32x4 acc = *reinterpret_cast<const f32x4*>(dst);
@@ -795,7 +860,8 @@ hipError_t launch_dx_gemm(const moe_problem_t& p, const uint16_t* dh, const uint
   constexpr size_t lds = F::G2::LDS_BYTES;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dx_gemm_kernel<F>, F::NT, lds)) != hipSuccess)
     return e;
-  bwd_dx_gemm_kernel<F><<<max(1, per_cu) * cus, F::NT, lds, s>>>(dh, w13t, offsets, dxr, p.E_local, p.d, p.I);
+  bwd_dx_gemm_kernel<F><<<max(1, per_cu) * cus, F::NT, lds, s>>>(dh, w13t, offsets, dxr, p.E_local, p.d,
+                                                                 gate_rows(p) * p.I);
   return hipGetLastError();
 }
 
@@ -822,24 +888,33 @@ hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const uint16_
                                                         C::LDS_BYTES)) != hipSuccess)
     return e;
   bwd_wgrad_kernel<C><<<max(1, per_cu) * cus, C::NTHREADS, C::LDS_BYTES, s>>>(
-      dht, awt, xst, dst, a.offsets, p.E_local, p.d, p.I, L.P_pad, a.dW1, a.dW3, a.dW2, partial);
+      dht, awt, xst, dst, a.offsets, p.E_local, p.d, p.I, gate_rows(p), L.P_pad, a.dW1, a.dW3, a.dW2, partial);
   return hipGetLastError();
 }
 
 // The recompute with the gradient epilogue on tile C.
+template <class C, bool GATED>
+hipError_t launch_dh_act(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, const uint16_t* xb,
+                         const uint16_t* w13, const float* g, uint16_t* dh, uint16_t* dht, uint16_t* awt,
+                         float* dwp, int cus, hipStream_t s) {
+  constexpr size_t lds = BwdDh<C, GATED>::LDS;
+  int per_cu = 0;
+  hipError_t e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel<C, GATED>, C::NTHREADS, lds)) !=
+      hipSuccess)
+    return e;
+  bwd_dh_kernel<C, GATED><<<max(1, per_cu) * cus, C::NTHREADS, lds, s>>>(
+      xb, w13, g, a.offsets, a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh, dht, awt,
+      dwp);
+  return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_dh(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, const uint16_t* xb,
                      const uint16_t* w13, const float* g, uint16_t* dh, uint16_t* dht, uint16_t* awt, float* dwp,
                      int cus, hipStream_t s) {
-  constexpr size_t lds = BwdDh<C>::LDS;
-  int per_cu = 0;
-  hipError_t e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel<C>, C::NTHREADS, lds)) != hipSuccess)
-    return e;
-  bwd_dh_kernel<C><<<max(1, per_cu) * cus, C::NTHREADS, lds, s>>>(xb, w13, g, a.offsets, a.sorted_token, a.pair_pos,
-                                                                  a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh,
-                                                                  dht, awt, dwp);
-  return hipGetLastError();
+  if (gate_rows(p) == 2) return launch_dh_act<C, true>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
+  return launch_dh_act<C, false>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
 }
 
 // The weight gradient's branch (the transposed x and dout rows, then the
@@ -925,7 +1000,7 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     // no rows: every gradient is zero (dx, dtopk_w and dlogits are empty)
     if (want_dw) {
       if ((e = fill_zero(a.dW1, words, s)) != hipSuccess) return e;
-      if ((e = fill_zero(a.dW3, words, s)) != hipSuccess) return e;
+      if (a.dW3 && (e = fill_zero(a.dW3, words, s)) != hipSuccess) return e;
       if ((e = fill_zero(a.dW2, words, s)) != hipSuccess) return e;
     }
     if (a.dWg) return fill_zero(a.dWg, static_cast<size_t>(p.d) * p.E_global, s);
@@ -960,20 +1035,21 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
   else
     e = launch_g<BwdCfgG>(p, a, w2b, g, cus, s);
   if (e != hipSuccess) return finish(e);
-  if ((2 * p.I) % BwdCfgL::BW == 0)
+  const int gr = gate_rows(p);
+  if ((gr * p.I) % BwdCfgL::BW == 0)
     e = launch_dh<BwdCfgL>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
   else
     e = launch_dh<BwdCfg>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
   if (e != hipSuccess) return finish(e);
   if (want_dw) {
     if ((e = fork_to(s, s2, fk.ev[1])) != hipSuccess) return finish(e);
-    if ((2 * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G1::BW == 0)
+    if ((gr * p.I) % FfnLarge::G1::BW == 0 && p.d % FfnLarge::G1::BW == 0)
       e = launch_wgrad<FfnLarge::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s2);
     else
       e = launch_wgrad<FfnMid::G1>(p, L, dht, awt, xst, dst, a, partial, cus, s2);
     if (e != hipSuccess) return finish(e);
-    wgrad_reduce_kernel<<<cus * 4, 256, 0, s2>>>(a.offsets, p.E_local, static_cast<size_t>(p.d) * p.I, a.dW1,
-                                                 a.dW3, a.dW2, partial);
+    wgrad_reduce_kernel<<<cus * 4, 256, 0, s2>>>(a.offsets, p.E_local, static_cast<size_t>(p.d) * p.I,
+                                                 gate_rows(p), a.dW1, a.dW3, a.dW2, partial);
     if ((e = hipGetLastError()) != hipSuccess) return finish(e);
   }
   if (want_data) {

@@ -119,7 +119,7 @@ int32_t moe_ffn_path(const moe_problem_t* p, int32_t num_cus, uint32_t flags) {
 }
 
 size_t moe_packed_bwd_size(const moe_problem_t* p) {
-  if (check_problem(p) != MOE_OK || p->activation != MOE_ACT_SWIGLU) return 0;
+  if (check_problem(p) != MOE_OK) return 0;
   return packed_bwd_layout(*p).total;
 }
 
@@ -127,9 +127,9 @@ moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const 
                                   const void* W2, void* packed_bwd, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
-  if (!Wg || !W1 || !W3 || !W2 || !packed_bwd) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(packed_bwd) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2))
+  const bool gated = p->activation == MOE_ACT_SWIGLU;
+  if (!Wg || !W1 || (gated && !W3) || !W2 || !packed_bwd) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed_bwd) || !aligned16(Wg) || !aligned16(W1) || (W3 && !aligned16(W3)) || !aligned16(W2))
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_pack_bwd(*p, Wg, W1, W3, W2, packed_bwd, static_cast<hipStream_t>(stream)));
 }
@@ -253,11 +253,13 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
                               moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
-  if (!packed || !packed_bwd || !expert_offsets || !dW1 || !dW3 || !dW2) return MOE_ERR_INVALID_ARG;
+  // dW3 exists for the gated expert only
+  const bool gated = p->activation == MOE_ACT_SWIGLU;
+  if (!packed || !packed_bwd || !expert_offsets || !dW1 || !dW2 || (gated != (dW3 != nullptr)))
+    return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !sorted_token || !pair_pos || !topk_w || !dout)) return MOE_ERR_INVALID_ARG;
   if ((x && !aligned16(x)) || (dout && !aligned16(dout)) || !aligned16(packed) || !aligned16(packed_bwd) ||
-      !aligned16(dW1) || !aligned16(dW3) || !aligned16(dW2))
+      !aligned16(dW1) || (dW3 && !aligned16(dW3)) || !aligned16(dW2))
     return MOE_ERR_INVALID_ARG;
   WsLayout L;
   if ((st = check_ws(p, ws, ws_bytes, &L, true)) != MOE_OK) return st;
@@ -284,11 +286,14 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
                           size_t ws_bytes, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (p->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (!packed || !packed_bwd || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !topk_idx || !topk_w || !sorted_token || !pair_pos || !dout || !dx))
     return MOE_ERR_INVALID_ARG;
-  const bool any_w = dW1 || dW3 || dW2, all_w = dW1 && dW3 && dW2;
+  // the weight gradient: dW1, dW2 (and dW3 for the gated expert; none for
+  // the ungated one), all or nothing
+  const bool gated = p->activation == MOE_ACT_SWIGLU;
+  const bool any_w = dW1 || dW3 || dW2;
+  const bool all_w = dW1 && dW2 && (gated ? dW3 != nullptr : dW3 == nullptr);
   if (any_w && !all_w) return MOE_ERR_INVALID_ARG;
   if ((x && !aligned16(x)) || !aligned16(packed) || !aligned16(packed_bwd) || (dout && !aligned16(dout)) ||
       (dx && !aligned16(dx)) || (dW1 && !aligned16(dW1)) || (dW3 && !aligned16(dW3)) ||

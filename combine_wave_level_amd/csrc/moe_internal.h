@@ -90,7 +90,7 @@ inline PackedBwdLayout packed_bwd_layout(const moe_problem_t& p) {
   L.wgt = off;
   off += align_up(static_cast<size_t>(p.E_global) * p.d * (p.x_dtype == MOE_BF16 ? 2 : 4), 256);
   L.w13t = off;
-  off += align_up(static_cast<size_t>(p.E_local) * p.d * 2 * p.I * 2, 256);
+  off += align_up(static_cast<size_t>(p.E_local) * p.d * (p.activation == MOE_ACT_SWIGLU ? 2 : 1) * p.I * 2, 256);
   L.w2b = off;
   off += align_up(static_cast<size_t>(p.E_local) * p.d * p.I * 2, 256);
   L.total = off;

@@ -104,16 +104,26 @@ hipError_t launch_pack_bwd(const moe_problem_t& p, const void* Wg, const void* W
                                                        reinterpret_cast<float*>(base + L.wgt), p.d, p.E_global);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // [W1 | W3]^T: [d][2I] per expert, K = 2I
-  const size_t slots = static_cast<size_t>(p.d) * (2 * p.I / 8);
-  dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
   const size_t src_stride = static_cast<size_t>(p.d) * p.I;
-  const size_t dst_stride = static_cast<size_t>(p.d) * 2 * p.I;
   uint16_t* dst = reinterpret_cast<uint16_t*>(base + L.w13t);
-  if (p.w_dtype == MOE_BF16)
-    pack_frag_kernel<true, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
-  else
-    pack_frag_kernel<false, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
+  if (p.activation == MOE_ACT_SWIGLU) {
+    // [W1 | W3]^T: [d][2I] per expert, K = 2I
+    const size_t slots = static_cast<size_t>(p.d) * (2 * p.I / 8);
+    dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
+    const size_t dst_stride = static_cast<size_t>(p.d) * 2 * p.I;
+    if (p.w_dtype == MOE_BF16)
+      pack_frag_kernel<true, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
+    else
+      pack_frag_kernel<false, 3><<<grid, threads, 0, s>>>(W1, W3, dst, 2 * p.I, p.d, p.I, src_stride, dst_stride);
+  } else {
+    // ungated: W1 itself is [d][I] = the dx product's weights with K = I
+    const size_t slots = static_cast<size_t>(p.d) * (p.I / 8);
+    dim3 grid(static_cast<unsigned>((slots + threads - 1) / threads), p.E_local);
+    if (p.w_dtype == MOE_BF16)
+      pack_frag_kernel<true, 2><<<grid, threads, 0, s>>>(W1, nullptr, dst, p.I, p.d, p.I, src_stride, src_stride);
+    else
+      pack_frag_kernel<false, 2><<<grid, threads, 0, s>>>(W1, nullptr, dst, p.I, p.d, p.I, src_stride, src_stride);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // W2 as [I][d] (K = d) for dA = dy W2^T
   {

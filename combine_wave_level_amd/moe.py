@@ -286,10 +286,11 @@ def combine(p: Problem, y, pair_pos, topk_w, out=None):
 
 
 def wgrad(p: Problem, x, packed, packed_bwd, disp: Dispatch, topk_w, dout, ws):
+    """dW1, dW3, dW2 (dW3 None for the ungated activation)."""
     dev = x.device
     shp13 = (p.E_local, p.d, p.I)
     dW1 = torch.empty(shp13, dtype=torch.float32, device=dev)
-    dW3 = torch.empty(shp13, dtype=torch.float32, device=dev)
+    dW3 = torch.empty(shp13, dtype=torch.float32, device=dev) if p.activation == MOE_ACT_SWIGLU else None
     dW2 = torch.empty((p.E_local, p.I, p.d), dtype=torch.float32, device=dev)
     _check(lib().moe_expert_wgrad(
         ctypes.byref(p), _p(x), _p(packed), _p(packed_bwd), _p(disp.offsets), _p(disp.sorted_token),
@@ -325,7 +326,8 @@ def backward(p: Problem, x, packed, packed_bwd, topk_idx, topk_w, disp: Dispatch
     dW1 = dW3 = dW2 = None
     if want_dw:
         dW1 = torch.empty((p.E_local, p.d, p.I), dtype=f32, device=dev)
-        dW3 = torch.empty((p.E_local, p.d, p.I), dtype=f32, device=dev)
+        if p.activation == MOE_ACT_SWIGLU:
+            dW3 = torch.empty((p.E_local, p.d, p.I), dtype=f32, device=dev)
         dW2 = torch.empty((p.E_local, p.I, p.d), dtype=f32, device=dev)
     _check(lib().moe_backward(
         ctypes.byref(p), _p(x), _p(packed), _p(packed_bwd), _p(topk_idx), _p(topk_w), _p(disp.offsets),

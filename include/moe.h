@@ -60,8 +60,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * launch digest (section 1.4, activation-function bullet) recommends instead
  * of SwiGLU, with no exponential, no division and no gating projection; the
  * pages do not name the function, the reading here is squared ReLU,
- * a = max(x W1, 0)^2, and W3 is not used.  The backward entry points
- * support SWIGLU only. */
+ * a = max(x W1, 0)^2, and W3 is not used.  The backward entry points take
+ * both: with RELU2 there is no W3 and no dW3 (its pointers are NULL) and
+ * dH1 = dA * 2 max(h1, 0) (the derivative of max(h, 0)^2, 0 at h = 0). */
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_activation_t;
 
 /* Shape of one layer share.  Limits checked by every call:
@@ -150,16 +151,16 @@ moe_status_t moe_pack_weights(const moe_problem_t* p, const void* Wg, const void
                               moe_stream_t stream);
 
 /* Bytes of the backward weight buffer moe_pack_weights_bwd writes. 0 on a
- * bad shape or an activation other than SWIGLU. */
+ * bad shape. */
 size_t moe_packed_bwd_size(const moe_problem_t* p);
 
 /* One-time re-layout of the weights the gradients read (weights are
  * parameters; forward-only callers never need this buffer): Wg^T in the
- * dtype of x, and per local expert [W1 | W3]^T and W2 (K = d) in the MFMA
- * fragment layout.
+ * dtype of x, and per local expert [W1 | W3]^T (W1^T alone for RELU2) and
+ * W2 (K = d) in the MFMA fragment layout.
  *   Wg [d, E_global] in x_dtype; W1, W3 [E_local, d, I] and W2 [E_local, I,
- *   d] in w_dtype (rounded to bf16 when F32).  packed_bwd:
- *   moe_packed_bwd_size(p) bytes, written entirely. */
+ *   d] in w_dtype (rounded to bf16 when F32); W3 may be NULL for RELU2.
+ *   packed_bwd: moe_packed_bwd_size(p) bytes, written entirely. */
 moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const void* Wg, const void* W1,
                                   const void* W3, const void* W2, void* packed_bwd,
                                   moe_stream_t stream);
@@ -279,11 +280,12 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* p
  *   dW2_e = a^T dy,  dW1_e = x^T dH1,  dW3_e = x^T dH3,
  *   dA = dy W2_e^T,  dH3 = dA * silu(h1),
  *   dH1 = dA * h3 * s * (1 + h1 (1 - s)),  s = sigmoid(h1),
- * with h1, h3 recomputed exactly as the forward computes them.
+ * with h1, h3 recomputed exactly as the forward computes them; RELU2:
+ *   dH1 = (2 dA) * max(h1, 0), a = max(h1, 0)^2, no dW3.
  *   packed, packed_bwd: from moe_pack_weights and moe_pack_weights_bwd.
- *   dout [T, d] bf16.  Out (fp32, math layout): dW1, dW3 [E_local, d, I],
- *   dW2 [E_local, I, d], every element written.  ws: the MOE_WS_BACKWARD
- *   size. */
+ *   dout [T, d] bf16.  Out (fp32, math layout): dW1, dW3 [E_local, d, I]
+ *   (dW3 NULL for RELU2, required for SWIGLU), dW2 [E_local, I, d], every
+ *   element written.  ws: the MOE_WS_BACKWARD size. */
 moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void* packed,
                               const void* packed_bwd, const int32_t* expert_offsets,
                               const int32_t* sorted_token,
@@ -299,7 +301,8 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
  * the token's own rows only; reductions over tokens use fixed chunks summed
  * in ascending order.  With dy = topk_w[t, j] * dout[t] per routed row and
  * h1, h3 recomputed exactly as the forward computes them:
- *   dA = dy W2^T, dH3 = dA * silu(h1), dH1 = dA * h3 * s * (1 + h1 (1 - s)),
+ *   dA = dy W2^T, dH3 = dA * silu(h1), dH1 = dA * h3 * s * (1 + h1 (1 - s))
+ *     (RELU2: dH1 = (2 dA) * max(h1, 0), no dH3),
  *   dtopk_w[t, j] = <dout[t], y> = <dout[t] W2^T, silu(h1) * h3> for a local
  *     pick (summed from fixed partials over 32 intermediate indices), 0 for a
  *     pick whose expert is not local;
@@ -321,8 +324,8 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
  *   Out: dx [T, d] in x_dtype (required when T > 0); dtopk_w [T, k] fp32,
  *   dlogits [T, E_global] fp32 (dense, zeros off the picks), dWg
  *   [d, E_global] fp32: each optional (NULL = not computed); dW1, dW3 [E_local,
- *   d, I] and dW2 [E_local, I, d] fp32: all three or none, the same bits as
- *   moe_expert_wgrad. */
+ *   d, I] and dW2 [E_local, I, d] fp32: all three or none (RELU2: dW1 and
+ *   dW2 or neither, dW3 NULL), the same bits as moe_expert_wgrad. */
 moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* packed,
                           const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
                           const int32_t* expert_offsets, const int32_t* sorted_token,

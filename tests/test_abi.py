@@ -237,22 +237,31 @@ def test_backward_rejects_before_launch(L):
     assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2 + 8 * 128 * 256 * 2
 
 
-def test_ungated_activation_sizes_and_backward_rejection(L):
-    """RELU2 packs W1 alone (no gating projection, W3 may be NULL) and has no
-    backward: its entry points return UNSUPPORTED before touching memory."""
+def test_ungated_activation_sizes_and_backward_arguments(L):
+    """RELU2 packs W1 alone (no gating projection, W3 may be NULL); its
+    backward buffer holds W1 in place of [W1 | W3], and its backward entry
+    points take no dW3: a dW3 is rejected before any launch, and SWIGLU still
+    requires one."""
     g, u = _p(), _p(activation=moe.MOE_ACT_RELU2)
     router = 128 * 256 * 2                       # Epad x d bf16
     w2 = 8 * 128 * 256 * 2                       # W2^T, E_local x d x I bf16
     assert moe.packed_weights_size(g) == router + 8 * 2 * 128 * 256 * 2 + w2
     assert moe.packed_weights_size(u) == router + 8 * 128 * 256 * 2 + w2
     assert moe.workspace_size(u) > 0
-    assert L.moe_packed_bwd_size(ctypes.byref(u)) == 0
-    assert L.moe_pack_weights_bwd(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    # Wg^T (8 x 256 bf16), W1 as [d][I] and W2 (K = d), each E_local x d x I bf16
+    assert L.moe_packed_bwd_size(ctypes.byref(u)) == 8 * 256 * 2 + 2 * (8 * 256 * 128 * 2)
+    assert L.moe_packed_bwd_size(ctypes.byref(g)) == 8 * 256 * 2 + 3 * (8 * 256 * 128 * 2)
+    assert L.moe_pack_weights_bwd(ctypes.byref(u), FAKE, None, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights_bwd(ctypes.byref(g), FAKE, FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     args = [FAKE] * 9
-    assert L.moe_backward(ctypes.byref(u), *args, FAKE, None, None, None, None, None, None, FAKE, 1 << 30,
-                          None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_backward(ctypes.byref(u), *args, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_backward(ctypes.byref(g), *args, FAKE, None, None, None, FAKE, None, FAKE, FAKE, 1 << 30,
+                          None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_expert_wgrad(ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+                              FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_wgrad(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                              FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     # W3 is required for SWIGLU only
     assert L.moe_pack_weights(ctypes.byref(g), FAKE, FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
 
