@@ -152,7 +152,7 @@ def time_ungated(args, wl, T, d, stream):
     from workloads import make_inputs, ungated
 
     uw = ungated(wl)
-    inp = make_inputs(uw, T=T)
+    inp = make_inputs(uw, T=T, need_dout=not args.no_backward)
     xdt = moe.MOE_F32 if uw.dtype == "f32" else moe.MOE_BF16
     p = moe.problem(T=T, d=uw.d, I=uw.I, E_global=uw.E_global, k=uw.k, e_begin=uw.e_begin,
                     E_local=uw.E_local, experts_per_wave=uw.G, x_dtype=xdt, w_dtype=xdt, out_dtype=xdt,
@@ -160,6 +160,9 @@ def time_ungated(args, wl, T, d, stream):
     x = d(inp["x"])
     bias = d(inp["bias"]) if inp.get("bias") is not None else None
     packed = moe.pack_weights(p, d(inp["Wg"]), d(inp["W1"]), None, d(inp["W2"]))
+    packed_bwd = None if args.no_backward else moe.pack_weights_bwd(p, d(inp["Wg"]), d(inp["W1"]), None,
+                                                                    d(inp["W2"]))
+    dout = None if args.no_backward else d(inp["dout"])
     ws = moe.workspace(p)
     del inp
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -196,9 +199,38 @@ def time_ungated(args, wl, T, d, stream):
     ffn /= n
     P_local = int(disp.offsets[-1].item())
     tflops = 4.0 * uw.d * uw.I * P_local / (ffn * 1e-3) / 1e12
-    return {"activation": "relu2", "I": uw.I, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "ffn_ms": round(ffn, 4), "grouped_gemm_tflops": round(tflops, 2),
-            "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    res = {"activation": "relu2", "I": uw.I, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "ffn_ms": round(ffn, 4), "grouped_gemm_tflops": round(tflops, 2),
+           "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    if packed_bwd is not None:
+        # its backward (dx, dtopk_w, dWg, dW1, dW2) on the last step's routing,
+        # on a backward-sized workspace
+        wsb = moe.workspace(p, backward=True)
+        idx, w_, _ = moe.route(p, x, packed, wsb, bias=bias)
+        dispb = moe.dispatch(p, idx, wsb)
+
+        def run():
+            return moe.backward(p, x, packed, packed_bwd, idx, w_, dispb, dout, wsb, want_dtopk_w=True,
+                                want_dlogits=False, want_dwg=True, want_dw=True)
+
+        for _ in range(max(1, args.warmup // 10)):
+            run()
+        torch.cuda.synchronize()
+        nb = max(3, args.steps // 2)
+        ev[0].record(stream)
+        for _ in range(nb):
+            run()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        moe.check_error(wsb)
+        bms = ev[0].elapsed_time(ev[1]) / nb
+        P_b = int(dispb.offsets[-1].item())
+        # recompute h1 (2 d I') + dA (2 d I') + dx rows (2 d I') + dW (4 d I') per
+        # routed pair, plus the dense dWg product (2 d E per token)
+        bfl = 10.0 * uw.d * uw.I * P_b + 2.0 * T * uw.d * uw.E_global
+        res["backward"] = {"ms": round(bms, 4), "tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
+                           "mfma_frac": round(bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, stream, P_local):
