@@ -11,7 +11,9 @@
  * token order weighted by the router.  Experts are processed in waves of a
  * few experts (digest section 1.2); inside one persistent kernel the current
  * wave's GEMMs overlap the dispatch pulls of the next wave and the combine of
- * finished tokens.  Results are batch invariant and deterministic (digest
+ * finished tokens (or, for the shapes where they measured faster on one
+ * GPU, the same tiles run as grid-wide phases; see moe_ffn_path).  Results
+ * are batch invariant and deterministic (digest
  * section 3; 10100.com section on batch-invariant and deterministic
  * operators): a token's output bits do not depend on the batch it sits in,
  * and repeated runs give identical bits, including the weight gradient.
@@ -224,8 +226,9 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx,
  *   packed: from moe_pack_weights.  expert_offsets, sorted_token, pair_pos,
  *   token_ready_wave: from moe_dispatch (same workspace).  topk_w [T, k].
  *   Out: y [P_max, d] bf16 expert outputs in sorted-row order; out [T, d] in
- *   out_dtype when non-NULL: the combine, fused into the same persistent
- *   kernel (tokens with no local pick get zeros).
+ *   out_dtype when non-NULL: the combine, fused into the persistent kernel
+ *   (on the phase schedule: its own grid-wide pass, the same bits; tokens
+ *   with no local pick get zeros).
  * Each GEMM accumulates in fp32 over K in one fixed ascending order with one
  * MFMA shape, never split; a is rounded to bf16 before the second GEMM and y
  * is rounded to bf16.  flags: 0 (the library picks the schedule, see
