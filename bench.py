@@ -117,9 +117,9 @@ def time_fp8_dispatch(args, p, x, bias, packed, idx, w, disp, ws, stream, out, y
     sc = torch.empty(p.T, dtype=torch.float32, device=x.device)
 
     def step():
-        check(L.moe_route(pp, P(x), P(packed), P(bias), P(idx), P(w), None, P(ws), nws, sp), "route")
-        check(L.moe_dispatch(pp, P(idx), P(disp.counts), P(disp.offsets), P(disp.sorted_token),
-                             P(disp.pair_pos), P(disp.ready_wave), P(ws), nws, sp), "dispatch")
+        check(L.moe_route_dispatch(pp, P(x), P(packed), P(bias), P(idx), P(w), None, P(disp.counts),
+                                   P(disp.offsets), P(disp.sorted_token), P(disp.pair_pos), P(disp.ready_wave),
+                                   P(ws), nws, sp), "route_dispatch")
         check(L.moe_quantize_fp8(pp, P(x), P(x8), P(sc), sp), "quantize")
         check(L.moe_expert_ffn_waved_fp8(pp, P(x8), P(sc), P(packed), P(disp.offsets), P(disp.sorted_token),
                                          P(disp.pair_pos), P(w), P(disp.ready_wave), P(y), P(out), 0,
@@ -171,8 +171,7 @@ def time_ungated(args, wl, T, d, stream):
     out = torch.empty((T, p.d), dtype=x.dtype, device=x.device)
 
     def step(timed_ffn=False):
-        idx, w, _ = moe.route(p, x, packed, ws, bias=bias)
-        disp = moe.dispatch(p, idx, ws)
+        idx, w, _, disp = moe.route_dispatch(p, x, packed, ws, bias=bias)
         if timed_ffn:
             ev[2].record(stream)
         moe.ffn_waved(p, x, packed, disp, w, ws, y=y, out=out)
@@ -414,8 +413,8 @@ def time_rows(args, stream, peaks=None):
 
         def step(ffn_only=False):
             if not ffn_only:
-                idx, w, _ = moe.route(p, x, packed, ws, bias=bias)
-                cache["disp"], cache["w"] = moe.dispatch(p, idx, ws), w
+                idx, w, _, cache["disp"] = moe.route_dispatch(p, x, packed, ws, bias=bias)
+                cache["w"] = w
             moe.ffn_waved(p, x, packed, cache["disp"], cache["w"], ws, y=y, out=out)
 
         for _ in range(max(10, args.warmup // 5)):
@@ -521,11 +520,9 @@ def main():
     def step(ev=None, fl=flags):
         if ev is not None:
             ev[0].record(stream)
-        check(L.moe_route(pp, P(x), P(packed), P(bias), P(idx), P(w), None, P(ws), nws, sp), "route")
-        if ev is not None:
-            ev[1].record(stream)
-        check(L.moe_dispatch(pp, P(idx), P(disp.counts), P(disp.offsets), P(disp.sorted_token),
-                             P(disp.pair_pos), P(disp.ready_wave), P(ws), nws, sp), "dispatch")
+        check(L.moe_route_dispatch(pp, P(x), P(packed), P(bias), P(idx), P(w), None, P(disp.counts),
+                                   P(disp.offsets), P(disp.sorted_token), P(disp.pair_pos), P(disp.ready_wave),
+                                   P(ws), nws, sp), "route_dispatch")
         if ev is not None:
             ev[2].record(stream)
         check(L.moe_expert_ffn_waved(pp, P(x), P(packed), P(disp.offsets), P(disp.sorted_token),
@@ -572,8 +569,7 @@ def main():
             step(evs[i], fl)
         torch.cuda.synchronize()
         per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
-        return {"route_ms": sum(e[0].elapsed_time(e[1]) for e in evs) / nsteps,
-                "dispatch_ms": sum(e[1].elapsed_time(e[2]) for e in evs) / nsteps,
+        return {"route_dispatch_ms": sum(e[0].elapsed_time(e[2]) for e in evs) / nsteps,
                 "ffn_ms": sum(e[2].elapsed_time(e[3]) for e in evs) / nsteps,
                 "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
                 "step_ms_max": per_step[-1]}
@@ -612,7 +608,7 @@ def main():
     for _ in range(1000):
         L.moe_combine(pp, P(y), P(disp.pair_pos), P(w), bad, sp)
     h3 = time.perf_counter()
-    host_us_per_call = (h1 - h0) / (3 * n_host) * 1e6
+    host_us_per_call = (h1 - h0) / (2 * n_host) * 1e6
     host_us_rejected = (h3 - h2) / 1000 * 1e6
 
     counts = disp.counts.cpu().numpy().astype(np.int64)

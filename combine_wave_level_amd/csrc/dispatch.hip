@@ -17,6 +17,7 @@
 //               chunk's base + the number of lower lanes in the same mask,
 //               so rows within a group follow ascending token id.
 #include "moe_internal.h"
+#include "route_topk.h"
 
 namespace moe {
 namespace {
@@ -139,17 +140,39 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 // more than the launches it saves (T = 4096: 27 us against 15-19 us).
 constexpr int kSmallChunks = 16;
 
+// The router's selection for the batch first (TOPK, route-and-dispatch
+// of small batches): one wavefront per token over the partial logits, the
+// same instructions as moe_route's top-k kernel (route_topk.h); topk_idx
+// and topk_w are written to global memory and read back below by the whole
+// workgroup after a barrier.
+struct SmallTopk {
+  const float* partial;
+  int splits;
+  const float* bias;
+  int E;
+  float* topk_w;
+  float* logits;
+};
+
+template <bool TOPK>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
-    const int32_t* __restrict__ topk_idx, int T, int k, int e_begin, int E_local, int G, int ngroups,
+    const int32_t* topk_idx, int T, int k, int e_begin, int E_local, int G, int ngroups,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ group_off,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ pair_pos, int32_t* __restrict__ ready_wave,
-    int32_t* __restrict__ ready_list, int32_t* __restrict__ err, int32_t* __restrict__ ctr, int n_ctr) {
+    int32_t* __restrict__ ready_list, int32_t* __restrict__ err, int32_t* __restrict__ ctr, int n_ctr,
+    SmallTopk tk) {
   extern __shared__ unsigned long long smask[];  // [nchunks][ngroups], then the int32 tables
   const int nchunks = (T + kWave - 1) / kWave;
   int32_t* sbase = reinterpret_cast<int32_t*>(smask + static_cast<size_t>(nchunks) * ngroups);  // [nchunks][ngroups]
   int32_t* sgoff = sbase + nchunks * ngroups;                                                   // [ngroups + 2]
   int32_t* stot = sgoff + ngroups + 2;                                                          // [ngroups]
   const int wave = wave_id(), lane = lane_id(), nwaves = blockDim.x / kWave;
+  if constexpr (TOPK) {
+    for (int t = wave; t < T; t += nwaves)
+      topk_token(tk.partial, tk.splits, tk.bias, T, tk.E, k, t, const_cast<int32_t*>(topk_idx), tk.topk_w,
+                 tk.logits);
+    __syncthreads();
+  }
   if (threadIdx.x == 0) *err = 0;  // a new layer call starts with a clean error word
   for (int i = threadIdx.x; i < n_ctr; i += blockDim.x) ctr[i] = 0;
   for (int i = threadIdx.x; i < nchunks * ngroups; i += blockDim.x) smask[i] = 0ull;
@@ -228,7 +251,29 @@ size_t dispatch_small_lds(const WsLayout& L) {
   return static_cast<size_t>(L.nchunks) * L.ngroups * 12 + (2 * static_cast<size_t>(L.ngroups) + 2) * 4;
 }
 
+bool dispatch_uses_small(const moe_problem_t& p, const WsLayout& L) {
+  return p.T > 0 && L.nchunks <= kSmallChunks && dispatch_small_lds(L) <= 64 * 1024;
+}
+
 }  // namespace
+
+bool route_dispatch_fuses(const moe_problem_t& p) {
+  const WsLayout L = ws_layout(p);
+  return p.T <= kFusedTopkMaxTokens && dispatch_uses_small(p, L);
+}
+
+hipError_t launch_dispatch_with_topk(const moe_problem_t& p, const WsLayout& L, const float* partial,
+                                     const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                                     int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                                     int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s) {
+  SmallTopk tk{partial, router_splits(p.d, p.E_global, p.x_dtype == MOE_BF16), bias, p.E_global, topk_w, logits};
+  dispatch_small_kernel<true><<<1, 1024, dispatch_small_lds(L), s>>>(
+      topk_idx, p.T, p.k, p.e_begin, p.E_local, p.experts_per_wave, L.ngroups, counts, offsets,
+      reinterpret_cast<int32_t*>(ws + L.group_off), sorted_token, pair_pos, ready_wave,
+      reinterpret_cast<int32_t*>(ws + L.ready_list), reinterpret_cast<int32_t*>(ws + L.err),
+      reinterpret_cast<int32_t*>(ws + L.sync), static_cast<int>(L.sync_words), tk);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* sorted_token,
@@ -238,11 +283,11 @@ hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int3
   auto* group_off = reinterpret_cast<int32_t*>(ws + L.group_off);
   auto* ready_list = reinterpret_cast<int32_t*>(ws + L.ready_list);
   const int blocks = (L.nchunks + kChunksPerBlock - 1) / kChunksPerBlock;
-  if (p.T > 0 && L.nchunks <= kSmallChunks && dispatch_small_lds(L) <= 64 * 1024) {
-    dispatch_small_kernel<<<1, 1024, dispatch_small_lds(L), s>>>(
+  if (dispatch_uses_small(p, L)) {
+    dispatch_small_kernel<false><<<1, 1024, dispatch_small_lds(L), s>>>(
         topk_idx, p.T, p.k, p.e_begin, p.E_local, p.experts_per_wave, L.ngroups, counts, offsets, group_off,
         sorted_token, pair_pos, ready_wave, ready_list, reinterpret_cast<int32_t*>(ws + L.err),
-        reinterpret_cast<int32_t*>(ws + L.sync), static_cast<int>(L.sync_words));
+        reinterpret_cast<int32_t*>(ws + L.sync), static_cast<int>(L.sync_words), SmallTopk{});
     return hipGetLastError();
   }
   if (p.T > 0) {

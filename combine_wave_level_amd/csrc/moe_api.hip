@@ -186,6 +186,31 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, int32
                                     static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_route_dispatch(const moe_problem_t* p, const void* x, const void* packed, const float* bias,
+                                int32_t* topk_idx, float* topk_w, float* logits, int32_t* expert_counts,
+                                int32_t* expert_offsets, int32_t* sorted_token, int32_t* pair_pos,
+                                int32_t* token_ready_wave, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!x || !packed || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (packed && !aligned16(packed))) return MOE_ERR_INVALID_ARG;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!sorted_token || !pair_pos || !token_ready_wave)) return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* partial = reinterpret_cast<float*>(w + L.logits);
+  hipError_t e = launch_route_logits(*p, x, packed, partial, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (route_dispatch_fuses(*p))
+    return hip_status(launch_dispatch_with_topk(*p, L, partial, bias, topk_idx, topk_w, logits, expert_counts,
+                                                expert_offsets, sorted_token, pair_pos, token_ready_wave, w, s));
+  if ((e = launch_topk(*p, partial, bias, topk_idx, topk_w, logits, s)) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_dispatch(*p, L, topk_idx, expert_counts, expert_offsets, sorted_token, pair_pos,
+                                    token_ready_wave, w, s));
+}
+
 moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const void* packed,
                                   const int32_t* expert_offsets, const int32_t* sorted_token,
                                   const int32_t* pair_pos, const float* topk_w,

@@ -145,6 +145,23 @@ hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int3
                            int32_t* counts, int32_t* offsets, int32_t* sorted_token,
                            int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s);
 
+// moe_route_dispatch: the router's logits kernel, then (small batches) the
+// top-k and the dispatch in one workgroup, or the top-k kernel and the
+// dispatch kernels.  kFusedTopkMaxTokens bounds the one-workgroup top-k to
+// one round of its 16 wavefronts (one token each): measured at decode, one
+// round saves a launch (T = 1: 25.9 -> 21.7 us for the two steps), two
+// rounds cost more than the launch (T = 32: 26 -> 30.6 us).
+constexpr int kFusedTopkMaxTokens = 16;
+bool route_dispatch_fuses(const moe_problem_t& p);
+hipError_t launch_route_logits(const moe_problem_t& p, const void* x, const void* packed, float* partial,
+                               hipStream_t s);
+hipError_t launch_topk(const moe_problem_t& p, const float* partial, const float* bias, int32_t* topk_idx,
+                       float* topk_w, float* logits, hipStream_t s);
+hipError_t launch_dispatch_with_topk(const moe_problem_t& p, const WsLayout& L, const float* partial,
+                                     const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                                     int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                                     int32_t* pair_pos, int32_t* ready_wave, char* ws, hipStream_t s);
+
 // Whether moe_expert_ffn_waved runs the persistent expert-wave kernel
 // (true) or the phase-by-phase kernels (false) on a device with `cus`
 // compute units, for flags as passed.  The persistent kernel deals its

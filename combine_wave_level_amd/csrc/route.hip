@@ -14,6 +14,7 @@
 // fixed reduction order.
 #include "gemm_tile.h"
 #include "moe_internal.h"
+#include "route_topk.h"
 
 namespace moe {
 namespace {
@@ -79,75 +80,14 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
 
 // ---------------------------------------------------------------- top-k
 
-// Order used by the selection: higher score first, lower expert id on ties.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-// One wavefront per token; lane l holds experts l, l+64, l+128, l+192.
-// The logit of expert e is the sum of the `splits` partial logits in
-// ascending split order, plus the bias; it is written to `logits` when that
-// is given.  Then k rounds of a butterfly arg-max; round j's winner is
-// recorded by lane j.
+// One wavefront per token (topk_token in route_topk.h).
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int splits,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w, float* __restrict__ logits) {
-  const int lane = lane_id();
   const int t = blockIdx.x * 4 + wave_id();
   if (t >= T) return;
-  float v[4];
-  bool live[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    live[q] = e < E;
-    float acc = 0.f;
-    if (live[q]) {
-      acc = partial[static_cast<size_t>(t) * E + e];
-      for (int sp = 1; sp < splits; ++sp) acc += partial[(static_cast<size_t>(sp) * T + t) * E + e];
-      if (bias) acc += bias[e];
-      if (logits) logits[static_cast<size_t>(t) * E + e] = acc;
-    }
-    v[q] = acc;
-  }
-  float my_v = 0.f;
-  int my_i = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (live[q] && better(v[q], lane + 64 * q, bv, bi)) {
-        bv = v[q];
-        bi = lane + 64 * q;
-      }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oi = __shfl_xor(bi, m, kWave);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    // every lane now holds the same winner (the order is a total order)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + 64 * q == bi) live[q] = false;
-    if (lane == j) {
-      my_v = bv;
-      my_i = bi;
-    }
-  }
-  const float vmax = __shfl(my_v, 0, kWave);
-  const float ex = (lane < k) ? expf(my_v - vmax) : 0.f;
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __shfl(ex, j, kWave);  // ascending rank order
-  if (lane < k) {
-    topk_idx[static_cast<size_t>(t) * k + lane] = my_i;
-    topk_w[static_cast<size_t>(t) * k + lane] = ex / sum;
-  }
+  topk_token(partial, splits, bias, T, E, k, t, topk_idx, topk_w, logits);
 }
 
 template <class C>
@@ -171,37 +111,44 @@ int router_splits(int d, int E_global, bool x_bf16) {
   return 1;
 }
 
-hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packed,
-                        const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
-                        float* partial, hipStream_t s) {
+hipError_t launch_route_logits(const moe_problem_t& p, const void* x, const void* packed, float* partial,
+                               hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   const bool xbf = p.x_dtype == MOE_BF16;
   const PackedLayout L = packed_layout(p.d, p.I, p.E_global, p.E_local, xbf, gate_rows(p));
   const char* base = static_cast<const char*>(packed);
   const int splits = router_splits(p.d, p.E_global, xbf);
-  hipError_t e;
   if (xbf) {
     // token tiles of 32 or 64 rows and the K split give the logits product
     // hundreds of workgroups at the mid and V3/V4 sizes and keep a decode
     // step's reduction short
     const uint16_t* wg = reinterpret_cast<const uint16_t*>(base + L.router);
-    if (p.E_global <= 32)
-      e = launch_logits_mfma<TileCfg<32, 32, 2, 2, 64, 4>>(p, x, wg, partial, splits, s);
-    else if (p.E_global <= 64)
-      e = launch_logits_mfma<TileCfg<64, 32, 2, 2, 64, 4>>(p, x, wg, partial, splits, s);
-    else
-      e = launch_logits_mfma<TileCfg<128, 128, 2, 2, 64, 3>>(p, x, wg, partial, splits, s);
-  } else {
-    const size_t n = static_cast<size_t>(p.T) * p.E_global;
-    router_logits_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-        static_cast<const float*>(x), reinterpret_cast<const float*>(base + L.router), partial, p.T, p.d,
-        p.E_global, L.Epad);
-    e = hipGetLastError();
+    if (p.E_global <= 32) return launch_logits_mfma<TileCfg<32, 32, 2, 2, 64, 4>>(p, x, wg, partial, splits, s);
+    if (p.E_global <= 64) return launch_logits_mfma<TileCfg<64, 32, 2, 2, 64, 4>>(p, x, wg, partial, splits, s);
+    return launch_logits_mfma<TileCfg<128, 128, 2, 2, 64, 3>>(p, x, wg, partial, splits, s);
   }
-  if (e != hipSuccess) return e;
+  const size_t n = static_cast<size_t>(p.T) * p.E_global;
+  router_logits_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      static_cast<const float*>(x), reinterpret_cast<const float*>(base + L.router), partial, p.T, p.d,
+      p.E_global, L.Epad);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const moe_problem_t& p, const float* partial, const float* bias, int32_t* topk_idx,
+                       float* topk_w, float* logits, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const int splits = router_splits(p.d, p.E_global, p.x_dtype == MOE_BF16);
   topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(partial, splits, bias, p.T, p.E_global, p.k, topk_idx, topk_w,
                                             logits);
   return hipGetLastError();
+}
+
+hipError_t launch_route(const moe_problem_t& p, const void* x, const void* packed,
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                        float* partial, hipStream_t s) {
+  hipError_t e = launch_route_logits(p, x, packed, partial, s);
+  if (e != hipSuccess) return e;
+  return launch_topk(p, partial, bias, topk_idx, topk_w, logits, s);
 }
 
 }  // namespace moe

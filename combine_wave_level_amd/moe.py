@@ -35,7 +35,8 @@ EXPORTED = (
     "moe_packed_weights_size", "moe_workspace_size", "moe_pack_weights", "moe_route",
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
     "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
-    "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc", "moe_probe_mfma", "moe_probe_copy",
+    "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc", "moe_route_dispatch", "moe_probe_mfma",
+    "moe_probe_copy",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
             "moe_route": (st, [P, vp, vp, f32p, i32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
             "moe_route_noalloc": (st, [P, vp, vp, f32p, i32p, f32p, f32p, vp]),
             "moe_dispatch": (st, [P, i32p, i32p, i32p, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]),
+            "moe_route_dispatch": (st, [P, vp, vp, f32p, i32p, f32p, f32p, i32p, i32p, i32p, i32p, i32p, vp,
+                                        ctypes.c_size_t, vp]),
             "moe_expert_ffn_waved": (st, [P, vp, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
                                           ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
             "moe_combine": (st, [P, vp, i32p, f32p, vp, vp]),
@@ -233,6 +236,27 @@ def dispatch(p: Problem, topk_idx, ws) -> Dispatch:
     return d
 
 
+def route_dispatch(p: Problem, x, packed, ws, bias=None, want_logits=False):
+    """moe_route then moe_dispatch in one call (the same bits; small batches
+    select and dispatch in one kernel).  Returns (topk_idx, topk_w, logits,
+    Dispatch)."""
+    dev = x.device
+    idx = torch.empty((p.T, p.k), dtype=torch.int32, device=dev)
+    w = torch.empty((p.T, p.k), dtype=torch.float32, device=dev)
+    logits = torch.empty((p.T, p.E_global), dtype=torch.float32, device=dev) if want_logits else None
+    disp = Dispatch(
+        counts=torch.empty(p.E_local, dtype=torch.int32, device=dev),
+        offsets=torch.empty(p.E_local + 1, dtype=torch.int32, device=dev),
+        sorted_token=torch.empty(max(1, p_max(p)), dtype=torch.int32, device=dev),
+        pair_pos=torch.empty((p.T, p.k), dtype=torch.int32, device=dev),
+        ready_wave=torch.empty(p.T, dtype=torch.int32, device=dev))
+    _check(lib().moe_route_dispatch(
+        ctypes.byref(p), _p(x), _p(packed), _p(bias), _p(idx), _p(w), _p(logits), _p(disp.counts),
+        _p(disp.offsets), _p(disp.sorted_token), _p(disp.pair_pos), _p(disp.ready_wave), _p(ws), ws.numel(),
+        _stream()), "moe_route_dispatch")
+    return idx, w, logits, disp
+
+
 def _out_dtype(p: Problem):
     return torch.bfloat16 if p.out_dtype == MOE_BF16 else torch.float32
 
@@ -361,8 +385,7 @@ def check_error(ws) -> None:
 
 
 def forward(p: Problem, x, packed, ws, bias=None, serial=False, want_logits=False, persistent=False):
-    """route -> dispatch -> waved expert FFN with fused combine."""
-    idx, w, logits = route(p, x, packed, ws, bias=bias, want_logits=want_logits)
-    disp = dispatch(p, idx, ws)
+    """route -> dispatch (one call) -> waved expert FFN with fused combine."""
+    idx, w, logits, disp = route_dispatch(p, x, packed, ws, bias=bias, want_logits=want_logits)
     y, out = ffn_waved(p, x, packed, disp, w, ws, fused_combine=True, serial=serial, persistent=persistent)
     return {"idx": idx, "w": w, "logits": logits, "disp": disp, "y": y, "out": out}

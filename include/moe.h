@@ -220,6 +220,18 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx,
                           int32_t* sorted_token, int32_t* pair_pos, int32_t* token_ready_wave,
                           void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_route followed by moe_dispatch in one call, with the same outputs
+ * bit for bit (both definitions above).  For small batches (T <= 16: one
+ * token per wavefront of the dispatch's one workgroup) the top-k selection
+ * runs inside the dispatch's workgroup, so the two steps take two kernel
+ * launches (logits; top-k and dispatch) instead of three: the launches
+ * dominate a decode step's router and dispatch.  Arguments: those
+ * of moe_route, then those of moe_dispatch (topk_idx written, then read). */
+moe_status_t moe_route_dispatch(const moe_problem_t* p, const void* x, const void* packed, const float* bias,
+                                int32_t* topk_idx, float* topk_w, float* logits, int32_t* expert_counts,
+                                int32_t* expert_offsets, int32_t* sorted_token, int32_t* pair_pos,
+                                int32_t* token_ready_wave, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* Expert FFN in expert waves (digest sections 1.1, 1.2, 1.4: per pair
  * h1 = x W1, h3 = x W3, a = silu(h1) * h3, y = a W2).
  *   x [T, d] in x_dtype: the staging buffer the dispatch pulls gather from.
