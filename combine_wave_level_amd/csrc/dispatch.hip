@@ -257,8 +257,7 @@ bool dispatch_uses_small(const moe_problem_t& p, const WsLayout& L) {
 
 }  // namespace
 
-bool route_dispatch_fuses(const moe_problem_t& p) {
-  const WsLayout L = ws_layout(p);
+bool route_dispatch_fuses(const moe_problem_t& p, const WsLayout& L) {
   return p.T <= kFusedTopkMaxTokens && dispatch_uses_small(p, L);
 }
 

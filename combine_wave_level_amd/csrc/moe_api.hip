@@ -203,7 +203,7 @@ moe_status_t moe_route_dispatch(const moe_problem_t* p, const void* x, const voi
   float* partial = reinterpret_cast<float*>(w + L.logits);
   hipError_t e = launch_route_logits(*p, x, packed, partial, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  if (route_dispatch_fuses(*p))
+  if (route_dispatch_fuses(*p, L))
     return hip_status(launch_dispatch_with_topk(*p, L, partial, bias, topk_idx, topk_w, logits, expert_counts,
                                                 expert_offsets, sorted_token, pair_pos, token_ready_wave, w, s));
   if ((e = launch_topk(*p, partial, bias, topk_idx, topk_w, logits, s)) != hipSuccess) return MOE_ERR_HIP;

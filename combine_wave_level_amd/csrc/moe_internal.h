@@ -152,7 +152,7 @@ hipError_t launch_dispatch(const moe_problem_t& p, const WsLayout& L, const int3
 // round saves a launch (T = 1: 25.9 -> 21.7 us for the two steps), two
 // rounds cost more than the launch (T = 32: 26 -> 30.6 us).
 constexpr int kFusedTopkMaxTokens = 16;
-bool route_dispatch_fuses(const moe_problem_t& p);
+bool route_dispatch_fuses(const moe_problem_t& p, const WsLayout& L);
 hipError_t launch_route_logits(const moe_problem_t& p, const void* x, const void* packed, float* partial,
                                hipStream_t s);
 hipError_t launch_topk(const moe_problem_t& p, const float* partial, const float* bias, int32_t* topk_idx,
