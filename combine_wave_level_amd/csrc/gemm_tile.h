@@ -20,6 +20,13 @@
 // 16-byte LDS reads.  NST stages are in flight; completion is tracked with
 // explicit vmcnt waits and raw barriers (a full __syncthreads would drain
 // the prefetch of later stages at every step).
+//
+// Gathered token rows are the costly operand: a load instruction whose
+// lanes read 64 bytes from each of 16 rows costs the vector-memory path
+// about 2.7 times as long per byte as one that reads whole 128-byte lines
+// (measured on gfx950 with the data in L2: ~15 against ~42 B per clock per
+// CU).  Tiles with TL set therefore fetch each token row as whole 128-byte
+// lines, 64 k per row, covering two 32-wide K steps per load (see TileCfg).
 #pragma once
 
 #include "moe_common.h"
@@ -27,7 +34,7 @@
 namespace moe {
 
 template <int BW_, int BT_, int WR_, int WT_, int BK_, int NST_, bool SKIPB_ = false, bool FP8T_ = false,
-          bool TCOH_ = false, bool WNT_ = false>
+          bool TCOH_ = false, bool WNT_ = false, bool TL_ = false>
 struct TileCfg {
   static constexpr int BW = BW_, BT = BT_, WR = WR_, WT = WT_, BK = BK_, NST = NST_;
   // SKIPB: skip the MFMA work of every 16-row token block past the valid
@@ -51,6 +58,18 @@ struct TileCfg {
   // 0.149 -> 0.138 ms; on the compute-bound shapes, whose weight tiles are
   // reused by several m-tiles through the L2, the hint cost up to 6%.
   static constexpr bool WNT = WNT_;
+  // TL: token rows as whole 128-byte lines.  One wavefront load covers 8
+  // rows x 64 k (8 lanes per row, 16 bytes each), i.e. the token operand of
+  // two consecutive K steps; the token tile of such a double step (BT x 64
+  // bf16) sits in one of two LDS slots after the NST weight stages.  Inside
+  // a 1 KiB load block, row r's 16-byte chunk c (k = 8c .. 8c+7) is stored
+  // at position c ^ (r % 8) ^ ((r / 8) % 2), so that the MFMA operand reads
+  // of 16 rows hit distinct LDS banks.  Only the data movement differs:
+  // the MFMA sequence over K, and so every result bit, is that of the same
+  // tile without TL.
+  static constexpr bool TL = TL_;
+  static_assert(!TL || (BK == 32 && NST_ == 4 && !FP8T_ && BT_ % 8 == 0),
+                "TL: 32-wide K steps, 4 weight stages, bf16 tokens");
   static constexpr int NW = WR * WT;            // wavefronts per workgroup
   static constexpr int NTHREADS = 64 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts per workgroup");
@@ -61,19 +80,26 @@ struct TileCfg {
   static constexpr int TKS = FP8T ? KS / 2 : KS;  // token fragments per 16-row block per K step
   static constexpr int NFW = BW / 16 * KS;      // weight fragments per K step
   static constexpr int NFT = BT / 16 * TKS;     // token fragments per K step
-  static_assert(NFW % NW == 0 && NFT % NW == 0, "fragments split evenly over the wavefronts");
+  static constexpr int NFT2 = BT / 8;           // TL: token loads (8 rows each) per double step
+  static_assert(NFW % NW == 0 && (TL ? NFT2 % NW == 0 : NFT % NW == 0),
+                "fragments split evenly over the wavefronts");
   static constexpr int LW = NFW / NW;           // weight fragments each wave loads per step
-  static constexpr int LT = NFT / NW;           // token fragments each wave loads per step
+  // token loads each wave issues per step (TL: per double step)
+  static constexpr int LT = TL ? NFT2 / NW : NFT / NW;
   static constexpr int AW = BW / WR / 16;       // MFMA row blocks per wave
   static constexpr int AT = BT / WT / 16;       // MFMA column blocks per wave
-  static constexpr int STAGE = (NFW + NFT) * 512;  // bf16 elements per LDS stage
-  static constexpr size_t LDS_BYTES = static_cast<size_t>(NST) * STAGE * 2;
-  static_assert((NST - 1) * (LW + LT) <= 63, "vmcnt budget: NST-1 steps of loads in flight");
+  // bf16 elements per LDS stage (TL: the weight fragments only)
+  static constexpr int STAGE = (NFW + (TL ? 0 : NFT)) * 512;
+  static constexpr int TSTAGE = TL ? BT * 64 : 0;  // TL: bf16 elements per token slot
+  static constexpr size_t LDS_BYTES = (static_cast<size_t>(NST) * STAGE + 2 * TSTAGE) * 2;
+  static_assert(TL ? 2 * LW + LT <= 63 : (NST - 1) * (LW + LT) <= 63,
+                "vmcnt budget: NST-1 steps of loads in flight");
   // Register double-buffering of the MFMA operands (4 wavefronts, one per
   // SIMD).  With 8 wavefronts two share a SIMD and hide each other's LDS
   // latency; their register budget (256 per lane) has no room for a second
   // operand set.
   static constexpr bool DBUF = (NW == 4);
+  static_assert(!TL || !DBUF, "TL: 8 wavefronts");
 };
 
 // Wave w of the workgroup computes weight row blocks wr * AW .. + AW - 1 and
@@ -113,9 +139,11 @@ struct TokScale {
   float s[C::FP8T ? C::AT : 1];
 };
 
-// Row index (0..BT-1) inside the tile of the token fragment i this lane loads.
+// Row index (0..BT-1) inside the tile of the token fragment i this lane loads
+// (TL: of load block NW i + wave, 8 rows, 8 lanes per row).
 template <class C>
 __device__ __forceinline__ int trow_index(int i) {
+  if constexpr (C::TL) return (C::NW * i + wave_id()) * 8 + (lane_id() >> 3);
   return tok_frag_block<C>(i) * 16 + (lane_id() & 15);
 }
 
@@ -143,12 +171,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // The same tile with device-coherent token-row loads.
 template <class C>
-using TokCoherent = TileCfg<C::BW, C::BT, C::WR, C::WT, C::BK, C::NST, C::SKIPB, C::FP8T, true, C::WNT>;
+using TokCoherent = TileCfg<C::BW, C::BT, C::WR, C::WT, C::BK, C::NST, C::SKIPB, C::FP8T, true, C::WNT, C::TL>;
 
-// Issues this wave's direct-to-LDS loads of K step kt into stage kt % NST.
+// Issues this wave's direct-to-LDS loads of the weight fragments of K step kt
+// into stage kt % NST.
 template <class C>
-__device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, int KB,
-                                           const TokRows<C>& trow, uint16_t* lds, int kt) {
+__device__ __forceinline__ void tile_issue_w(const uint16_t* __restrict__ wtile, int KB, uint16_t* lds, int kt) {
   const int lane = lane_id(), wave = wave_id();
   uint16_t* st = lds + (kt % C::NST) * C::STAGE;
 #pragma unroll
@@ -160,6 +188,34 @@ __device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, i
     else
       lds_dma16(wtile + frag_offset(nb, kt * C::KS + kc, KB) + lane * 8, st + f * 512);
   }
+}
+
+// TL: the token lines of double step j (k = 64 j .. 64 j + 63) into token
+// slot j % 2.  Load block b = NW i + wave holds rows 8b .. 8b+7; lane l
+// takes row 8b + l/8 and the chunk that belongs at position l % 8.
+template <class C>
+__device__ __forceinline__ void tile_issue_tl(const TokRows<C>& trow, uint16_t* lds, int j) {
+  const int lane = lane_id(), wave = wave_id();
+  uint16_t* ts = lds + C::NST * C::STAGE + (j & 1) * C::TSTAGE;
+#pragma unroll
+  for (int i = 0; i < C::LT; ++i) {
+    const int b = C::NW * i + wave;
+    const int chunk = (lane & 7) ^ (lane >> 3) ^ (b & 1);
+    if constexpr (C::TCOH)
+      lds_dma16_coherent(trow.p[i] + j * 64 + chunk * 8, ts + b * 512);
+    else
+      lds_dma16(trow.p[i] + j * 64 + chunk * 8, ts + b * 512);
+  }
+}
+
+// Issues this wave's direct-to-LDS loads of K step kt into stage kt % NST.
+template <class C>
+__device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ wtile, int KB,
+                                           const TokRows<C>& trow, uint16_t* lds, int kt) {
+  static_assert(!C::TL, "TL tiles issue weights and token lines separately");
+  const int lane = lane_id(), wave = wave_id();
+  uint16_t* st = lds + (kt % C::NST) * C::STAGE;
+  tile_issue_w<C>(wtile, KB, lds, kt);
 #pragma unroll
   for (int i = 0; i < C::LT; ++i) {
     const int f = C::NW * i + wave;  // token fragment of the step
@@ -220,6 +276,27 @@ __device__ __forceinline__ void tile_read_frags(const uint16_t* st, int ks, Tile
       else
         f.b[b] = ld16(st + (C::NFW + (wt * C::AT + b) * C::KS + ks) * 512 + lane * 8);
     }
+}
+
+// TL: the operands of K step kt: weights from stage kt % NST, tokens from
+// slot (kt / 2) % 2, k-slice kt % 2 of the slot's 64 k.
+template <class C, bool ACT>
+__device__ __forceinline__ void tile_read_frags_tl(const uint16_t* lds, int kt, TileFrags<C>& f, int nbv) {
+  if constexpr (!ACT) return;
+  const int lane = lane_id();
+  const int wr = tile_wr<C>(), wt = tile_wt<C>();
+  const uint16_t* st = lds + (kt % C::NST) * C::STAGE;
+  const uint16_t* ts = lds + C::NST * C::STAGE + ((kt >> 1) & 1) * C::TSTAGE;
+#pragma unroll
+  for (int a = 0; a < C::AW; ++a) f.a[a] = ld16(st + (wr * C::AW + a) * 512 + lane * 8);
+  // lane l: row 16 tb + l % 16 (block 2 tb + (l / 8) % 2, row l % 8 of it),
+  // chunk 4 (kt % 2) + l / 16
+  const int hb = (lane >> 3) & 1, rr = lane & 7;
+  const int pos = ((4 * (kt & 1) + (lane >> 4)) ^ rr ^ hb);
+  const uint16_t* tl = ts + hb * 512 + rr * 64 + pos * 8;
+#pragma unroll
+  for (int b = 0; b < C::AT; ++b)
+    if (!C::SKIPB || b < nbv) f.b[b] = ld16(tl + (wt * C::AT + b) * 1024);
 }
 
 template <class C, bool ACT>
@@ -287,7 +364,43 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
                                              const TokRows<C>& trow, uint16_t* lds, TileAcc<C>& acc,
                                              int nbv, const TokScale<C>& tsc) {
 
-  if constexpr (!C::DBUF) {
+  if constexpr (C::TL) {
+    // Weights NST-1 = 3 steps ahead, token lines one double step ahead.  In
+    // issue order: T(0), W(0), W(1), W(2), then at step s: T(s/2 + 1) (s
+    // even), W(s + 3).  At the top of step kt the loads issued after the
+    // last one kt needs are: even kt (needs T(kt/2), issued at step kt-2):
+    // W(kt+1), W(kt+2); odd kt (needs W(kt), issued at step kt-3): W(kt+1),
+    // T(kt/2 + 1), W(kt+2) -- each only where it exists.  K = 64 * (nk/2).
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+      if (s < nk) {
+        if (s == 0) tile_issue_tl<C>(trow, lds, 0);
+        tile_issue_w<C>(wtile, KB, lds, s);
+      }
+    for (int kt = 0; kt < nk; kt += 2) {
+      // even step kt
+      if (kt + 2 < nk) wait_vmcnt<2 * C::LW>(); else wait_vmcnt<C::LW>();
+      raw_barrier();
+      if (kt + 2 < nk) tile_issue_tl<C>(trow, lds, kt / 2 + 1);
+      if (kt + 3 < nk) tile_issue_w<C>(wtile, KB, lds, kt + 3);
+      {
+        TileFrags<C> f;
+        tile_read_frags_tl<C, ACT>(lds, kt, f, nbv);
+        tile_mfma<C, ACT>(f, acc, nbv);
+      }
+      // odd step kt + 1
+      if (kt + 2 < nk) wait_vmcnt<2 * C::LW + C::LT>(); else wait_vmcnt<0>();
+      raw_barrier();
+      if (kt + 4 < nk) tile_issue_w<C>(wtile, KB, lds, kt + 4);
+      {
+        TileFrags<C> f;
+        tile_read_frags_tl<C, ACT>(lds, kt + 1, f, nbv);
+        tile_mfma<C, ACT>(f, acc, nbv);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    raw_barrier();
+  } else if constexpr (!C::DBUF) {
     // single operand set: steps 0 .. NST-2 in flight; step kt waits for its
     // own loads, passes a barrier (stage kt-1 is then free), issues step
     // kt + NST - 1 into that stage and computes from LDS
@@ -308,29 +421,29 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();
-    return;
-  }
-  // prologue: steps 0 .. NST-2 in flight, wait for step 0, then issue step
-  // NST-1 (at most NST-1 steps of loads are ever outstanding)
+  } else {
+    // prologue: steps 0 .. NST-2 in flight, wait for step 0, then issue step
+    // NST-1 (at most NST-1 steps of loads are ever outstanding)
 #pragma unroll
-  for (int s = 0; s < C::NST - 1; ++s)
-    if (s < nk) tile_issue<C>(wtile, KB, trow, lds, s);
-  wait_steps_left<C>(min(C::NST - 2, nk - 1));
-  if (C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, C::NST - 1);
-  raw_barrier();
-  TileFrags<C> f0, f1;
-  tile_read_frags<C, ACT>(lds, 0, f0, nbv, tsc);
+    for (int s = 0; s < C::NST - 1; ++s)
+      if (s < nk) tile_issue<C>(wtile, KB, trow, lds, s);
+    wait_steps_left<C>(min(C::NST - 2, nk - 1));
+    if (C::NST - 1 < nk) tile_issue<C>(wtile, KB, trow, lds, C::NST - 1);
+    raw_barrier();
+    TileFrags<C> f0, f1;
+    tile_read_frags<C, ACT>(lds, 0, f0, nbv, tsc);
 
-  constexpr int P1 = C::KS & 1;  // register-set parity of the step after an even step
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv, tsc);
-    tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc, nbv, tsc);
+    constexpr int P1 = C::KS & 1;  // register-set parity of the step after an even step
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv, tsc);
+      tile_step<C, P1, ACT>(wtile, KB, nk, kt + 1, trow, lds, f0, f1, acc, nbv, tsc);
+    }
+    if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv, tsc);
+    // all LDS reads of this tile done before anyone refills the stages
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    raw_barrier();
   }
-  if (kt < nk) tile_step<C, 0, ACT>(wtile, KB, nk, kt, trow, lds, f0, f1, acc, nbv, tsc);
-  // all LDS reads of this tile done before anyone refills the stages
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  raw_barrier();
 }
 
 

@@ -14,7 +14,7 @@ import oracle
 from combine_wave_level_amd import moe
 from helpers import (OUT_TOL, Layer, check_dispatch_exact, check_dispatch_valid, check_routing,
                      host_f64, oracle_inputs, rel_err_rows)
-from workloads import get, make_inputs
+from workloads import Workload, get, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,21 @@ def test_mid_layer_ragged_cut_full():
 
 def test_mid_layer_benchmark_size_sampled():
     _full_compare(inputs("mid"), sample=48)
+
+
+def test_odd_widths_run_the_128_wide_tiles():
+    """d = 384 and 2I = 384 are not multiples of 256, so both expert GEMMs
+    run the 128-wide tile shape; 3 local experts of 7 starting at 2, k = 3,
+    a ragged batch; full comparison, then the phase kernels against the
+    persistent kernel bit for bit."""
+    wl = Workload("odd", T=157, d=384, I=192, E_global=7, E_local=3, k=3, G=1, e_begin=2, seed=11)
+    inp = make_inputs(wl)
+    L, r, _ = _full_compare(inp)
+    a = L.forward(serial=False)
+    b = L.forward(serial=True)
+    assert torch.equal(a["out"], b["out"])
+    P = int(a["disp"].offsets[-1])
+    assert torch.equal(a["y"][:P], b["y"][:P])
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 128])
