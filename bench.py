@@ -16,7 +16,9 @@ The step is the forward (the metric's configuration is a forward).  The same
 run also times the layer's backward on the same batch (data gradient,
 combine-weight and logits gradients, dWg and the expert weight gradient, one
 moe_backward call) and reports it under "extra.backward" (--no-backward
-skips it), and the forward with FP8 dispatch (per-token e4m3 staging, then
+skips it), with the expert FFN that keeps the first GEMM's pre-activations
+and the backward that reads them instead of recomputing under
+"extra.backward.saved_h", and the forward with FP8 dispatch (per-token e4m3 staging, then
 the expert FFN pulling it) under "extra.fp8_dispatch" (--no-fp8 skips it).
 
 Only one GPU is used: --gpus above 1 exits with a message.
@@ -266,8 +268,40 @@ def time_backward(args, wl, T, p, inp, d, x, packed, idx, w, disp, stream, P_loc
     # per routed pair, plus the dense dWg product (2 d E per token)
     flops = 16.0 * wl.d * wl.I * P_local + 2.0 * T * wl.d * wl.E_global
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms": round(ms, 4), "tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-            "flops_per_step": flops, "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    res = {"ms": round(ms, 4), "tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+           "flops_per_step": flops, "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    # the saved pre-activation path: the expert FFN that keeps h1 | h3
+    # (fp32, P x 2I) and the backward that reads them instead of recomputing
+    h = torch.empty(moe.saved_h_shape(p), dtype=torch.float32, device=x.device)
+
+    def fwd_save():
+        return moe.ffn_waved(p, x, packed, disp, w, ws, save_h=h)
+
+    def bwd_saved():
+        return moe.backward(p, x, packed, packed_bwd, idx, w, disp, dout, ws, want_dtopk_w=True,
+                            want_dlogits=False, want_dwg=True, want_dw=True, saved_h=h)
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup // 2)):
+            fn()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(n):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        moe.check_error(ws)
+        return t0.elapsed_time(t1) / n
+
+    fms = timed(fwd_save)
+    sms = timed(bwd_saved)
+    sflops = flops - 4.0 * wl.d * wl.I * P_local
+    stf = sflops / (sms * 1e-3) / 1e12
+    res["saved_h"] = {"ffn_save_ms": round(fms, 4), "ms": round(sms, 4), "tflops": round(stf, 2),
+                      "mfma_frac": round(stf / PEAK_BF16_TFLOPS, 4), "flops_per_step": sflops,
+                      "tokens_per_s": round(T / (sms * 1e-3), 1),
+                      "h_bytes": int(h.numel() * 4)}
+    return res
 
 
 MALL_FLUSH_BYTES = 512 << 20   # twice the MI355X's 256 MB last-level cache

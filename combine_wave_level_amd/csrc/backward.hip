@@ -138,7 +138,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
   }
 }
 
-// h1, h3 recomputed with the forward's GEMM1 arithmetic (BW packed rows =
+// h1, h3 recomputed with the forward's GEMM1 arithmetic, or read from the
+// forward's saved accumulators hsaved [P][GR I] (the same bits; BW packed rows =
 // BW/2 intermediate indices x BT routed rows per tile, K = d ascending; the
 // tile shape never changes the bits), then per element
 //   dA = w g, s = sigmoid(h1), silu = h1 s, a = silu h3,
@@ -149,13 +150,13 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
 // Outputs: dH rows [P][2I] (dH1 | dH3) for the dx product and, when dht is
 // not null, (dH1 | dH3)^T fragments and (w a)^T rows for the weight
 // gradient, transposed through an LDS stage.
-template <class C, bool GATED>
+template <class C, bool GATED, bool SAVED>
 __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13, const float* __restrict__ g,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d, int I,
     int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht, uint16_t* __restrict__ awt,
-    float* __restrict__ dwp) {
+    float* __restrict__ dwp, const float* __restrict__ hsaved) {
   using D = BwdDh<C, GATED>;
   static_assert(!GATED || C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   constexpr int GR = GATED ? 2 : 1;  // packed W13 rows per intermediate index
@@ -189,15 +190,40 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
       }
       wrow[r] = r < count ? w : 0.f;
     }
-    TokRows<C> trow;
+    TileAcc<C> acc;
+    if constexpr (SAVED) {
+      // the forward's accumulators, laid out as this product leaves them:
+      // a row past count holds row count-1's values (its operand row is
+      // clamped to that row) in a wavefront with a valid row, and zeros in
+      // a wavefront with none (tile_mma skips it)
 #pragma unroll
-    for (int i = 0; i < C::LT; ++i) {
-      const int r = min(trow_index<C>(i), count - 1);
-      trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+      for (int a = 0; a < C::AW; ++a)
+#pragma unroll
+        for (int b = 0; b < C::AT; ++b) acc.v[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (wt * C::AT * 16 < count) {
+        const size_t ncol = static_cast<size_t>(GR) * I;
+#pragma unroll
+        for (int b = 0; b < C::AT; ++b) {
+          const int tr = min((wt * C::AT + b) * 16 + (lane & 15), count - 1);
+#pragma unroll
+          for (int a = 0; a < C::AW; ++a) {
+            const int n = nt * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);
+            acc.v[a][b] = *reinterpret_cast<const f32x4*>(hsaved + static_cast<size_t>(row0 + tr) * ncol + n);
+          }
+        }
+      }
+      __syncthreads();  // the wrow writes before the reads below
+    } else {
+      TokRows<C> trow;
+#pragma unroll
+      for (int i = 0; i < C::LT; ++i) {
+        const int r = min(trow_index<C>(i), count - 1);
+        trow.p[i] = xb + static_cast<size_t>(sorted_token[row0 + r]) * d;
+      }
+      // barriers inside order the wrow writes before the reads below
+      tile_mma<C>(w13 + static_cast<size_t>(e) * GR * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
+                  d / C::BK, trow, lds, acc, count);
     }
-    TileAcc<C> acc;  // barriers inside order the wrow writes before the reads below
-    tile_mma<C>(w13 + static_cast<size_t>(e) * GR * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
-                d / C::BK, trow, lds, acc, count);
     // second-pass staging keeps the tile's w a values as bf16 pairs (not the
     // accumulators) across the read-out of the first stage (gated; the
     // ungated epilogue recomputes w a from the accumulators instead)
@@ -893,20 +919,28 @@ hipError_t launch_wgrad(const moe_problem_t& p, const WsLayout& L, const uint16_
 }
 
 // The recompute with the gradient epilogue on tile C.
+template <class C, bool GATED, bool SAVED>
+hipError_t launch_dh_kind(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, const uint16_t* xb,
+                          const uint16_t* w13, const float* g, uint16_t* dh, uint16_t* dht, uint16_t* awt,
+                          float* dwp, int cus, hipStream_t s) {
+  constexpr size_t lds = BwdDh<C, GATED>::LDS;
+  int per_cu = 0;
+  hipError_t e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel<C, GATED, SAVED>, C::NTHREADS,
+                                                        lds)) != hipSuccess)
+    return e;
+  bwd_dh_kernel<C, GATED, SAVED><<<max(1, per_cu) * cus, C::NTHREADS, lds, s>>>(
+      xb, w13, g, a.offsets, a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh, dht, awt,
+      dwp, a.hsaved);
+  return hipGetLastError();
+}
+
 template <class C, bool GATED>
 hipError_t launch_dh_act(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, const uint16_t* xb,
                          const uint16_t* w13, const float* g, uint16_t* dh, uint16_t* dht, uint16_t* awt,
                          float* dwp, int cus, hipStream_t s) {
-  constexpr size_t lds = BwdDh<C, GATED>::LDS;
-  int per_cu = 0;
-  hipError_t e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel<C, GATED>, C::NTHREADS, lds)) !=
-      hipSuccess)
-    return e;
-  bwd_dh_kernel<C, GATED><<<max(1, per_cu) * cus, C::NTHREADS, lds, s>>>(
-      xb, w13, g, a.offsets, a.sorted_token, a.pair_pos, a.topk_w, p.E_local, p.d, p.I, p.k, L.P_pad, dh, dht, awt,
-      dwp);
-  return hipGetLastError();
+  if (a.hsaved) return launch_dh_kind<C, GATED, true>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
+  return launch_dh_kind<C, GATED, false>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
 }
 
 template <class C>

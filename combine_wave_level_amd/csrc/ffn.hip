@@ -60,7 +60,8 @@ template <class F, bool GATED>
 __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w13,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_token,
-    uint16_t* __restrict__ act, int E_local, int d, int I, const float* __restrict__ xscale) {
+    uint16_t* __restrict__ act, int E_local, int d, int I, const float* __restrict__ xscale,
+    float* __restrict__ hsave) {
   constexpr int gr = GATED ? 2 : 1;  // packed W13 rows per intermediate index
   using C = typename F::G1;
   extern __shared__ __align__(16) uint16_t lds[];
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
     gemm1_tile<C, GATED>(xb, w13 + static_cast<size_t>(e) * gr * I * d, sorted_token, act, row0, count, nt, d,
-                         I, lds, xscale);
+                         I, lds, xscale, hsave);
   }
 }
 
@@ -474,18 +475,21 @@ template <class F>
 hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint16_t* xb, const float* xscale,
                           const uint16_t* w13, const uint16_t* w2, const int32_t* offsets,
                           const int32_t* sorted_token, const int32_t* pair_pos, const float* topk_w,
-                          void* y, void* out, uint32_t flags, char* ws, hipStream_t s) {
+                          void* y, void* out, float* hsave, uint32_t flags, char* ws, hipStream_t s) {
   hipError_t e;
   int dev = 0, cus = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   const bool out_bf16 = p.out_dtype == MOE_BF16;
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
-  if (!ffn_uses_persistent(p, cus, flags)) {
+  // saving the pre-activations runs the phase kernels: the persistent
+  // kernel's register budget has no room for the stores (same bits)
+  if (hsave != nullptr || !ffn_uses_persistent(p, cus, flags)) {
     constexpr size_t l1 = F::G1::LDS_BYTES, l2 = F::G2::LDS_BYTES;
     auto g1 = gate_rows(p) == 2 ? gemm1_phase_kernel<F, true> : gemm1_phase_kernel<F, false>;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g1, F::NT, l1)) != hipSuccess) return e;
-    g1<<<max(1, per_cu) * cus, F::NT, l1, s>>>(xb, w13, offsets, sorted_token, act, p.E_local, p.d, p.I, xscale);
+    g1<<<max(1, per_cu) * cus, F::NT, l1, s>>>(xb, w13, offsets, sorted_token, act, p.E_local, p.d, p.I, xscale,
+                                               hsave);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm2_phase_kernel<F>, F::NT, l2)) != hipSuccess)
       return e;
@@ -599,7 +603,7 @@ hipError_t stage_x_bf16(const moe_problem_t& p, const WsLayout& L, const void* x
 
 hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
                       const int32_t* offsets, const int32_t* sorted_token, const int32_t* pair_pos,
-                      const float* topk_w, const int32_t* ready_wave, void* y, void* out,
+                      const float* topk_w, const int32_t* ready_wave, void* y, void* out, float* hsave,
                       uint32_t flags, char* ws, hipStream_t s) {
   (void)ready_wave;
   const PackedLayout PL = packed_layout(p.d, p.I, p.E_global, p.E_local, p.x_dtype == MOE_BF16, gate_rows(p));
@@ -612,16 +616,16 @@ hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, 
   switch (pick_ffn_shape(p)) {
     case FfnShape::Small:
       return launch_ffn_cfg<FfnSmall>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
-                                      out, flags, ws, s);
+                                      out, hsave, flags, ws, s);
     case FfnShape::Small64:
       return launch_ffn_cfg<FfnSmall64>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
-                                         out, flags, ws, s);
+                                         out, hsave, flags, ws, s);
     case FfnShape::Large:
       return launch_ffn_cfg<FfnLarge>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
-                                      out, flags, ws, s);
+                                      out, hsave, flags, ws, s);
     default:
       return launch_ffn_cfg<FfnMid>(p, L, xb, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
-                                    out, flags, ws, s);
+                                    out, hsave, flags, ws, s);
   }
 }
 
@@ -638,10 +642,10 @@ hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8
   const FfnShape shape = pick_ffn_shape(p);
   if (shape == FfnShape::Small)
     return launch_ffn_cfg<FfnSmallF8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
-                                      flags, ws, s);
+                                      nullptr, flags, ws, s);
   if (shape == FfnShape::Small64)
     return launch_ffn_cfg<FfnSmall64F8>(p, L, xb, xscale, w13, w2, offsets, sorted_token, pair_pos, topk_w, y,
-                                        out, flags, ws, s);
+                                        out, nullptr, flags, ws, s);
   // Large and mid batches are compute-bound: the rows are dequantized once
   // on arrival (T x d bytes read, 2 T x d written, exact in bf16) and the
   // bf16 tiles run on them; the conversions inside the GEMM1 tile would
@@ -651,9 +655,9 @@ hipError_t launch_ffn_fp8(const moe_problem_t& p, const WsLayout& L, const uint8
   if (e != hipSuccess) return e;
   if (shape == FfnShape::Large)
     return launch_ffn_cfg<FfnLarge>(p, L, xs, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
-                                    flags, ws, s);
-  return launch_ffn_cfg<FfnMid>(p, L, xs, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out, flags,
-                                ws, s);
+                                    nullptr, flags, ws, s);
+  return launch_ffn_cfg<FfnMid>(p, L, xs, nullptr, w13, w2, offsets, sorted_token, pair_pos, topk_w, y, out,
+                                nullptr, flags, ws, s);
 }
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pair_pos,

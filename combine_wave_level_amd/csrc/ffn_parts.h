@@ -159,13 +159,19 @@ __device__ __forceinline__ void out_flush(const uint16_t* lds, uint16_t* __restr
 // the dispatch pull lands in LDS.
 // FP8T tiles: xb is the e4m3 staging buffer (d bytes per token) and xscale
 // the tokens' scales.
+// hsave (optional, wave-uniform): the tile's fp32 accumulators h of its
+// valid rows are also stored to hsave [P][gr I], packed column order (16
+// columns of W1, then the same 16 intermediate indices of W3, ... when
+// gated; W1's columns in order when not), for a backward that reads the
+// pre-activations instead of recomputing them.
 template <class C, bool GATED = true>
 __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            const uint16_t* __restrict__ w13e,
                                            const int32_t* __restrict__ sorted_token,
                                            uint16_t* __restrict__ act, int row0, int count, int nt,
                                            int d, int I, uint16_t* lds,
-                                           const float* __restrict__ xscale = nullptr) {
+                                           const float* __restrict__ xscale = nullptr,
+                                           float* __restrict__ hsave = nullptr) {
   static_assert(!GATED || C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   constexpr int COLS = C::BW / 2;
   static_assert(static_cast<size_t>(C::BT) * COLS * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
@@ -189,6 +195,20 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
   }
   TileAcc<C> acc;
   tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc, count, &tsc);
+  if (hsave != nullptr) {
+    const size_t ncol = static_cast<size_t>(GATED ? 2 : 1) * I;
+#pragma unroll
+    for (int b = 0; b < C::AT; ++b) {
+      if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones
+      const int t = (wt * C::AT + b) * 16 + (lane & 15);
+      if (t >= count) continue;
+#pragma unroll
+      for (int a = 0; a < C::AW; ++a) {
+        const int n = nt * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);
+        *reinterpret_cast<f32x4*>(hsave + static_cast<size_t>(row0 + t) * ncol + n) = acc.v[a][b];
+      }
+    }
+  }
   if constexpr (!GATED) {
     // ungated: every row block is W1; a = max(h, 0)^2 for BW intermediate
     // indices per tile

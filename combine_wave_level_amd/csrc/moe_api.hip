@@ -211,24 +211,48 @@ moe_status_t moe_route_dispatch(const moe_problem_t* p, const void* x, const voi
                                     token_ready_wave, w, s));
 }
 
-moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const void* packed,
-                                  const int32_t* expert_offsets, const int32_t* sorted_token,
-                                  const int32_t* pair_pos, const float* topk_w,
-                                  const int32_t* token_ready_wave, void* y, void* out,
-                                  uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
+namespace {
+
+// moe_expert_ffn_waved, and with hsave != nullptr moe_expert_ffn_waved_save_h.
+moe_status_t ffn_waved_call(const moe_problem_t* p, const void* x, const void* packed,
+                            const int32_t* expert_offsets, const int32_t* sorted_token, const int32_t* pair_pos,
+                            const float* topk_w, const int32_t* token_ready_wave, void* y, void* out,
+                            float* hsave, uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (!ffn_flags_ok(flags)) return MOE_ERR_INVALID_ARG;
   if (!packed || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !sorted_token || !y)) return MOE_ERR_INVALID_ARG;
   if (out && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
-  if ((x && !aligned16(x)) || !aligned16(packed) || (y && !aligned16(y)) || (out && !aligned16(out)))
+  if ((x && !aligned16(x)) || !aligned16(packed) || (y && !aligned16(y)) || (out && !aligned16(out)) ||
+      (hsave && !aligned16(hsave)))
     return MOE_ERR_INVALID_ARG;
   WsLayout L;
   if ((st = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return st;
   return hip_status(launch_ffn(*p, L, x, packed, expert_offsets, sorted_token, pair_pos, topk_w,
-                               token_ready_wave, y, out, flags, static_cast<char*>(ws),
+                               token_ready_wave, y, out, hsave, flags, static_cast<char*>(ws),
                                static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const void* packed,
+                                  const int32_t* expert_offsets, const int32_t* sorted_token,
+                                  const int32_t* pair_pos, const float* topk_w,
+                                  const int32_t* token_ready_wave, void* y, void* out,
+                                  uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return ffn_waved_call(p, x, packed, expert_offsets, sorted_token, pair_pos, topk_w, token_ready_wave, y, out,
+                        nullptr, flags, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_expert_ffn_waved_save_h(const moe_problem_t* p, const void* x, const void* packed,
+                                         const int32_t* expert_offsets, const int32_t* sorted_token,
+                                         const int32_t* pair_pos, const float* topk_w,
+                                         const int32_t* token_ready_wave, void* y, void* out, float* h,
+                                         uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (p && p->T > 0 && !h) return MOE_ERR_INVALID_ARG;
+  return ffn_waved_call(p, x, packed, expert_offsets, sorted_token, pair_pos, topk_w, token_ready_wave, y, out, h,
+                        flags, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_quantize_fp8(const moe_problem_t* p, const void* x, uint8_t* x_fp8, float* x_scale,
@@ -303,12 +327,15 @@ moe_status_t moe_expert_wgrad(const moe_problem_t* p, const void* x, const void*
   return hip_status(launch_backward(*p, L, a, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* packed,
-                          const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
-                          const int32_t* expert_offsets, const int32_t* sorted_token,
-                          const int32_t* pair_pos, const void* dout, void* dx, float* dtopk_w,
-                          float* dlogits, float* dWg, float* dW1, float* dW3, float* dW2, void* ws,
-                          size_t ws_bytes, moe_stream_t stream) {
+namespace {
+
+// moe_backward, and with hsaved != nullptr moe_backward_saved_h.
+moe_status_t backward_call(const moe_problem_t* p, const void* x, const void* packed,
+                           const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
+                           const int32_t* expert_offsets, const int32_t* sorted_token,
+                           const int32_t* pair_pos, const void* dout, void* dx, float* dtopk_w,
+                           float* dlogits, float* dWg, float* dW1, float* dW3, float* dW2, const float* hsaved,
+                           void* ws, size_t ws_bytes, moe_stream_t stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (!packed || !packed_bwd || !expert_offsets) return MOE_ERR_INVALID_ARG;
@@ -322,7 +349,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
   if (any_w && !all_w) return MOE_ERR_INVALID_ARG;
   if ((x && !aligned16(x)) || !aligned16(packed) || !aligned16(packed_bwd) || (dout && !aligned16(dout)) ||
       (dx && !aligned16(dx)) || (dW1 && !aligned16(dW1)) || (dW3 && !aligned16(dW3)) ||
-      (dW2 && !aligned16(dW2)))
+      (dW2 && !aligned16(dW2)) || (hsaved && !aligned16(hsaved)))
     return MOE_ERR_INVALID_ARG;
   WsLayout L;
   if ((st = check_ws(p, ws, ws_bytes, &L, true)) != MOE_OK) return st;
@@ -343,7 +370,31 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
   a.dW1 = dW1;
   a.dW3 = dW3;
   a.dW2 = dW2;
+  a.hsaved = hsaved;
   return hip_status(launch_backward(*p, L, a, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* packed,
+                          const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
+                          const int32_t* expert_offsets, const int32_t* sorted_token,
+                          const int32_t* pair_pos, const void* dout, void* dx, float* dtopk_w,
+                          float* dlogits, float* dWg, float* dW1, float* dW3, float* dW2, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  return backward_call(p, x, packed, packed_bwd, topk_idx, topk_w, expert_offsets, sorted_token, pair_pos, dout,
+                       dx, dtopk_w, dlogits, dWg, dW1, dW3, dW2, nullptr, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_backward_saved_h(const moe_problem_t* p, const void* x, const void* packed,
+                                  const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
+                                  const int32_t* expert_offsets, const int32_t* sorted_token,
+                                  const int32_t* pair_pos, const void* dout, const float* h, void* dx,
+                                  float* dtopk_w, float* dlogits, float* dWg, float* dW1, float* dW3,
+                                  float* dW2, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (p && p->T > 0 && !h) return MOE_ERR_INVALID_ARG;
+  return backward_call(p, x, packed, packed_bwd, topk_idx, topk_w, expert_offsets, sorted_token, pair_pos, dout,
+                       dx, dtopk_w, dlogits, dWg, dW1, dW3, dW2, h, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_check_error(void* ws, moe_stream_t stream) {

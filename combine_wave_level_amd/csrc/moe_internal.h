@@ -116,6 +116,9 @@ struct BackwardArgs {
   float* dW1;
   float* dW3;
   float* dW2;
+  // the forward's GEMM1 pre-activations [P][gr I] fp32 (packed column
+  // order) or nullptr: recompute them
+  const float* hsaved;
 };
 
 // ------------------------------------------------------------ launchers
@@ -173,7 +176,7 @@ bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags);
 
 hipError_t launch_ffn(const moe_problem_t& p, const WsLayout& L, const void* x, const void* packed,
                       const int32_t* offsets, const int32_t* sorted_token, const int32_t* pair_pos,
-                      const float* topk_w, const int32_t* ready_wave, void* y, void* out,
+                      const float* topk_w, const int32_t* ready_wave, void* y, void* out, float* hsave,
                       uint32_t flags, char* ws, hipStream_t s);
 
 // Returns the bf16 token-order staging copy of x used by the expert GEMMs:

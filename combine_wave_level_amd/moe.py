@@ -36,7 +36,7 @@ EXPORTED = (
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
     "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
     "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc", "moe_route_dispatch", "moe_probe_mfma",
-    "moe_probe_copy",
+    "moe_probe_copy", "moe_expert_ffn_waved_save_h", "moe_backward_saved_h",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, vp]),
             "moe_expert_ffn_waved": (st, [P, vp, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
                                           ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
+            "moe_expert_ffn_waved_save_h": (st, [P, vp, vp, i32p, i32p, i32p, f32p, i32p, vp, vp, f32p,
+                                                 ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
             "moe_combine": (st, [P, vp, i32p, f32p, vp, vp]),
             "moe_expert_wgrad": (st, [P, vp, vp, vp, i32p, i32p, i32p, f32p, vp, f32p, f32p, f32p,
                                       vp, ctypes.c_size_t, vp]),
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
             "moe_pack_weights_bwd": (st, [P, vp, vp, vp, vp, vp, vp]),
             "moe_backward": (st, [P, vp, vp, vp, i32p, f32p, i32p, i32p, i32p, vp, vp, f32p, f32p, f32p,
                                   f32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
+            "moe_backward_saved_h": (st, [P, vp, vp, vp, i32p, f32p, i32p, i32p, i32p, vp, f32p, vp, f32p, f32p,
+                                          f32p, f32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
             "moe_quantize_fp8": (st, [P, vp, vp, f32p, vp]),
             "moe_expert_ffn_waved_fp8": (st, [P, vp, f32p, vp, i32p, i32p, i32p, f32p, i32p, vp, vp,
                                               ctypes.c_uint32, vp, ctypes.c_size_t, vp]),
@@ -261,19 +265,31 @@ def _out_dtype(p: Problem):
     return torch.bfloat16 if p.out_dtype == MOE_BF16 else torch.float32
 
 
+def saved_h_shape(p: Problem):
+    """Shape of the fp32 pre-activation buffer of ffn_waved(save_h=...)."""
+    gr = 2 if p.activation == MOE_ACT_SWIGLU else 1
+    return (max(1, p_max(p)), gr * p.I)
+
+
 def ffn_waved(p: Problem, x, packed, disp: Dispatch, topk_w, ws, fused_combine=True,
-              serial=False, y=None, out=None, persistent=False):
+              serial=False, y=None, out=None, persistent=False, save_h=None):
+    """save_h: an fp32 tensor of saved_h_shape(p) that receives the GEMM1
+    pre-activations (moe_expert_ffn_waved_save_h), for backward(saved_h=...)."""
     dev = x.device
     if y is None:
         y = torch.empty((max(1, p_max(p)), p.d), dtype=torch.bfloat16, device=dev)
     if fused_combine and out is None:
         out = torch.empty((p.T, p.d), dtype=_out_dtype(p), device=dev)
     flags = _ffn_flags(serial, persistent)
-    _check(lib().moe_expert_ffn_waved(
-        ctypes.byref(p), _p(x), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
-        _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y),
-        _p(out) if fused_combine else None, flags, _p(ws), ws.numel(), _stream()),
-        "moe_expert_ffn_waved")
+    args = (ctypes.byref(p), _p(x), _p(packed), _p(disp.offsets), _p(disp.sorted_token),
+            _p(disp.pair_pos), _p(topk_w), _p(disp.ready_wave), _p(y), _p(out) if fused_combine else None)
+    if save_h is None:
+        _check(lib().moe_expert_ffn_waved(*args, flags, _p(ws), ws.numel(), _stream()), "moe_expert_ffn_waved")
+    else:
+        if tuple(save_h.shape) != saved_h_shape(p) or save_h.dtype != torch.float32:
+            raise ValueError(f"save_h must be float32 of shape {saved_h_shape(p)}")
+        _check(lib().moe_expert_ffn_waved_save_h(*args, _p(save_h), flags, _p(ws), ws.numel(), _stream()),
+               "moe_expert_ffn_waved_save_h")
     return y, (out if fused_combine else None)
 
 
@@ -338,9 +354,10 @@ def pack_weights_bwd(p: Problem, Wg, W1, W3, W2) -> torch.Tensor:
 
 
 def backward(p: Problem, x, packed, packed_bwd, topk_idx, topk_w, disp: Dispatch, dout, ws,
-             want_dtopk_w=True, want_dlogits=False, want_dwg=True, want_dw=False):
+             want_dtopk_w=True, want_dlogits=False, want_dwg=True, want_dw=False, saved_h=None):
     """Data gradient dx (always) and, on request, dtopk_w, dlogits, dWg and the
-    expert weight gradient, in one call."""
+    expert weight gradient, in one call.  saved_h: the pre-activations a
+    ffn_waved(save_h=...) call kept (moe_backward_saved_h: no recompute)."""
     dev = x.device
     f32 = torch.float32
     dx = torch.empty((p.T, p.d), dtype=x.dtype, device=dev)
@@ -353,10 +370,15 @@ def backward(p: Problem, x, packed, packed_bwd, topk_idx, topk_w, disp: Dispatch
         if p.activation == MOE_ACT_SWIGLU:
             dW3 = torch.empty((p.E_local, p.d, p.I), dtype=f32, device=dev)
         dW2 = torch.empty((p.E_local, p.I, p.d), dtype=f32, device=dev)
-    _check(lib().moe_backward(
-        ctypes.byref(p), _p(x), _p(packed), _p(packed_bwd), _p(topk_idx), _p(topk_w), _p(disp.offsets),
-        _p(disp.sorted_token), _p(disp.pair_pos), _p(dout), _p(dx), _p(dtw), _p(dlg), _p(dwg),
-        _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(), _stream()), "moe_backward")
+    head = (ctypes.byref(p), _p(x), _p(packed), _p(packed_bwd), _p(topk_idx), _p(topk_w), _p(disp.offsets),
+            _p(disp.sorted_token), _p(disp.pair_pos), _p(dout))
+    tail = (_p(dx), _p(dtw), _p(dlg), _p(dwg), _p(dW1), _p(dW3), _p(dW2), _p(ws), ws.numel(), _stream())
+    if saved_h is None:
+        _check(lib().moe_backward(*head, *tail), "moe_backward")
+    else:
+        if tuple(saved_h.shape) != saved_h_shape(p) or saved_h.dtype != torch.float32:
+            raise ValueError(f"saved_h must be float32 of shape {saved_h_shape(p)}")
+        _check(lib().moe_backward_saved_h(*head, _p(saved_h), *tail), "moe_backward_saved_h")
     return {"dx": dx, "dtopk_w": dtw, "dlogits": dlg, "dWg": dwg, "dW1": dW1, "dW3": dW3, "dW2": dW2}
 
 
@@ -384,8 +406,11 @@ def check_error(ws) -> None:
     _check(lib().moe_check_error(_p(ws), _stream()), "moe_check_error")
 
 
-def forward(p: Problem, x, packed, ws, bias=None, serial=False, want_logits=False, persistent=False):
-    """route -> dispatch (one call) -> waved expert FFN with fused combine."""
+def forward(p: Problem, x, packed, ws, bias=None, serial=False, want_logits=False, persistent=False,
+            save_h=None):
+    """route -> dispatch (one call) -> waved expert FFN with fused combine
+    (save_h: see ffn_waved)."""
     idx, w, logits, disp = route_dispatch(p, x, packed, ws, bias=bias, want_logits=want_logits)
-    y, out = ffn_waved(p, x, packed, disp, w, ws, fused_combine=True, serial=serial, persistent=persistent)
+    y, out = ffn_waved(p, x, packed, disp, w, ws, fused_combine=True, serial=serial, persistent=persistent,
+                       save_h=save_h)
     return {"idx": idx, "w": w, "logits": logits, "disp": disp, "y": y, "out": out}

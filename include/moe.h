@@ -257,6 +257,28 @@ moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const v
                                   uint32_t flags, void* ws, size_t ws_bytes,
                                   moe_stream_t stream);
 
+/* moe_expert_ffn_waved that also keeps the first GEMM's pre-activations for
+ * the backward: activation saving in place of recomputation (the launch
+ * digest, itsolotime.com, names flexible activation checkpointing among the
+ * training framework's features, section 5.4, without details; which tensor
+ * to keep is this library's choice).  Outputs y and out are bit-identical
+ * to moe_expert_ffn_waved's.
+ *   h [P_max, gr * I] fp32 (gr = 2 for SWIGLU, 1 for RELU2), caller-owned,
+ *   16-byte aligned, required when T > 0: row r (sorted-row order, r <
+ *   expert_offsets[E_local]) gets the fp32 accumulators of that routed row,
+ *   in packed column order: for SWIGLU, columns 32 q .. 32 q + 15 hold h1 =
+ *   x W1 for intermediate indices 16 q .. 16 q + 15 and columns 32 q + 16 ..
+ *   32 q + 31 hold h3 = x W3 for the same indices; for RELU2, column i holds
+ *   h1 for index i.  Rows past the routed ones are not written.  Pass h, the
+ *   same routing and the same workspace's dispatch to moe_backward_saved_h.
+ * Errors as moe_expert_ffn_waved, plus MOE_ERR_INVALID_ARG for a NULL or
+ * misaligned h. */
+moe_status_t moe_expert_ffn_waved_save_h(const moe_problem_t* p, const void* x, const void* packed,
+                                         const int32_t* expert_offsets, const int32_t* sorted_token,
+                                         const int32_t* pair_pos, const float* topk_w,
+                                         const int32_t* token_ready_wave, void* y, void* out, float* h,
+                                         uint32_t flags, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* FP8 dispatch (digest section 1.4, compute/communication bullet: tokens go
  * to the experts in FP8, results come back in BF16).  Per token t:
  * scale[t] = 2^k, k the smallest integer with max_i |x[t, i]| <= 448 * 2^k
@@ -347,6 +369,20 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
                           const int32_t* pair_pos, const void* dout, void* dx, float* dtopk_w,
                           float* dlogits, float* dWg, float* dW1, float* dW3, float* dW2, void* ws,
                           size_t ws_bytes, moe_stream_t stream);
+
+/* moe_backward with h1, h3 read from h (written by moe_expert_ffn_waved_save_h
+ * on the same x, weights and dispatch) instead of recomputed: the first
+ * GEMM, half of the backward's matrix products before the weight gradient,
+ * is skipped.  The stored values are the accumulators the recomputation
+ * produces, so every output is bit-identical to moe_backward's.  Arguments
+ * as moe_backward, plus h [P_max, gr * I] fp32 (16-byte aligned, required
+ * when T > 0; only routed rows are read). */
+moe_status_t moe_backward_saved_h(const moe_problem_t* p, const void* x, const void* packed,
+                                  const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
+                                  const int32_t* expert_offsets, const int32_t* sorted_token,
+                                  const int32_t* pair_pos, const void* dout, const float* h, void* dx,
+                                  float* dtopk_w, float* dlogits, float* dWg, float* dW1, float* dW3,
+                                  float* dW2, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Synchronises `stream`, then reads the device error word of the workspace
  * (set by a bounded wait of moe_expert_ffn_waved that expired) and clears

@@ -237,6 +237,36 @@ def test_backward_rejects_before_launch(L):
     assert L.moe_packed_bwd_size(ctypes.byref(p)) == 8 * 256 * 2 + 8 * 256 * 256 * 2 + 8 * 128 * 256 * 2
 
 
+def test_saved_pre_activation_entry_points_reject_before_launch(L):
+    """moe_expert_ffn_waved_save_h and moe_backward_saved_h need their h
+    buffer (16-byte aligned) when T > 0, and otherwise validate as the plain
+    entry points do."""
+    p = _p()
+    ffn = [FAKE] * 9  # x, packed, offsets, sorted_token, pair_pos, topk_w, ready, y, out
+
+    def fwd(h, flags=0, nbytes=1 << 30):
+        return L.moe_expert_ffn_waved_save_h(ctypes.byref(p), *ffn, h, flags, FAKE, nbytes, None)
+
+    assert fwd(None) == moe.MOE_ERR_INVALID_ARG
+    assert fwd(ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG       # misaligned h
+    assert fwd(FAKE, flags=0x80) == moe.MOE_ERR_INVALID_ARG                # unknown flag
+    assert fwd(FAKE, nbytes=100) == moe.MOE_ERR_WORKSPACE
+    bwd = [FAKE] * 9  # x, packed, packed_bwd, idx, w, offsets, sorted_token, pair_pos, dout
+
+    def back(h, dx=FAKE, nbytes=1 << 30):
+        return L.moe_backward_saved_h(ctypes.byref(p), *bwd, h, dx, None, None, None, None, None, None, FAKE,
+                                      nbytes, None)
+
+    assert back(None) == moe.MOE_ERR_INVALID_ARG
+    assert back(ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG
+    assert back(FAKE, dx=None) == moe.MOE_ERR_INVALID_ARG                 # dx required for T > 0
+    assert back(FAKE, nbytes=moe.workspace_size(p)) == moe.MOE_ERR_WORKSPACE  # forward size only
+    g = moe.problem(T=8, d=256, I=128, E_global=8, k=2)
+    assert moe.saved_h_shape(g) == (moe.p_max(g), 256)
+    u = moe.problem(T=8, d=256, I=128, E_global=8, k=2, activation=moe.MOE_ACT_RELU2)
+    assert moe.saved_h_shape(u) == (moe.p_max(u), 128)
+
+
 def test_ungated_activation_sizes_and_backward_arguments(L):
     """RELU2 packs W1 alone (no gating projection, W3 may be NULL); its
     backward buffer holds W1 in place of [W1 | W3], and its backward entry
