@@ -977,7 +977,7 @@ hipError_t side_stream(hipStream_t* out) {
 }
 
 struct ForkEvents {
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   hipError_t create() {
     for (auto& e : ev) {
       const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
@@ -1092,6 +1092,13 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     bwd_gate_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(dwp, p.I / 16, a.pair_pos, a.topk_idx, a.topk_w, p.T, p.k,
                                                   p.E_global, L.Ep, a.dtopk_w, dlc, a.dlogits, dld);
     if ((e = hipGetLastError()) != hipSuccess) return finish(e);
+    // dWg needs only x and the gate's dl: with a weight gradient it goes to
+    // s2 behind the weight-gradient tiles, next to the dx rows and scatter
+    hipStream_t sg = s;
+    if (a.dWg && want_dw) {
+      if ((e = fork_to(s, s2, fk.ev[3])) != hipSuccess) return finish(e);
+      sg = s2;
+    }
     switch (pick_dx_shape(p)) {
       case DxShape::Small: e = launch_dx_gemm<FfnSmall>(p, dh, w13t, a.offsets, dxr, cus, s); break;
       case DxShape::Small64: e = launch_dx_gemm<FfnSmall64>(p, dh, w13t, a.offsets, dxr, cus, s); break;
@@ -1114,13 +1121,13 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
       if (xbf) {
         using C = TileCfg<128, 128, 2, 2, 64, 2>;
         float* part = reinterpret_cast<float*>(ws + L.bwd_dwg);
-        bwd_dwg_kernel<<<cus * 2, 256, C::LDS_BYTES, s>>>(dld, xb, p.T, p.d, L.Ep, part);
+        bwd_dwg_kernel<<<cus * 2, 256, C::LDS_BYTES, sg>>>(dld, xb, p.T, p.d, L.Ep, part);
         if ((e = hipGetLastError()) != hipSuccess) return finish(e);
-        bwd_dwg_reduce_kernel<<<blocks, 256, 0, s>>>(part, (p.T + kDwgChunkRows - 1) / kDwgChunkRows, p.d,
-                                                     p.E_global, L.Ep, a.dWg);
+        bwd_dwg_reduce_kernel<<<blocks, 256, 0, sg>>>(part, (p.T + kDwgChunkRows - 1) / kDwgChunkRows, p.d,
+                                                      p.E_global, L.Ep, a.dWg);
       } else {
-        bwd_dwg_f32_kernel<<<blocks, 256, 0, s>>>(static_cast<const float*>(a.x), a.topk_idx, dlc, p.T, p.k,
-                                                  p.d, p.E_global, a.dWg);
+        bwd_dwg_f32_kernel<<<blocks, 256, 0, sg>>>(static_cast<const float*>(a.x), a.topk_idx, dlc, p.T, p.k,
+                                                   p.d, p.E_global, a.dWg);
       }
       if ((e = hipGetLastError()) != hipSuccess) return finish(e);
     }
