@@ -66,7 +66,9 @@ constexpr int kGatherRow = 72;
 // The recompute's epilogue stages (dH1 | dH3)^T and (w a)^T of the tile in
 // LDS for the transposed weight-gradient operands: in one pass when the
 // three fit, else (the 256-wide tile) dH first and w a in a second pass.
-template <class C, bool GATED = true>
+// SAVED: the accumulators come from the forward's saved pre-activations (no
+// product, so no operand stages in LDS).
+template <class C, bool GATED = true, bool SAVED = false>
 struct BwdDh {
   static constexpr int NI = GATED ? C::BW / 2 : C::BW;  // intermediate indices per tile
   static constexpr int NH = GATED ? 2 * NI : NI;        // staged dH rows: (dH1 | dH3) or dH1
@@ -74,7 +76,7 @@ struct BwdDh {
   static constexpr size_t AW_BYTES = static_cast<size_t>(NI) * kStageRow * 2;
   static constexpr bool ONE_PASS = DH_BYTES + AW_BYTES <= 160 * 1024 - 8 * 1024;
   static constexpr size_t STAGE = ONE_PASS ? DH_BYTES + AW_BYTES : DH_BYTES;
-  static constexpr size_t LDS = STAGE > C::LDS_BYTES ? STAGE : C::LDS_BYTES;
+  static constexpr size_t LDS = (SAVED || STAGE > C::LDS_BYTES) ? STAGE : C::LDS_BYTES;
   static_assert(LDS <= 160 * 1024 - 8 * 1024, "recompute LDS (with the static tables) fits a CU");
 };
 
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
     const int32_t* __restrict__ pair_pos, const float* __restrict__ topk_w, int E_local, int d, int I,
     int k, int P_pad, uint16_t* __restrict__ dh, uint16_t* __restrict__ dht, uint16_t* __restrict__ awt,
     float* __restrict__ dwp, const float* __restrict__ hsaved) {
-  using D = BwdDh<C, GATED>;
+  using D = BwdDh<C, GATED, SAVED>;
   static_assert(!GATED || C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   constexpr int GR = GATED ? 2 : 1;  // packed W13 rows per intermediate index
   extern __shared__ __align__(16) uint16_t lds[];
@@ -923,7 +925,7 @@ template <class C, bool GATED, bool SAVED>
 hipError_t launch_dh_kind(const moe_problem_t& p, const WsLayout& L, const BackwardArgs& a, const uint16_t* xb,
                           const uint16_t* w13, const float* g, uint16_t* dh, uint16_t* dht, uint16_t* awt,
                           float* dwp, int cus, hipStream_t s) {
-  constexpr size_t lds = BwdDh<C, GATED>::LDS;
+  constexpr size_t lds = BwdDh<C, GATED, SAVED>::LDS;
   int per_cu = 0;
   hipError_t e;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dh_kernel<C, GATED, SAVED>, C::NTHREADS,
@@ -1070,7 +1072,9 @@ hipError_t launch_backward(const moe_problem_t& p, const WsLayout& L, const Back
     e = launch_g<BwdCfgG>(p, a, w2b, g, cus, s);
   if (e != hipSuccess) return finish(e);
   const int gr = gate_rows(p);
-  if ((gr * p.I) % BwdCfgL::BW == 0)
+  // from saved pre-activations the kernel only streams memory: the 128-wide
+  // tiles (twice as many, half the work each) leave a shorter last round
+  if (!a.hsaved && (gr * p.I) % BwdCfgL::BW == 0)
     e = launch_dh<BwdCfgL>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
   else
     e = launch_dh<BwdCfg>(p, L, a, xb, w13, g, dh, dht, awt, dwp, cus, s);
