@@ -80,25 +80,13 @@ struct BwdDh {
   static_assert(LDS <= 160 * 1024 - 8 * 1024, "recompute LDS (with the static tables) fits a CU");
 };
 
-// seg[e] = first column of expert e in the transposed weight-gradient
-// operands: the routed rows of the experts before it, each rounded up to 64.
-__device__ __forceinline__ void build_seg_prefix(const int32_t* __restrict__ offsets, int E_local, int32_t* seg) {
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E_local; ++e) {
-      seg[e] = run;
-      run += (offsets[e + 1] - offsets[e] + 63) & ~63;
-    }
-    seg[E_local] = run;
-  }
-}
-
 // ---------------------------------------------------------------- stage 1
 
-// g = dout W2^T per routed row, fp32 [P][I]: BW intermediate indices x BT
-// routed rows per tile, K = d in ascending order (256 wide when I % 256 ==
-// 0, BwdCfg when I % 128 == 0, else the 64-wide BwdCfgG; the shape does not
-// change the bits).
+// g = dout W2^T per routed row, fp32, block-fragment layout [P_pad][I] over
+// the padded row space (seg): BW intermediate indices x BT routed rows per
+// tile, K = d in ascending order (256 wide when I % 256 == 0, BwdCfg when
+// I % 128 == 0, else the 64-wide BwdCfgG; the shape does not change the
+// bits).
 using BwdCfgG = TileCfg<64, 256, 1, 8, 64, 3>;
 
 template <class C>
@@ -108,7 +96,9 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
     int I, float* __restrict__ g) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t seg[kMaxLocalExperts + 1];
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  build_seg_prefix(offsets, E_local, seg);
   __syncthreads();
   const int NT = I / C::BW;
   const int total = uniform(mt_pre[E_local] * NT);
@@ -127,14 +117,16 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
     TileAcc<C> acc;
     tile_mma<C>(w2b + static_cast<size_t>(e) * I * d + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32,
                 d / C::BK, trow, lds, acc, count);
+    const int hrow0 = uniform(seg[e] + (mt - mt_pre[e]) * C::BT);
 #pragma unroll
     for (int b = 0; b < C::AT; ++b) {
       const int t = (wt * C::AT + b) * 16 + (lane & 15);
       if (t >= count) continue;
+      const size_t rb = static_cast<size_t>(hrow0 / 16 + wt * C::AT + b);
 #pragma unroll
       for (int a = 0; a < C::AW; ++a) {
-        const int i = nt * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);
-        *reinterpret_cast<f32x4*>(g + static_cast<size_t>(row0 + t) * I + i) = acc.v[a][b];
+        const int cb = nt * (C::BW / 16) + wr * C::AW + a;
+        *reinterpret_cast<f32x4*>(g + blockfrag_offset(rb, cb, I / 16, lane)) = acc.v[a][b];
       }
     }
   }
@@ -192,6 +184,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
       }
       wrow[r] = r < count ? w : 0.f;
     }
+    // first row of the tile in the padded row space of g and hsaved
+    const int hrow0 = uniform(seg[e] + (mt - mt_pre[e]) * C::BT);
     TileAcc<C> acc;
     if constexpr (SAVED) {
       // the forward's accumulators, laid out as this product leaves them:
@@ -203,14 +197,15 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
 #pragma unroll
         for (int b = 0; b < C::AT; ++b) acc.v[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (wt * C::AT * 16 < count) {
-        const size_t ncol = static_cast<size_t>(GR) * I;
+        const int ncb = GR * I / 16;
 #pragma unroll
         for (int b = 0; b < C::AT; ++b) {
-          const int tr = min((wt * C::AT + b) * 16 + (lane & 15), count - 1);
+          const int hr = hrow0 + min((wt * C::AT + b) * 16 + (lane & 15), count - 1);
+          const int hl = (hr & 15) + 16 * (lane / 16);  // lane of that row in its block
 #pragma unroll
           for (int a = 0; a < C::AW; ++a) {
-            const int n = nt * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);
-            acc.v[a][b] = *reinterpret_cast<const f32x4*>(hsaved + static_cast<size_t>(row0 + tr) * ncol + n);
+            const int cb = nt * (C::BW / 16) + wr * C::AW + a;
+            acc.v[a][b] = *reinterpret_cast<const f32x4*>(hsaved + blockfrag_offset(hr / 16, cb, ncb, hl));
           }
         }
       }
@@ -247,7 +242,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
         for (int a = 0; a < C::AW; ++a) {
           const int il = (wr * C::AW + a) * 16 + 4 * (lane / 16);
           const int i0 = nt * NI + il;
-          const f32x4 g4 = valid ? *reinterpret_cast<const f32x4*>(g + static_cast<size_t>(row0 + t) * I + i0)
+          const f32x4 g4 = valid ? *reinterpret_cast<const f32x4*>(
+                                       g + blockfrag_offset((hrow0 + t) / 16, i0 / 16, I / 16, lane))
                                  : f32x4{0.f, 0.f, 0.f, 0.f};
           float v1[4], va[4];
           float part = 0.f;  // <g, a> over the lane's 4 indices
@@ -286,7 +282,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
       for (int a = 0; a < C::AW; a += 2) {
         const int il = ((wr * C::AW + a) / 2) * 16 + 4 * (lane / 16);
         const int i0 = nt * NI + il;
-        const f32x4 g4 = valid ? *reinterpret_cast<const f32x4*>(g + static_cast<size_t>(row0 + t) * I + i0)
+        const f32x4 g4 = valid ? *reinterpret_cast<const f32x4*>(
+                                     g + blockfrag_offset((hrow0 + t) / 16, i0 / 16, I / 16, lane))
                                : f32x4{0.f, 0.f, 0.f, 0.f};
         float v1[4], v3[4], va[4];
         float part = 0.f;  // <g, a> over the lane's 4 indices
@@ -333,7 +330,7 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
       // the tile's rows are columns k0 .. k0 + BT - 1 of the transposed
       // operands; columns up to the expert's rows rounded to 64 are written
       __syncthreads();
-      const int k0 = uniform(seg[e] + (mt - mt_pre[e]) * C::BT);
+      const int k0 = hrow0;
       const int rows_pad = (count + 63) & ~63;
       const int KB = P_pad / 32;
       // (dH1 | dH3)^T (or dH1^T) fragments: NH / 16 row blocks x rows_pad / 32 k blocks

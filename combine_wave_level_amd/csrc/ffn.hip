@@ -66,7 +66,9 @@ __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
   using C = typename F::G1;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t seg[kMaxLocalExperts + 1];
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  if (hsave != nullptr) build_seg_prefix(offsets, E_local, seg);
   __syncthreads();
   const int NT = gr * I / C::BW;
   const int total = uniform(mt_pre[E_local] * NT);
@@ -75,8 +77,9 @@ __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
     const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
+    const int hrow0 = hsave != nullptr ? uniform(seg[e] + (mt - mt_pre[e]) * C::BT) : 0;
     gemm1_tile<C, GATED>(xb, w13 + static_cast<size_t>(e) * gr * I * d, sorted_token, act, row0, count, nt, d,
-                         I, lds, xscale, hsave);
+                         I, lds, xscale, hsave, hrow0);
   }
 }
 

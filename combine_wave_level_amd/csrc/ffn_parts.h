@@ -94,6 +94,30 @@ __device__ __forceinline__ void build_mtile_prefix(const int32_t* __restrict__ o
   }
 }
 
+// seg[e] = first row of expert e in the padded row space of the saved
+// pre-activations and the backward's per-row buffers: the routed rows of the
+// experts before it, each rounded up to 64 (so that every m-tile starts on
+// a 16-row block).  seg[E_local] = total.  Built by thread 0.
+__device__ __forceinline__ void build_seg_prefix(const int32_t* __restrict__ offsets, int E_local, int32_t* seg) {
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E_local; ++e) {
+      seg[e] = run;
+      run += (offsets[e + 1] - offsets[e] + 63) & ~63;
+    }
+    seg[E_local] = run;
+  }
+}
+
+// Block-fragment layout of an fp32 matrix [rows][16 ncb] (rows in the padded
+// row space): the 16 x 16 block (rb, cb) is 256 contiguous floats, lane l
+// of a wavefront holding row 16 rb + l % 16, columns 16 cb + 4 (l / 16) ..
+// + 3 -- the MFMA accumulator layout of one block, so a wavefront stores or
+// loads a block as one contiguous 1 KiB.  Float offset of lane l's 4 values:
+__host__ __device__ __forceinline__ size_t blockfrag_offset(size_t rb, int cb, int ncb, int lane) {
+  return ((rb * static_cast<size_t>(ncb) + static_cast<size_t>(cb)) * 64 + static_cast<size_t>(lane)) * 4;
+}
+
 // Expert owning global m-tile mt (binary search in mt_pre[lo..hi]).
 __device__ __forceinline__ int expert_of_mtile(const int32_t* mt_pre, int lo, int hi, int mt) {
   // invariant: mt_pre[lo] <= mt < mt_pre[hi]
@@ -160,10 +184,11 @@ __device__ __forceinline__ void out_flush(const uint16_t* lds, uint16_t* __restr
 // FP8T tiles: xb is the e4m3 staging buffer (d bytes per token) and xscale
 // the tokens' scales.
 // hsave (optional, wave-uniform): the tile's fp32 accumulators h of its
-// valid rows are also stored to hsave [P][gr I], packed column order (16
-// columns of W1, then the same 16 intermediate indices of W3, ... when
-// gated; W1's columns in order when not), for a backward that reads the
-// pre-activations instead of recomputing them.
+// valid rows are also stored to hsave, block-fragment layout over packed
+// columns (16 columns of W1, then the same 16 intermediate indices of W3,
+// ... when gated; W1's columns in order when not), the tile's rows from row
+// hrow0 (a multiple of 16) of the padded row space, for a backward that
+// reads the pre-activations instead of recomputing them.
 template <class C, bool GATED = true>
 __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            const uint16_t* __restrict__ w13e,
@@ -171,7 +196,7 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
                                            uint16_t* __restrict__ act, int row0, int count, int nt,
                                            int d, int I, uint16_t* lds,
                                            const float* __restrict__ xscale = nullptr,
-                                           float* __restrict__ hsave = nullptr) {
+                                           float* __restrict__ hsave = nullptr, int hrow0 = 0) {
   static_assert(!GATED || C::AW % 2 == 0, "gate/up row blocks pair up inside a wave");
   constexpr int COLS = C::BW / 2;
   static_assert(static_cast<size_t>(C::BT) * COLS * 2 <= C::LDS_BYTES, "output stage fits the tile's LDS");
@@ -196,16 +221,16 @@ __device__ __forceinline__ void gemm1_tile(const uint16_t* __restrict__ xb,
   TileAcc<C> acc;
   tile_mma<C>(w13e + frag_offset(nt * (C::BW / 16), 0, d / 32), d / 32, d / C::BK, trow, lds, acc, count, &tsc);
   if (hsave != nullptr) {
-    const size_t ncol = static_cast<size_t>(GATED ? 2 : 1) * I;
+    const int ncb = (GATED ? 2 : 1) * I / 16;
 #pragma unroll
     for (int b = 0; b < C::AT; ++b) {
       if ((wt * C::AT + b) * 16 >= count) continue;  // wave-uniform: rows past the valid ones
-      const int t = (wt * C::AT + b) * 16 + (lane & 15);
-      if (t >= count) continue;
+      if ((wt * C::AT + b) * 16 + (lane & 15) >= count) continue;
+      const size_t rb = static_cast<size_t>(hrow0 / 16 + wt * C::AT + b);
 #pragma unroll
       for (int a = 0; a < C::AW; ++a) {
-        const int n = nt * C::BW + (wr * C::AW + a) * 16 + 4 * (lane / 16);
-        *reinterpret_cast<f32x4*>(hsave + static_cast<size_t>(row0 + t) * ncol + n) = acc.v[a][b];
+        const int cb = nt * (C::BW / 16) + wr * C::AW + a;
+        *reinterpret_cast<f32x4*>(hsave + blockfrag_offset(rb, cb, ncb, lane)) = acc.v[a][b];
       }
     }
   }

@@ -73,7 +73,7 @@ WsLayout ws_layout(const moe_problem_t& p) {
   L.bwd_xst = take(ppad * p.d * 2);
   L.bwd_dst = take(ppad * p.d * 2);
   L.wgrad = take(L.wgrad_bytes);
-  L.bwd_g = take(static_cast<size_t>(L.P_max) * p.I * 4);
+  L.bwd_g = take(ppad * p.I * 4);
   L.bwd_dwp = take(static_cast<size_t>(L.P_max) * (p.I / 16) * 4);
   L.bwd_dlc = take(static_cast<size_t>(p.T) * p.k * 4);
   L.bwd_dld = take(xbf ? static_cast<size_t>(p.T) * L.Ep * 2 : 0);
@@ -116,6 +116,11 @@ int32_t moe_ffn_path(const moe_problem_t* p, int32_t num_cus, uint32_t flags) {
   if (st != MOE_OK) return st;
   if (num_cus <= 0 || !ffn_flags_ok(flags)) return MOE_ERR_INVALID_ARG;
   return ffn_uses_persistent(*p, num_cus, flags) ? MOE_PATH_PERSISTENT : MOE_PATH_PHASES;
+}
+
+size_t moe_saved_h_bytes(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return static_cast<size_t>(ws_layout(*p).P_pad) * gate_rows(*p) * p->I * 4;
 }
 
 size_t moe_packed_bwd_size(const moe_problem_t* p) {

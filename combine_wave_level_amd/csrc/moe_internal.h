@@ -39,7 +39,8 @@ namespace moe {
 //   bwd_xst    bf16 [d][P_pad]  x^T of the routed rows, rows
 //   bwd_dst    bf16 [d][P_pad]  dout^T of the routed rows, fragment layout
 //   wgrad      fp32 isolated partial buffers of the weight gradient
-//   bwd_g      fp32 [P_max][I]: dout W2^T per routed row
+//   bwd_g      fp32 [P_pad][I]: dout W2^T per routed row, block-fragment
+//              layout over the padded row space (ffn_parts.h)
 //   bwd_dwp    fp32 [P_max][I / 16]: partial sums of the combine-weight
 //              gradient of each routed row, one per 16 intermediate indices
 //   bwd_dlc    fp32 [T][k]: gradient of the picked logits

@@ -36,7 +36,7 @@ EXPORTED = (
     "moe_dispatch", "moe_expert_ffn_waved", "moe_combine", "moe_expert_wgrad",
     "moe_packed_bwd_size", "moe_pack_weights_bwd", "moe_backward", "moe_quantize_fp8",
     "moe_expert_ffn_waved_fp8", "moe_ffn_path", "moe_route_noalloc", "moe_route_dispatch", "moe_probe_mfma",
-    "moe_probe_copy", "moe_expert_ffn_waved_save_h", "moe_backward_saved_h",
+    "moe_probe_copy", "moe_expert_ffn_waved_save_h", "moe_backward_saved_h", "moe_saved_h_bytes",
     "moe_check_error", "moe_status_string", "moe_version",
 )
 
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "moe_expert_wgrad": (st, [P, vp, vp, vp, i32p, i32p, i32p, f32p, vp, f32p, f32p, f32p,
                                       vp, ctypes.c_size_t, vp]),
             "moe_packed_bwd_size": (ctypes.c_size_t, [P]),
+            "moe_saved_h_bytes": (ctypes.c_size_t, [P]),
             "moe_pack_weights_bwd": (st, [P, vp, vp, vp, vp, vp, vp]),
             "moe_backward": (st, [P, vp, vp, vp, i32p, f32p, i32p, i32p, i32p, vp, vp, f32p, f32p, f32p,
                                   f32p, f32p, f32p, vp, ctypes.c_size_t, vp]),
@@ -266,9 +267,14 @@ def _out_dtype(p: Problem):
 
 
 def saved_h_shape(p: Problem):
-    """Shape of the fp32 pre-activation buffer of ffn_waved(save_h=...)."""
+    """Shape (padded rows, gr I) of the fp32 buffer of ffn_waved(save_h=...):
+    moe_saved_h_bytes(p) bytes, in the library's block-fragment order (see
+    moe_expert_ffn_waved_save_h in include/moe.h)."""
     gr = 2 if p.activation == MOE_ACT_SWIGLU else 1
-    return (max(1, p_max(p)), gr * p.I)
+    n = lib().moe_saved_h_bytes(ctypes.byref(p))
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, "moe_saved_h_bytes")
+    return (n // (4 * gr * p.I), gr * p.I)
 
 
 def ffn_waved(p: Problem, x, packed, disp: Dispatch, topk_w, ws, fused_combine=True,

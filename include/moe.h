@@ -263,16 +263,26 @@ moe_status_t moe_expert_ffn_waved(const moe_problem_t* p, const void* x, const v
  * training framework's features, section 5.4, without details; which tensor
  * to keep is this library's choice).  Outputs y and out are bit-identical
  * to moe_expert_ffn_waved's.
- *   h [P_max, gr * I] fp32 (gr = 2 for SWIGLU, 1 for RELU2), caller-owned,
- *   16-byte aligned, required when T > 0: row r (sorted-row order, r <
- *   expert_offsets[E_local]) gets the fp32 accumulators of that routed row,
- *   in packed column order: for SWIGLU, columns 32 q .. 32 q + 15 hold h1 =
- *   x W1 for intermediate indices 16 q .. 16 q + 15 and columns 32 q + 16 ..
- *   32 q + 31 hold h3 = x W3 for the same indices; for RELU2, column i holds
- *   h1 for index i.  Rows past the routed ones are not written.  Pass h, the
- *   same routing and the same workspace's dispatch to moe_backward_saved_h.
+ *   h: moe_saved_h_bytes(p) bytes, caller-owned, 16-byte aligned, required
+ *   when T > 0.  It receives the fp32 accumulators of every routed row:
+ *   columns in packed order (gr = 2 for SWIGLU: columns 32 q .. 32 q + 15
+ *   hold h1 = x W1 for intermediate indices 16 q .. 16 q + 15, columns
+ *   32 q + 16 .. 32 q + 31 hold h3 = x W3 for the same indices; gr = 1 for
+ *   RELU2: column i holds h1 for index i); rows in a padded row space where
+ *   routed row r of local expert e (sorted-row order) is row s = seg[e] + r
+ *   - expert_offsets[e], seg[e] = the sum over local experts e' < e of their
+ *   row counts each rounded up to 64; element (s, c) at float offset
+ *   ((s / 16) * (gr I / 16) + c / 16) * 256 + ((s % 16) + 16 ((c % 16) / 4))
+ *   * 4 + c % 4 (16 x 16 blocks in the MFMA accumulator order).  Other
+ *   bytes are not written.  Pass h, the same routing and the same
+ *   workspace's dispatch to moe_backward_saved_h.
  * Errors as moe_expert_ffn_waved, plus MOE_ERR_INVALID_ARG for a NULL or
  * misaligned h. */
+/* Bytes of the h buffer of moe_expert_ffn_waved_save_h / moe_backward_saved_h:
+ * P_pad * gr * I * 4 with P_pad = P_max + 64 E_local rounded up to 64 (0
+ * for an invalid problem). */
+size_t moe_saved_h_bytes(const moe_problem_t* p);
+
 moe_status_t moe_expert_ffn_waved_save_h(const moe_problem_t* p, const void* x, const void* packed,
                                          const int32_t* expert_offsets, const int32_t* sorted_token,
                                          const int32_t* pair_pos, const float* topk_w,
@@ -375,8 +385,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* pac
  * GEMM, half of the backward's matrix products before the weight gradient,
  * is skipped.  The stored values are the accumulators the recomputation
  * produces, so every output is bit-identical to moe_backward's.  Arguments
- * as moe_backward, plus h [P_max, gr * I] fp32 (16-byte aligned, required
- * when T > 0; only routed rows are read). */
+ * as moe_backward, plus h (moe_saved_h_bytes(p) bytes, 16-byte aligned,
+ * required when T > 0; only the routed rows are read). */
 moe_status_t moe_backward_saved_h(const moe_problem_t* p, const void* x, const void* packed,
                                   const void* packed_bwd, const int32_t* topk_idx, const float* topk_w,
                                   const int32_t* expert_offsets, const int32_t* sorted_token,

@@ -261,10 +261,13 @@ def test_saved_pre_activation_entry_points_reject_before_launch(L):
     assert back(ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG
     assert back(FAKE, dx=None) == moe.MOE_ERR_INVALID_ARG                 # dx required for T > 0
     assert back(FAKE, nbytes=moe.workspace_size(p)) == moe.MOE_ERR_WORKSPACE  # forward size only
+    # padded row space: P_max + 64 E_local rounded up to 64, gr I columns
     g = moe.problem(T=8, d=256, I=128, E_global=8, k=2)
-    assert moe.saved_h_shape(g) == (moe.p_max(g), 256)
+    assert moe.saved_h_shape(g) == (576, 256)
+    assert L.moe_saved_h_bytes(ctypes.byref(g)) == 576 * 256 * 4
     u = moe.problem(T=8, d=256, I=128, E_global=8, k=2, activation=moe.MOE_ACT_RELU2)
-    assert moe.saved_h_shape(u) == (moe.p_max(u), 128)
+    assert moe.saved_h_shape(u) == (576, 128)
+    assert L.moe_saved_h_bytes(ctypes.byref(_p(d=96))) == 0
 
 
 def test_ungated_activation_sizes_and_backward_arguments(L):

@@ -61,6 +61,25 @@ def _ffn_x(inp):
     return f64(x) if x.dtype == np.uint16 else f64(bf16_bits(x))
 
 
+def _saved_rows(h, offsets, rows, ncol):
+    """Rows (sorted-row order) of the saved buffer as [len(rows), ncol],
+    decoded from its documented layout: routed row r of local expert e at
+    padded row s = seg[e] + r - offsets[e] (seg: row counts rounded up to 64),
+    element (s, c) at float ((s // 16) * (ncol // 16) + c // 16) * 256 +
+    ((s % 16) + 16 * ((c % 16) // 4)) * 4 + c % 4."""
+    counts = np.diff(offsets)
+    seg = np.concatenate([[0], np.cumsum((counts + 63) // 64 * 64)])
+    flat = h.reshape(-1).cpu().numpy()
+    c = np.arange(ncol)
+    out = np.empty((len(rows), ncol), np.float64)
+    for n, r in enumerate(rows):
+        e = int(np.searchsorted(offsets, r, "right") - 1)
+        s = int(seg[e] + r - offsets[e])
+        off = ((s // 16) * (ncol // 16) + c // 16) * 256 + ((s % 16) + 16 * ((c % 16) // 4)) * 4 + c % 4
+        out[n] = flat[off]
+    return out
+
+
 def _check_saved_rows(inp, L, disp, h, relu2, nrows=24):
     """Sampled routed rows of h against the oracle's h1 | h3, unpacked from
     the packed column order (gated: 16 columns of h1, then the same 16
@@ -76,8 +95,8 @@ def _check_saved_rows(inp, L, disp, h, relu2, nrows=24):
     r64 = lambda a: f64(bf16_bits(a)) if a.dtype != np.uint16 else f64(a)  # noqa: E731
     W1, W2 = r64(inp["W1"]), r64(inp["W2"])
     W3 = None if relu2 else r64(inp["W3"])
-    hg = h[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     I = L.p.I
+    hg = _saved_rows(h, offsets, rows, (1 if relu2 else 2) * I)
     for n, r in enumerate(rows):
         e = int(np.searchsorted(offsets, r, "right") - 1)  # local expert (the weights are the local ones)
         _, h1, h3, _ = oracle.expert_ffn(x[sorted_token[r]][None], W1[e], None if relu2 else W3[e], W2[e],
@@ -111,7 +130,9 @@ def test_saved_pre_activations_forward_and_backward(name):
     P = int(disp.offsets[-1])
     assert torch.equal(out0, out1)
     assert torch.equal(y0[:P], y1[:P])
-    assert not torch.isnan(h[:P]).any(), "every routed row is written"
+    offsets = disp.offsets.cpu().numpy()
+    ncol = h.shape[1]
+    assert not np.isnan(_saved_rows(h, offsets, np.arange(P), ncol)).any(), "every routed row is written"
     _check_saved_rows(inp, L, disp, h, relu2)
     # backward: recompute against saved, every output bit for bit
     dout = dev(inp["dout"])
