@@ -530,7 +530,9 @@ __device__ __forceinline__ void load_wgt8(const void* __restrict__ wgt, int e, i
 // One wavefront per (token, column part), 16-byte column chunks of dx:
 //   dx[t] = sum_j dxr[pair_pos[t, j]] (fp32 adds, ascending j, local picks)
 //         + sum_j dl[t, j] Wg[:, idx[t, j]] (fused multiply-adds, ascending j)
-// rounded once to the dtype of x.  Up to kCombineGroup row reads in flight.
+// rounded once to the dtype of x.  As in the forward combine, a lane takes
+// kCombineChunks chunks at a time and issues a group's row reads before
+// adding them: up to kCombineChunks * kCombineGroup reads in flight.
 template <bool XBF>
 __global__ __launch_bounds__(256) void bwd_dx_scatter_kernel(
     const uint16_t* __restrict__ dxr, const int32_t* __restrict__ pair_pos,
@@ -544,44 +546,67 @@ __global__ __launch_bounds__(256) void bwd_dx_scatter_kernel(
   const int32_t* pp = pair_pos + static_cast<size_t>(t) * k;
   const int32_t* pi = topk_idx + static_cast<size_t>(t) * k;
   const float* pg = dlc + static_cast<size_t>(t) * k;
-  for (int c = cb + lane; c < ce; c += kWave) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c0 = cb; c0 < ce; c0 += kCombineChunks * kWave) {
+    int c[kCombineChunks];
+    bool h[kCombineChunks];
+    float acc[kCombineChunks][8];
+#pragma unroll
+    for (int u = 0; u < kCombineChunks; ++u) {
+      c[u] = c0 + u * kWave + lane;
+      h[u] = c[u] < ce;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+    }
     for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
       int r[kCombineGroup];
-      u32x4 v[kCombineGroup];
+      u32x4 v[kCombineGroup][kCombineChunks];
 #pragma unroll
       for (int q = 0; q < kCombineGroup; ++q) {
         r[q] = uniform(j0 + q < k ? pp[j0 + q] : -1);
-        if (r[q] >= 0) v[q] = ld16(dxr + static_cast<size_t>(r[q]) * d + c * 8);
+        if (r[q] >= 0) {
+#pragma unroll
+          for (int u = 0; u < kCombineChunks; ++u)
+            if (h[u]) v[q][u] = ld16(dxr + static_cast<size_t>(r[q]) * d + c[u] * 8);
+        }
       }
 #pragma unroll
       for (int q = 0; q < kCombineGroup; ++q) {
         if (r[q] < 0) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = acc[2 * i] + __uint_as_float(v[q][i] << 16);
-          acc[2 * i + 1] = acc[2 * i + 1] + __uint_as_float(v[q][i] & 0xffff0000u);
-        }
+        for (int u = 0; u < kCombineChunks; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] = acc[u][2 * i] + __uint_as_float(v[q][u][i] << 16);
+            acc[u][2 * i + 1] = acc[u][2 * i + 1] + __uint_as_float(v[q][u][i] & 0xffff0000u);
+          }
       }
     }
     for (int j = 0; j < k; ++j) {
       const int e = uniform(pi[j]);
       if (e < 0 || e >= E) continue;  // not a router id: no router row to read
       const float g = pg[j];
-      float wv[8];
-      load_wgt8<XBF>(wgt, e, d, c, wv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, wv[i], acc[i]);
+      for (int u = 0; u < kCombineChunks; ++u) {
+        if (!h[u]) continue;
+        float wv[8];
+        load_wgt8<XBF>(wgt, e, d, c[u], wv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g, wv[i], acc[u][i]);
+      }
     }
-    if constexpr (XBF) {
-      u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      st16(static_cast<uint16_t*>(dx) + static_cast<size_t>(t) * d + c * 8, o);
-    } else {
-      float* o = static_cast<float*>(dx) + static_cast<size_t>(t) * d + c * 8;
-      *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    for (int u = 0; u < kCombineChunks; ++u) {
+      if (!h[u]) continue;
+      if constexpr (XBF) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
+        st16(static_cast<uint16_t*>(dx) + static_cast<size_t>(t) * d + c[u] * 8, o);
+      } else {
+        float* o = static_cast<float*>(dx) + static_cast<size_t>(t) * d + c[u] * 8;
+        *reinterpret_cast<f32x4*>(o) = f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[u][4], acc[u][5], acc[u][6], acc[u][7]};
+      }
     }
   }
 }
