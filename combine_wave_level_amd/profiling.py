@@ -206,6 +206,67 @@ def _stats(a) -> None:
         f.write("\n".join(lines))
 
 
+def _counters(a) -> None:
+    """Per-dispatch means of the tile counters of the given kernels (a
+    --pmc CSV per pass; counters may repeat across passes, the first pass
+    that has one is used)."""
+    vals: dict = {}
+    for path in a.pmc:
+        for r in _rows(path):
+            for k in a.kernels:
+                if re.search(k, r["Kernel_Name"]):
+                    d = vals.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+                    d.setdefault(path, []).append(float(r["Counter_Value"]))
+
+    def m(k, name):
+        per = vals.get(k, {}).get(name)
+        if not per:
+            return float("nan")
+        v = next(iter(per.values()))
+        return sum(v) / len(v)
+
+    cus, simds = 256, 1024
+    figs = []
+    for k in a.kernels:
+        act = m(k, "GRBM_GUI_ACTIVE") / 8
+        req = m(k, "TCP_TCC_READ_REQ")
+        hit, miss = m(k, "TCC_HIT"), m(k, "TCC_MISS")
+        figs.append([
+            f"{act / 1e3:.0f} K",
+            f"{100 * m(k, 'SQ_VALU_MFMA_BUSY_CYCLES') / simds / act:.0f}%",
+            f"{m(k, 'SQ_INSTS_VALU_MFMA_MOPS_BF16') * 512 / 1e9:.0f} G",
+            f"{100 * m(k, 'SQ_LDS_IDX_ACTIVE') / cus / act:.0f}%",
+            f"{100 * m(k, 'SQ_LDS_BANK_CONFLICT') / m(k, 'SQ_LDS_IDX_ACTIVE'):.1f}%",
+            f"{100 * m(k, 'SQ_WAIT_ANY') / m(k, 'SQ_WAVE_CYCLES'):.0f}%",
+            f"{m(k, 'VmemLatency'):.0f} cycles",
+            f"{100 * m(k, 'TA_TA_BUSY') / cus / act:.0f}%",
+            f"{100 * m(k, 'TD_TD_BUSY') / cus / act:.0f}%",
+            f"{100 * m(k, 'TD_TC_STALL') / cus / act:.0f}%",
+            f"{req / 1e6:.1f} M",
+            f"{m(k, 'TCP_TCC_READ_REQ_LATENCY') / req:.0f} cycles",
+            f"{100 * hit / (hit + miss):.0f}%",
+        ])
+    names = ["GPU-active cycles per XCD", "MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / active)",
+             "bf16 MFMA FLOPs (MOPS_BF16 x 512)", "LDS busy (SQ_LDS_IDX_ACTIVE / CUs / active)",
+             "LDS bank-conflict cycles / LDS active cycles",
+             "wave-cycles waiting in s_waitcnt (SQ_WAIT_ANY / SQ_WAVE_CYCLES)",
+             "mean vector-memory latency (VmemLatency)", "TA busy per CU", "TD busy per CU",
+             "TD stalled on the L1 (TD_TC_STALL per CU)", "L1 -> L2 read requests",
+             "mean L1 -> L2 read latency", "L2 hit rate (TCC_HIT / (HIT + MISS))"]
+    lines = [f"# {a.title}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = the profiler output folder):", ""]
+    for c in a.command:
+        lines.append(f"    {c}")
+    lines += ["", "Per-dispatch means over the profiled dispatches.  GRBM_GUI_ACTIVE is summed over the 8 XCDs",
+              "(divided by 8 below); SQ/TA/TD counters are chip totals, divided by the 1024 SIMDs or 256 CUs.", "",
+              "| figure | " + " | ".join(a.kernels) + " |", "|---|" + "---|" * len(a.kernels)]
+    for i, n in enumerate(names):
+        lines.append(f"| {n} | " + " | ".join(f[i] for f in figs) + " |")
+    lines.append("")
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(prog="python -m combine_wave_level_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -218,6 +279,12 @@ def main(argv=None) -> None:
     t.add_argument("--command", action="append", default=[])
     t.add_argument("--out-md", required=True)
     t.add_argument("--top", type=int, default=16)
+    q = sub.add_parser("counters")
+    q.add_argument("--pmc", action="append", required=True)
+    q.add_argument("--kernels", nargs="+", required=True)
+    q.add_argument("--title", required=True)
+    q.add_argument("--command", action="append", default=[])
+    q.add_argument("--out-md", required=True)
     s = sub.add_parser("summarize")
     s.add_argument("--stats", required=True)
     s.add_argument("--fetch", required=True)
@@ -250,6 +317,8 @@ def main(argv=None) -> None:
         _stats(a)
     elif a.cmd == "steptraffic":
         _step_traffic(a)
+    elif a.cmd == "counters":
+        _counters(a)
     else:
         _summarize(a)
 
