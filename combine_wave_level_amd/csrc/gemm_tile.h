@@ -362,6 +362,18 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ wtile, in
   }
 }
 
+// TL: after iteration i's issues, wait for the loads of step i+1 (see
+// tile_mma_run).
+template <class C>
+__device__ __forceinline__ void tl_wait_next(int i, int nk) {
+  if (i + 1 >= nk) return;
+  if (i & 1) {
+    if (i + 3 < nk) wait_vmcnt<C::LW>(); else wait_vmcnt<0>();
+  } else {
+    if (i + 2 < nk) wait_vmcnt<2 * C::LW + C::LT>(); else wait_vmcnt<0>();
+  }
+}
+
 template <class C, bool ACT>
 __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile, int KB, int nk,
                                              const TokRows<C>& trow, uint16_t* lds, TileAcc<C>& acc,
@@ -369,38 +381,48 @@ __device__ __forceinline__ void tile_mma_run(const uint16_t* __restrict__ wtile,
 
   if constexpr (C::TL) {
     // Weights NST-1 = 3 steps ahead, token lines one double step ahead.  In
-    // issue order: T(0), W(0), W(1), W(2), then at step s: T(s/2 + 1) (s
-    // even), W(s + 3).  At the top of step kt the loads issued after the
-    // last one kt needs are: even kt (needs T(kt/2), issued at step kt-2):
-    // W(kt+1), W(kt+2); odd kt (needs W(kt), issued at step kt-3): W(kt+1),
-    // T(kt/2 + 1), W(kt+2) -- each only where it exists.  K = 64 * (nk/2).
+    // issue order: T(0), W(0), W(1), W(2), then iteration i issues W(i+3)
+    // and, for even i, T(i/2+1).  After iteration i's issues, the loads
+    // issued after the last one step i+1 needs are: even i (needs T(i/2),
+    // issued with W(i+1) at iteration i-2): W(i+2), W(i+3), T(i/2+1); odd i
+    // (needs T((i+1)/2), issued at iteration i-1): W(i+3) -- each only where
+    // it exists.  K = 64 * (nk/2).
+    //
+    // Ping-pong: every wavefront runs the same loop body -- read step i's
+    // operands, barrier, multiply step i, barrier -- but waves 4-7 pass one
+    // extra barrier before the loop and waves 0-3 one after it, so the two
+    // wavefronts of a SIMD (w and w + 4) run one phase apart: while one
+    // multiplies, the other reads from LDS, and the matrix core no longer
+    // waits out every step's read latency.  Both barriers of iteration i are
+    // preceded by the wait for step i+1's loads (a wave reaches barrier
+    // 2i+2, the one before step i+1's first read, through one of them) and
+    // the first by lgkmcnt(0) (no stage is refilled before its last reader
+    // has its data).  Measured against the same loop without the offset:
+    // 4-8% faster tiles in a dense benchmark, same bits.
+    const bool late = uniform(wave_id()) >= C::NW / 2;
+    TileFrags<C> f;
+    tile_issue_tl<C>(trow, lds, 0);
 #pragma unroll
     for (int s = 0; s < C::NST - 1; ++s)
-      if (s < nk) {
-        if (s == 0) tile_issue_tl<C>(trow, lds, 0);
-        tile_issue_w<C>(wtile, KB, lds, s);
-      }
-    for (int kt = 0; kt < nk; kt += 2) {
-      // even step kt
-      if (kt + 2 < nk) wait_vmcnt<2 * C::LW>(); else wait_vmcnt<C::LW>();
+      if (s < nk) tile_issue_w<C>(wtile, KB, lds, s);
+    if (nk > 2) wait_vmcnt<2 * C::LW>(); else wait_vmcnt<C::LW>();
+    raw_barrier();
+    if (late) raw_barrier();
+    for (int i = 0; i < nk; ++i) {
+      if (i + 3 < nk) tile_issue_w<C>(wtile, KB, lds, i + 3);
+      if (!(i & 1) && i + 2 < nk) tile_issue_tl<C>(trow, lds, i / 2 + 1);
+      tile_read_frags_tl<C, ACT>(lds, i, f, nbv);
+      tl_wait_next<C>(i, nk);
+      wait_lgkm0();
       raw_barrier();
-      if (kt + 2 < nk) tile_issue_tl<C>(trow, lds, kt / 2 + 1);
-      if (kt + 3 < nk) tile_issue_w<C>(wtile, KB, lds, kt + 3);
-      {
-        TileFrags<C> f;
-        tile_read_frags_tl<C, ACT>(lds, kt, f, nbv);
-        tile_mfma<C, ACT>(f, acc, nbv);
-      }
-      // odd step kt + 1
-      if (kt + 2 < nk) wait_vmcnt<2 * C::LW + C::LT>(); else wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      tile_mfma<C, ACT>(f, acc, nbv);
+      __builtin_amdgcn_sched_barrier(0);
+      tl_wait_next<C>(i, nk);
       raw_barrier();
-      if (kt + 4 < nk) tile_issue_w<C>(wtile, KB, lds, kt + 4);
-      {
-        TileFrags<C> f;
-        tile_read_frags_tl<C, ACT>(lds, kt + 1, f, nbv);
-        tile_mfma<C, ACT>(f, acc, nbv);
-      }
     }
+    if (!late) raw_barrier();
+    wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();
   } else if constexpr (!C::DBUF) {
