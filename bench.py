@@ -4,10 +4,10 @@ Default workload (the mid layer): T=4096 tokens, d=4096, I=1024, 16 experts,
 top-4, 4 experts per wave, bf16 with fp32 accumulation; synthetic seeded
 inputs (x ~ N(0,1), weights ~ N(0, 0.02)).  A step is one pass of the layer's
 hot path over the batch: router, dispatch, and the expert FFN in waves (pull,
-GEMM1 + SwiGLU, GEMM2, fused combine) on the schedule the library picks for
-the shape (the persistent expert-wave kernel on the mid layer; --serial and
---persistent force the phase kernels or the persistent kernel), all inputs
-resident in HBM.  One JSON line is printed on stdout.
+GEMM1 + SwiGLU, GEMM2, combine) on the library's default schedule (the
+phase kernels; --serial and --persistent force the phase kernels or the
+persistent expert-wave kernel), all inputs resident in HBM.  One JSON line
+is printed on stdout.
 
     python bench.py [--steps K] [--warmup W] [--workload mid|v4share|decode|stress]
                     [--T T] [--no-cpu] [--serial | --persistent] [--no-backward]
@@ -663,11 +663,12 @@ def main():
     roof["kernel"] = ("ffn_waved_kernel" if persistent_path
                       else "gemm1_phase_kernel+gemm2_phase_kernel+combine_kernel")
     # HBM bytes per launch from the committed rocprofv3 counter runs
-    # (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy), reported only
-    # while the kernel sources are the ones that were measured
+    # (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy; on the phase
+    # schedule the sum over its three kernels), reported only while the
+    # kernel sources are the ones that were measured
     from combine_wave_level_amd import profiling
-    trec = None if not persistent_path else profiling.load_traffic(
-        os.path.join(ROOT, "profiles", f"traffic_ffn_waved_kernel_{wl.name}_T{T}.json"), wl.name, T)
+    tname = "ffn_waved_kernel" if persistent_path else "phase_kernels"
+    trec = profiling.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{tname}_{wl.name}_T{T}.json"), wl.name, T)
     roof["traffic"] = trec["traffic_bytes"] if trec else None
     peaks = measure_peaks(stream)
     meas = peaks["mfma_bf16_tflops"] if roof["bound"] == "mfma" else peaks["copy_gbs"]

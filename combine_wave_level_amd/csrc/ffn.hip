@@ -55,6 +55,52 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, size_t n) {
 
 // ---------------------------------------------------------------- phase kernels
 
+// XCD-affine tile order of the phase kernels (the large tile shapes, when
+// the routed-to experts average at least two m-tiles).  The tiles are
+// listed expert by expert, n-tile-major inside an expert (the m-tiles of an
+// expert that read one weight tile are adjacent), and the list is cut into
+// 8 contiguous runs of equal length; workgroup b runs tiles of run b % 8,
+// since the dispatcher deals consecutive workgroups to the 8 XCDs in turn
+// (only locality depends on that, never correctness).  So an m-tile's token
+// rows are fetched by one or two XCDs instead of by every XCD that holds one
+// of its n-tiles, and the m-tiles of an expert that read the same weight
+// tile run side by side under one L2.  Measured on MI355X against the plain
+// order (m-tile-major over the whole grid), FFN on the phase kernels: mid
+// layer T=4096 (4.5 m-tiles per expert) 1.4% faster, stress layer T=4096
+// (2.1) 2.9% and T=16384 (6.4) 3 to 5% faster; the V3/V4-scale share
+// (1.6 m-tiles per expert, most experts one full m-tile and a short tail)
+// 1.6% slower, so there the plain order stays.
+__device__ __forceinline__ bool phase_xcd_order(const int32_t* mt_pre, int E_local) {
+  int routed = 0;
+  for (int e = 0; e < E_local; ++e) routed += mt_pre[e + 1] > mt_pre[e];
+  return mt_pre[E_local] >= 2 * routed;
+}
+struct PhaseTiles {
+  int begin, end, first, stride;  // run [begin, end) of the list; tiles begin + first + j * stride
+};
+__device__ __forceinline__ PhaseTiles phase_tiles(int total, bool xcd_order) {
+  if (!xcd_order || gridDim.x % kXcds != 0) return {0, total, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x)};
+  const int x = blockIdx.x % kXcds;
+  const long long t = total;
+  return {static_cast<int>(t * x / kXcds), static_cast<int>(t * (x + 1) / kXcds), static_cast<int>(blockIdx.x / kXcds),
+          static_cast<int>(gridDim.x / kXcds)};
+}
+// Tile g of the list (NT n-tiles per m-tile): its expert e, m-tile mt and
+// n-tile nt.  The plain order: m-tile g / NT, n-tile g % NT.
+__device__ __forceinline__ void phase_tile(const int32_t* mt_pre, int E_local, int NT, int g, bool xcd_order,
+                                           int& e, int& mt, int& nt) {
+  e = expert_of_mtile(mt_pre, 0, E_local, g / NT);
+  if (!xcd_order) {
+    mt = g / NT;
+    nt = g % NT;
+    return;
+  }
+  const int n = mt_pre[e + 1] - mt_pre[e];
+  const int r = g - NT * mt_pre[e];
+  nt = r / n;
+  mt = mt_pre[e] + r % n;
+}
+
 // GATED: W13 holds W1 and W3 (SwiGLU); else W1 only (squared ReLU).
 template <class F, bool GATED>
 __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
@@ -67,14 +113,20 @@ __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
   __shared__ int32_t seg[kMaxLocalExperts + 1];
+  __shared__ int32_t xcd_order;
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  if (threadIdx.x == 0) xcd_order = F::WHOLE_EXPERTS && phase_xcd_order(mt_pre, E_local);
   if (hsave != nullptr) build_seg_prefix(offsets, E_local, seg);
   __syncthreads();
   const int NT = gr * I / C::BW;
-  const int total = uniform(mt_pre[E_local] * NT);
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / NT, nt = tile % NT;
-    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+  const bool xo = uniform(xcd_order) != 0;
+  const PhaseTiles r = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  for (int g = r.begin + r.first; g < r.end; g += r.stride) {
+    int e, mt, nt;
+    phase_tile(mt_pre, E_local, NT, g, xo, e, mt, nt);
+    e = uniform(e);
+    mt = uniform(mt);
+    nt = uniform(nt);
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
     const int hrow0 = hsave != nullptr ? uniform(seg[e] + (mt - mt_pre[e]) * C::BT) : 0;
@@ -90,13 +142,19 @@ __global__ __launch_bounds__(F::NT) void gemm2_phase_kernel(
   using C = typename F::G2;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t xcd_order;
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  if (threadIdx.x == 0) xcd_order = F::WHOLE_EXPERTS && phase_xcd_order(mt_pre, E_local);
   __syncthreads();
   const int NT = d / C::BW;
-  const int total = uniform(mt_pre[E_local] * NT);
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / NT, nt = tile % NT;
-    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+  const bool xo = uniform(xcd_order) != 0;
+  const PhaseTiles r = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  for (int g = r.begin + r.first; g < r.end; g += r.stride) {
+    int e, mt, nt;
+    phase_tile(mt_pre, E_local, NT, g, xo, e, mt, nt);
+    e = uniform(e);
+    mt = uniform(mt);
+    nt = uniform(nt);
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
     gemm2_tile<C>(act, w2 + static_cast<size_t>(e) * d * I, y, row0, count, nt, d, I, lds);
@@ -544,36 +602,24 @@ hipError_t launch_ffn_cfg(const moe_problem_t& p, const WsLayout& L, const uint1
 
 }  // namespace
 
-// The schedule the library picks when the caller does not force one.  Both
-// give the same bits.  The persistent kernel hides the combine of finished
-// waves under later waves' GEMMs and has no phase boundaries, but it deals
-// the work to the XCDs in whole m-tiles (whole experts for the large tile
-// shapes) and keeps an m-tile's GEMM1 -> GEMM2 hand-off inside one XCD;
-// the phase kernels spread every phase's tiles over all 256 CUs.  Measured
-// on MI355X, FFN with the fused combine, persistent against phases:
-//   mid layer, T=4096, 16 experts, top-4 (1024 rows per expert):
-//     0.514 against 0.533 ms;
-//   stress layer, T=4096, 64 experts, top-6, one hot expert (384 rows per
-//     expert on average): 1.31 against 1.36 ms;
-//   V3/V4-scale share, T=8192, 32 of 256 experts, top-8 (256 rows per
-//     expert: about one m-tile each, so the XCDs' loads differ by whole
-//     m-tiles): 1.21 against 1.20 ms;
-//   stress layer, T=16384 (98304 local rows): 4.24 to 4.32 against 4.02 to
-//     4.07 ms;
-//   decode, T = 1, 32, 128 (small tile shapes, weight streaming): 7 to 12%
-//     slower (2.6% faster at T = 8).
-// Hence: the persistent kernel for the large tile shapes when the experts
-// average at least one and a half m-tiles and the share holds at most
-// 32768 expected local rows (uniform routing assumed, as for the tile
-// shape); the phases otherwise.
-bool ffn_prefers_persistent(const moe_problem_t& p) {
-  const FfnShape shape = pick_ffn_shape(p);
-  if (shape != FfnShape::Large && shape != FfnShape::Mid) return false;
-  const double rows_per_expert = static_cast<double>(p.T) * p.k / p.E_global;
-  const double local_rows = rows_per_expert * p.E_local;
-  return rows_per_expert >= 1.5 * ffn_mtile_rows(p) && local_rows <= 32768.0;
-}
-
+// The schedule the library picks when the caller does not force one: the
+// phase kernels.  Both give the same bits.  The persistent kernel hides the
+// combine of finished waves under later waves' GEMMs and has no phase
+// boundaries, but it deals the work to the XCDs in whole m-tiles (whole
+// experts for the large tile shapes) from per-XCD ticket streams and keeps
+// an m-tile's GEMM1 -> GEMM2 hand-off inside one XCD; the phase kernels
+// spread every phase's tiles over all 256 CUs, in the XCD-affine order
+// where experts average two m-tiles or more.  Measured on MI355X (one box,
+// FFN with the fused combine), phases against the persistent kernel:
+//   mid layer, T=4096, 16 experts, top-4: 0.471 to 0.478 against 0.498 ms;
+//   stress layer, T=4096, 64 experts, top-6, one hot expert: 1.198 to
+//     1.202 against 1.215 to 1.231 ms;
+//   V3/V4-scale share, T=8192, 32 of 256 experts, top-8: 1.078 against
+//     1.156 to 1.163 ms;
+//   stress layer, T=16384: 3.42 against 3.95 to 3.97 ms;
+//   decode, T = 1, 32, 128 (small tile shapes): the persistent kernel 7 to
+//     12% slower.
+// So the persistent kernel runs only when MOE_FLAG_PERSISTENT asks for it.
 bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags) {
   if (flags & MOE_FLAG_SERIAL) return false;
   // every per-XCD ticket stream needs workgroups: the whole device
@@ -584,7 +630,7 @@ bool ffn_uses_persistent(const moe_problem_t& p, int cus, uint32_t flags) {
   const long long P_max = static_cast<long long>(p.T) * (p.k < p.E_local ? p.k : p.E_local);
   const long long mt_bound = P_max / ffn_mtile_rows(p) + p.E_local + 1;
   if (mt_bound / kXcds + W + 1 > kSchedMaxLocal) return false;
-  return (flags & MOE_FLAG_PERSISTENT) || ffn_prefers_persistent(p);
+  return (flags & MOE_FLAG_PERSISTENT) != 0;
 }
 
 hipError_t fill_zero(void* p, size_t n, hipStream_t s) {

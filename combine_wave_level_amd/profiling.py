@@ -11,9 +11,11 @@
 
     python -m combine_wave_level_amd.profiling steptraffic --fetch F.csv --write W.csv
         --copy-fetch CF.csv --copy-write CW.csv --kernels K1 K2 ... --title T
-        --command "..." --out-md X.md
+        --command "..." --out-md X.md [--out-json X.json --workload W --T T]
         Writes the calibrated HBM bytes of one pass over kernels that each
-        run once per pass (the phase schedule's GEMM1, GEMM2 and combine).
+        run once per pass (the phase schedule's GEMM1, GEMM2 and combine),
+        and optionally the JSON record bench.py reports as roofline.traffic
+        for that schedule.
 
     python -m combine_wave_level_amd.profiling summarize --stats S.csv
         --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
@@ -46,6 +48,7 @@ CSRC = os.path.join(HERE, "csrc")
 # Sources each measured kernel is compiled from (device code and its launch).
 KERNEL_SOURCES = {
     "ffn_waved_kernel": ["ffn.hip", "ffn_parts.h", "gemm_tile.h", "moe_common.h", "wave_sched.h"],
+    "phase_kernels": ["ffn.hip", "ffn_parts.h", "gemm_tile.h", "moe_common.h", "wave_sched.h"],
 }
 
 
@@ -183,9 +186,21 @@ def _step_traffic(a) -> None:
         lines.append(f"| {k} | {nf} / {nw} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
     lines += ["", f"One pass: {tot_r / 1e6:.1f} MB read + {tot_w / 1e6:.1f} MB written = "
               f"{(tot_r + tot_w) / 1e6:.1f} MB.", ""]
+    rec = {"read_bytes": round(tot_r), "write_bytes": round(tot_w)}
+    if a.out_json:
+        if a.workload is None or a.T is None:
+            raise SystemExit("--out-json needs --workload and --T")
+        rec = {"kernel": "phase_kernels", "kernels": a.kernels, "workload": a.workload, "T": a.T,
+               "source_digest": source_digest("phase_kernels"),
+               "sources": [os.path.basename(p) for p in _sources("phase_kernels")],
+               "fetch_bytes": round(tot_r), "write_bytes": round(tot_w), "traffic_bytes": round(tot_r + tot_w),
+               "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}
+        lines += [f"Source digest of the measured kernels: `{rec['source_digest'][:16]}`", ""]
+        with open(a.out_json, "w") as f:
+            json.dump(rec, f, indent=1)
     with open(a.out_md, "w") as f:
         f.write("\n".join(lines))
-    print(json.dumps({"read_bytes": round(tot_r), "write_bytes": round(tot_w)}))
+    print(json.dumps(rec))
 
 
 def _stats(a) -> None:
@@ -310,6 +325,9 @@ def main(argv=None) -> None:
     st.add_argument("--title", required=True)
     st.add_argument("--command", action="append", default=[])
     st.add_argument("--out-md", required=True)
+    st.add_argument("--out-json", default=None)
+    st.add_argument("--workload", default=None)
+    st.add_argument("--T", type=int, default=None)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         _copy(a)

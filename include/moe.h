@@ -11,8 +11,8 @@
  * token order weighted by the router.  Experts are processed in waves of a
  * few experts (digest section 1.2); inside one persistent kernel the current
  * wave's GEMMs overlap the dispatch pulls of the next wave and the combine of
- * finished tokens (or, for the shapes where they measured faster on one
- * GPU, the same tiles run as grid-wide phases; see moe_ffn_path).  Results
+ * finished tokens, or the same tiles run as grid-wide phases, which measured
+ * faster on one GPU and are the default (see moe_ffn_path).  Results
  * are batch invariant and deterministic (digest
  * section 3; 10100.com section on batch-invariant and deterministic
  * operators): a token's output bits do not depend on the batch it sits in,
@@ -94,11 +94,10 @@ typedef struct {
 /* Flags for moe_expert_ffn_waved (at most one of the two).  With neither,
  * the library picks the schedule (moe_ffn_path). */
 #define MOE_FLAG_SERIAL 0x1u /* run gather+GEMM1, GEMM2, combine as separate
-                                grid-wide phases instead of the persistent
-                                expert-wave kernel (same bits, no overlap)   */
+                                grid-wide phases (the library's default;
+                                same bits, no overlap)                       */
 #define MOE_FLAG_PERSISTENT 0x2u /* run the persistent expert-wave kernel
-                                whenever it fits, also where the library
-                                would pick the phases (same bits)            */
+                                whenever it fits (same bits)                 */
 
 /* ------------------------------------------------------------ sizing */
 
@@ -126,14 +125,11 @@ size_t moe_workspace_size(const moe_problem_t* p, uint32_t flags);
  *     without workgroups) and at most 512 m-tiles per XCD;
  *   MOE_PATH_PHASES: gather + GEMM1, GEMM2 and combine as grid-wide phases
  *     (MOE_FLAG_SERIAL, or when the persistent kernel does not fit).
- * With neither flag the library picks: the persistent kernel for batches
- * that run the large tile shapes (at least 96 routed rows per expert) when
- * the experts average at least one and a half m-tiles and the share holds
- * at most 32768 expected local rows (T k E_local / E_global), the phases
- * otherwise (small-batch weight streaming, about one m-tile per expert, or
- * very long batches), where they measured faster.  MOE_FLAG_PERSISTENT
- * takes the persistent kernel whenever it fits.  Both schedules give the
- * same bits.  The library calls this with the current device's CU count.
+ * With neither flag the library runs the phases: on MI355X they measured
+ * 1 to 14% faster than the persistent kernel on every benchmark shape (mid
+ * and stress layers, V3/V4-scale share, decode).  MOE_FLAG_PERSISTENT takes
+ * the persistent kernel whenever it fits.  Both schedules give the same
+ * bits.  The library calls this with the current device's CU count.
  * Returns a moe_status_t (< 0) on a bad argument. */
 #define MOE_PATH_PERSISTENT 0
 #define MOE_PATH_PHASES 1
@@ -238,12 +234,12 @@ moe_status_t moe_route_dispatch(const moe_problem_t* p, const void* x, const voi
  *   packed: from moe_pack_weights.  expert_offsets, sorted_token, pair_pos,
  *   token_ready_wave: from moe_dispatch (same workspace).  topk_w [T, k].
  *   Out: y [P_max, d] bf16 expert outputs in sorted-row order; out [T, d] in
- *   out_dtype when non-NULL: the combine, fused into the persistent kernel
- *   (on the phase schedule: its own grid-wide pass, the same bits; tokens
+ *   out_dtype when non-NULL: the combine (on the phase schedule its own
+ *   grid-wide pass, fused into the persistent kernel; the same bits; tokens
  *   with no local pick get zeros).
  * Each GEMM accumulates in fp32 over K in one fixed ascending order with one
  * MFMA shape, never split; a is rounded to bf16 before the second GEMM and y
- * is rounded to bf16.  flags: 0 (the library picks the schedule, see
+ * is rounded to bf16.  flags: 0 (the library's schedule, see
  * moe_ffn_path), MOE_FLAG_SERIAL or MOE_FLAG_PERSISTENT; any other value is
  * MOE_ERR_INVALID_ARG.
  * After one moe_dispatch the call may be repeated on the same workspace any

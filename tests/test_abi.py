@@ -107,35 +107,23 @@ def test_forward_workspace_and_pack_exclude_the_backward(L):
 
 
 def test_ffn_path_decision(L):
-    """The persistent kernel runs only on the whole 8-XCD device; any other
-    CU count (partition modes, harvested parts) and MOE_FLAG_SERIAL take the
-    phase kernels.  With no flag the library takes the persistent kernel for
-    large-tile batches whose experts average at least 1.5 m-tiles, with at
-    most 32768 expected local rows; MOE_FLAG_PERSISTENT forces it wherever
-    it fits; the two flags together are rejected."""
+    """The persistent kernel runs only on the whole 8-XCD device and only
+    when MOE_FLAG_PERSISTENT asks for it; with no flag, with MOE_FLAG_SERIAL
+    and on any other CU count (partition modes, harvested parts) the phase
+    kernels run; the two flags together are rejected."""
     p = _p(T=4096, d=4096, I=1024, E_global=16, E_local=16, k=4)
-    assert moe.ffn_path(p, 256) == moe.MOE_PATH_PERSISTENT
+    assert moe.ffn_path(p, 256) == moe.MOE_PATH_PHASES
     assert moe.ffn_path(p, 256, serial=True) == moe.MOE_PATH_PHASES
     assert moe.ffn_path(p, 256, persistent=True) == moe.MOE_PATH_PERSISTENT
     for cus in (32, 64, 128, 224, 240, 304):
         assert moe.ffn_path(p, cus) == moe.MOE_PATH_PHASES, cus
         assert moe.ffn_path(p, cus, persistent=True) == moe.MOE_PATH_PHASES, cus
-    # stress layer, T = 4096 (384 rows per expert: 1.5 m-tiles of 256)
-    stress = dict(d=4096, I=1536, E_global=64, E_local=64, k=6)
-    assert moe.ffn_path(_p(T=4096, **stress), 256) == moe.MOE_PATH_PERSISTENT
-    assert moe.ffn_path(_p(T=4095, **stress), 256) == moe.MOE_PATH_PHASES
-    # more than 32768 expected local rows
-    assert moe.ffn_path(_p(T=16384, **stress), 256) == moe.MOE_PATH_PHASES
-    assert moe.ffn_path(_p(T=16384, **stress), 256, persistent=True) == moe.MOE_PATH_PERSISTENT
-    # V3/V4-scale share: 256 rows per expert, about one m-tile each
-    share = dict(d=7168, I=2048, E_global=256, E_local=32, k=8)
-    assert moe.ffn_path(_p(T=8192, **share), 256) == moe.MOE_PATH_PHASES
-    assert moe.ffn_path(_p(T=8192, **share), 256, persistent=True) == moe.MOE_PATH_PERSISTENT
-    # small batches (weight streaming)
-    for T in (1, 8, 32, 128):
-        dec = _p(T=T, d=7168, I=2048, E_global=32, E_local=32, k=8)
-        assert moe.ffn_path(dec, 256) == moe.MOE_PATH_PHASES, T
-        assert moe.ffn_path(dec, 256, persistent=True) == moe.MOE_PATH_PERSISTENT, T
+    shapes = [_p(T=T, d=4096, I=1536, E_global=64, E_local=64, k=6) for T in (4096, 16384)]   # stress
+    shapes.append(_p(T=8192, d=7168, I=2048, E_global=256, E_local=32, k=8))                 # V3/V4 share
+    shapes += [_p(T=T, d=7168, I=2048, E_global=32, E_local=32, k=8) for T in (1, 8, 32, 128)]  # decode
+    for q in shapes:
+        assert moe.ffn_path(q, 256) == moe.MOE_PATH_PHASES, q.T
+        assert moe.ffn_path(q, 256, persistent=True) == moe.MOE_PATH_PERSISTENT, q.T
     # more m-tiles per XCD than the schedule holds
     big = _p(T=1 << 20, d=4096, I=1024, E_global=16, E_local=16, k=4)
     assert moe.ffn_path(big, 256) == moe.MOE_PATH_PHASES

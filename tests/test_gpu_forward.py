@@ -301,12 +301,13 @@ def test_edge_k_equals_E_and_single_expert():
     assert rel_err_rows(host_f64(out), ref) <= OUT_TOL
 
 
-@pytest.mark.parametrize("name,T,want", [("mid", 4096, "persistent"), ("stress", 4096, "persistent"),
+@pytest.mark.parametrize("name,T,want", [("mid", 4096, "phases"), ("stress", 4096, "phases"),
                                          ("stress", 16384, "phases"), ("decode", 1, "phases"),
                                          ("v4share", 2048, "phases")])
 def test_default_schedule_choice_gives_the_same_bits(name, T, want):
-    """With no flag the library picks the schedule (moe_ffn_path on the
-    device's CU count); the call gives the bits of both forced schedules."""
+    """With no flag the library runs its default schedule (moe_ffn_path on
+    the device's CU count: the phase kernels); the call gives the bits of
+    both forced schedules."""
     L = Layer(inputs(name, T=T))
     print(f"[case] default schedule {name} T={T}", flush=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
