@@ -97,15 +97,21 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
   __shared__ int32_t seg[kMaxLocalExperts + 1];
+  __shared__ int32_t xcd_order;
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   build_seg_prefix(offsets, E_local, seg);
+  if (threadIdx.x == 0) xcd_order = phase_xcd_order(mt_pre, E_local);
   __syncthreads();
   const int NT = I / C::BW;
-  const int total = uniform(mt_pre[E_local] * NT);
+  const bool xo = uniform(xcd_order) != 0;
+  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
   const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / NT, nt = tile % NT;
-    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+  for (int tile = pt.begin + pt.first; tile < pt.end; tile += pt.stride) {
+    int e, mt, nt;
+    phase_tile(mt_pre, E_local, NT, tile, xo, e, mt, nt);
+    e = uniform(e);
+    mt = uniform(mt);
+    nt = uniform(nt);
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
     TokRows<C> trow;
@@ -158,8 +164,10 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
   __shared__ int32_t seg[kMaxLocalExperts + 1];
   __shared__ float wrow[C::BT];
+  __shared__ int32_t xcd_order;
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
   build_seg_prefix(offsets, E_local, seg);
+  if (threadIdx.x == 0) xcd_order = phase_xcd_order(mt_pre, E_local);
   __syncthreads();
   constexpr int NI = D::NI;
   uint16_t* sdh = lds;  // [NH][kStageRow]: (dH1 | dH3)^T (or dH1^T) of the tile
@@ -167,11 +175,15 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
   uint16_t* saw = D::ONE_PASS ? lds + D::NH * kStageRow : lds;
   const bool trans = dht != nullptr;
   const int NT = GR * I / C::BW, NQ = I / 16;
-  const int total = uniform(mt_pre[E_local] * NT);
+  const bool xo = uniform(xcd_order) != 0;
+  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
   const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / NT, nt = tile % NT;
-    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+  for (int tile = pt.begin + pt.first; tile < pt.end; tile += pt.stride) {
+    int e, mt, nt;
+    phase_tile(mt_pre, E_local, NT, tile, xo, e, mt, nt);
+    e = uniform(e);
+    mt = uniform(mt);
+    nt = uniform(nt);
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
     // router weight of each row of the tile (0 past the valid rows)
@@ -493,13 +505,19 @@ __global__ __launch_bounds__(F::NT) void bwd_dx_gemm_kernel(
   using C = typename F::G2;
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int32_t mt_pre[kMaxLocalExperts + 1];
+  __shared__ int32_t xcd_order;
   build_mtile_prefix(offsets, E_local, C::BT, mt_pre);
+  if (threadIdx.x == 0) xcd_order = phase_xcd_order(mt_pre, E_local);
   __syncthreads();
   const int NT = d / C::BW;
-  const int total = uniform(mt_pre[E_local] * NT);
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / NT, nt = tile % NT;
-    const int e = uniform(expert_of_mtile(mt_pre, 0, E_local, mt));
+  const bool xo = uniform(xcd_order) != 0;
+  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  for (int tile = pt.begin + pt.first; tile < pt.end; tile += pt.stride) {
+    int e, mt, nt;
+    phase_tile(mt_pre, E_local, NT, tile, xo, e, mt, nt);
+    e = uniform(e);
+    mt = uniform(mt);
+    nt = uniform(nt);
     const int row0 = uniform(offsets[e] + (mt - mt_pre[e]) * C::BT);
     const int count = uniform(min(C::BT, offsets[e + 1] - row0));
     gemm2_tile<C>(dh, w13t + static_cast<size_t>(e) * d * K2, dxr, row0, count, nt, d, K2, lds);
