@@ -104,7 +104,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_g_kernel(
   __syncthreads();
   const int NT = I / C::BW;
   const bool xo = uniform(xcd_order) != 0;
-  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo, static_cast<int>(blockIdx.x),
+                                    static_cast<int>(gridDim.x));
   const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
   for (int tile = pt.begin + pt.first; tile < pt.end; tile += pt.stride) {
     int e, mt, nt;
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(C::NTHREADS) void bwd_dh_kernel(
   const bool trans = dht != nullptr;
   const int NT = GR * I / C::BW, NQ = I / 16;
   const bool xo = uniform(xcd_order) != 0;
-  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo, static_cast<int>(blockIdx.x),
+                                    static_cast<int>(gridDim.x));
   const int lane = lane_id(), wr = tile_wr<C>(), wt = tile_wt<C>();
   for (int tile = pt.begin + pt.first; tile < pt.end; tile += pt.stride) {
     int e, mt, nt;
@@ -511,7 +513,8 @@ __global__ __launch_bounds__(F::NT) void bwd_dx_gemm_kernel(
   __syncthreads();
   const int NT = d / C::BW;
   const bool xo = uniform(xcd_order) != 0;
-  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  const PhaseTiles pt = phase_tiles(uniform(mt_pre[E_local] * NT), xo, static_cast<int>(blockIdx.x),
+                                    static_cast<int>(gridDim.x));
   for (int tile = pt.begin + pt.first; tile < pt.end; tile += pt.stride) {
     int e, mt, nt;
     phase_tile(mt_pre, E_local, NT, tile, xo, e, mt, nt);

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(F::NT) void gemm1_phase_kernel(
   __syncthreads();
   const int NT = gr * I / C::BW;
   const bool xo = uniform(xcd_order) != 0;
-  const PhaseTiles r = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  const PhaseTiles r = phase_tiles(uniform(mt_pre[E_local] * NT), xo, static_cast<int>(blockIdx.x),
+                                   static_cast<int>(gridDim.x));
   for (int g = r.begin + r.first; g < r.end; g += r.stride) {
     int e, mt, nt;
     phase_tile(mt_pre, E_local, NT, g, xo, e, mt, nt);
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(F::NT) void gemm2_phase_kernel(
   __syncthreads();
   const int NT = d / C::BW;
   const bool xo = uniform(xcd_order) != 0;
-  const PhaseTiles r = phase_tiles(uniform(mt_pre[E_local] * NT), xo);
+  const PhaseTiles r = phase_tiles(uniform(mt_pre[E_local] * NT), xo, static_cast<int>(blockIdx.x),
+                                   static_cast<int>(gridDim.x));
   for (int g = r.begin + r.first; g < r.end; g += r.stride) {
     int e, mt, nt;
     phase_tile(mt_pre, E_local, NT, g, xo, e, mt, nt);
