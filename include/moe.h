@@ -126,8 +126,9 @@ size_t moe_workspace_size(const moe_problem_t* p, uint32_t flags);
  *   MOE_PATH_PHASES: gather + GEMM1, GEMM2 and combine as grid-wide phases
  *     (MOE_FLAG_SERIAL, or when the persistent kernel does not fit).
  * With neither flag the library runs the phases: on MI355X they measured
- * 1 to 16% faster than the persistent kernel on every benchmark shape (mid
- * and stress layers, V3/V4-scale share, decode).  MOE_FLAG_PERSISTENT takes
+ * 1 to 16% faster than the persistent kernel on the mid and stress layers,
+ * the V3/V4-scale share and decode at T = 1, 32 and 128 (at T = 8 the
+ * persistent kernel measured up to 2% faster).  MOE_FLAG_PERSISTENT takes
  * the persistent kernel whenever it fits.  Both schedules give the same
  * bits.  The library calls this with the current device's CU count.
  * Returns a moe_status_t (< 0) on a bad argument. */
